@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Decode throughput of one DSA layer step at 128K context on one MI355X.
+
+Workload (the headline): batch 16, context 131072 per sequence, RoPE layer, fp8 E4M3FN index keys
+(one fp32 scale per token) and fp8 latent cache (one fp32 scale per 64 elements), bf16 queries.
+One step = lightning-indexer scores over every cached key -> exact top-2048 -> sparse MLA decode
+(64 heads, 512 + 64 dims).  The NoPE-layer and shared-indexer variants are timed the same way and
+reported beside it.  All inputs are seeded synthetic tensors generated on the GPU and resident in
+HBM before timing starts.
+
+Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s at 128K ctx (indexer+top-2048+sparse MLA); % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+INDEX_BYTES_PER_KEY = 128 + 4 + 4      # fp8 key row + fp32 scale read, fp32 score written
+LATENT_BYTES_PER_KEY = 576 + 9 * 4     # fp8 latent row + 9 fp32 scales
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_slice(wl, t):
+    """CPU copy of query t and its sequence only (B = 1), for timing the oracle."""
+    import torch
+    from workloads import Workload
+    b = int(wl.q_seq[t])
+    sl = lambda x: None if x is None else x[b:b + 1].cpu()
+    return Workload(name=wl.name + f"[q{t}]", num_heads=wl.num_heads, rope_dim=wl.rope_dim,
+                    softmax_scale=wl.softmax_scale, topk=wl.topk, q_seq=torch.zeros(1, dtype=torch.int32),
+                    q_pos=wl.q_pos[t:t + 1].cpu(), seq_len=wl.seq_len[b:b + 1].cpu(), max_ctx=wl.max_ctx,
+                    index_q=wl.index_q[t:t + 1].cpu(), index_w=wl.index_w[t:t + 1].cpu(),
+                    ssmax_s=None if wl.ssmax_s is None else wl.ssmax_s.cpu(),
+                    ssmax_b=None if wl.ssmax_b is None else wl.ssmax_b.cpu(),
+                    inv_freq=None if wl.inv_freq is None else wl.inv_freq.cpu(),
+                    index_k=sl(wl.index_k), index_k_scale=sl(wl.index_k_scale), mla_q=wl.mla_q[t:t + 1].cpu(),
+                    kv=sl(wl.kv), kv_scale=sl(wl.kv_scale), mla_heads=wl.mla_heads)
+
+
+def cpu_baseline(wl, seconds):
+    """The float64 oracle on whole queries of the same workload, on this host's cores."""
+    from oracle import dsa_oracle as O
+    threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads") or 1) for i in info) if info else None
+    except Exception:
+        pass
+    done, elapsed, t = 0, 0.0, 0
+    while done == 0 or (elapsed < seconds and done < wl.num_q):
+        sub = cpu_slice(wl, t)
+        t0 = time.perf_counter()
+        O.decode_layer(sub, [0])
+        elapsed += time.perf_counter() - t0
+        done += 1
+        t += 1
+    return {"value": done / elapsed, "unit": "tok/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"{done} of {wl.num_q} decode queries at context {wl.max_ctx} (full indexer scan, "
+                      f"top-{wl.topk}, sparse MLA), float64 numpy, {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the DSA path here is built and measured on one MI355X; "
+              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from dsa_sparse_attention_indexer_amd import pipeline
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calib_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "dispatches": 5}))
+        return
+
+    log("generating config 2 (a: RoPE layer) on the GPU ...")
+    wa = workloads.config2("a", device=dev)
+    T = wa.num_q
+    buf_a = pipeline.alloc_buffers(wa)
+    wb = bb = None
+    if not args.no_variants:
+        log("generating config 2 (b: NoPE layer) ...")
+        wb = workloads.config2("b", device=dev)
+        bb = pipeline.alloc_buffers(wb)
+        buf_c = pipeline.alloc_buffers(wa)   # shared-indexer layer: its own outputs, a's selection
+    torch.cuda.synchronize()
+
+    def step_a():
+        pipeline.layer_step(wa, buf_a)
+
+    # ---- headline: K timed layer steps (variant a) -------------------------------------------
+    for _ in range(args.warmup):
+        step_a()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_a()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    log(f"layer step (a): {ms_per_step * 1e3:.1f} us")
+
+    # ---- per-stage durations with events on the launch stream --------------------------------
+    stream = torch.cuda.current_stream()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[E() for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        pipeline.index_scores(wa, buf_a)
+        ev[i][1].record(stream)
+        pipeline.select(wa, buf_a)
+        ev[i][2].record(stream)
+        pipeline.attend(wa, buf_a)
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    st = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps * 1e3 for j in range(3)]
+    t_idx, t_topk, t_mla = st
+    keys = int((wa.q_pos.long() + 1).sum())
+    idx_bytes = keys * INDEX_BYTES_PER_KEY
+    achieved = idx_bytes / (t_idx * 1e-6) / 1e9
+    sel = int(buf_a.length.long().sum())
+    mla_flops = sel * wa.mla_heads * (576 + 512) * 2
+    mla_tflops = mla_flops / (t_mla * 1e-6) / 1e12
+    mla_gbs = sel * LATENT_BYTES_PER_KEY / (t_mla * 1e-6) / 1e9
+
+    variants = {}
+    if not args.no_variants:
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            s0 = time.perf_counter()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - s0) / args.steps
+        tb = timed(lambda: pipeline.layer_step(wb, bb))
+        tc = timed(lambda: pipeline.layer_step(wa, buf_c, shared_from=buf_a))
+        variants = {"nope_layer": {"us_per_step": tb * 1e6, "tok_per_s": T / tb},
+                    "shared_indexer_layer": {"us_per_step": tc * 1e6, "tok_per_s": T / tc}}
+        log(f"NoPE layer {tb * 1e6:.1f} us, shared-indexer layer {tc * 1e6:.1f} us")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on host cores ...")
+        cpu = cpu_baseline(wa, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": T / (elapsed / args.steps),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 caches; f16 (indexer) / bf16 (MLA) MFMA; fp32 accumulate",
+        "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "decode layer step (RoPE layer): indexer + top-2048 + sparse MLA",
+                   "batch": T, "context": wa.max_ctx, "index_heads": wa.num_heads, "mla_heads": wa.mla_heads,
+                   "topk": wa.topk, "kv_cache": "fp8 e4m3fn + fp32 scales"},
+        "roofline": {"bound": "hbm", "kernel": "index scores (fp8 keys)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": idx_bytes},
+        "stages_us": {"index_scores": t_idx, "topk": t_topk, "sparse_mla": t_mla},
+        "keys_scored_per_s": keys / (t_idx * 1e-6),
+        "sparse_mla": {"tflops": mla_tflops, "frac_bf16_peak": mla_tflops / BF16_PEAK_TFLOPS,
+                       "gather_gbs": mla_gbs, "frac_hbm_peak": mla_gbs / HBM_PEAK_GBS},
+        "variants": variants,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,248 @@
+"""Python binding of libdsa, the MI355X (gfx950) DSA hot path: lightning-indexer scores, top-k /
+block selection and sparse absorbed-MLA attention.
+
+Every function here only marshals arguments: it checks tensor dtypes, shapes, devices and
+contiguity, passes raw device pointers and the current HIP stream to the C ABI in
+``include/dsa.h`` and raises on a non-OK status with the library's error text.  All arithmetic
+runs in the library's HIP kernels.  There is no CPU or PyTorch fallback: if ``libdsa.so`` is
+missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_HIP = 0, 1, 2, 3
+DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = 0, 1, 2
+ABI_VERSION = 1
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+class IndexerDesc(ctypes.Structure):
+    _fields_ = [("num_q", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("k_dtype", ctypes.c_int32)]
+
+
+class MlaDesc(ctypes.Structure):
+    _fields_ = [("num_q", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("kv_lora", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("kv_scale_block", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("num_splits", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m dsa_sparse_attention_indexer_amd.build` "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "dsa_last_error": (ctypes.c_char_p, []),
+        "dsa_abi_version": (I32, []),
+        "dsa_indexer_scores": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, P]),
+        "dsa_topk_workspace_size": (SZ, [I32, I64, I32]),
+        "dsa_topk": (I32, [P, I64, P, I32, I32, P, P, P, SZ, P]),
+        "dsa_block_select_workspace_size": (SZ, [I32, I64, I32]),
+        "dsa_block_select": (I32, [P, I64, P, I32, I32, I32, I32, P, P, P, SZ, P]),
+        "dsa_sparse_mla_workspace_size": (SZ, [ctypes.POINTER(MlaDesc)]),
+        "dsa_sparse_mla_decode": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dsa_sparse_mla_prefill": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if lib.dsa_abi_version() != ABI_VERSION:
+        raise ImportError(f"libdsa ABI version {lib.dsa_abi_version()} != {ABI_VERSION}")
+    return lib
+
+
+_lib = _load()
+EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
+            "dsa_block_select_workspace_size", "dsa_block_select", "dsa_sparse_mla_workspace_size",
+            "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill"]
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int):
+    if status != DSA_OK:
+        raise DsaError(status, _lib.dsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(name, t, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _qdtype(t):
+    return {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}[t.dtype]
+
+
+def _kdtype(t):
+    return {torch.float32: DSA_F32, torch.uint8: DSA_FP8_E4M3FN, torch.float8_e4m3fn: DSA_FP8_E4M3FN}[t.dtype]
+
+
+# ------------------------------------------------------------------------------------------------
+# 1. indexer scores
+# ------------------------------------------------------------------------------------------------
+
+def dsa_indexer_scores(q, w, q_seq, q_pos, k_cache, scores, k_scale=None, ssmax_s=None, ssmax_b=None,
+                       inv_freq=None, stream=None):
+    """Fills scores[t, 0..q_pos[t]] with the lightning-indexer score of every visible key.
+
+    q [T][H][128] f32|bf16, w [T][H] f32, q_seq/q_pos [T] i32, k_cache [B][max_ctx][128] f32 or
+    fp8 bytes (uint8 / float8_e4m3fn), k_scale [B][max_ctx] f32 (fp8 only), ssmax_s/b [H] f32,
+    inv_freq [32] f32 on RoPE layers (None on NoPE layers), scores [T][ld] f32 with ld >= max_ctx.
+    """
+    T, H, D = q.shape
+    B, max_ctx, _ = k_cache.shape
+    _dev("q", q, (torch.float32, torch.bfloat16))
+    _dev("w", w, torch.float32, (T, H))
+    _dev("q_seq", q_seq, torch.int32, (T,))
+    _dev("q_pos", q_pos, torch.int32, (T,))
+    _dev("k_cache", k_cache, (torch.float32, torch.uint8, torch.float8_e4m3fn))
+    _dev("k_scale", k_scale, torch.float32, (B, max_ctx))
+    _dev("ssmax_s", ssmax_s, torch.float32, (H,))
+    _dev("ssmax_b", ssmax_b, torch.float32, (H,))
+    _dev("inv_freq", inv_freq, torch.float32)
+    _dev("scores", scores, torch.float32)
+    if scores.dim() != 2 or scores.shape[0] != T:
+        raise ValueError("scores must be [T][ld]")
+    rope = 0 if inv_freq is None else 2 * int(inv_freq.numel())
+    d = IndexerDesc(T, H, D, rope, B, max_ctx, _qdtype(q), _kdtype(k_cache))
+    _check(_lib.dsa_indexer_scores(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
+                                   _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores),
+                                   scores.shape[1], _stream(stream)))
+    return scores
+
+
+# ------------------------------------------------------------------------------------------------
+# 2. selection
+# ------------------------------------------------------------------------------------------------
+
+def dsa_topk_workspace_size(num_q: int, ld: int, k: int) -> int:
+    return int(_lib.dsa_topk_workspace_size(num_q, ld, k))
+
+
+def dsa_topk(scores, q_pos, k, idx, length=None, ws=None, stream=None):
+    """Top-k of each score row (n = q_pos + 1 columns): idx [T][k] ascending, -1 padded; length [T]."""
+    T, ld = scores.shape
+    _dev("scores", scores, torch.float32)
+    _dev("q_pos", q_pos, torch.int32, (T,))
+    _dev("idx", idx, torch.int32, (T, k))
+    _dev("length", length, torch.int32, (T,))
+    need = dsa_topk_workspace_size(T, ld, k)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=scores.device)
+    _dev("ws", ws, torch.uint8)
+    _check(_lib.dsa_topk(_ptr(scores), ld, _ptr(q_pos), T, k, _ptr(idx), _ptr(length), _ptr(ws), ws.numel(),
+                         _stream(stream)))
+    return idx, length
+
+
+def dsa_block_select_workspace_size(num_q: int, ld: int, block: int) -> int:
+    return int(_lib.dsa_block_select_workspace_size(num_q, ld, block))
+
+
+def dsa_block_select(scores, q_pos, idx, length=None, block=128, nblocks=16, ws=None, stream=None):
+    """Block-sparse selection: best `nblocks` blocks of `block` keys, the query's own block forced."""
+    T, ld = scores.shape
+    topk = idx.shape[1]
+    _dev("scores", scores, torch.float32)
+    _dev("q_pos", q_pos, torch.int32, (T,))
+    _dev("idx", idx, torch.int32, (T, topk))
+    _dev("length", length, torch.int32, (T,))
+    need = dsa_block_select_workspace_size(T, ld, block)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=scores.device)
+    _dev("ws", ws, torch.uint8)
+    _check(_lib.dsa_block_select(_ptr(scores), ld, _ptr(q_pos), T, block, nblocks, topk, _ptr(idx),
+                                 _ptr(length), _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, length
+
+
+# ------------------------------------------------------------------------------------------------
+# 3. sparse MLA
+# ------------------------------------------------------------------------------------------------
+
+def mla_desc(q, kv, idx, softmax_scale, num_splits=0) -> MlaDesc:
+    T, H, DQ = q.shape
+    B, max_ctx, row = kv.shape
+    rope = DQ - 512
+    return MlaDesc(T, H, 512, rope, B, max_ctx, idx.shape[1], _qdtype(q), _kdtype(kv), 64, float(softmax_scale),
+                   int(num_splits))
+
+
+def dsa_sparse_mla_workspace_size(desc: MlaDesc) -> int:
+    return int(_lib.dsa_sparse_mla_workspace_size(ctypes.byref(desc)))
+
+
+def _mla(fn, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale, num_splits, ws, stream):
+    T, H, DQ = q.shape
+    B, max_ctx, row = kv.shape
+    _dev("q", q, (torch.float32, torch.bfloat16))
+    _dev("kv", kv, (torch.float32, torch.uint8, torch.float8_e4m3fn))
+    _dev("kv_scale", kv_scale, torch.float32, (B, max_ctx, row // 64))
+    _dev("q_seq", q_seq, torch.int32, (T,))
+    _dev("idx", idx, torch.int32)
+    _dev("length", length, torch.int32, (T,))
+    _dev("out", out, torch.float32, (T, H, 512))
+    _dev("lse", lse, torch.float32, (T, H))
+    if row != 576 or DQ not in (512, 576):
+        raise ValueError("kv rows must be 576 wide and q 512 (NoPE) or 576 (RoPE) wide")
+    d = mla_desc(q, kv, idx, softmax_scale, num_splits)
+    need = dsa_sparse_mla_workspace_size(d)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev("ws", ws, torch.uint8)
+    _check(fn(ctypes.byref(d), _ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(q_seq), _ptr(idx), _ptr(length), _ptr(out),
+              _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def dsa_sparse_mla_decode(q, kv, kv_scale, q_seq, idx, length, out, lse=None, softmax_scale=None, num_splits=0,
+                          ws=None, stream=None):
+    """Sparse MLA for decode (each query's selection split over several workgroups)."""
+    return _mla(_lib.dsa_sparse_mla_decode, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale,
+                num_splits, ws, stream)
+
+
+def dsa_sparse_mla_prefill(q, kv, kv_scale, q_seq, idx, length, out, lse=None, softmax_scale=None, ws=None,
+                           stream=None):
+    """Sparse MLA for chunked prefill (one workgroup per query)."""
+    return _mla(_lib.dsa_sparse_mla_prefill, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale, 0,
+                ws, stream)

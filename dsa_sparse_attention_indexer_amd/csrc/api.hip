@@ -1,0 +1,235 @@
+// C ABI of libdsa: argument validation (default-deny: every violated condition is reported and
+// nothing is launched) and dispatch to the gfx950 kernels.  See include/dsa.h for the contract.
+
+#include "dsa_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+namespace {
+
+thread_local std::string g_err;
+
+struct Checker {
+  std::string msg;
+  bool unsupported = false;
+  bool arg = false;
+  void fail(bool is_arg, const char* fmt, ...) {
+    char buf[256];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (!msg.empty()) msg += "; ";
+    msg += buf;
+    if (is_arg) arg = true; else unsupported = true;
+  }
+  void need(bool ok, const char* what) { if (!ok) fail(true, "%s", what); }
+  void support(bool ok, const char* what) { if (!ok) fail(false, "%s", what); }
+  dsa_status_t finish(const char* fn) {
+    if (msg.empty()) { g_err.clear(); return DSA_OK; }
+    g_err = std::string(fn) + ": " + msg;
+    return arg ? DSA_ERR_ARG : DSA_ERR_UNSUPPORTED;
+  }
+};
+
+dsa_status_t hip_status(const char* fn, hipError_t e) {
+  if (e == hipSuccess) { g_err.clear(); return DSA_OK; }
+  g_err = std::string(fn) + ": HIP launch failed: " + hipGetErrorString(e);
+  return DSA_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* d, const void* q, const float* w,
+                                const int32_t* q_seq, const int32_t* q_pos,
+                                const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                                const void* k_cache, const float* k_scale,
+                                float* scores, int64_t ld_scores, void* stream) {
+  Checker ck;
+  if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_scores"); }
+  ck.need(d->num_q >= 0 && d->num_q <= 65535, "num_q must be in [0, 65535]");
+  ck.need(d->num_seqs >= 1, "num_seqs must be >= 1");
+  ck.need(d->max_ctx >= 1 && d->max_ctx <= (1 << 26), "max_ctx must be in [1, 2^26]");
+  ck.support(d->head_dim == 128, "head_dim must be 128");
+  ck.support(d->num_heads >= 1 && d->num_heads <= 32, "num_heads must be in [1, 32]");
+  ck.support(d->rope_dim == 0 || d->rope_dim == 64, "rope_dim must be 0 or 64");
+  ck.support(d->q_dtype == DSA_F32 || d->q_dtype == DSA_BF16, "q_dtype must be F32 or BF16");
+  ck.support(d->k_dtype == DSA_F32 || d->k_dtype == DSA_FP8_E4M3FN, "k_dtype must be F32 or FP8_E4M3FN");
+  ck.need(ld_scores >= d->max_ctx, "ld_scores must be >= max_ctx");
+  if (d->num_q > 0) {
+    ck.need(q && w && q_seq && q_pos && k_cache && scores, "q, w, q_seq, q_pos, k_cache and scores must be non-NULL");
+    ck.need((ssmax_s == nullptr) == (ssmax_b == nullptr), "ssmax_s and ssmax_b must be both NULL or both set");
+    ck.need((inv_freq != nullptr) == (d->rope_dim > 0), "inv_freq must be set iff rope_dim > 0");
+    ck.need(d->k_dtype != DSA_FP8_E4M3FN || k_scale != nullptr, "k_scale is required for FP8 keys");
+    ck.need(aligned(k_cache, 16), "k_cache must be 16-byte aligned");
+    ck.need(aligned(q, d->q_dtype == DSA_BF16 ? 2 : 4), "q must be aligned to its element size");
+  }
+  dsa_status_t st = ck.finish("dsa_indexer_scores");
+  if (st != DSA_OK || d->num_q == 0) return st;
+  dsa::IndexerLaunch a{d->num_q, d->num_heads, d->rope_dim, d->num_seqs, d->max_ctx, d->q_dtype, d->k_dtype,
+                       q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores};
+  return hip_status("dsa_indexer_scores", dsa::launch_indexer(a, (hipStream_t)stream));
+}
+
+size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k) {
+  (void)k;
+  if (num_q <= 0 || ld_scores <= 0) return 0;
+  return (size_t)num_q * dsa::topk_row_bytes(ld_scores);
+}
+
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t num_q,
+                      int32_t k, int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream) {
+  Checker ck;
+  ck.need(num_q >= 0 && num_q <= 65535, "num_q must be in [0, 65535]");
+  ck.need(ld_scores >= 1, "ld_scores must be >= 1");
+  ck.support(ld_scores <= dsa::kTopkMaxCols, "ld_scores must be <= 4194304");
+  ck.need(ld_scores % 4 == 0, "ld_scores must be a multiple of 4");
+  ck.support(k >= 1 && k <= 65536, "k must be in [1, 65536]");
+  if (num_q > 0) {
+    ck.need(scores && q_pos && idx, "scores, q_pos and idx must be non-NULL");
+    ck.need(aligned(scores, 16), "scores must be 16-byte aligned");
+    ck.need(ws != nullptr && ws_bytes >= dsa_topk_workspace_size(num_q, ld_scores, k),
+            "workspace missing or smaller than dsa_topk_workspace_size()");
+    ck.need(aligned(ws, 16), "workspace must be 16-byte aligned");
+  }
+  dsa_status_t st = ck.finish("dsa_topk");
+  if (st != DSA_OK || num_q == 0) return st;
+  dsa::TopkLaunch a{scores, ld_scores, q_pos, num_q, k, idx, len, ws};
+  return hip_status("dsa_topk", dsa::launch_topk(a, (hipStream_t)stream));
+}
+
+size_t dsa_block_select_workspace_size(int32_t num_q, int64_t ld_scores, int32_t block) {
+  if (num_q <= 0 || ld_scores <= 0 || block <= 0) return 0;
+  return dsa::block_select_ws_bytes(num_q, ld_scores, block);
+}
+
+dsa_status_t dsa_block_select(const float* scores, int64_t ld_scores, const int32_t* q_pos,
+                              int32_t num_q, int32_t block, int32_t nblocks, int32_t topk,
+                              int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream) {
+  Checker ck;
+  ck.need(num_q >= 0 && num_q <= 65535, "num_q must be in [0, 65535]");
+  ck.need(ld_scores >= 1 && ld_scores <= (int64_t(1) << 30), "ld_scores must be in [1, 2^30]");
+  ck.support(block >= 1 && block <= 4096, "block must be in [1, 4096]");
+  ck.support(nblocks >= 1 && nblocks <= 64, "nblocks must be in [1, 64]");
+  ck.need(topk >= 1, "topk must be >= 1");
+  ck.need((int64_t)nblocks * block <= topk, "nblocks * block must be <= topk");
+  if (num_q > 0) {
+    ck.need(scores && q_pos && idx, "scores, q_pos and idx must be non-NULL");
+    ck.need(block <= 0 || (ws != nullptr && ws_bytes >= dsa_block_select_workspace_size(num_q, ld_scores, block)),
+            "workspace missing or smaller than dsa_block_select_workspace_size()");
+  }
+  dsa_status_t st = ck.finish("dsa_block_select");
+  if (st != DSA_OK || num_q == 0) return st;
+  dsa::BlockSelectLaunch a{scores, ld_scores, q_pos, num_q, block, nblocks, topk, idx, len, ws};
+  return hip_status("dsa_block_select", dsa::launch_block_select(a, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+int auto_splits(const dsa_mla_desc_t* d, bool decode) {
+  if (!decode) return 1;
+  if (d->num_splits > 0) return d->num_splits;
+  // Enough workgroups to cover the 256 CUs once; each split keeps >= 32 selected keys.
+  int s = (256 + d->num_q - 1) / (d->num_q > 0 ? d->num_q : 1);
+  const int max_by_keys = (d->topk + 31) / 32;
+  if (s > max_by_keys) s = max_by_keys;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  return s;
+}
+
+void split_geometry(const dsa_mla_desc_t* d, bool decode, int* splits, int* per_split) {
+  int s = auto_splits(d, decode);
+  int per = (d->topk + s - 1) / s;
+  per = (per + 31) / 32 * 32;
+  s = (d->topk + per - 1) / per;
+  if (s < 1) s = 1;
+  *splits = s;
+  *per_split = per;
+}
+
+size_t mla_ws_bytes(const dsa_mla_desc_t* d, bool decode) {
+  int s, per;
+  split_geometry(d, decode, &s, &per);
+  if (s <= 1) return 0;
+  return (size_t)d->num_q * s * d->num_heads * ((size_t)d->kv_lora + 2) * sizeof(float);
+}
+
+dsa_status_t mla_call(const char* fn, bool decode, const dsa_mla_desc_t* d, const void* q, const void* kv,
+                      const float* kv_scale, const int32_t* q_seq, const int32_t* idx, const int32_t* len,
+                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Checker ck;
+  if (!d) { ck.need(false, "desc is NULL"); return ck.finish(fn); }
+  ck.need(d->num_q >= 0 && d->num_q <= 65535, "num_q must be in [0, 65535]");
+  ck.need(d->num_seqs >= 1, "num_seqs must be >= 1");
+  ck.need(d->max_ctx >= 1 && d->max_ctx <= (1 << 26), "max_ctx must be in [1, 2^26]");
+  ck.need(d->topk >= 1 && d->topk <= (1 << 20), "topk must be in [1, 2^20]");
+  ck.support(d->kv_lora == 512, "kv_lora must be 512");
+  ck.support(d->rope_dim == 0 || d->rope_dim == 64, "rope_dim must be 0 or 64");
+  ck.support(d->kv_scale_block == 64, "kv_scale_block must be 64");
+  ck.need(d->num_splits >= 0 && d->num_splits <= 64, "num_splits must be in [0, 64]");
+  ck.need(d->softmax_scale > 0.f, "softmax_scale must be > 0");
+  const bool fp8 = d->kv_dtype == DSA_FP8_E4M3FN;
+  if (fp8) {
+    ck.support(d->q_dtype == DSA_BF16, "the FP8 cache path takes BF16 queries");
+    ck.support(d->num_heads >= 16 && d->num_heads <= 64 && d->num_heads % 16 == 0,
+               "num_heads must be 16, 32, 48 or 64 on the FP8 path");
+  } else {
+    ck.support(d->kv_dtype == DSA_F32, "kv_dtype must be F32 or FP8_E4M3FN");
+    ck.support(d->q_dtype == DSA_F32, "the F32 cache path takes F32 queries");
+    ck.support(d->num_heads >= 1 && d->num_heads <= 64, "num_heads must be in [1, 64] on the F32 path");
+  }
+  if (d->num_q > 0) {
+    ck.need(q && kv && q_seq && idx && out, "q, kv, q_seq, idx and out must be non-NULL");
+    ck.need(!fp8 || kv_scale != nullptr, "kv_scale is required for an FP8 cache");
+    ck.need(aligned(q, 16) && aligned(kv, 16) && aligned(out, 16), "q, kv and out must be 16-byte aligned");
+    const size_t need = mla_ws_bytes(d, decode);
+    ck.need(need == 0 || (ws != nullptr && ws_bytes >= need && aligned(ws, 16)),
+            "workspace missing, misaligned or smaller than dsa_sparse_mla_workspace_size()");
+  }
+  dsa_status_t st = ck.finish(fn);
+  if (st != DSA_OK || d->num_q == 0) return st;
+  dsa::MlaLaunch a{};
+  a.T = d->num_q; a.H = d->num_heads; a.kv_lora = d->kv_lora; a.rope_dim = d->rope_dim;
+  a.B = d->num_seqs; a.max_ctx = d->max_ctx; a.topk = d->topk;
+  split_geometry(d, decode, &a.splits, &a.per_split);
+  a.q_dtype = d->q_dtype; a.kv_dtype = d->kv_dtype; a.softmax_scale = d->softmax_scale;
+  a.q = q; a.kv = kv; a.kv_scale = kv_scale; a.q_seq = q_seq; a.idx = idx; a.len = len;
+  a.out = out; a.lse = lse; a.ws = reinterpret_cast<float*>(ws);
+  return hip_status(fn, dsa::launch_sparse_mla(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_sparse_mla_workspace_size(const dsa_mla_desc_t* d) {
+  if (!d || d->num_q <= 0 || d->topk <= 0) return 0;
+  return mla_ws_bytes(d, true);
+}
+
+dsa_status_t dsa_sparse_mla_decode(const dsa_mla_desc_t* d, const void* q, const void* kv, const float* kv_scale,
+                                   const int32_t* q_seq, const int32_t* idx, const int32_t* len, float* out,
+                                   float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return mla_call("dsa_sparse_mla_decode", true, d, q, kv, kv_scale, q_seq, idx, len, out, lse, ws, ws_bytes, stream);
+}
+
+dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* d, const void* q, const void* kv, const float* kv_scale,
+                                    const int32_t* q_seq, const int32_t* idx, const int32_t* len, float* out,
+                                    float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return mla_call("dsa_sparse_mla_prefill", false, d, q, kv, kv_scale, q_seq, idx, len, out, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal declarations shared by the HIP translation units of libdsa (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+// ---- launch parameter blocks (host-validated, passed by value to the launchers) -------------
+
+struct IndexerLaunch {
+  int T, H, rope_dim, B, max_ctx;
+  dsa_dtype_t q_dtype, k_dtype;
+  const void* q;
+  const float* w;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const float* ssmax_s;
+  const float* ssmax_b;
+  const float* inv_freq;
+  const void* k_cache;
+  const float* k_scale;
+  float* scores;
+  int64_t ld;
+};
+
+struct TopkLaunch {
+  const float* scores;
+  int64_t ld;
+  const int32_t* q_pos;
+  int T, k;
+  int32_t* idx;
+  int32_t* len;
+  void* ws;
+};
+
+struct BlockSelectLaunch {
+  const float* scores;
+  int64_t ld;
+  const int32_t* q_pos;
+  int T, block, nblocks, topk;
+  int32_t* idx;
+  int32_t* len;
+  void* ws;
+};
+
+struct MlaLaunch {
+  int T, H, kv_lora, rope_dim, B, max_ctx, topk, splits, per_split;
+  dsa_dtype_t q_dtype, kv_dtype;
+  float softmax_scale;
+  const void* q;
+  const void* kv;
+  const float* kv_scale;
+  const int32_t* q_seq;
+  const int32_t* idx;
+  const int32_t* len;
+  float* out;
+  float* lse;
+  float* ws;  // split partials: [T][splits][H][kv_lora] O, then [T][splits][H] m and l
+};
+
+// ---- sizes shared between validation and the kernels ----------------------------------------
+
+constexpr int kTopkThreads = 256;
+constexpr int kTopkSeg = 4096;          // scores per segment workgroup (16 per thread)
+constexpr int kTopkBins0 = 2048;        // first radix digit: key bits 31..21
+constexpr int kTopkCap = 8192;          // candidates kept per row for the exact resolve
+constexpr int64_t kTopkMaxCols = int64_t(1) << 22;
+constexpr int kTopkMaxSegs = int(kTopkMaxCols / kTopkSeg);
+
+size_t topk_row_bytes(int64_t ld);
+size_t block_select_ws_bytes(int T, int64_t ld, int block);
+
+// ---- launchers (return the HIP status of the last launch) -----------------------------------
+
+hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s);
+hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s);
+
+}  // namespace dsa
+
+// ---- small device helpers --------------------------------------------------------------------
+
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+namespace dsa {
+
+// Order-preserving map float -> u32 (larger float -> larger key); -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(uint32_t(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+}  // namespace dsa
+#endif

@@ -1,0 +1,91 @@
+"""One DSA layer step over device-resident inputs, built from the C-ABI calls.
+
+A layer step is: index scores (with the query's RoPE and SSMax) -> top-k (or block) selection ->
+sparse MLA.  A shared-indexer layer skips the first two and reuses another layer's selection
+("Day 0 support for Mistral Large 4 on vLLM", the architecture table: 28 of the 72 layers reuse
+the top-k of the nearest earlier indexer layer).  Buffers are allocated once and reused, so a
+timed step only enqueues kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import (dsa_block_select, dsa_block_select_workspace_size, dsa_indexer_scores, dsa_sparse_mla_decode,
+               dsa_sparse_mla_prefill, dsa_sparse_mla_workspace_size, dsa_topk, dsa_topk_workspace_size,
+               mla_desc)
+
+
+@dataclasses.dataclass
+class StepBuffers:
+    scores: torch.Tensor
+    idx: torch.Tensor
+    length: torch.Tensor
+    out: torch.Tensor
+    lse: torch.Tensor
+    ws_topk: torch.Tensor
+    ws_block: Optional[torch.Tensor]
+    ws_mla: Optional[torch.Tensor]
+
+
+def _ld(max_ctx: int) -> int:
+    return (max_ctx + 3) // 4 * 4
+
+
+def alloc_buffers(wl, *, prefill: bool = False, block_sparse: bool = False, num_splits: int = 0) -> StepBuffers:
+    dev = wl.index_q.device
+    T, k = wl.num_q, wl.topk
+    ld = _ld(wl.max_ctx)
+    scores = torch.empty(T, ld, dtype=torch.float32, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    length = torch.empty(T, dtype=torch.int32, device=dev)
+    out = torch.empty(T, wl.mla_heads, 512, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, wl.mla_heads, dtype=torch.float32, device=dev)
+    ws_topk = torch.empty(max(16, dsa_topk_workspace_size(T, ld, k)), dtype=torch.uint8, device=dev)
+    ws_block = None
+    if block_sparse:
+        ws_block = torch.empty(max(16, dsa_block_select_workspace_size(T, ld, 128)), dtype=torch.uint8, device=dev)
+    ws_mla = None
+    if not prefill:
+        need = dsa_sparse_mla_workspace_size(mla_desc(wl.mla_q, wl.kv, idx, wl.softmax_scale, num_splits))
+        if need:
+            ws_mla = torch.empty(need, dtype=torch.uint8, device=dev)
+    return StepBuffers(scores, idx, length, out, lse, ws_topk, ws_block, ws_mla)
+
+
+def index_scores(wl, buf: StepBuffers, stream=None):
+    return dsa_indexer_scores(wl.index_q, wl.index_w, wl.q_seq, wl.q_pos, wl.index_k, buf.scores,
+                              k_scale=wl.index_k_scale, ssmax_s=wl.ssmax_s, ssmax_b=wl.ssmax_b,
+                              inv_freq=wl.inv_freq, stream=stream)
+
+
+def select(wl, buf: StepBuffers, *, block_sparse: bool = False, stream=None):
+    if block_sparse:
+        return dsa_block_select(buf.scores, wl.q_pos, buf.idx, buf.length, block=128, nblocks=16, ws=buf.ws_block,
+                                stream=stream)
+    return dsa_topk(buf.scores, wl.q_pos, wl.topk, buf.idx, buf.length, ws=buf.ws_topk, stream=stream)
+
+
+def attend(wl, buf: StepBuffers, *, prefill: bool = False, num_splits: int = 0, idx=None, length=None,
+           stream=None):
+    idx = buf.idx if idx is None else idx
+    length = buf.length if length is None else length
+    if prefill:
+        return dsa_sparse_mla_prefill(wl.mla_q, wl.kv, wl.kv_scale, wl.q_seq, idx, length, buf.out, buf.lse,
+                                      softmax_scale=wl.softmax_scale, stream=stream)
+    return dsa_sparse_mla_decode(wl.mla_q, wl.kv, wl.kv_scale, wl.q_seq, idx, length, buf.out, buf.lse,
+                                 softmax_scale=wl.softmax_scale, num_splits=num_splits, ws=buf.ws_mla,
+                                 stream=stream)
+
+
+def layer_step(wl, buf: StepBuffers, *, prefill: bool = False, block_sparse: bool = False,
+               shared_from: Optional[StepBuffers] = None, num_splits: int = 0, stream=None):
+    """Scores -> selection -> sparse MLA; with shared_from, only the MLA over that selection."""
+    if shared_from is not None:
+        return attend(wl, buf, prefill=prefill, num_splits=num_splits, idx=shared_from.idx,
+                      length=shared_from.length, stream=stream)
+    index_scores(wl, buf, stream)
+    select(wl, buf, block_sparse=block_sparse, stream=stream)
+    return attend(wl, buf, prefill=prefill, num_splits=num_splits, stream=stream)

@@ -1,0 +1,204 @@
+/*
+ * dsa.h -- C ABI of the DSA (DeepSeek-style sparse attention) hot path for MI355X (gfx950).
+ *
+ * Three stages, as Mistral Large 4 runs them on every decode step
+ * ("Day 0 support for Mistral Large 4 on vLLM", Highlights, the architecture table and
+ * "Sparse MLA + DSA indexer"; formulas from "mistral-large4.md", section
+ * "What differs from GLM-5.2"):
+ *
+ *   1. dsa_indexer_scores   lightning-indexer score of every visible cached key per query
+ *   2. dsa_topk             keep the k (= 2048) highest-scoring keys per query
+ *      dsa_block_select     block-sparse alternative: top-16 128-token blocks, recent block kept
+ *   3. dsa_sparse_mla_decode / dsa_sparse_mla_prefill
+ *                           exact absorbed-MLA attention over the selected keys only
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer (HIP global memory); sizes and descriptors are
+ *    host values.  Tensors are dense row-major with the layouts given per argument.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work: they never
+ *    allocate, free or synchronise, and keep no state besides the loaded code object and the
+ *    calling thread's error string.  The caller owns every buffer, including workspaces sized
+ *    by the *_workspace_size queries.
+ *  - Errors: every host-checkable condition (null pointers, unsupported sizes or dtype
+ *    combinations, a workspace that is too small) is checked before anything is launched.
+ *    A failing call returns DSA_ERR_ARG or DSA_ERR_UNSUPPORTED, launches nothing, and
+ *    dsa_last_error() lists every violated condition.  A failed launch returns DSA_ERR_HIP with
+ *    the HIP error text.
+ *  - Data-dependent preconditions are the caller's: 0 <= q_pos[t] < max_ctx, 0 <= q_seq[t] <
+ *    num_seqs, cache scales finite and >= 0, index entries in [0, max_ctx) or -1.  The kernels
+ *    clamp positions and sequence ids and skip out-of-range indices so that a violation never
+ *    reads outside the given buffers, but the results of such a call are unspecified.
+ *  - Keys visible to a query at 0-based position p are cache rows 0..p of its sequence (its own
+ *    key is already in the cache).  Index lists hold row numbers within the query's sequence.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_ARG = 1,          /* a null pointer, a bad size or an inconsistent argument        */
+  DSA_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the kernels implement            */
+  DSA_ERR_HIP = 3           /* the HIP runtime reported an error while launching             */
+} dsa_status_t;
+
+typedef enum {
+  DSA_F32 = 0,              /* IEEE binary32                                                  */
+  DSA_BF16 = 1,             /* bfloat16, stored as 16-bit patterns                            */
+  DSA_FP8_E4M3FN = 2        /* OCP FP8 E4M3FN bytes (bias 7, max 448, no infinities)          */
+} dsa_dtype_t;
+
+/* Text of the last failure on the calling thread ("" after a success).  Owned by the library. */
+const char* dsa_last_error(void);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int32_t dsa_abi_version(void);
+#define DSA_ABI_VERSION 1
+
+/* ============================================================================================
+ * 1. Lightning-indexer scores
+ * --------------------------------------------------------------------------------------------
+ * Defined by "mistral-large4.md", "What differs from GLM-5.2", bullets "The indexer", "SSMax"
+ * and "RoPE and the rest".  For query t at position p = q_pos[t] in sequence b = q_seq[t]:
+ *
+ *   q'_h  = m_h * RoPE_p(q[t][h])             m_h = s_h * ln(p + 1) + b_h   (SSMax)
+ *           RoPE_p rotates pairs (2j, 2j+1), j < rope_dim/2, by the angle p * inv_freq[j]
+ *   S(i)  = sum_h (w[t][h] / sqrt(H)) * max(0, q'_h . k_i / sqrt(head_dim)),   i = 0..p
+ *   k_i   = key row i of sequence b, times its per-token scale for fp8 keys
+ *
+ * Arguments
+ *   q        [num_q][num_heads][head_dim]  q_dtype (F32 or BF16)
+ *   w        [num_q][num_heads] f32        weights_proj(x) per head
+ *   q_seq    [num_q] i32                   sequence of each query
+ *   q_pos    [num_q] i32                   0-based position of each query
+ *   ssmax_s, ssmax_b  [num_heads] f32      per-head SSMax parameters; both NULL = no SSMax
+ *   inv_freq [rope_dim/2] f32              rotary frequencies; NULL iff rope_dim == 0
+ *   k_cache  [num_seqs][max_ctx][head_dim] k_dtype (F32, or FP8_E4M3FN bytes)
+ *   k_scale  [num_seqs][max_ctx] f32       per-token key scale (FP8 keys; NULL for F32 keys)
+ *   scores   [num_q][ld_scores] f32        row t gets S(0..p); entries past p are not written
+ *   ld_scores >= max_ctx
+ *
+ * Supported: head_dim == 128; 1 <= num_heads <= 32; rope_dim in {0, 64}; q_dtype F32 or BF16;
+ * k_dtype F32 (fp32 vector path) or FP8_E4M3FN (matrix-core path).  The FP8 path computes q'
+ * in float64, splits it into two fp16 terms and accumulates in fp32; its scores agree with
+ * the real-number definition to about 1e-6 of the score scale.
+ * ==========================================================================================*/
+typedef struct {
+  int32_t num_q;       /* T: query tokens                                                   */
+  int32_t num_heads;   /* H: index heads (32 on Mistral Large 4; 4 in the block-sparse scan) */
+  int32_t head_dim;    /* 128                                                                */
+  int32_t rope_dim;    /* 64 on RoPE layers, 0 on NoPE layers                               */
+  int32_t num_seqs;    /* B: sequences in the cache                                         */
+  int32_t max_ctx;     /* rows per sequence in the cache                                     */
+  dsa_dtype_t q_dtype;
+  dsa_dtype_t k_dtype;
+} dsa_indexer_desc_t;
+
+dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* desc, const void* q, const float* w,
+                                const int32_t* q_seq, const int32_t* q_pos,
+                                const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                                const void* k_cache, const float* k_scale,
+                                float* scores, int64_t ld_scores, void* stream);
+
+/* ============================================================================================
+ * 2a. Top-k selection
+ * --------------------------------------------------------------------------------------------
+ * Keep the k highest scores of each row ("the top 2048 keys kept": "mistral-large4.md", bullet
+ * "The indexer"; top-k 2048 in the vLLM page's architecture table).  Row t has n = q_pos[t]+1
+ * valid scores (columns 0..n-1 of scores[t]).
+ *   - n <= k: every column is selected.
+ *   - otherwise the k largest are selected; equal scores go to the lower column; -0.0 == +0.0.
+ *   - idx[t][0..len) lists the selected columns in ascending order, idx[t][len..k) = -1, and
+ *     len[t] = min(n, k) (the -1 slots and top-k length of the vLLM page's "Top-k compaction").
+ * Scores must not be NaN.  Selection is exact: it depends only on the fp32 score values.
+ *
+ * Arguments
+ *   scores   [num_q][ld_scores] f32;  q_pos [num_q] i32 (n = q_pos + 1, clamped to ld_scores)
+ *   idx      [num_q][k] i32;          len [num_q] i32 (may be NULL)
+ *   ws       device workspace of at least dsa_topk_workspace_size(num_q, ld_scores, k) bytes
+ * Supported: 1 <= k <= 65536; ld_scores <= 2^30.
+ * ==========================================================================================*/
+size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k);
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t num_q,
+                      int32_t k, int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream);
+
+/* ============================================================================================
+ * 2b. Block-sparse selection
+ * --------------------------------------------------------------------------------------------
+ * The MiniMax Sparse Attention steps ("vLLM adds NVFP4 serving for MiniMax M3.1 Flash at 76
+ * concurrent sequences"): the cache is cut into `block`-token blocks; a block's score is the
+ * largest index score among its visible keys; the block holding the query position (the most
+ * recent one) is always kept and the other nblocks-1 are the best of the rest (ties to the
+ * lower block); the selection is every visible key of the kept blocks, ascending.
+ *   idx [num_q][topk] i32 (-1 padded), len [num_q] i32 (may be NULL).
+ * Supported: block in [1, 4096], nblocks >= 1, nblocks * block <= topk, nblocks <= 64.
+ * ==========================================================================================*/
+size_t dsa_block_select_workspace_size(int32_t num_q, int64_t ld_scores, int32_t block);
+dsa_status_t dsa_block_select(const float* scores, int64_t ld_scores, const int32_t* q_pos,
+                              int32_t num_q, int32_t block, int32_t nblocks, int32_t topk,
+                              int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream);
+
+/* ============================================================================================
+ * 3. Sparse MLA (absorbed form, V = latent)
+ * --------------------------------------------------------------------------------------------
+ * For query t and head g over the selected rows r in idx[t][0..len[t]) (entries < 0 skipped):
+ *   z_r  = softmax_scale * (q[t][g][0:kv_lora] . c_r[0:kv_lora]
+ *                           + q[t][g][kv_lora:kv_lora+rope_dim] . c_r[kv_lora:kv_lora+rope_dim])
+ *   out[t][g] = sum_r softmax(z)_r * c_r[0:kv_lora],   lse[t][g] = ln sum_r exp(z_r)
+ * ("Day 0 support for Mistral Large 4 on vLLM": MLA with KV LoRA rank 512 and RoPE dim 64,
+ * one latent KV head shared by all heads; NoPE layers are the same with zero RoPE dims on the
+ * same cache layout.)  q arrives final: SSMax and RoPE of the MLA query are applied upstream.
+ * A query with no selected row gets out = 0 and lse = -inf.
+ *
+ * Arguments
+ *   q        [num_q][num_heads][kv_lora + rope_dim]  q_dtype
+ *   kv       [num_seqs][max_ctx][kv_lora + 64]       kv_dtype (the row is 576 wide on every layer)
+ *   kv_scale [num_seqs][max_ctx][(kv_lora+64)/kv_scale_block] f32 for FP8, NULL for F32
+ *   q_seq    [num_q] i32;  idx [num_q][topk] i32;  len [num_q] i32 or NULL (then -1 ends a list)
+ *   out      [num_q][num_heads][kv_lora] f32;        lse [num_q][num_heads] f32 or NULL
+ *   ws       workspace of dsa_sparse_mla_workspace_size(desc) bytes (0 is allowed when the
+ *            query count alone fills the GPU and no split is needed)
+ * Supported: num_heads a multiple of 16 up to 128; kv_lora == 512; rope_dim in {0, 64};
+ * kv_scale_block == 64; (q F32, kv F32) on the fp32 path, (q BF16, kv FP8) on the matrix-core
+ * path (fp8 x scale rounded to bf16, bf16 probabilities, fp32 accumulation).
+ *
+ * _decode splits each query's selection over several workgroups (split-K with an exact
+ * log-sum-exp merge) so that a handful of queries still fills the GPU; _prefill gives each
+ * query one workgroup (chunked prefill: thousands of queries).  Both compute the same values.
+ * ==========================================================================================*/
+typedef struct {
+  int32_t num_q;            /* T                                                             */
+  int32_t num_heads;        /* 64                                                            */
+  int32_t kv_lora;          /* 512                                                           */
+  int32_t rope_dim;         /* 64 (RoPE layer) or 0 (NoPE layer)                             */
+  int32_t num_seqs;         /* B                                                             */
+  int32_t max_ctx;          /* rows per sequence                                             */
+  int32_t topk;             /* width of an index row (2048)                                  */
+  dsa_dtype_t q_dtype;
+  dsa_dtype_t kv_dtype;
+  int32_t kv_scale_block;   /* 64                                                            */
+  float softmax_scale;      /* 1/sqrt(192) on RoPE layers, 1/sqrt(128) on NoPE layers        */
+  int32_t num_splits;       /* decode only: 0 = choose automatically, else 1..64             */
+} dsa_mla_desc_t;
+
+size_t dsa_sparse_mla_workspace_size(const dsa_mla_desc_t* desc);
+dsa_status_t dsa_sparse_mla_decode(const dsa_mla_desc_t* desc, const void* q, const void* kv,
+                                   const float* kv_scale, const int32_t* q_seq, const int32_t* idx,
+                                   const int32_t* len, float* out, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream);
+dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* desc, const void* q, const void* kv,
+                                    const float* kv_scale, const int32_t* q_seq, const int32_t* idx,
+                                    const int32_t* len, float* out, float* lse,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

@@ -1,0 +1,57 @@
+"""Comparison helpers shared by the GPU parity tests (no method arithmetic lives here)."""
+import math
+
+import numpy as np
+
+# Selection: sets must be equal except for keys whose oracle score lies within this relative
+# band of the oracle's k-th score (ties broken toward the lower index elsewhere).
+SELECT_BAND = 1e-5
+# Attention on fp8 caches with fp32 accumulation: per element |d| <= ATOL + RTOL |ref|, plus a
+# relative-RMS bound (outputs are ~1e-3, so the absolute bound alone would pass zeros).
+ATOL, RTOL, REL_RMS_FP8 = 2e-2, 1e-2, 1e-2
+REL_RMS_F32 = 1e-5
+
+
+def check_selection(gpu_idx, gpu_len, scores, k, where=""):
+    """GPU selection vs the oracle's scores: equal size, differences only inside the tie band."""
+    from oracle import dsa_oracle as O
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    gi = np.asarray(gpu_idx)
+    gl = int(gpu_len)
+    assert gl == min(n, k), f"{where}: len {gl} != {min(n, k)}"
+    assert np.all(gi[gl:] == -1), f"{where}: padding is not -1"
+    sel = gi[:gl]
+    assert np.all(np.diff(sel) > 0), f"{where}: selection not strictly ascending"
+    if n <= k:
+        assert np.array_equal(sel, np.arange(n)), f"{where}: n <= k must select every key"
+        return 0
+    ref, _ = O.topk_row(s, k)
+    kth = O.kth_score(s, k)
+    rms = math.sqrt(float(np.mean(s * s)))
+    band = SELECT_BAND * max(abs(kth), rms)
+    diff = np.setxor1d(sel, ref)
+    outside = [int(t) for t in diff if abs(s[t] - kth) > band]
+    assert not outside, (f"{where}: {len(outside)} keys differ outside the band (k-th {kth:.9g}, band {band:.3g}); "
+                         f"e.g. {[(t, s[t]) for t in outside[:5]]}")
+    return len(diff)
+
+
+def check_attention(out, lse, ref_out, ref_lse, fp8, where=""):
+    out = np.asarray(out, dtype=np.float64)
+    ref_out = np.asarray(ref_out, dtype=np.float64)
+    d = np.abs(out - ref_out)
+    assert np.all(d <= ATOL + RTOL * np.abs(ref_out)), f"{where}: max abs err {d.max():.3g}"
+    rel = np.linalg.norm(out - ref_out) / max(np.linalg.norm(ref_out), 1e-300)
+    lim = REL_RMS_FP8 if fp8 else REL_RMS_F32
+    assert rel <= lim, f"{where}: rel-RMS {rel:.3g} > {lim}"
+    if lse is not None:
+        lse = np.asarray(lse, dtype=np.float64)
+        ref_lse = np.asarray(ref_lse, dtype=np.float64)
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(lse), fin), f"{where}: lse finiteness differs"
+        lim_lse = 1e-2 if fp8 else 1e-5
+        if fin.any():
+            dl = np.abs(lse[fin] - ref_lse[fin])
+            assert dl.max() <= lim_lse * max(1.0, np.abs(ref_lse[fin]).max()), f"{where}: lse err {dl.max():.3g}"
+    return rel

@@ -1,0 +1,90 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point include/dsa.h
+declares, and rejects bad arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    lib_path = os.path.join(ROOT, "dsa_sparse_attention_indexer_amd", "libdsa.so")
+    if not os.path.exists(lib_path):
+        from dsa_sparse_attention_indexer_amd.build import build
+        build()
+    import dsa_sparse_attention_indexer_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_stages():
+    fns = declared_functions()
+    for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_function(dsa):
+    lib = ctypes.CDLL(dsa.LIB_PATH)
+    for f in declared_functions():
+        assert hasattr(lib, f), f"{f} declared in dsa.h but not exported"
+    assert set(declared_functions()) == set(dsa.EXPORTED)
+    assert dsa.lib().dsa_abi_version() == 1
+
+
+def test_topk_rejects_bad_arguments_listing_every_reason(dsa):
+    L = dsa.lib()
+    st = L.dsa_topk(None, 6, None, 3, 0, None, None, None, 0, None)
+    assert st == dsa.DSA_ERR_ARG
+    msg = L.dsa_last_error().decode()
+    for frag in ("multiple of 4", "k must be", "non-NULL", "workspace"):
+        assert frag in msg, msg
+
+
+def test_indexer_rejects_unsupported_shapes(dsa):
+    L = dsa.lib()
+    d = dsa.IndexerDesc(1, 64, 96, 32, 1, 100, dsa.DSA_BF16, dsa.DSA_BF16)
+    st = L.dsa_indexer_scores(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 50, None)
+    assert st == dsa.DSA_ERR_ARG            # the NULLs and ld < max_ctx are argument errors
+    msg = L.dsa_last_error().decode()
+    for frag in ("head_dim", "num_heads", "rope_dim", "k_dtype", "ld_scores", "non-NULL"):
+        assert frag in msg, msg
+    d = dsa.IndexerDesc(0, 64, 128, 64, 1, 100, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN)
+    st = L.dsa_indexer_scores(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 100, None)
+    assert st == dsa.DSA_ERR_UNSUPPORTED and "num_heads" in L.dsa_last_error().decode()
+
+
+def test_mla_rejects_bad_dtype_combinations(dsa):
+    L = dsa.lib()
+    d = dsa.MlaDesc(4, 64, 512, 64, 1, 1000, 2048, dsa.DSA_F32, dsa.DSA_FP8_E4M3FN, 64, 0.07, 0)
+    st = L.dsa_sparse_mla_decode(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None)
+    msg = L.dsa_last_error().decode()
+    assert st == dsa.DSA_ERR_ARG and "BF16 queries" in msg and "non-NULL" in msg
+    d = dsa.MlaDesc(0, 64, 256, 32, 1, 1000, 2048, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN, 32, 0.07, 0)
+    st = L.dsa_sparse_mla_prefill(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None)
+    msg = L.dsa_last_error().decode()
+    assert st == dsa.DSA_ERR_UNSUPPORTED and "kv_lora" in msg and "rope_dim" in msg and "kv_scale_block" in msg
+
+
+def test_workspace_queries(dsa):
+    assert dsa.dsa_topk_workspace_size(16, 131072, 2048) > 0
+    assert dsa.dsa_topk_workspace_size(0, 131072, 2048) == 0
+    assert dsa.dsa_block_select_workspace_size(4, 524288, 128) == 4 * 4096 * 4
+    d = dsa.MlaDesc(16, 64, 512, 64, 16, 131072, 2048, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN, 64, 0.07, 0)
+    assert dsa.dsa_sparse_mla_workspace_size(d) == 16 * 16 * 64 * 514 * 4
+    d.num_splits = 1
+    assert dsa.dsa_sparse_mla_workspace_size(d) == 0
+
+
+def test_zero_queries_is_a_no_op(dsa):
+    L = dsa.lib()
+    assert L.dsa_topk(None, 8, None, 0, 2048, None, None, None, 0, None) == dsa.DSA_OK
+    assert L.dsa_last_error().decode() == ""

@@ -1,0 +1,335 @@
+"""GPU parity: every stage of the HIP path against the float64 CPU oracle, through the C ABI.
+
+Small cases span several tiles and ragged tails and finish in seconds on the oracle; the
+full-size configurations are checked on sampled queries in the same launch configuration the
+benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import dsa_oracle as O
+from tests.parity_util import check_attention, check_selection
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    import dsa_sparse_attention_indexer_amd as m
+    return m
+
+
+def _pipe():
+    from dsa_sparse_attention_indexer_amd import pipeline
+    return pipeline
+
+
+def _score_tol(ref):
+    # fp32 / two-term fp16 scores agree with float64 to ~1e-6 of the row's RMS
+    return 2e-6 * math.sqrt(float(np.mean(ref * ref))) + 2e-6 * np.abs(ref)
+
+
+# ---------------------------------------------------------------------------------------------
+# index scores
+# ---------------------------------------------------------------------------------------------
+
+SCORE_CASES = [
+    # name, kwargs for make_workload
+    ("fp32_rope", dict(seq_lens=[3000], max_ctx=3000, fp8=False, q_dtype=torch.float32)),
+    ("fp8_rope_ragged", dict(seq_lens=[700, 2049, 4100, 1], max_ctx=4104)),
+    ("fp8_nope", dict(seq_lens=[1500, 2600], max_ctx=2600, rope=False)),
+    ("fp8_h4", dict(seq_lens=[5000, 333], max_ctx=5000, num_heads=4)),
+    ("fp8_f32q_nossmax", dict(seq_lens=[1025], max_ctx=1028, q_dtype=torch.float32, ssmax=False)),
+    ("f32_bf16q_h7", dict(seq_lens=[900], max_ctx=900, fp8=False, num_heads=7)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_index_scores_match_oracle(dsa, name, kw):
+    wl = workloads.make_workload(name=name, seed=101, **kw)
+    g = wl.to("cuda")
+    buf = _pipe().alloc_buffers(g)
+    _pipe().index_scores(g, buf)
+    torch.cuda.synchronize()
+    sc = buf.scores.cpu().numpy()
+    for t in range(wl.num_q):
+        ref = O.index_scores(wl, t)
+        got = sc[t, :ref.shape[0]].astype(np.float64)
+        err = np.abs(got - ref)
+        assert np.all(err <= _score_tol(ref)), f"{name} q{t}: max err {err.max():.3g} rms {np.sqrt(np.mean(ref**2)):.3g}"
+
+
+def test_index_scores_exact_on_integers(dsa):
+    """Integer q, fp8 keys and weights, unit scales, no RoPE / SSMax: S * 64 is an exact integer."""
+    T, H, L = 2, 32, 700
+    gen = torch.Generator().manual_seed(5)
+    wl = workloads.make_workload(name="int", seed=5, seq_lens=[L, L], max_ctx=L, rope=False, ssmax=False,
+                                 q_dtype=torch.float32)
+    wl.index_q = torch.randint(-3, 4, (T, H, 128), generator=gen).float()
+    wl.index_w = torch.randint(-5, 6, (T, H), generator=gen).float()
+    keys = torch.randint(-8, 9, (2, L, 128), generator=gen).float()
+    wl.index_k = keys.to(torch.float8_e4m3fn).view(torch.uint8)
+    wl.index_k_scale = torch.ones(2, L)
+    g = wl.to("cuda")
+    buf = _pipe().alloc_buffers(g)
+    _pipe().index_scores(g, buf)
+    torch.cuda.synchronize()
+    sc = buf.scores.cpu().numpy().astype(np.float64)
+    q = wl.index_q.numpy().astype(np.int64)
+    w = wl.index_w.numpy().astype(np.int64)
+    k = keys.numpy().astype(np.int64)
+    for t in range(T):
+        dots = q[t] @ k[t].T                                   # exact integers [H][L]
+        exact = (w[t][:, None] * np.maximum(dots, 0)).sum(0)   # = 64 * S, exactly
+        assert np.array_equal(sc[t, :L] * 64.0, exact.astype(np.float64)), f"q{t}"
+        assert np.allclose(O.index_scores(wl, t) * 64.0, exact, rtol=0, atol=1e-9)
+
+
+def test_index_scores_position_zero_and_untouched_tail(dsa):
+    wl = workloads.make_workload(name="p0", seed=7, seq_lens=[1, 300], max_ctx=300)
+    g = wl.to("cuda")
+    buf = _pipe().alloc_buffers(g)
+    buf.scores.fill_(12345.0)
+    _pipe().index_scores(g, buf)
+    torch.cuda.synchronize()
+    sc = buf.scores.cpu().numpy()
+    assert np.all(sc[0, 1:] == 12345.0) and np.all(sc[1, 300:] == 12345.0)
+    ref = O.index_scores(wl, 0)
+    assert abs(sc[0, 0] - ref[0]) <= _score_tol(ref)[0]
+
+
+# ---------------------------------------------------------------------------------------------
+# top-k: bit-exact on the GPU's own fp32 scores
+# ---------------------------------------------------------------------------------------------
+
+def _run_topk(dsa, rows, qpos, k, ld=None):
+    T = len(rows)
+    ld = ld or max(4, (max(len(r) for r in rows) + 3) // 4 * 4)
+    sc = torch.full((T, ld), float("nan"), dtype=torch.float32)
+    for t, r in enumerate(rows):
+        sc[t, :len(r)] = torch.as_tensor(r, dtype=torch.float32)
+    sc = sc.cuda()
+    qp = torch.as_tensor(qpos, dtype=torch.int32).cuda()
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    ln = torch.empty(T, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(sc, qp, k, idx, ln)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), ln.cpu().numpy()
+
+
+TOPK_CASES = [
+    ("random_mixed_lengths", 2048, [5000, 2047, 2048, 2049, 4096, 4097, 12289, 1, 0]),
+    ("small_k", 16, [15, 16, 17, 100, 4095, 4096, 4097, 9000]),
+    ("k1", 1, [1, 2, 5000]),
+    ("big_row", 2048, [131072]),
+]
+
+
+@pytest.mark.parametrize("name,k,lens", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+@pytest.mark.parametrize("dist", ["normal", "ties3", "allequal", "signed_zero"])
+def test_topk_bit_exact(dsa, name, k, lens, dist):
+    rng = np.random.default_rng(len(lens) * 1000 + k)
+    rows = []
+    for n in lens:
+        if dist == "normal":
+            r = rng.standard_normal(n).astype(np.float32)
+        elif dist == "ties3":
+            r = rng.choice(np.array([-1.5, 0.25, 3.0], np.float32), n)
+        elif dist == "allequal":
+            r = np.full(n, 0.5, np.float32)
+        else:
+            r = rng.choice(np.array([-0.0, 0.0, 1.0, -2.0], np.float32), n)
+        rows.append(r)
+    qpos = [n - 1 for n in lens]
+    idx, ln = _run_topk(dsa, rows, qpos, k)
+    for t, r in enumerate(rows):
+        ref, rl = O.topk_row(r.astype(np.float64), k)
+        assert ln[t] == rl, f"{name}/{dist} row {t}: len {ln[t]} != {rl}"
+        assert np.array_equal(idx[t], ref), f"{name}/{dist} row {t} (n={len(r)}): selections differ"
+
+
+def test_topk_heavy_threshold_bin_overflow(dsa):
+    """More than the candidate buffer's worth of keys share the threshold's top bits."""
+    rng = np.random.default_rng(3)
+    n = 60000
+    r = (1.0 + rng.integers(0, 4, n) * 2.0 ** -20).astype(np.float32)    # 4 values in one top-11-bit bin
+    r[rng.choice(n, 100, replace=False)] = 7.0
+    idx, ln = _run_topk(dsa, [r], [n - 1], 2048)
+    ref, _ = O.topk_row(r.astype(np.float64), 2048)
+    assert np.array_equal(idx[0], ref)
+
+
+def test_topk_row_shorter_than_ld_and_deterministic(dsa):
+    rng = np.random.default_rng(11)
+    rows = [rng.standard_normal(9000).astype(np.float32) for _ in range(3)]
+    a, _ = _run_topk(dsa, rows, [8999, 4000, 2100], 2048, ld=9000)
+    b, _ = _run_topk(dsa, rows, [8999, 4000, 2100], 2048, ld=9000)
+    assert np.array_equal(a, b)
+    for t, p in enumerate([8999, 4000, 2100]):
+        ref, _ = O.topk_row(rows[t][:p + 1].astype(np.float64), 2048)
+        assert np.array_equal(a[t], ref)
+
+
+# ---------------------------------------------------------------------------------------------
+# block selection: bit-exact on the GPU's own fp32 scores
+# ---------------------------------------------------------------------------------------------
+
+def test_block_select_bit_exact(dsa):
+    rng = np.random.default_rng(21)
+    lens = [128 * 40 + 17, 128 * 16, 128 * 16 + 1, 1000, 128 * 100]
+    T = len(lens)
+    ld = (max(lens) + 3) // 4 * 4
+    sc = rng.standard_normal((T, ld)).astype(np.float32)
+    sc[0, 128 * 40:] -= 50.0                        # the recent block scores lowest: still kept
+    sc[4, :] = np.round(sc[4, :])                   # many equal block maxima: lower block wins
+    qp = torch.as_tensor([n - 1 for n in lens], dtype=torch.int32).cuda()
+    idx = torch.empty(T, 2048, dtype=torch.int32, device="cuda")
+    ln = torch.empty(T, dtype=torch.int32, device="cuda")
+    dsa.dsa_block_select(torch.from_numpy(sc).cuda(), qp, idx, ln)
+    torch.cuda.synchronize()
+    gi, gl = idx.cpu().numpy(), ln.cpu().numpy()
+    for t, n in enumerate(lens):
+        ref, rl = O.block_select_row(sc[t, :n].astype(np.float64), n - 1)
+        assert gl[t] == rl and np.array_equal(gi[t], ref), f"row {t}"
+
+
+# ---------------------------------------------------------------------------------------------
+# sparse MLA on a given selection
+# ---------------------------------------------------------------------------------------------
+
+MLA_CASES = [
+    ("fp8_rope_decode", dict(seq_lens=[3000, 2500, 900], max_ctx=3000), False, 0),
+    ("fp8_nope_decode", dict(seq_lens=[2600, 2100], max_ctx=2600, rope=False), False, 0),
+    ("fp8_rope_prefill", dict(seq_lens=[2600], max_ctx=2600, q_positions=[2100, 2300, 2599, 100]), True, 0),
+    ("fp8_rope_split3", dict(seq_lens=[4000, 3000], max_ctx=4000), False, 3),
+    ("f32_rope_decode", dict(seq_lens=[2500, 3000], max_ctx=3000, fp8=False, q_dtype=torch.float32), False, 0),
+    ("f32_nope_prefill", dict(seq_lens=[2200], max_ctx=2200, fp8=False, q_dtype=torch.float32, rope=False,
+                              q_positions=[2199, 50]), True, 0),
+]
+
+
+@pytest.mark.parametrize("name,kw,prefill,splits", MLA_CASES, ids=[c[0] for c in MLA_CASES])
+def test_sparse_mla_matches_oracle(dsa, name, kw, prefill, splits):
+    wl = workloads.make_workload(name=name, seed=202, **kw)
+    g = wl.to("cuda")
+    P = _pipe()
+    buf = P.alloc_buffers(g, prefill=prefill, num_splits=splits)
+    P.layer_step(g, buf, prefill=prefill, num_splits=splits)
+    torch.cuda.synchronize()
+    idx, ln = buf.idx.cpu().numpy(), buf.length.cpu().numpy()
+    out, lse = buf.out.cpu().numpy(), buf.lse.cpu().numpy()
+    for t in range(wl.num_q):
+        ro, rl = O.sparse_mla_row(wl, t, idx[t], int(ln[t]))
+        check_attention(out[t], lse[t], ro, rl, wl.fp8, f"{name} q{t}")
+
+
+def test_sparse_mla_ragged_lists_and_empty(dsa):
+    """-1 entries inside a list are skipped; len = 0 gives zeros and -inf."""
+    wl = workloads.make_workload(name="rag", seed=303, seq_lens=[3000, 3000, 3000], max_ctx=3000)
+    rng = np.random.default_rng(0)
+    idx = np.full((3, 2048), -1, np.int32)
+    idx[0, :1500] = np.sort(rng.choice(3000, 1500, replace=False))
+    idx[0, 100:140] = -1
+    idx[1, :77] = np.sort(rng.choice(3000, 77, replace=False))
+    lens = np.array([1500, 77, 0], np.int32)
+    g = wl.to("cuda")
+    for prefill in (False, True):
+        out = torch.empty(3, 64, 512, device="cuda")
+        lse = torch.empty(3, 64, device="cuda")
+        fn = dsa.dsa_sparse_mla_prefill if prefill else dsa.dsa_sparse_mla_decode
+        fn(g.mla_q, g.kv, g.kv_scale, g.q_seq, torch.from_numpy(idx).cuda(), torch.from_numpy(lens).cuda(), out, lse,
+           softmax_scale=wl.softmax_scale)
+        torch.cuda.synchronize()
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+        for t in range(2):
+            sel = idx[t, :lens[t]]
+            ro, rl = O.mla_attend(wl.mla_q[t], O.cache_rows(wl, t, sel[sel >= 0]), 64, wl.softmax_scale)
+            check_attention(o[t], l[t], ro, rl, True, f"prefill={prefill} q{t}")
+        assert np.all(o[2] == 0) and np.all(np.isneginf(l[2]))
+
+
+def test_sparse_equals_dense_when_selection_covers_context(dsa):
+    wl = workloads.make_workload(name="dense", seed=404, seq_lens=[1800, 2048], max_ctx=2048)
+    g = wl.to("cuda")
+    P = _pipe()
+    buf = P.alloc_buffers(g)
+    P.layer_step(g, buf)
+    torch.cuda.synchronize()
+    out, lse = buf.out.cpu().numpy(), buf.lse.cpu().numpy()
+    ln = buf.length.cpu().numpy()
+    for t in range(2):
+        assert ln[t] == int(wl.q_pos[t]) + 1
+        ro, rl = O.dense_mla_row(wl, t)
+        check_attention(out[t], lse[t], ro, rl, True, f"dense q{t}")
+
+
+# ---------------------------------------------------------------------------------------------
+# end to end on small workloads: selection within the band, attention within tolerance
+# ---------------------------------------------------------------------------------------------
+
+E2E_CASES = [
+    ("rope", dict(seq_lens=[9000, 4097, 12000], max_ctx=12000), False),
+    ("nope", dict(seq_lens=[7000, 2049], max_ctx=7000, rope=False), False),
+    ("prefill", dict(seq_lens=[6000], max_ctx=6000, q_positions=[1000, 2047, 2048, 4095, 5999]), False),
+    ("block", dict(seq_lens=[128 * 70 + 5, 128 * 30], max_ctx=128 * 70 + 8, num_heads=4), True),
+]
+
+
+@pytest.mark.parametrize("name,kw,block", E2E_CASES, ids=[c[0] for c in E2E_CASES])
+def test_layer_step_end_to_end(dsa, name, kw, block):
+    wl = workloads.make_workload(name=name, seed=505, **kw)
+    g = wl.to("cuda")
+    P = _pipe()
+    prefill = "q_positions" in kw
+    buf = P.alloc_buffers(g, prefill=prefill, block_sparse=block)
+    P.layer_step(g, buf, prefill=prefill, block_sparse=block)
+    torch.cuda.synchronize()
+    idx, ln = buf.idx.cpu().numpy(), buf.length.cpu().numpy()
+    out, lse = buf.out.cpu().numpy(), buf.lse.cpu().numpy()
+    for t in range(wl.num_q):
+        s = O.index_scores(wl, t)
+        if block:
+            ref, rl = O.block_select_row(s, int(wl.q_pos[t]))
+            assert ln[t] == rl and np.array_equal(idx[t], ref), f"{name} q{t}: block selection differs"
+        else:
+            check_selection(idx[t], ln[t], s, wl.topk, f"{name} q{t}")
+        ro, rl = O.sparse_mla_row(wl, t, idx[t], int(ln[t]))
+        check_attention(out[t], lse[t], ro, rl, True, f"{name} q{t}")
+
+
+def test_shared_indexer_layer_reuses_selection(dsa):
+    a = workloads.make_workload(name="a", seed=606, seq_lens=[5000, 6000], max_ctx=6000)
+    c = workloads.make_workload(name="c", seed=607, seq_lens=[5000, 6000], max_ctx=6000)
+    ga, gc = a.to("cuda"), c.to("cuda")
+    P = _pipe()
+    ba, bc = P.alloc_buffers(ga), P.alloc_buffers(gc)
+    P.layer_step(ga, ba)
+    idx_before = ba.idx.clone()
+    P.layer_step(gc, bc, shared_from=ba)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_before, ba.idx)
+    idx, ln = ba.idx.cpu().numpy(), ba.length.cpu().numpy()
+    out, lse = bc.out.cpu().numpy(), bc.lse.cpu().numpy()
+    for t in range(2):
+        ro, rl = O.sparse_mla_row(c, t, idx[t], int(ln[t]))
+        check_attention(out[t], lse[t], ro, rl, True, f"shared q{t}")
+
+
+def test_repeat_runs_are_bit_identical(dsa):
+    wl = workloads.make_workload(name="rep", seed=707, seq_lens=[20000, 9000], max_ctx=20000)
+    g = wl.to("cuda")
+    P = _pipe()
+    buf = P.alloc_buffers(g)
+    res = []
+    for _ in range(3):
+        P.layer_step(g, buf)
+        torch.cuda.synchronize()
+        res.append((buf.scores.clone(), buf.idx.clone(), buf.out.clone(), buf.lse.clone()))
+    for r in res[1:]:
+        for x, y in zip(res[0], r):
+            assert torch.equal(x, y)
