@@ -45,14 +45,15 @@ class MlaDesc(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m dsa_sparse_attention_indexer_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python dsa_sparse_attention_indexer_amd/build.py` "
                           "(there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_abi_version": (I32, []),
-        "dsa_indexer_scores": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, P]),
+        "dsa_indexer_workspace_size": (SZ, [ctypes.POINTER(IndexerDesc)]),
+        "dsa_indexer_scores": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, P, SZ, P]),
         "dsa_topk_workspace_size": (SZ, [I32, I64, I32]),
         "dsa_topk": (I32, [P, I64, P, I32, I32, P, P, P, SZ, P]),
         "dsa_block_select_workspace_size": (SZ, [I32, I64, I32]),
@@ -62,6 +63,8 @@ def _load():
         "dsa_sparse_mla_prefill": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
+        if not hasattr(lib, name):
+            raise ImportError(f"{LIB_PATH} does not export {name}: it is stale, rebuild it")
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
@@ -71,8 +74,8 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
-            "dsa_block_select_workspace_size", "dsa_block_select", "dsa_sparse_mla_workspace_size",
+EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_workspace_size", "dsa_indexer_scores",
+            "dsa_topk_workspace_size", "dsa_topk", "dsa_block_select_workspace_size", "dsa_block_select", "dsa_sparse_mla_workspace_size",
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill"]
 
 
@@ -120,8 +123,19 @@ def _kdtype(t):
 # 1. indexer scores
 # ------------------------------------------------------------------------------------------------
 
+def dsa_indexer_workspace_size(desc: IndexerDesc) -> int:
+    return int(_lib.dsa_indexer_workspace_size(ctypes.byref(desc)))
+
+
+def indexer_desc(q, k_cache, inv_freq=None) -> IndexerDesc:
+    T, H, D = q.shape
+    B, max_ctx, _ = k_cache.shape
+    rope = 0 if inv_freq is None else 2 * int(inv_freq.numel())
+    return IndexerDesc(T, H, D, rope, B, max_ctx, _qdtype(q), _kdtype(k_cache))
+
+
 def dsa_indexer_scores(q, w, q_seq, q_pos, k_cache, scores, k_scale=None, ssmax_s=None, ssmax_b=None,
-                       inv_freq=None, stream=None):
+                       inv_freq=None, ws=None, stream=None):
     """Fills scores[t, 0..q_pos[t]] with the lightning-indexer score of every visible key.
 
     q [T][H][128] f32|bf16, w [T][H] f32, q_seq/q_pos [T] i32, k_cache [B][max_ctx][128] f32 or
@@ -142,11 +156,13 @@ def dsa_indexer_scores(q, w, q_seq, q_pos, k_cache, scores, k_scale=None, ssmax_
     _dev("scores", scores, torch.float32)
     if scores.dim() != 2 or scores.shape[0] != T:
         raise ValueError("scores must be [T][ld]")
-    rope = 0 if inv_freq is None else 2 * int(inv_freq.numel())
-    d = IndexerDesc(T, H, D, rope, B, max_ctx, _qdtype(q), _kdtype(k_cache))
+    d = indexer_desc(q, k_cache, inv_freq)
+    if ws is None:
+        ws = torch.empty(max(16, dsa_indexer_workspace_size(d)), dtype=torch.uint8, device=q.device)
+    _dev("ws", ws, torch.uint8)
     _check(_lib.dsa_indexer_scores(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
                                    _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores),
-                                   scores.shape[1], _stream(stream)))
+                                   scores.shape[1], _ptr(ws), ws.numel(), _stream(stream)))
     return scores
 
 

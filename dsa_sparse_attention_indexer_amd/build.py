@@ -1,6 +1,7 @@
 """Builds libdsa.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m dsa_sparse_attention_indexer_amd.build
+Usage: python dsa_sparse_attention_indexer_amd/build.py
+(run as a file: importing the package itself loads the library this script builds)
 """
 from __future__ import annotations
 

@@ -50,11 +50,16 @@ const char* dsa_last_error(void) { return g_err.c_str(); }
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
 
+size_t dsa_indexer_workspace_size(const dsa_indexer_desc_t* d) {
+  if (!d || d->num_q <= 0) return 0;
+  return dsa::indexer_ws_bytes(d->num_q);
+}
+
 dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* d, const void* q, const float* w,
                                 const int32_t* q_seq, const int32_t* q_pos,
                                 const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                                 const void* k_cache, const float* k_scale,
-                                float* scores, int64_t ld_scores, void* stream) {
+                                float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, void* stream) {
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_scores"); }
   ck.need(d->num_q >= 0 && d->num_q <= 65535, "num_q must be in [0, 65535]");
@@ -73,12 +78,14 @@ dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* d, const void* q, cons
     ck.need(d->k_dtype != DSA_FP8_E4M3FN || k_scale != nullptr, "k_scale is required for FP8 keys");
     ck.need(aligned(k_cache, 16), "k_cache must be 16-byte aligned");
     ck.need(aligned(q, d->q_dtype == DSA_BF16 ? 2 : 4), "q must be aligned to its element size");
+    ck.need(ws != nullptr && ws_bytes >= dsa_indexer_workspace_size(d) && aligned(ws, 16),
+            "workspace missing, misaligned or smaller than dsa_indexer_workspace_size()");
   }
   dsa_status_t st = ck.finish("dsa_indexer_scores");
   if (st != DSA_OK || d->num_q == 0) return st;
   dsa::IndexerLaunch a{d->num_q, d->num_heads, d->rope_dim, d->num_seqs, d->max_ctx, d->q_dtype, d->k_dtype,
                        q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores};
-  return hip_status("dsa_indexer_scores", dsa::launch_indexer(a, (hipStream_t)stream));
+  return hip_status("dsa_indexer_scores", dsa::launch_indexer(a, ws, (hipStream_t)stream));
 }
 
 size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k) {

@@ -72,11 +72,12 @@ constexpr int64_t kTopkMaxCols = int64_t(1) << 22;
 constexpr int kTopkMaxSegs = int(kTopkMaxCols / kTopkSeg);
 
 size_t topk_row_bytes(int64_t ld);
+size_t indexer_ws_bytes(int T);
 size_t block_select_ws_bytes(int T, int64_t ld, int block);
 
 // ---- launchers (return the HIP status of the last launch) -----------------------------------
 
-hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
+hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s);

@@ -17,8 +17,8 @@
 //    the wave are summed with v_permlane32_swap, and lanes 0..31 store 32 consecutive scores.
 //  * fp32 keys (the reference-precision path): one thread per key, fp32 FMAs against q' in LDS.
 //
-// Query prep (RoPE angles formed and evaluated in float64, SSMax in float64) happens inside each
-// workgroup; the first key tile is already in flight while it runs.
+// Query prep (RoPE angles formed and evaluated in float64, SSMax in float64) runs once per query in
+// its own small kernel, which writes the prepared operands to the caller's workspace.
 
 #include "dsa_internal.h"
 
@@ -94,61 +94,42 @@ __device__ void prep_query(PrepSmem& sm, const IndexerLaunch& a, int t, int p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// fp8 keys: MFMA stream
+// Query prep: one workgroup per query writes the prepared query to the workspace
 // ------------------------------------------------------------------------------------------
-
-__device__ __forceinline__ half8 fp8x8_to_half8(uint32_t d0, uint32_t d1) {
-  half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
-  half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
-  half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
-  half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
-  half8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-struct KeyTile {
-  u32x4 x[4];   // 64 bytes of this lane's key row: bytes [32c + 16g, +16) for c = 0..3
-  float sc;     // the row's fp8 scale
+// Per-query workspace record.  fp8 keys: the MFMA A operands of every lane of a wave
+// (j = 2*s + term, term 0 = hi, 1 = lo) and each lane's 16 accumulator-row weights.
+// fp32 keys: q' as fp32 [32][128] and the 32 head weights.
+struct QPrepFp8 {
+  u32x4 a[16][64];
+  float cf[16][64];
 };
+struct QPrepF32 {
+  float q[kHPad][kD];
+  float coef[kHPad];
+};
+constexpr size_t kQPrepBytes = sizeof(QPrepFp8) > sizeof(QPrepF32) ? sizeof(QPrepFp8) : sizeof(QPrepF32);
 
-__device__ __forceinline__ void load_tile(KeyTile& kt, const uint8_t* kseq, const float* sseq,
-                                          int row, int g) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(kseq + (size_t)row * kD + 16 * g);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) kt.x[c] = __builtin_nontemporal_load(p + 2 * c);
-  kt.sc = sseq[row];
+__device__ __forceinline__ uint32_t pack_half2(_Float16 lo, _Float16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
-__global__ void __launch_bounds__(kThreads)
-k_index_scores_fp8(IndexerLaunch a, int chunk) {
+__global__ void __launch_bounds__(kThreads) k_index_qprep(IndexerLaunch a, void* ws) {
   __shared__ PrepSmem sm;
-  const int t = blockIdx.y;
+  const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, col = lane & 31;
-
-  const int b = clampi(a.q_seq[t], 0, a.B - 1);
   const int p = clampi(a.q_pos[t], -1, a.max_ctx - 1);
-  const int n = p + 1;
-  const int c0 = blockIdx.x * chunk;
-  if (c0 >= n) return;
-  const int c1 = min(n, c0 + chunk);
-
-  const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)b * a.max_ctx * kD;
-  const float* sseq = a.k_scale + (size_t)b * a.max_ctx;
-  float* srow = a.scores + (size_t)t * a.ld;
-
-  // First tile of this wave goes out before the query prep.
-  int kb = c0 + wave * kTile;
-  KeyTile cur;
-  load_tile(cur, kseq, sseq, min(kb + col, n - 1), g);
-
-  prep_query(sm, a, t, p);
-
+  prep_query(sm, a, t, p < 0 ? 0 : p);
+  uint8_t* rec = reinterpret_cast<uint8_t*>(ws) + (size_t)t * kQPrepBytes;
+  const double inv_norm = 1.0 / (sqrt((double)a.H) * sqrt((double)kD));
+  if (a.k_dtype != DSA_FP8_E4M3FN) {
+    QPrepF32* o = reinterpret_cast<QPrepF32*>(rec);
+    for (int e = tid; e < kHPad * kD; e += kThreads) o->q[e / kD][e % kD] = (float)sm.qs[e / kD][e % kD];
+    if (tid < kHPad) o->coef[tid] = tid < a.H ? (float)((double)a.w[(size_t)t * a.H + tid] * inv_norm) : 0.f;
+    return;
+  }
   // Per-head power-of-two scale: max|q'_h| * 2^e_h in [2^14, 2^15) keeps both fp16 terms normal.
   {
     const int h = tid >> 3, part = tid & 7;   // 32 heads x 8 lanes
@@ -165,58 +146,157 @@ k_index_scores_fp8(IndexerLaunch a, int chunk) {
         e = 15 - x;
       }
       sm.ex[h] = e;
-      double wv = 0.0;
-      if (h < a.H) wv = (double)a.w[(size_t)t * a.H + h] / (sqrt((double)a.H) * sqrt((double)kD));
+      const double wv = h < a.H ? (double)a.w[(size_t)t * a.H + h] * inv_norm : 0.0;
       sm.coef[h] = (float)ldexp(wv, -e);
     }
   }
   __syncthreads();
-
-  // A operands: lane (row m = col, half g); K-step s covers dims [32(s>>1) + 16g + 8(s&1), +8).
-  half8 ahi[8], alo[8];
+  QPrepFp8* o = reinterpret_cast<QPrepFp8*>(rec);
+  // A operand of lane l (row m = l & 31, half g = l >> 5) for K-step s: q'[m][32(s>>1) + 16g + 8(s&1) + i]
   {
-    const int e = sm.ex[col];
+    const int l = tid & 63, sg = tid >> 6;
+    const int m = l & 31, g = l >> 5;
+    const int e = sm.ex[m];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int ss = 0; ss < 2; ++ss) {
+      const int s = 2 * sg + ss;
       const int base = 32 * (s >> 1) + 16 * g + 8 * (s & 1);
+      _Float16 hi[8], lo[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const double v = ldexp(sm.qs[col][base + i], e);
-        const _Float16 hi = (_Float16)v;
-        ahi[s][i] = hi;
-        alo[s][i] = (_Float16)(v - (double)hi);
+        const double v = ldexp(sm.qs[m][base + i], e);
+        hi[i] = (_Float16)(float)v;                        // |v| < 2^15: normal, exact residual below
+        lo[i] = (_Float16)(float)(v - (double)(float)hi[i]);
       }
+      u32x4 h4, l4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h4[i] = pack_half2(hi[2 * i], hi[2 * i + 1]);
+        l4[i] = pack_half2(lo[2 * i], lo[2 * i + 1]);
+      }
+      o->a[2 * s][l] = h4;
+      o->a[2 * s + 1][l] = l4;
     }
   }
-  // Accumulator row r of this lane is head 8(r>>2) + 4g + (r&3).
+  if (tid < 64) {
+    const int g = tid >> 5;
+    // accumulator row r of a lane in half g is head 8(r>>2) + 4g + (r&3)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o->cf[r][tid] = sm.coef[8 * (r >> 2) + 4 * g + (r & 3)];
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// fp8 keys: MFMA stream
+// ------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ half8 fp8x8_to_half8(uint32_t d0, uint32_t d1) {
+  half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+  half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+  half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+  half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+  half8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+struct KeyTile {
+  u32x4 x[4];   // 64 bytes of this lane's key row: bytes [32c + 16g, +16) for c = 0..3
+  float sc;     // the row's fp8 scale
+};
+
+// Buffer resource (gfx9 raw buffer, no swizzle) over `bytes` bytes from `base`.  Accesses at or past
+// `bytes` are dropped by the hardware (loads return 0, stores do nothing), which keeps tail
+// handling free of branches -- and the compiler's wait counts static.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void load_tile(KeyTile& kt, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t srs,
+                                          uint32_t rel_row, int g) {
+  const uint32_t off = rel_row * kD + 16u * g;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    kt.x[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 32u * c, 0, 0));
+  kt.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, rel_row * 4u, 0, 0));
+}
+
+// One 32-key tile: 16 MFMAs (8 K-steps x hi/lo), ReLU + head weights, halves summed across the wave.
+__device__ __forceinline__ float tile_scores(const KeyTile& kt, const half8* ahi, const half8* alo, const float* cf) {
+  float16v acc = {};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const half8 b0 = fp8x8_to_half8(kt.x[c][0], kt.x[c][1]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[2 * c], b0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[2 * c], b0, acc, 0, 0, 0);
+    const half8 b1 = fp8x8_to_half8(kt.x[c][2], kt.x[c][3]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[2 * c + 1], b1, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[2 * c + 1], b1, acc, 0, 0, 0);
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part = fmaf(cf[r], fmaxf(acc[r], 0.f), part);
+  // lanes l and l^32 hold the two halves of key column l&31's head sum
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+  return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * kt.sc;
+}
+
+template <int TPW>   // 32-key tiles per wave; a workgroup covers 4 * 32 * TPW keys
+__global__ void __launch_bounds__(kThreads)
+k_index_scores_fp8(IndexerLaunch a, const void* ws) {
+  constexpr int chunk = 4 * kTile * TPW;
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar) loop control
+  const int g = lane >> 5, col = lane & 31;
+  const int b = clampi(a.q_seq[t], 0, a.B - 1);
+  const int p = clampi(a.q_pos[t], -1, a.max_ctx - 1);
+  const int n = p + 1;
+  const int c0 = blockIdx.x * chunk;
+  if (c0 >= n) return;
+  const int c1 = min(n, c0 + chunk);
+  const uint32_t nrow = (uint32_t)(c1 - c0);
+  const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.k_cache) + ((size_t)b * a.max_ctx + c0) * kD;
+  const float* sseq = a.k_scale + (size_t)b * a.max_ctx + c0;
+  float* srow = a.scores + (size_t)t * a.ld + c0;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kseq, nrow * kD);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(sseq, nrow * 4u);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(srow, nrow * 4u);
+  constexpr uint32_t kStride = 4 * kTile;   // the 4 waves interleave 32-key tiles
+
+  // Prepared query first (L2-resident), then three key tiles in flight per wave.  The loop is
+  // unrolled three ways so the tile buffers rotate by name: a buffer is refilled right after it is
+  // consumed and the two younger loads stay outstanding across the MFMAs.
+  const QPrepFp8* qp = reinterpret_cast<const QPrepFp8*>(reinterpret_cast<const uint8_t*>(ws) + (size_t)t * kQPrepBytes);
+  half8 ahi[8], alo[8];
   float cf[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) cf[r] = sm.coef[8 * (r >> 2) + 4 * g + (r & 3)];
-
-  for (; kb < c1; kb += 4 * kTile) {
-    const int nkb = kb + 4 * kTile;
-    KeyTile nxt;
-    if (nkb < c1) load_tile(nxt, kseq, sseq, min(nkb + col, n - 1), g);
-
-    float16v acc = {};
+  for (int s = 0; s < 8; ++s) {
+    ahi[s] = __builtin_bit_cast(half8, qp->a[2 * s][lane]);
+    alo[s] = __builtin_bit_cast(half8, qp->a[2 * s + 1][lane]);
+  }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const half8 b0 = fp8x8_to_half8(cur.x[c][0], cur.x[c][1]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[2 * c], b0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[2 * c], b0, acc, 0, 0, 0);
-      const half8 b1 = fp8x8_to_half8(cur.x[c][2], cur.x[c][3]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[2 * c + 1], b1, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[2 * c + 1], b1, acc, 0, 0, 0);
-    }
-    float part = 0.f;
+  for (int r = 0; r < 16; ++r) cf[r] = qp->cf[r][lane];
+
+  // rel: this wave's current tile, relative to the chunk start (rows past the chunk read as zero)
+  uint32_t rel = wave * kTile;
+  KeyTile tb[3];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part = fmaf(cf[r], fmaxf(acc[r], 0.f), part);
-    // lanes l and l^32 hold the two halves of key column l&31's head sum
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int row = kb + col;
-    if (g == 0 && row < c1) srow[row] = tot * cur.sc;
-    if (nkb < c1) cur = nxt;
+  for (int i = 0; i < 3; ++i) load_tile(tb[i], krs, srs, rel + i * kStride + col, g);
+  // only lanes 0..31 store (lanes 32..63 hold the same columns); the others aim past the range
+  const uint32_t out_off = g == 0 ? 4u * col : 0x80000000u;
+
+  // Fully unrolled: straight-line code gives the compiler exact wait counts, so two tiles stay in
+  // flight behind the one being multiplied.  Past the chunk the loads read zeros and the stores
+  // are dropped, so there is no per-tile guard.
+#pragma unroll
+  for (int it = 0; it < TPW; ++it) {
+    KeyTile& cur = tb[it % 3];
+    const float sc = tile_scores(cur, ahi, alo, cf);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
+    if (it + 3 < TPW) load_tile(cur, krs, srs, rel + 3 * kStride + col, g);
+    rel += kStride;
   }
 }
 
@@ -225,9 +305,9 @@ k_index_scores_fp8(IndexerLaunch a, int chunk) {
 // ------------------------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(kThreads)
-k_index_scores_f32(IndexerLaunch a) {
-  __shared__ PrepSmem sm;
+k_index_scores_f32(IndexerLaunch a, const void* ws) {
   __shared__ float qf[kHPad][kD];
+  __shared__ float coef[kHPad];
   const int t = blockIdx.y;
   const int tid = threadIdx.x;
   const int b = clampi(a.q_seq[t], 0, a.B - 1);
@@ -235,13 +315,9 @@ k_index_scores_f32(IndexerLaunch a) {
   const int n = p + 1;
   const int c0 = blockIdx.x * kThreads;
   if (c0 >= n) return;
-  prep_query(sm, a, t, p);
-  for (int e = tid; e < kHPad * kD; e += kThreads) qf[e / kD][e % kD] = (float)sm.qs[e / kD][e % kD];
-  if (tid < kHPad) {
-    double wv = 0.0;
-    if (tid < a.H) wv = (double)a.w[(size_t)t * a.H + tid] / (sqrt((double)a.H) * sqrt((double)kD));
-    sm.coef[tid] = (float)wv;
-  }
+  const QPrepF32* qp = reinterpret_cast<const QPrepF32*>(reinterpret_cast<const uint8_t*>(ws) + (size_t)t * kQPrepBytes);
+  for (int e = tid; e < kHPad * kD; e += kThreads) qf[e / kD][e % kD] = qp->q[e / kD][e % kD];
+  if (tid < kHPad) coef[tid] = qp->coef[tid];
   __syncthreads();
   const int row = c0 + tid;
   if (row >= n) return;
@@ -262,23 +338,30 @@ k_index_scores_f32(IndexerLaunch a) {
   }
   float s = 0.f;
 #pragma unroll
-  for (int h = 0; h < kHPad; ++h) s = fmaf(sm.coef[h], fmaxf(acc[h], 0.f), s);
+  for (int h = 0; h < kHPad; ++h) s = fmaf(coef[h], fmaxf(acc[h], 0.f), s);
   a.scores[(size_t)t * a.ld + row] = s;
 }
 
 }  // namespace
 
-hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s) {
+size_t indexer_ws_bytes(int T) { return (size_t)T * kQPrepBytes; }
+
+hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
   if (a.T == 0 || a.max_ctx == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_index_qprep, dim3(a.T), dim3(kThreads), 0, s, a, ws);
   if (a.k_dtype == DSA_FP8_E4M3FN) {
-    // ~2K workgroups over the largest context; chunks are multiples of the 4-wave tile stride.
-    int chunk = 1024;
-    while (chunk > 128 && (int64_t)a.T * ((a.max_ctx + chunk - 1) / chunk) < 2048) chunk /= 2;
-    dim3 grid((a.max_ctx + chunk - 1) / chunk, a.T);
-    hipLaunchKernelGGL(k_index_scores_fp8, grid, dim3(kThreads), 0, s, a, chunk);
+    // 4096-key chunks (32 tiles per wave) when that still gives >= 512 workgroups, else 1024.
+    const int64_t big = (int64_t)a.T * ((a.max_ctx + 4095) / 4096);
+    if (big >= 512) {
+      dim3 grid((a.max_ctx + 4095) / 4096, a.T);
+      hipLaunchKernelGGL(k_index_scores_fp8<32>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
+    } else {
+      dim3 grid((a.max_ctx + 1023) / 1024, a.T);
+      hipLaunchKernelGGL(k_index_scores_fp8<8>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
+    }
   } else {
     dim3 grid((a.max_ctx + kThreads - 1) / kThreads, a.T);
-    hipLaunchKernelGGL(k_index_scores_f32, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(k_index_scores_f32, grid, dim3(kThreads), 0, s, a, (const void*)ws);
   }
   return hipGetLastError();
 }

@@ -4,15 +4,18 @@
 // the same with zero RoPE dims on the same cache layout).
 //
 // fp8 cache, bf16 query (matrix-core path), one workgroup = 4 waves = up to 64 heads:
-//   * 32-key tiles are gathered by row index into LDS as raw fp8 bytes plus their per-64 scales,
-//     then dequantised once per workgroup to bf16 (code * scale, rounded to nearest even) in two
-//     layouts: key-major rows for Q.K^T and a dim-major transpose for P.V.
+//   * 32-key tiles are gathered by row index straight from HBM into registers (16 bytes per lane,
+//     issued one tile ahead of the compute), dequantised once per workgroup to bf16 (code * scale,
+//     v_cvt_pk_f32_fp8 / v_cvt_pk_bf16_f32, round to nearest even) and stored key-major in LDS.
 //   * wave w owns heads 16w..16w+15.  Its bf16 query stays in registers as the B operand of
 //     v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, keys as M).  The key rows are placed in LDS in an
 //     order that makes the S^T accumulator of each lane hold exactly the 8 consecutive keys that
 //     the P.V step needs in its B operand, so probabilities go from accumulators to MFMA operands
 //     without touching LDS.
-//   * online softmax in the log2 domain with fp32 statistics; O^T = V^T P^T accumulates in fp32.
+//   * P.V (O^T = V^T P^T) reads its V^T operand from the same key-major tile with
+//     ds_read_b64_tr_b16: a 16-lane group that points lane j at row 4*(j/4)+.., dims 4*(j%4)..+3
+//     gets back, per lane, four consecutive keys of one dim -- the MFMA operand layout.
+//   * online softmax in the log2 domain with fp32 statistics; fp32 accumulation.
 // fp32 cache, fp32 query: the same tiling with fp32 vector FMAs (8 lanes per head).
 //
 // Decode splits a query's selection over `splits` workgroups; each writes an unnormalised partial
@@ -28,6 +31,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int kTileK = 32;
@@ -35,18 +39,8 @@ constexpr int kRow = 576;                 // latent row: 512 + 64
 constexpr int kLora = 512;
 constexpr int kBlocks = kRow / 64;        // scales per row
 constexpr int kKsStride = kRow + 8;       // bf16 per key-major row (1168 B: rows shift by 4 banks)
-constexpr int kVtStride = kTileK + 8;     // bf16 per dim-major row (80 B)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-struct Fp8Smem {
-  uint8_t raw[kTileK][kRow];
-  float sc[kTileK][kBlocks];
-  int row[kTileK];
-  int valid[kTileK];
-  uint16_t ks[kTileK][kKsStride];
-  uint16_t vt[kLora][kVtStride];
-};
 
 // Key kappa (0..31) of a tile lives in key-major LDS row 16*((kappa>>2)&1) + 4*(kappa>>3) + (kappa&3).
 __device__ __forceinline__ int ks_row_of_key(int kappa) {
@@ -84,12 +78,36 @@ __device__ __forceinline__ void write_stats(const MlaLaunch& a, int t, int split
   }
 }
 
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt2_bf16(float2v v) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// 16 fp8 codes times one scale -> 16 bf16 (8 dwords), nearest even.
+__device__ __forceinline__ void dequant16(const u32x4 raw, float s, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float2v a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[w], false) * s;
+    const float2v b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[w], true) * s;
+    const uint32_t pa = cvt2_bf16(a), pb = cvt2_bf16(b);
+    if (w < 2) { lo[2 * w] = pa; lo[2 * w + 1] = pb; } else { hi[2 * w - 4] = pa; hi[2 * w - 3] = pb; }
+  }
+}
+
 template <int ROPE>
 __global__ void __launch_bounds__(kThreads)
 k_mla_fp8(MlaLaunch a) {
   constexpr int DQ = kLora + ROPE;
   constexpr int KSTEPS = DQ / 32;
-  __shared__ Fp8Smem sm;
+  constexpr int CHUNKS = DQ / 16;                     // 16-byte chunks of a row that are used
+  constexpr int NCH = kTileK * CHUNKS;
+  constexpr int PER = (NCH + kThreads - 1) / kThreads;
+  __shared__ uint16_t ks[kTileK][kKsStride];
+  __shared__ int srow[2][kTileK];
+  __shared__ int svalid[2][kTileK];
   const int t = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -100,6 +118,29 @@ k_mla_fp8(MlaLaunch a) {
   const bool active = 16 * wave < a.H;
   const int head = 16 * wave + c;
   const float zscale = a.softmax_scale * kLog2e;
+  const int32_t* irow = a.idx + (size_t)t * a.topk;
+  const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(a.kv) + (size_t)b * a.max_ctx * kRow;
+  const float* scseq = a.kv_scale + (size_t)b * a.max_ctx * kBlocks;
+
+  auto fetch_idx = [&](int tile_base) -> int {   // row of slot tile_base + tid (tid < 32), -1 if none
+    const int slot = tile_base + tid;
+    const int r = slot < slot1 ? irow[slot] : -1;
+    return (r >= 0 && r < a.max_ctx) ? r : -1;
+  };
+  u32x4 raw[PER];
+  float rsc[PER];
+  auto issue_loads = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int ch = tid + kThreads * m;
+      if (ch < NCH) {
+        const int r = ch / CHUNKS, cc = ch % CHUNKS;
+        const int row = srow[buf][r];
+        raw[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kvseq + (size_t)row * kRow) + cc);
+        rsc[m] = scseq[(size_t)row * kBlocks + (cc >> 2)];
+      }
+    }
+  };
 
   bf16x8 qreg[KSTEPS];
   if (active) {
@@ -113,64 +154,51 @@ k_mla_fp8(MlaLaunch a) {
 #pragma unroll
   for (int md = 0; md < kLora / 16; ++md) oacc[md] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* irow = a.idx + (size_t)t * a.topk;
-  const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(a.kv) + (size_t)b * a.max_ctx * kRow;
-  const float* scseq = a.kv_scale + (size_t)b * a.max_ctx * kBlocks;
-
-  for (int tb = slot0; tb < slot1; tb += kTileK) {
+  // prologue: rows of tile 0 -> LDS, its data in flight, rows of tile 1 in a register
+  if (slot0 < slot1) {
     if (tid < kTileK) {
-      const int slot = tb + tid;
-      const int r = slot < slot1 ? irow[slot] : -1;
-      const bool ok = r >= 0 && r < a.max_ctx;
-      sm.valid[tid] = ok;
-      sm.row[tid] = ok ? r : 0;
+      const int r = fetch_idx(slot0);
+      srow[0][tid] = r < 0 ? 0 : r;
+      svalid[0][tid] = r >= 0;
     }
     __syncthreads();
-    for (int ch = tid; ch < kTileK * (kRow / 16); ch += kThreads) {
-      const int r = ch / (kRow / 16), cc = ch % (kRow / 16);
-      const u32x4 v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(kvseq + (size_t)sm.row[r] * kRow) + cc);
-      *reinterpret_cast<u32x4*>(&sm.raw[r][16 * cc]) = v;
-    }
-    for (int e = tid; e < kTileK * kBlocks; e += kThreads) {
-      const int r = e / kBlocks, blk = e % kBlocks;
-      sm.sc[r][blk] = scseq[(size_t)sm.row[r] * kBlocks + blk];
-    }
-    __syncthreads();
-    // key-major bf16 rows (Q.K^T operand)
-    for (int it = tid; it < kTileK * (DQ / 8); it += kThreads) {
-      const int r = it / (DQ / 8), grp = it % (DQ / 8);
-      const uint2 raw8 = *reinterpret_cast<const uint2*>(&sm.raw[r][8 * grp]);
-      const float s = sm.sc[r][grp >> 3];
-      u32x4 pk;
-      pk[0] = pack2(__builtin_amdgcn_cvt_f32_fp8(raw8.x, 0) * s, __builtin_amdgcn_cvt_f32_fp8(raw8.x, 1) * s);
-      pk[1] = pack2(__builtin_amdgcn_cvt_f32_fp8(raw8.x, 2) * s, __builtin_amdgcn_cvt_f32_fp8(raw8.x, 3) * s);
-      pk[2] = pack2(__builtin_amdgcn_cvt_f32_fp8(raw8.y, 0) * s, __builtin_amdgcn_cvt_f32_fp8(raw8.y, 1) * s);
-      pk[3] = pack2(__builtin_amdgcn_cvt_f32_fp8(raw8.y, 2) * s, __builtin_amdgcn_cvt_f32_fp8(raw8.y, 3) * s);
-      *reinterpret_cast<u32x4*>(&sm.ks[ks_row_of_key(r)][8 * grp]) = pk;
-    }
-    // dim-major bf16 transpose of the latent part (P.V operand)
-    for (int it = tid; it < kLora * (kTileK / 8); it += kThreads) {
-      const int d = it % kLora, oct = it / kLora;
-      float v[8];
+    issue_loads(0);
+  }
+  int next_row = -1;
+  if (tid < kTileK && slot0 + kTileK < slot1) next_row = fetch_idx(slot0 + kTileK);
+
+  int cur = 0;
+  for (int tb = slot0; tb < slot1; tb += kTileK, cur ^= 1) {
+    __syncthreads();                       // the previous tile's readers of ks are done
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int r = 8 * oct + kk;
-        v[kk] = __builtin_amdgcn_cvt_f32_fp8((uint32_t)sm.raw[r][d], 0) * sm.sc[r][d >> 6];
+    for (int m = 0; m < PER; ++m) {
+      const int ch = tid + kThreads * m;
+      if (ch < NCH) {
+        const int r = ch / CHUNKS, cc = ch % CHUNKS;
+        u32x4 lo, hi;
+        dequant16(raw[m], rsc[m], lo, hi);
+        uint16_t* dst = &ks[ks_row_of_key(r)][16 * cc];
+        *reinterpret_cast<u32x4*>(dst) = lo;
+        *reinterpret_cast<u32x4*>(dst + 8) = hi;
       }
-      u32x4 pk;
-      pk[0] = pack2(v[0], v[1]); pk[1] = pack2(v[2], v[3]);
-      pk[2] = pack2(v[4], v[5]); pk[3] = pack2(v[6], v[7]);
-      *reinterpret_cast<u32x4*>(&sm.vt[d][8 * oct]) = pk;
     }
-    __syncthreads();
+    const bool more = tb + kTileK < slot1;
+    if (tid < kTileK && more) {
+      srow[cur ^ 1][tid] = next_row < 0 ? 0 : next_row;
+      svalid[cur ^ 1][tid] = next_row >= 0;
+    }
+    __syncthreads();                       // ks and the next tile's rows are ready
+    if (more) {
+      issue_loads(cur ^ 1);
+      if (tid < kTileK) next_row = tb + 2 * kTileK < slot1 ? fetch_idx(tb + 2 * kTileK) : -1;
+    }
     if (active) {
       float4v sacc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.ks[16 * mb + c][32 * s + 8 * g]));
+          const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&ks[16 * mb + c][32 * s + 8 * g]));
           sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[s], sacc[mb], 0, 0, 0);
         }
       }
@@ -182,7 +210,7 @@ k_mla_fp8(MlaLaunch a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kappa = 8 * g + 4 * mb + i;
-          const float v = sm.valid[kappa] ? sacc[mb][i] * zscale : -INFINITY;
+          const float v = svalid[cur][kappa] ? sacc[mb][i] * zscale : -INFINITY;
           z[4 * mb + i] = v;
           tmax = fmaxf(tmax, v);
         }
@@ -209,16 +237,20 @@ k_mla_fp8(MlaLaunch a) {
         for (int md = 0; md < kLora / 16; ++md) oacc[md] *= alpha;
       }
       u32x4 pk;
-      pk[0] = pack2(p[0], p[1]); pk[1] = pack2(p[2], p[3]);
-      pk[2] = pack2(p[4], p[5]); pk[3] = pack2(p[6], p[7]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = cvt2_bf16(float2v{p[2 * e], p[2 * e + 1]});
       const bf16x8 pop = __builtin_bit_cast(bf16x8, pk);
+      // V^T operand rows: LDS rows 16h + 4g + j/4 hold keys 8g + 4h + j/4
+      const int trow = 4 * g + (c >> 2), tcol = 4 * (c & 3);
 #pragma unroll
       for (int md = 0; md < kLora / 16; ++md) {
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.vt[16 * md + c][8 * g]));
-        oacc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, oacc[md], 0, 0, 0);
+        typedef __attribute__((address_space(3))) short4v* lds_s4p;
+        const short4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(&ks[trow][16 * md + tcol]));
+        const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(&ks[16 + trow][16 * md + tcol]));
+        const short8v vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pop, oacc[md], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
   if (!active) return;
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -334,36 +366,41 @@ k_mla_f32(MlaLaunch a) {
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s;  lse = ln2 (M + log2 L).
+// One workgroup per (query, 4 heads).
+constexpr int kCombineHeads = 4;
+
 __global__ void __launch_bounds__(kThreads) k_mla_combine(MlaLaunch a) {
-  __shared__ float wts[128][65];
-  const int t = blockIdx.x;
+  __shared__ float wts[kCombineHeads][64];
+  const int t = blockIdx.y, h0 = blockIdx.x * kCombineHeads;
   const float* stats = a.ws + (size_t)a.T * a.splits * a.H * a.kv_lora;
-  for (int h = threadIdx.x; h < a.H; h += kThreads) {
+  if (threadIdx.x < kCombineHeads && h0 + threadIdx.x < a.H) {
+    const int h = h0 + threadIdx.x;
     float M = -INFINITY;
     for (int s = 0; s < a.splits; ++s) M = fmaxf(M, stats[2 * (((size_t)t * a.splits + s) * a.H + h)]);
     float Ls = 0.f;
     for (int s = 0; s < a.splits; ++s) {
       const size_t i = ((size_t)t * a.splits + s) * a.H + h;
       const float w = (M == -INFINITY) ? 0.f : exp2f(stats[2 * i] - M);
-      wts[h][s] = w;
+      wts[threadIdx.x][s] = w;
       Ls += w * stats[2 * i + 1];
     }
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    for (int s = 0; s < a.splits; ++s) wts[h][s] *= inv;
+    for (int s = 0; s < a.splits; ++s) wts[threadIdx.x][s] *= inv;
     if (a.lse) a.lse[(size_t)t * a.H + h] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  const int n4 = a.H * a.kv_lora / 4;
+  const int nh = min(kCombineHeads, a.H - h0);
+  const int n4 = nh * a.kv_lora / 4;
   for (int e = threadIdx.x; e < n4; e += kThreads) {
-    const int h = (4 * e) / a.kv_lora;
+    const int hl = (4 * e) / a.kv_lora;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < a.splits; ++s) {
-      const float w = wts[h][s];
-      const float4 v = reinterpret_cast<const float4*>(a.ws + (((size_t)t * a.splits + s) * a.H) * a.kv_lora)[e];
+      const float w = wts[hl][s];
+      const float4 v = reinterpret_cast<const float4*>(a.ws + (((size_t)t * a.splits + s) * a.H + h0) * a.kv_lora)[e];
       acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
       acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
     }
-    reinterpret_cast<float4*>(a.out + (size_t)t * a.H * a.kv_lora)[e] = acc;
+    reinterpret_cast<float4*>(a.out + ((size_t)t * a.H + h0) * a.kv_lora)[e] = acc;
   }
 }
 
@@ -379,7 +416,8 @@ hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s) {
     if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_f32<64>, grid, dim3(kF32Threads), 0, s, a);
     else hipLaunchKernelGGL(k_mla_f32<0>, grid, dim3(kF32Threads), 0, s, a);
   }
-  if (a.splits > 1) hipLaunchKernelGGL(k_mla_combine, dim3(a.T), dim3(kThreads), 0, s, a);
+  if (a.splits > 1)
+    hipLaunchKernelGGL(k_mla_combine, dim3((a.H + kCombineHeads - 1) / kCombineHeads, a.T), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -177,19 +177,28 @@ __global__ void __launch_bounds__(kT) k_topk_collect(TopkLaunch a) {
   load_keys16(a.scores + (size_t)t * a.ld, n, seg * kSeg, key, ok, col);
   uint32_t gt = 0;
   const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  // one returning atomic per wave: count this wave's candidates first, then place them
+  uint64_t masks[16];
+  uint32_t wave_cnt = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t d = key[i] >> 21;
     gt += (ok[i] && d > b0) ? 1u : 0u;
-    const bool cand = ok[i] && d == b0;
-    const uint64_t m = __ballot(cand);
-    if (m) {
-      uint32_t base = 0;
-      const int leader = __ffsll((unsigned long long)m) - 1;
-      if (lane == leader) base = atomicAdd(&r.ctrl[0], (uint32_t)__popcll(m));
-      base = __shfl(base, leader);
-      const uint32_t pos = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-      if (cand && pos < (uint32_t)kCap) { r.ckey[pos] = key[i]; r.cidx[pos] = (uint32_t)col[i]; }
+    masks[i] = __ballot(ok[i] && d == b0);
+    wave_cnt += (uint32_t)__popcll(masks[i]);
+  }
+  if (wave_cnt) {
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&r.ctrl[0], wave_cnt);
+    base = __shfl(base, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((masks[i] >> lane) & 1ull) {
+        const uint32_t pos = base + (uint32_t)__popcll(masks[i] & below);
+        if (pos < (uint32_t)kCap) { r.ckey[pos] = key[i]; r.cidx[pos] = (uint32_t)col[i]; }
+      }
+      base += (uint32_t)__popcll(masks[i]);
     }
   }
   uint32_t tot;

@@ -13,9 +13,9 @@ from typing import Optional
 
 import torch
 
-from . import (dsa_block_select, dsa_block_select_workspace_size, dsa_indexer_scores, dsa_sparse_mla_decode,
-               dsa_sparse_mla_prefill, dsa_sparse_mla_workspace_size, dsa_topk, dsa_topk_workspace_size,
-               mla_desc)
+from . import (dsa_block_select, dsa_block_select_workspace_size, dsa_indexer_scores,
+               dsa_indexer_workspace_size, dsa_sparse_mla_decode, dsa_sparse_mla_prefill,
+               dsa_sparse_mla_workspace_size, dsa_topk, dsa_topk_workspace_size, indexer_desc, mla_desc)
 
 
 @dataclasses.dataclass
@@ -25,6 +25,7 @@ class StepBuffers:
     length: torch.Tensor
     out: torch.Tensor
     lse: torch.Tensor
+    ws_index: torch.Tensor
     ws_topk: torch.Tensor
     ws_block: Optional[torch.Tensor]
     ws_mla: Optional[torch.Tensor]
@@ -43,6 +44,8 @@ def alloc_buffers(wl, *, prefill: bool = False, block_sparse: bool = False, num_
     length = torch.empty(T, dtype=torch.int32, device=dev)
     out = torch.empty(T, wl.mla_heads, 512, dtype=torch.float32, device=dev)
     lse = torch.empty(T, wl.mla_heads, dtype=torch.float32, device=dev)
+    ws_index = torch.empty(max(16, dsa_indexer_workspace_size(indexer_desc(wl.index_q, wl.index_k, wl.inv_freq))),
+                           dtype=torch.uint8, device=dev)
     ws_topk = torch.empty(max(16, dsa_topk_workspace_size(T, ld, k)), dtype=torch.uint8, device=dev)
     ws_block = None
     if block_sparse:
@@ -52,13 +55,13 @@ def alloc_buffers(wl, *, prefill: bool = False, block_sparse: bool = False, num_
         need = dsa_sparse_mla_workspace_size(mla_desc(wl.mla_q, wl.kv, idx, wl.softmax_scale, num_splits))
         if need:
             ws_mla = torch.empty(need, dtype=torch.uint8, device=dev)
-    return StepBuffers(scores, idx, length, out, lse, ws_topk, ws_block, ws_mla)
+    return StepBuffers(scores, idx, length, out, lse, ws_index, ws_topk, ws_block, ws_mla)
 
 
 def index_scores(wl, buf: StepBuffers, stream=None):
     return dsa_indexer_scores(wl.index_q, wl.index_w, wl.q_seq, wl.q_pos, wl.index_k, buf.scores,
                               k_scale=wl.index_k_scale, ssmax_s=wl.ssmax_s, ssmax_b=wl.ssmax_b,
-                              inv_freq=wl.inv_freq, stream=stream)
+                              inv_freq=wl.inv_freq, ws=buf.ws_index, stream=stream)
 
 
 def select(wl, buf: StepBuffers, *, block_sparse: bool = False, stream=None):

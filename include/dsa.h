@@ -84,6 +84,8 @@ int32_t dsa_abi_version(void);
  *   k_scale  [num_seqs][max_ctx] f32       per-token key scale (FP8 keys; NULL for F32 keys)
  *   scores   [num_q][ld_scores] f32        row t gets S(0..p); entries past p are not written
  *   ld_scores >= max_ctx
+ *   ws       device workspace of at least dsa_indexer_workspace_size(desc) bytes (the prepared
+ *            queries: one small kernel forms q' once per query before the key stream starts)
  *
  * Supported: head_dim == 128; 1 <= num_heads <= 32; rope_dim in {0, 64}; q_dtype F32 or BF16;
  * k_dtype F32 (fp32 vector path) or FP8_E4M3FN (matrix-core path).  The FP8 path computes q'
@@ -101,11 +103,13 @@ typedef struct {
   dsa_dtype_t k_dtype;
 } dsa_indexer_desc_t;
 
+size_t dsa_indexer_workspace_size(const dsa_indexer_desc_t* desc);
 dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* desc, const void* q, const float* w,
                                 const int32_t* q_seq, const int32_t* q_pos,
                                 const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                                 const void* k_cache, const float* k_scale,
-                                float* scores, int64_t ld_scores, void* stream);
+                                float* scores, int64_t ld_scores,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* ============================================================================================
  * 2a. Top-k selection

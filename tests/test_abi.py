@@ -14,8 +14,8 @@ HEADER = os.path.join(ROOT, "include", "dsa.h")
 def dsa():
     lib_path = os.path.join(ROOT, "dsa_sparse_attention_indexer_amd", "libdsa.so")
     if not os.path.exists(lib_path):
-        from dsa_sparse_attention_indexer_amd.build import build
-        build()
+        import __graft_entry__
+        __graft_entry__._builder().build()
     import dsa_sparse_attention_indexer_amd as m
     return m
 
@@ -52,13 +52,15 @@ def test_topk_rejects_bad_arguments_listing_every_reason(dsa):
 def test_indexer_rejects_unsupported_shapes(dsa):
     L = dsa.lib()
     d = dsa.IndexerDesc(1, 64, 96, 32, 1, 100, dsa.DSA_BF16, dsa.DSA_BF16)
-    st = L.dsa_indexer_scores(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 50, None)
+    st = L.dsa_indexer_scores(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 50, None, 0,
+                              None)
     assert st == dsa.DSA_ERR_ARG            # the NULLs and ld < max_ctx are argument errors
     msg = L.dsa_last_error().decode()
-    for frag in ("head_dim", "num_heads", "rope_dim", "k_dtype", "ld_scores", "non-NULL"):
+    for frag in ("head_dim", "num_heads", "rope_dim", "k_dtype", "ld_scores", "non-NULL", "workspace"):
         assert frag in msg, msg
     d = dsa.IndexerDesc(0, 64, 128, 64, 1, 100, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN)
-    st = L.dsa_indexer_scores(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 100, None)
+    st = L.dsa_indexer_scores(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 100, None, 0,
+                              None)
     assert st == dsa.DSA_ERR_UNSUPPORTED and "num_heads" in L.dsa_last_error().decode()
 
 
