@@ -131,9 +131,11 @@ def main():
     log(f"layer step (a): {ms_per_step * 1e3:.1f} us")
 
     # ---- per-stage durations with events on the launch stream --------------------------------
+    # (the index-score call is one kernel; scores + top-k is also timed as the fused call the
+    # layer step uses)
     stream = torch.cuda.current_stream()
     E = lambda: torch.cuda.Event(enable_timing=True)
-    ev = [[E() for _ in range(4)] for _ in range(args.steps)]
+    ev = [[E() for _ in range(5)] for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record(stream)
         pipeline.index_scores(wa, buf_a)
@@ -142,9 +144,11 @@ def main():
         ev[i][2].record(stream)
         pipeline.attend(wa, buf_a)
         ev[i][3].record(stream)
+        pipeline.index_and_select(wa, buf_a)
+        ev[i][4].record(stream)
     torch.cuda.synchronize()
-    st = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps * 1e3 for j in range(3)]
-    t_idx, t_topk, t_mla = st
+    st = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps * 1e3 for j in range(4)]
+    t_idx, t_topk, t_mla, t_fused = st
     keys = int((wa.q_pos.long() + 1).sum())
     idx_bytes = keys * INDEX_BYTES_PER_KEY
     achieved = idx_bytes / (t_idx * 1e-6) / 1e9
@@ -194,7 +198,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "index scores (fp8 keys)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "bytes_per_launch": idx_bytes},
-        "stages_us": {"index_scores": t_idx, "topk": t_topk, "sparse_mla": t_mla},
+        "stages_us": {"index_scores": t_idx, "topk": t_topk, "sparse_mla": t_mla, "index_topk_fused": t_fused},
         "keys_scored_per_s": keys / (t_idx * 1e-6),
         "sparse_mla": {"tflops": mla_tflops, "frac_bf16_peak": mla_tflops / BF16_PEAK_TFLOPS,
                        "gather_gbs": mla_gbs, "frac_hbm_peak": mla_gbs / HBM_PEAK_GBS},

@@ -54,6 +54,8 @@ def _load():
         "dsa_abi_version": (I32, []),
         "dsa_indexer_workspace_size": (SZ, [ctypes.POINTER(IndexerDesc)]),
         "dsa_indexer_scores": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, P, SZ, P]),
+        "dsa_indexer_topk": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, P, P, P, SZ,
+                                   P, SZ, P]),
         "dsa_topk_workspace_size": (SZ, [I32, I64, I32]),
         "dsa_topk": (I32, [P, I64, P, I32, I32, P, P, P, SZ, P]),
         "dsa_block_select_workspace_size": (SZ, [I32, I64, I32]),
@@ -74,7 +76,7 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_workspace_size", "dsa_indexer_scores",
+EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_indexer_topk",
             "dsa_topk_workspace_size", "dsa_topk", "dsa_block_select_workspace_size", "dsa_block_select", "dsa_sparse_mla_workspace_size",
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill"]
 
@@ -166,12 +168,52 @@ def dsa_indexer_scores(q, w, q_seq, q_pos, k_cache, scores, k_scale=None, ssmax_
     return scores
 
 
+def dsa_indexer_topk(q, w, q_seq, q_pos, k_cache, scores, k, idx, length=None, k_scale=None, ssmax_s=None,
+                     ssmax_b=None, inv_freq=None, ws=None, topk_ws=None, stream=None):
+    """Scores and top-k selection in one call (the fp8 score kernel also builds the first radix
+    digit's histogram).  Arguments as dsa_indexer_scores plus dsa_topk's."""
+    T, H, D = q.shape
+    B, max_ctx, _ = k_cache.shape
+    _dev("q", q, (torch.float32, torch.bfloat16))
+    _dev("w", w, torch.float32, (T, H))
+    _dev("q_seq", q_seq, torch.int32, (T,))
+    _dev("q_pos", q_pos, torch.int32, (T,))
+    _dev("k_cache", k_cache, (torch.float32, torch.uint8, torch.float8_e4m3fn))
+    _dev("k_scale", k_scale, torch.float32, (B, max_ctx))
+    _dev("ssmax_s", ssmax_s, torch.float32, (H,))
+    _dev("ssmax_b", ssmax_b, torch.float32, (H,))
+    _dev("inv_freq", inv_freq, torch.float32)
+    _dev("scores", scores, torch.float32)
+    _dev("idx", idx, torch.int32, (T, k))
+    _dev("length", length, torch.int32, (T,))
+    if scores.dim() != 2 or scores.shape[0] != T:
+        raise ValueError("scores must be [T][ld]")
+    ld = scores.shape[1]
+    d = indexer_desc(q, k_cache, inv_freq)
+    if ws is None:
+        ws = torch.empty(max(16, dsa_indexer_workspace_size(d)), dtype=torch.uint8, device=q.device)
+    if topk_ws is None:
+        topk_ws = topk_workspace(T, ld, k, q.device)
+    _dev("ws", ws, torch.uint8)
+    _dev("topk_ws", topk_ws, torch.uint8)
+    _check(_lib.dsa_indexer_topk(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
+                                 _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores), ld, k,
+                                 _ptr(idx), _ptr(length), _ptr(ws), ws.numel(), _ptr(topk_ws), topk_ws.numel(),
+                                 _stream(stream)))
+    return idx, length
+
+
 # ------------------------------------------------------------------------------------------------
 # 2. selection
 # ------------------------------------------------------------------------------------------------
 
 def dsa_topk_workspace_size(num_q: int, ld: int, k: int) -> int:
     return int(_lib.dsa_topk_workspace_size(num_q, ld, k))
+
+
+def topk_workspace(num_q: int, ld: int, k: int, device) -> torch.Tensor:
+    """A zero-filled top-k workspace (the library keeps it zeroed between calls)."""
+    return torch.zeros(max(16, dsa_topk_workspace_size(num_q, ld, k)), dtype=torch.uint8, device=device)
 
 
 def dsa_topk(scores, q_pos, k, idx, length=None, ws=None, stream=None):
@@ -181,9 +223,8 @@ def dsa_topk(scores, q_pos, k, idx, length=None, ws=None, stream=None):
     _dev("q_pos", q_pos, torch.int32, (T,))
     _dev("idx", idx, torch.int32, (T, k))
     _dev("length", length, torch.int32, (T,))
-    need = dsa_topk_workspace_size(T, ld, k)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=scores.device)
+        ws = topk_workspace(T, ld, k, scores.device)
     _dev("ws", ws, torch.uint8)
     _check(_lib.dsa_topk(_ptr(scores), ld, _ptr(q_pos), T, k, _ptr(idx), _ptr(length), _ptr(ws), ws.numel(),
                          _stream(stream)))

@@ -52,16 +52,17 @@ int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
 
 size_t dsa_indexer_workspace_size(const dsa_indexer_desc_t* d) {
   if (!d || d->num_q <= 0) return 0;
-  return dsa::indexer_ws_bytes(d->num_q);
+  return dsa::indexer_ws_bytes(d->num_q, d->k_dtype);
 }
 
-dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* d, const void* q, const float* w,
-                                const int32_t* q_seq, const int32_t* q_pos,
-                                const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
-                                const void* k_cache, const float* k_scale,
-                                float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, void* stream) {
-  Checker ck;
-  if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_scores"); }
+}  // extern "C"
+
+namespace {
+
+void check_indexer(Checker& ck, const dsa_indexer_desc_t* d, const void* q, const float* w, const int32_t* q_seq,
+                   const int32_t* q_pos, const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                   const void* k_cache, const float* k_scale, const float* scores, int64_t ld_scores, const void* ws,
+                   size_t ws_bytes) {
   ck.need(d->num_q >= 0 && d->num_q <= 65535, "num_q must be in [0, 65535]");
   ck.need(d->num_seqs >= 1, "num_seqs must be >= 1");
   ck.need(d->max_ctx >= 1 && d->max_ctx <= (1 << 26), "max_ctx must be in [1, 2^26]");
@@ -77,26 +78,15 @@ dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* d, const void* q, cons
     ck.need((inv_freq != nullptr) == (d->rope_dim > 0), "inv_freq must be set iff rope_dim > 0");
     ck.need(d->k_dtype != DSA_FP8_E4M3FN || k_scale != nullptr, "k_scale is required for FP8 keys");
     ck.need(aligned(k_cache, 16), "k_cache must be 16-byte aligned");
-    ck.need(aligned(q, d->q_dtype == DSA_BF16 ? 2 : 4), "q must be aligned to its element size");
-    ck.need(ws != nullptr && ws_bytes >= dsa_indexer_workspace_size(d) && aligned(ws, 16),
+    ck.need(aligned(q, 16), "q must be 16-byte aligned");
+    const size_t need = dsa_indexer_workspace_size(d);
+    ck.need(need == 0 || (ws != nullptr && ws_bytes >= need && aligned(ws, 16)),
             "workspace missing, misaligned or smaller than dsa_indexer_workspace_size()");
   }
-  dsa_status_t st = ck.finish("dsa_indexer_scores");
-  if (st != DSA_OK || d->num_q == 0) return st;
-  dsa::IndexerLaunch a{d->num_q, d->num_heads, d->rope_dim, d->num_seqs, d->max_ctx, d->q_dtype, d->k_dtype,
-                       q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores};
-  return hip_status("dsa_indexer_scores", dsa::launch_indexer(a, ws, (hipStream_t)stream));
 }
 
-size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k) {
-  (void)k;
-  if (num_q <= 0 || ld_scores <= 0) return 0;
-  return (size_t)num_q * dsa::topk_row_bytes(ld_scores);
-}
-
-dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t num_q,
-                      int32_t k, int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream) {
-  Checker ck;
+void check_topk(Checker& ck, int32_t num_q, int64_t ld_scores, int32_t k, const void* scores, const int32_t* q_pos,
+                const int32_t* idx) {
   ck.need(num_q >= 0 && num_q <= 65535, "num_q must be in [0, 65535]");
   ck.need(ld_scores >= 1, "ld_scores must be >= 1");
   ck.support(ld_scores <= dsa::kTopkMaxCols, "ld_scores must be <= 4194304");
@@ -105,14 +95,83 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
   if (num_q > 0) {
     ck.need(scores && q_pos && idx, "scores, q_pos and idx must be non-NULL");
     ck.need(aligned(scores, 16), "scores must be 16-byte aligned");
-    ck.need(ws != nullptr && ws_bytes >= dsa_topk_workspace_size(num_q, ld_scores, k),
-            "workspace missing or smaller than dsa_topk_workspace_size()");
-    ck.need(aligned(ws, 16), "workspace must be 16-byte aligned");
   }
+}
+
+void check_topk_ws(Checker& ck, int32_t num_q, const void* ws, size_t ws_bytes) {
+  if (num_q <= 0) return;
+  ck.need(ws != nullptr && ws_bytes >= dsa::topk_ws_bytes(num_q),
+          "top-k workspace missing or smaller than dsa_topk_workspace_size()");
+  ck.need(aligned(ws, 16), "top-k workspace must be 16-byte aligned");
+}
+
+dsa::IndexerLaunch indexer_launch(const dsa_indexer_desc_t* d, const void* q, const float* w, const int32_t* q_seq,
+                                  const int32_t* q_pos, const float* ssmax_s, const float* ssmax_b,
+                                  const float* inv_freq, const void* k_cache, const float* k_scale, float* scores,
+                                  int64_t ld_scores) {
+  return dsa::IndexerLaunch{d->num_q, d->num_heads, d->rope_dim, d->num_seqs, d->max_ctx, d->q_dtype, d->k_dtype,
+                            q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores,
+                            nullptr, 0};
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* d, const void* q, const float* w,
+                                const int32_t* q_seq, const int32_t* q_pos,
+                                const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                                const void* k_cache, const float* k_scale,
+                                float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, void* stream) {
+  Checker ck;
+  if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_scores"); }
+  check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
+                ws_bytes);
+  dsa_status_t st = ck.finish("dsa_indexer_scores");
+  if (st != DSA_OK || d->num_q == 0) return st;
+  dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
+                                        ld_scores);
+  return hip_status("dsa_indexer_scores", dsa::launch_indexer(a, ws, (hipStream_t)stream));
+}
+
+dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const float* w,
+                              const int32_t* q_seq, const int32_t* q_pos,
+                              const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                              const void* k_cache, const float* k_scale,
+                              float* scores, int64_t ld_scores, int32_t k, int32_t* idx, int32_t* len,
+                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream) {
+  Checker ck;
+  if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_topk"); }
+  check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
+                ws_bytes);
+  check_topk(ck, d->num_q, ld_scores, k, scores, q_pos, idx);
+  check_topk_ws(ck, d->num_q, topk_ws, topk_ws_bytes);
+  dsa_status_t st = ck.finish("dsa_indexer_topk");
+  if (st != DSA_OK || d->num_q == 0) return st;
+  dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
+                                        ld_scores);
+  const bool fused = d->k_dtype == DSA_FP8_E4M3FN;
+  if (fused) { a.topk_ws = topk_ws; a.topk_k = k; }
+  hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status("dsa_indexer_topk", e);
+  dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws};
+  return hip_status("dsa_indexer_topk", dsa::launch_topk(tk, fused, (hipStream_t)stream));
+}
+
+size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k) {
+  if (num_q <= 0 || ld_scores <= 0 || k <= 0) return 0;
+  return dsa::topk_ws_bytes(num_q);
+}
+
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t num_q,
+                      int32_t k, int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream) {
+  Checker ck;
+  check_topk(ck, num_q, ld_scores, k, scores, q_pos, idx);
+  check_topk_ws(ck, num_q, ws, ws_bytes);
   dsa_status_t st = ck.finish("dsa_topk");
   if (st != DSA_OK || num_q == 0) return st;
-  dsa::TopkLaunch a{scores, ld_scores, q_pos, num_q, k, idx, len, ws};
-  return hip_status("dsa_topk", dsa::launch_topk(a, (hipStream_t)stream));
+  dsa::TopkLaunch a{scores, ld_scores, ld_scores, q_pos, num_q, k, idx, len, ws};
+  return hip_status("dsa_topk", dsa::launch_topk(a, false, (hipStream_t)stream));
 }
 
 size_t dsa_block_select_workspace_size(int32_t num_q, int64_t ld_scores, int32_t block) {

@@ -25,16 +25,21 @@ struct IndexerLaunch {
   const float* k_scale;
   float* scores;
   int64_t ld;
+  // optional fused first top-k digit: when set, the score kernel adds the histogram of its
+  // scores' first radix digit into this per-row workspace for a k-selection; NULL = scores only
+  void* topk_ws;
+  int topk_k;
 };
 
 struct TopkLaunch {
   const float* scores;
   int64_t ld;
+  int64_t ncap;   // a row holds min(q_pos + 1, ncap) scores
   const int32_t* q_pos;
   int T, k;
   int32_t* idx;
   int32_t* len;
-  void* ws;
+  void* ws;       // per-row first-digit histograms (fused path only)
 };
 
 struct BlockSelectLaunch {
@@ -64,21 +69,16 @@ struct MlaLaunch {
 
 // ---- sizes shared between validation and the kernels ----------------------------------------
 
-constexpr int kTopkThreads = 256;
-constexpr int kTopkSeg = 4096;          // scores per segment workgroup (16 per thread)
-constexpr int kTopkBins0 = 2048;        // first radix digit: key bits 31..21
-constexpr int kTopkCap = 8192;          // candidates kept per row for the exact resolve
-constexpr int64_t kTopkMaxCols = int64_t(1) << 22;
-constexpr int kTopkMaxSegs = int(kTopkMaxCols / kTopkSeg);
+constexpr int64_t kTopkMaxCols = int64_t(1) << 22;   // columns a top-k row may have
 
-size_t topk_row_bytes(int64_t ld);
-size_t indexer_ws_bytes(int T);
+size_t topk_ws_bytes(int T);
+size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype);
 size_t block_select_ws_bytes(int T, int64_t ld, int block);
 
 // ---- launchers (return the HIP status of the last launch) -----------------------------------
 
 hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s);
-hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+hipError_t launch_topk(const TopkLaunch& a, bool hist_given, hipStream_t s);
 hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s);
 

@@ -17,10 +17,11 @@
 //    the wave are summed with v_permlane32_swap, and lanes 0..31 store 32 consecutive scores.
 //  * fp32 keys (the reference-precision path): one thread per key, fp32 FMAs against q' in LDS.
 //
-// Query prep (RoPE angles formed and evaluated in float64, SSMax in float64) runs once per query in
-// its own small kernel, which writes the prepared operands to the caller's workspace.
+// Query prep (RoPE angles formed and evaluated in float64, SSMax in float64): on the fp8 path each
+// workgroup prepares its query in LDS while its first key tiles are in flight; on the fp32 path a
+// small kernel prepares each query once into the caller's workspace.
 
-#include "dsa_internal.h"
+#include "topk_common.h"
 
 #include <math.h>
 
@@ -30,6 +31,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;          // index head dim
 constexpr int kHPad = 32;        // heads padded to the MFMA M dimension
@@ -41,63 +43,111 @@ struct PrepSmem {
   double qs[kHPad][kQsStride];   // q' (rotated, SSMax-scaled), float64
   double cs[32], sn[32];         // cos / sin of the 32 rotary angles
   double mh[kHPad];              // SSMax multipliers
+  double wv[kHPad];              // raw head weights
   float coef[kHPad];             // w_h / (sqrt(H) sqrt(128)) * 2^-e_h   (fp8 path)
   int ex[kHPad];                 // per-head power-of-two exponent e_h   (fp8 path)
 };
 
-__device__ __forceinline__ double load_q(const void* q, dsa_dtype_t dt, size_t i) {
-  if (dt == DSA_BF16) return (double)bf16_bits_to_float(reinterpret_cast<const uint16_t*>(q)[i]);
-  return (double)reinterpret_cast<const float*>(q)[i];
+// Query prep in two phases so the fp8 kernel can put its key loads between them.
+// Load phase: thread (h = tid / 8, part = tid % 8) owns dims [16 part, 16 part + 16) of head h and
+// issues its 16 elements as two (bf16) or four (f32) 16-byte loads; threads < 32 also fetch one
+// rotary frequency, one head's SSMax pair and one head weight.
+struct PrepIn {
+  u32x4 raw[4];   // the 16 query elements as loaded: 2 (bf16) or 4 (f32) 16-byte chunks
+  float invf, ss, sb, wv;
+};
+
+template <bool BF16Q>
+__device__ inline PrepIn prep_load(const IndexerLaunch& a, int t) {
+  // Every load is unconditional (indices clamped into range, values masked afterwards) so that the
+  // compiler can issue them together, ahead of the key stream.
+  const int tid = threadIdx.x;
+  const int h = tid >> 3, part = tid & 7;
+  const int hc = min(h, a.H - 1);
+  PrepIn in;
+  const size_t base = ((size_t)t * a.H + hc) * kD + 16 * part;
+  if (BF16Q) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + base);
+    in.raw[0] = src[0];
+    in.raw[1] = src[1];
+  } else {
+    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.q) + base);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) in.raw[i] = src[i];
+  }
+  const int th = min(tid, a.H - 1);
+  const float* pf = a.rope_dim > 0 ? a.inv_freq : a.w;            // a.w is a valid dummy source
+  const float* ps = a.ssmax_s ? a.ssmax_s : a.w;
+  const float* pb = a.ssmax_s ? a.ssmax_b : a.w;
+  in.invf = pf[a.rope_dim > 0 ? min(tid, a.rope_dim / 2 - 1) : 0];
+  in.ss = ps[th];
+  in.sb = pb[th];
+  in.wv = a.w[(size_t)t * a.H + th];
+  return in;
 }
 
-// Fills sm.qs with q' for query t (heads >= H zeroed).  All 256 threads participate.
-__device__ void prep_query(PrepSmem& sm, const IndexerLaunch& a, int t, int p) {
+// Compute phase: fills sm.qs with q' (heads >= H zeroed) and sm.wv with the raw head weights.
+template <bool BF16Q>
+__device__ void prep_compute(PrepSmem& sm, const PrepIn& in, const IndexerLaunch& a, int p) {
   const int tid = threadIdx.x;
+  const int h = tid >> 3, part = tid & 7;
   const int npairs = a.rope_dim / 2;
   if (tid < npairs) {
     // p * inv_freq[j] is exact in float64 (24-bit times 31-bit); sin/cos evaluated in float64.
-    double ang = (double)p * (double)a.inv_freq[tid];
-    double s, c;
-    sincos(ang, &s, &c);
-    sm.cs[tid] = c;
-    sm.sn[tid] = s;
+    const double ang = (double)p * (double)in.invf;
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    sm.cs[tid] = cs;
+    sm.sn[tid] = sn;
   }
   if (tid < kHPad) {
-    double m = 1.0;
-    if (a.ssmax_s != nullptr && tid < a.H)
-      m = (double)a.ssmax_s[tid] * log((double)p + 1.0) + (double)a.ssmax_b[tid];
-    sm.mh[tid] = m;
+    sm.mh[tid] = (a.ssmax_s != nullptr && tid < a.H) ? (double)in.ss * log((double)p + 1.0) + (double)in.sb : 1.0;
+    sm.wv[tid] = tid < a.H ? (double)in.wv : 0.0;
   }
-  __syncthreads();
-  // 32 heads x 64 pairs = 2048 pairs, 8 per thread.
-  for (int e = tid; e < kHPad * (kD / 2); e += kThreads) {
-    const int h = e >> 6, j = e & 63;
-    double x0 = 0.0, x1 = 0.0;
-    if (h < a.H) {
-      const size_t base = ((size_t)t * a.H + h) * kD + 2 * j;
-      x0 = load_q(a.q, a.q_dtype, base);
-      x1 = load_q(a.q, a.q_dtype, base + 1);
-      if (j < npairs) {
-        const double c = sm.cs[j], s = sm.sn[j];
-        const double r0 = x0 * c - x1 * s;
-        const double r1 = x0 * s + x1 * c;
-        x0 = r0;
-        x1 = r1;
-      }
-      x0 *= sm.mh[h];
-      x1 *= sm.mh[h];
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (BF16Q) {
+      const uint32_t w = in.raw[i >> 2][i & 3];
+      x[2 * i] = __uint_as_float(w << 16);
+      x[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      x[2 * i] = __uint_as_float(in.raw[i >> 1][2 * (i & 1)]);
+      x[2 * i + 1] = __uint_as_float(in.raw[i >> 1][2 * (i & 1) + 1]);
     }
-    sm.qs[h][2 * j] = x0;
-    sm.qs[h][2 * j + 1] = x1;
   }
   __syncthreads();
+  const double m = h < a.H ? sm.mh[h] : 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = 8 * part + i;          // pair (2j, 2j + 1)
+    double x0 = (double)x[2 * i], x1 = (double)x[2 * i + 1];
+    if (j < npairs) {
+      const double c = sm.cs[j], sn = sm.sn[j];
+      const double r0 = x0 * c - x1 * sn;
+      const double r1 = x0 * sn + x1 * c;
+      x0 = r0;
+      x1 = r1;
+    }
+    sm.qs[h][2 * j] = x0 * m;
+    sm.qs[h][2 * j + 1] = x1 * m;
+  }
+  __syncthreads();
+}
+
+__device__ inline void prep_query(PrepSmem& sm, const IndexerLaunch& a, int t, int p) {
+  if (a.q_dtype == DSA_BF16) {
+    const PrepIn in = prep_load<true>(a, t);
+    prep_compute<true>(sm, in, a, p);
+  } else {
+    const PrepIn in = prep_load<false>(a, t);
+    prep_compute<false>(sm, in, a, p);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
 // Query prep: one workgroup per query writes the prepared query to the workspace
 // ------------------------------------------------------------------------------------------
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Per-query workspace record.  fp8 keys: the MFMA A operands of every lane of a wave
 // (j = 2*s + term, term 0 = hi, 1 = lo) and each lane's 16 accumulator-row weights.
@@ -116,21 +166,12 @@ __device__ __forceinline__ uint32_t pack_half2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
-__global__ void __launch_bounds__(kThreads) k_index_qprep(IndexerLaunch a, void* ws) {
-  __shared__ PrepSmem sm;
-  const int t = blockIdx.x;
+// From q' in sm.qs: per-head power-of-two scales, head weights and the hi/lo fp16 MFMA A operands
+// of every lane, written to `o` (LDS or global).  All 256 threads participate.
+__device__ void build_fp8_operands(PrepSmem& sm, QPrepFp8* o, const IndexerLaunch& a, int t) {
   const int tid = threadIdx.x;
-  const int p = clampi(a.q_pos[t], -1, a.max_ctx - 1);
-  prep_query(sm, a, t, p < 0 ? 0 : p);
-  uint8_t* rec = reinterpret_cast<uint8_t*>(ws) + (size_t)t * kQPrepBytes;
   const double inv_norm = 1.0 / (sqrt((double)a.H) * sqrt((double)kD));
-  if (a.k_dtype != DSA_FP8_E4M3FN) {
-    QPrepF32* o = reinterpret_cast<QPrepF32*>(rec);
-    for (int e = tid; e < kHPad * kD; e += kThreads) o->q[e / kD][e % kD] = (float)sm.qs[e / kD][e % kD];
-    if (tid < kHPad) o->coef[tid] = tid < a.H ? (float)((double)a.w[(size_t)t * a.H + tid] * inv_norm) : 0.f;
-    return;
-  }
-  // Per-head power-of-two scale: max|q'_h| * 2^e_h in [2^14, 2^15) keeps both fp16 terms normal.
+  // max|q'_h| * 2^e_h in [2^14, 2^15) keeps both fp16 terms normal
   {
     const int h = tid >> 3, part = tid & 7;   // 32 heads x 8 lanes
     double mx = 0.0;
@@ -146,12 +187,11 @@ __global__ void __launch_bounds__(kThreads) k_index_qprep(IndexerLaunch a, void*
         e = 15 - x;
       }
       sm.ex[h] = e;
-      const double wv = h < a.H ? (double)a.w[(size_t)t * a.H + h] * inv_norm : 0.0;
+      const double wv = h < a.H ? sm.wv[h] * inv_norm : 0.0;
       sm.coef[h] = (float)ldexp(wv, -e);
     }
   }
   __syncthreads();
-  QPrepFp8* o = reinterpret_cast<QPrepFp8*>(rec);
   // A operand of lane l (row m = l & 31, half g = l >> 5) for K-step s: q'[m][32(s>>1) + 16g + 8(s&1) + i]
   {
     const int l = tid & 63, sg = tid >> 6;
@@ -184,6 +224,20 @@ __global__ void __launch_bounds__(kThreads) k_index_qprep(IndexerLaunch a, void*
 #pragma unroll
     for (int r = 0; r < 16; ++r) o->cf[r][tid] = sm.coef[8 * (r >> 2) + 4 * g + (r & 3)];
   }
+  __syncthreads();
+}
+
+// fp32 keys: q' as fp32 and the head weights, one workgroup per query, to the workspace.
+__global__ void __launch_bounds__(kThreads) k_index_qprep(IndexerLaunch a, void* ws) {
+  __shared__ PrepSmem sm;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int p = clampi(a.q_pos[t], -1, a.max_ctx - 1);
+  prep_query(sm, a, t, p < 0 ? 0 : p);
+  QPrepF32* o = reinterpret_cast<QPrepF32*>(reinterpret_cast<uint8_t*>(ws) + (size_t)t * kQPrepBytes);
+  const double inv_norm = 1.0 / (sqrt((double)a.H) * sqrt((double)kD));
+  for (int e = tid; e < kHPad * kD; e += kThreads) o->q[e / kD][e % kD] = (float)sm.qs[e / kD][e % kD];
+  if (tid < kHPad) o->coef[tid] = tid < a.H ? (float)(sm.wv[tid] * inv_norm) : 0.f;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -242,10 +296,15 @@ __device__ __forceinline__ float tile_scores(const KeyTile& kt, const half8* ahi
   return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * kt.sc;
 }
 
-template <int TPW>   // 32-key tiles per wave; a workgroup covers 4 * 32 * TPW keys
+// TPW: 32-key tiles per wave (a workgroup covers 4 * 32 * TPW keys).  HIST: also histogram the
+// first top-k digit of this chunk's scores into the top-k workspace (the fused selection path).
+template <int TPW, bool HIST, bool BF16Q>
 __global__ void __launch_bounds__(kThreads)
-k_index_scores_fp8(IndexerLaunch a, const void* ws) {
+k_index_scores_fp8(IndexerLaunch a) {
   constexpr int chunk = 4 * kTile * TPW;
+  __shared__ PrepSmem sm;
+  __shared__ QPrepFp8 qa;
+  __shared__ uint32_t lh[HIST ? kTkBins : 1];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar) loop control
@@ -265,27 +324,34 @@ k_index_scores_fp8(IndexerLaunch a, const void* ws) {
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(srow, nrow * 4u);
   constexpr uint32_t kStride = 4 * kTile;   // the 4 waves interleave 32-key tiles
 
-  // Prepared query first (L2-resident), then three key tiles in flight per wave.  The loop is
-  // unrolled three ways so the tile buffers rotate by name: a buffer is refilled right after it is
-  // consumed and the two younger loads stay outstanding across the MFMAs.
-  const QPrepFp8* qp = reinterpret_cast<const QPrepFp8*>(reinterpret_cast<const uint8_t*>(ws) + (size_t)t * kQPrepBytes);
-  half8 ahi[8], alo[8];
-  float cf[16];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    ahi[s] = __builtin_bit_cast(half8, qp->a[2 * s][lane]);
-    alo[s] = __builtin_bit_cast(half8, qp->a[2 * s + 1][lane]);
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) cf[r] = qp->cf[r][lane];
-
-  // rel: this wave's current tile, relative to the chunk start (rows past the chunk read as zero)
+  // Three key tiles go out first; the query prep (float64 RoPE and SSMax, power-of-two scaling,
+  // hi/lo fp16 split) runs in LDS while they are in flight.
+  const PrepIn pin = prep_load<BF16Q>(a, t);
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t rel = wave * kTile;
   KeyTile tb[3];
 #pragma unroll
   for (int i = 0; i < 3; ++i) load_tile(tb[i], krs, srs, rel + i * kStride + col, g);
+  __builtin_amdgcn_sched_barrier(0);
+  prep_compute<BF16Q>(sm, pin, a, p);
+  build_fp8_operands(sm, &qa, a, t);
+  half8 ahi[8], alo[8];
+  float cf[16];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    ahi[s] = __builtin_bit_cast(half8, qa.a[2 * s][lane]);
+    alo[s] = __builtin_bit_cast(half8, qa.a[2 * s + 1][lane]);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cf[r] = qa.cf[r][lane];
+
   // only lanes 0..31 store (lanes 32..63 hold the same columns); the others aim past the range
   const uint32_t out_off = g == 0 ? 4u * col : 0x80000000u;
+  const bool hist = HIST && n > a.topk_k;
+  if (hist) {
+    for (int i = threadIdx.x; i < kTkBins; i += kThreads) lh[i] = 0;
+    __syncthreads();
+  }
 
   // Fully unrolled: straight-line code gives the compiler exact wait counts, so two tiles stay in
   // flight behind the one being multiplied.  Past the chunk the loads read zeros and the stores
@@ -295,8 +361,15 @@ k_index_scores_fp8(IndexerLaunch a, const void* ws) {
     KeyTile& cur = tb[it % 3];
     const float sc = tile_scores(cur, ahi, alo, cf);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
+    if (hist && g == 0 && rel + col < nrow) atomicAdd(&lh[score_key(sc) >> kTkShift0], 1u);
     if (it + 3 < TPW) load_tile(cur, krs, srs, rel + 3 * kStride + col, g);
     rel += kStride;
+  }
+  if (hist) {   // this chunk's counts into the row's histogram (read by the next kernel)
+    __syncthreads();
+    uint32_t* gh = tk_hist(a.topk_ws, t);
+    for (int i = threadIdx.x; i < kTkBins; i += kThreads)
+      if (lh[i]) atomicAdd(&gh[i], lh[i]);
   }
 }
 
@@ -344,22 +417,28 @@ k_index_scores_f32(IndexerLaunch a, const void* ws) {
 
 }  // namespace
 
-size_t indexer_ws_bytes(int T) { return (size_t)T * kQPrepBytes; }
+size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype) { return k_dtype == DSA_FP8_E4M3FN ? 0 : (size_t)T * kQPrepBytes; }
 
 hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
   if (a.T == 0 || a.max_ctx == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_index_qprep, dim3(a.T), dim3(kThreads), 0, s, a, ws);
   if (a.k_dtype == DSA_FP8_E4M3FN) {
     // 4096-key chunks (32 tiles per wave) when that still gives >= 512 workgroups, else 1024.
     const int64_t big = (int64_t)a.T * ((a.max_ctx + 4095) / 4096);
+    const bool hist = a.topk_ws != nullptr;
+    const bool bf = a.q_dtype == DSA_BF16;
+    auto go = [&](auto kernel, int chunk) {
+      dim3 grid((a.max_ctx + chunk - 1) / chunk, a.T);
+      hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
+    };
     if (big >= 512) {
-      dim3 grid((a.max_ctx + 4095) / 4096, a.T);
-      hipLaunchKernelGGL(k_index_scores_fp8<32>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
+      if (hist) bf ? go(k_index_scores_fp8<32, true, true>, 4096) : go(k_index_scores_fp8<32, true, false>, 4096);
+      else bf ? go(k_index_scores_fp8<32, false, true>, 4096) : go(k_index_scores_fp8<32, false, false>, 4096);
     } else {
-      dim3 grid((a.max_ctx + 1023) / 1024, a.T);
-      hipLaunchKernelGGL(k_index_scores_fp8<8>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
+      if (hist) bf ? go(k_index_scores_fp8<8, true, true>, 1024) : go(k_index_scores_fp8<8, true, false>, 1024);
+      else bf ? go(k_index_scores_fp8<8, false, true>, 1024) : go(k_index_scores_fp8<8, false, false>, 1024);
     }
   } else {
+    hipLaunchKernelGGL(k_index_qprep, dim3(a.T), dim3(kThreads), 0, s, a, ws);
     dim3 grid((a.max_ctx + kThreads - 1) / kThreads, a.T);
     hipLaunchKernelGGL(k_index_scores_f32, grid, dim3(kThreads), 0, s, a, (const void*)ws);
   }

@@ -370,26 +370,34 @@ k_mla_f32(MlaLaunch a) {
 constexpr int kCombineHeads = 4;
 
 __global__ void __launch_bounds__(kThreads) k_mla_combine(MlaLaunch a) {
+  __shared__ float sm_m[kCombineHeads][64], sm_l[kCombineHeads][64];
   __shared__ float wts[kCombineHeads][64];
   const int t = blockIdx.y, h0 = blockIdx.x * kCombineHeads;
+  const int nh = min(kCombineHeads, a.H - h0);
   const float* stats = a.ws + (size_t)a.T * a.splits * a.H * a.kv_lora;
-  if (threadIdx.x < kCombineHeads && h0 + threadIdx.x < a.H) {
-    const int h = h0 + threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, stats[2 * (((size_t)t * a.splits + s) * a.H + h)]);
-    float Ls = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const size_t i = ((size_t)t * a.splits + s) * a.H + h;
-      const float w = (M == -INFINITY) ? 0.f : exp2f(stats[2 * i] - M);
-      wts[threadIdx.x][s] = w;
-      Ls += w * stats[2 * i + 1];
-    }
-    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    for (int s = 0; s < a.splits; ++s) wts[threadIdx.x][s] *= inv;
-    if (a.lse) a.lse[(size_t)t * a.H + h] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+  // all (head, split) statistics in one parallel load
+  for (int e = threadIdx.x; e < nh * a.splits; e += kThreads) {
+    const int hl = e / a.splits, s = e % a.splits;
+    const size_t i = ((size_t)t * a.splits + s) * a.H + h0 + hl;
+    sm_m[hl][s] = stats[2 * i];
+    sm_l[hl][s] = stats[2 * i + 1];
   }
   __syncthreads();
-  const int nh = min(kCombineHeads, a.H - h0);
+  if (threadIdx.x < nh) {
+    const int hl = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, sm_m[hl][s]);
+    float Ls = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      const float w = (M == -INFINITY) ? 0.f : exp2f(sm_m[hl][s] - M);
+      wts[hl][s] = w;
+      Ls += w * sm_l[hl][s];
+    }
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    for (int s = 0; s < a.splits; ++s) wts[hl][s] *= inv;
+    if (a.lse) a.lse[(size_t)t * a.H + h0 + hl] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
   const int n4 = nh * a.kv_lora / 4;
   for (int e = threadIdx.x; e < n4; e += kThreads) {
     const int hl = (4 * e) / a.kv_lora;

@@ -1,404 +1,411 @@
-// Exact per-row top-k selection on gfx950 (radix select over order-preserving u32 keys).
+// Exact per-row top-k selection on gfx950 (radix select over order-preserving u32 score keys).
 //
 // Keeps the k highest scores of each row, equal scores going to the lower column, and emits the
 // kept columns in ascending order with -1 padding and the row length ("mistral-large4.md", bullet
 // "The indexer": the top 2048 keys are kept; the -1 slots and top-k length bound follow the vLLM
 // page's "Top-k compaction" bullet).
 //
-// A row is cut into 4096-score segments, each handled by one workgroup, so that 16 long rows
-// still fill the GPU.  Five launches:
-//   1. init     zero the row's digit-0 histogram and candidate counter
-//   2. hist     each segment builds an LDS histogram of key bits 31..21 and adds it to the row's
-//   3. collect  every segment finds the threshold bin b0 from the row histogram, counts its keys
-//               above b0 and appends the keys inside b0 (wave ballot + one atomic per wave)
-//   4. resolve  one workgroup per row finishes the radix select on the candidates (bits 20..10,
-//               then 9..0) in LDS -- or, when the threshold bin overflowed the candidate buffer
-//               (heavy ties), by re-reading the row -- giving the exact k-th key `thr`, how many
-//               keys equal to thr are kept (lowest columns first), and per-segment counts
-//   5. emit     each segment computes its output offset from the per-segment counts and writes
-//               its kept columns in order (block-wide prefix sums)
-// Every decision is made on the integer keys, so the result is exact and deterministic.
+// Three launches; rows are cut into 8192-column segments and only the last one works per row:
+//   hist     one workgroup per segment histograms the first digit (key bits 31..20) in LDS and
+//            adds it to the row's histogram.  The fused path skips it: the index-score kernel
+//            has already built that histogram.
+//   collect  one workgroup per segment finds, from the row's histogram, the bin b0 that holds
+//            the k-th largest key and appends every key whose first digit is >= b0 (all keys
+//            above b0 plus the candidates inside it; a few thousand per row) to the row's item
+//            list, in column order within the segment, with ballot/mbcnt compaction.
+//   resolve  one workgroup per row loads the items into LDS in column order, finds the exact
+//            k-th key among the candidates (bits 19..10, then 9..0), and with one ordered pass
+//            keeps the keys above it and the lowest columns among the keys equal to it.  The
+//            output is ascending by construction: no sort and no merge.
+// If a row's items do not fit in LDS (heavy ties) or k is large, the resolve workgroup instead
+// streams the row.  Every decision is made on the integer keys, so the result is exact and
+// deterministic.
 
-#include "dsa_internal.h"
+#include "topk_common.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kT = kTopkThreads;
-constexpr int kSeg = kTopkSeg;
-constexpr int kBins0 = kTopkBins0;
-constexpr int kCap = kTopkCap;
-constexpr int kResolveThreads = 1024;
-
-// Per-row workspace layout (u32 words).
-struct RowWs {
-  uint32_t* hist;     // [2048]
-  uint32_t* ctrl;     // [16]: 0 cand_cnt, 1 b0, 2 need0, 3 thr, 4 need_eq
-  uint32_t* gt;       // [nseg]  keys above the threshold (after resolve: above thr)
-  uint32_t* eq;       // [nseg]  keys equal to thr
-  uint32_t* ckey;     // [kCap]
-  uint32_t* cidx;     // [kCap]
-};
-
-__host__ __device__ inline int64_t nseg_of(int64_t ld) { return (ld + kSeg - 1) / kSeg; }
-__host__ __device__ inline size_t row_words(int64_t ld) {
-  const int64_t ns = nseg_of(ld);
-  size_t w = kBins0 + 16 + 2 * (size_t)ns;
-  w = (w + 63) & ~size_t(63);
-  return w + 2 * (size_t)kCap;
-}
-
-__device__ inline RowWs row_ws(void* ws, int64_t ld, int t) {
-  uint32_t* base = reinterpret_cast<uint32_t*>(ws) + (size_t)t * row_words(ld);
-  const int64_t ns = nseg_of(ld);
-  RowWs r;
-  r.hist = base;
-  r.ctrl = base + kBins0;
-  r.gt = r.ctrl + 16;
-  r.eq = r.gt + ns;
-  size_t off = (kBins0 + 16 + 2 * (size_t)ns + 63) & ~size_t(63);
-  r.ckey = base + off;
-  r.cidx = r.ckey + kCap;
-  return r;
-}
+constexpr int kCT = 256;                   // hist / collect threads
+constexpr int kCQ = kTkSeg / (4 * kCT);    // float4 slices per collect thread (8)
+constexpr int kRT = 1024;                  // resolve threads
+constexpr int kSQ = 4;                     // float4 slices per resolve thread and streaming round
 
 __device__ inline int row_n(const TopkLaunch& a, int t) {
   int64_t n = (int64_t)a.q_pos[t] + 1;
   if (n < 0) n = 0;
-  if (n > a.ld) n = a.ld;
+  if (n > a.ncap) n = a.ncap;
   return (int)n;
 }
 
-// Block-wide exclusive prefix sum over blockDim.x threads (multiple of 64, <= 1024).
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* sbuf /* >= 17 words */) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sbuf[wave] = x;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < nw; ++w) { uint32_t s = sbuf[w]; sbuf[w] = run; run += s; }
-    sbuf[16] = run;
-  }
-  __syncthreads();
-  const uint32_t r = sbuf[wave] + x - v;
-  if (total) *total = sbuf[16];
-  __syncthreads();
-  return r;
+__device__ inline uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Finds the bin holding the `need`-th largest key of a histogram with nb bins (nb a multiple of
-// blockDim.x).  Returns the bin through *bin and the count still needed inside it through *need_in;
-// exactly one thread writes them.
-__device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* sbuf, int* bin, uint32_t* need_in) {
-  const int tid = threadIdx.x;
-  const int per = nb / (int)blockDim.x;
-  const int hi = nb - per * tid;           // thread 0 owns the top bins
-  uint32_t local = 0;
-  for (int i = 1; i <= per; ++i) local += h[hi - i];
-  uint32_t above = block_excl_scan(local, nullptr, sbuf);
-  for (int i = 1; i <= per; ++i) {
-    const uint32_t c = h[hi - i];
-    if (above < need && need <= above + c) { *bin = hi - i; *need_in = need - above; }
-    above += c;
-  }
-  __syncthreads();
-}
-
-__global__ void __launch_bounds__(kT) k_topk_init(TopkLaunch a) {
-  RowWs r = row_ws(a.ws, a.ld, blockIdx.x);
-  for (int i = threadIdx.x; i < kBins0; i += kT) r.hist[i] = 0;
-  if (threadIdx.x < 16) r.ctrl[threadIdx.x] = 0;
-}
-
-// Loads this thread's 16 scores of segment `seg` (coalesced float4s), as keys; invalid -> flagged.
-__device__ __forceinline__ void load_keys16(const float* row, int n, int s0, uint32_t key[16], bool ok[16], int col[16]) {
+// Element (q, e) of thread tid stands for column c0 + 4*NT*q + 4*tid + e: each float4 load of a
+// wave covers 1 KiB of contiguous scores.  Loads keys; bit 4q+e of the mask is set when the
+// column is < n.  All loads are issued before any is used.
+template <int Q, int NT>
+__device__ __forceinline__ uint32_t load_slices(const float* row, int n, int c0, uint32_t key[Q][4]) {
+  float4 v[Q];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = s0 + 1024 * i + 4 * threadIdx.x;
-    if (c + 3 < n) {
-      const float4 v = *reinterpret_cast<const float4*>(row + c);
-      key[4 * i + 0] = score_key(v.x); key[4 * i + 1] = score_key(v.y);
-      key[4 * i + 2] = score_key(v.z); key[4 * i + 3] = score_key(v.w);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ok[4 * i + j] = true;
+  for (int q = 0; q < Q; ++q) {
+    const int c = c0 + 4 * NT * q + 4 * (int)threadIdx.x;
+    if (c + 4 <= n) {
+      v[q] = *reinterpret_cast<const float4*>(row + c);
     } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ok[4 * i + j] = c + j < n;
-        key[4 * i + j] = ok[4 * i + j] ? score_key(row[c + j]) : 0u;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) col[4 * i + j] = c + j;
-  }
-}
-
-__global__ void __launch_bounds__(kT) k_topk_hist(TopkLaunch a) {
-  __shared__ uint32_t lh[kBins0];
-  const int t = blockIdx.y, seg = blockIdx.x;
-  const int n = row_n(a, t);
-  if (n <= a.k || seg * kSeg >= n) return;
-  for (int i = threadIdx.x; i < kBins0; i += kT) lh[i] = 0;
-  __syncthreads();
-  uint32_t key[16]; bool ok[16]; int col[16];
-  load_keys16(a.scores + (size_t)t * a.ld, n, seg * kSeg, key, ok, col);
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (ok[i]) atomicAdd(&lh[key[i] >> 21], 1u);
-  __syncthreads();
-  RowWs r = row_ws(a.ws, a.ld, t);
-  for (int i = threadIdx.x; i < kBins0; i += kT)
-    if (lh[i]) atomicAdd(&r.hist[i], lh[i]);
-}
-
-__global__ void __launch_bounds__(kT) k_topk_collect(TopkLaunch a) {
-  __shared__ uint32_t lh[kBins0];
-  __shared__ uint32_t sbuf[24];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_need;
-  const int t = blockIdx.y, seg = blockIdx.x;
-  const int n = row_n(a, t);
-  if (n <= a.k || seg * kSeg >= n) return;
-  RowWs r = row_ws(a.ws, a.ld, t);
-  for (int i = threadIdx.x; i < kBins0; i += kT) lh[i] = r.hist[i];
-  __syncthreads();
-  int bin = -1; uint32_t need = 0;
-  find_bin(lh, kBins0, (uint32_t)a.k, sbuf, &bin, &need);
-  if (bin >= 0) { s_bin = bin; s_need = need; }
-  __syncthreads();
-  const uint32_t b0 = (uint32_t)s_bin;
-  uint32_t key[16]; bool ok[16]; int col[16];
-  load_keys16(a.scores + (size_t)t * a.ld, n, seg * kSeg, key, ok, col);
-  uint32_t gt = 0;
-  const int lane = threadIdx.x & 63;
-  const uint64_t below = (1ull << lane) - 1ull;
-  // one returning atomic per wave: count this wave's candidates first, then place them
-  uint64_t masks[16];
-  uint32_t wave_cnt = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t d = key[i] >> 21;
-    gt += (ok[i] && d > b0) ? 1u : 0u;
-    masks[i] = __ballot(ok[i] && d == b0);
-    wave_cnt += (uint32_t)__popcll(masks[i]);
-  }
-  if (wave_cnt) {
-    uint32_t base = 0;
-    if (lane == 0) base = atomicAdd(&r.ctrl[0], wave_cnt);
-    base = __shfl(base, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if ((masks[i] >> lane) & 1ull) {
-        const uint32_t pos = base + (uint32_t)__popcll(masks[i] & below);
-        if (pos < (uint32_t)kCap) { r.ckey[pos] = key[i]; r.cidx[pos] = (uint32_t)col[i]; }
-      }
-      base += (uint32_t)__popcll(masks[i]);
+      v[q].x = c < n ? row[c] : 0.f;
+      v[q].y = c + 1 < n ? row[c + 1] : 0.f;
+      v[q].z = c + 2 < n ? row[c + 2] : 0.f;
+      v[q].w = c + 3 < n ? row[c + 3] : 0.f;
     }
   }
-  uint32_t tot;
-  block_excl_scan(gt, &tot, sbuf);
+  uint32_t mask = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = c0 + 4 * NT * q + 4 * (int)threadIdx.x;
+    key[q][0] = score_key(v[q].x);
+    key[q][1] = score_key(v[q].y);
+    key[q][2] = score_key(v[q].z);
+    key[q][3] = score_key(v[q].w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mask |= (c + e < n ? 1u : 0u) << (4 * q + e);
+  }
+  return mask;
+}
+
+// Ordered compaction over the workgroup for the layout above (column order = slice, wave, lane,
+// element).  fl[q] holds this thread's 4-bit selection of slice q; returns in pos[q] the slot of
+// its first selected element of slice q, and the workgroup's total.  wsum: Q * NT/64 LDS words.
+template <int Q, int NT>
+__device__ uint32_t ordered_slots(const uint32_t fl[Q], uint32_t pos[Q], uint32_t* wsum) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t below[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    uint32_t bl = 0, wt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint64_t b = __ballot((fl[q] >> e) & 1u);
+      bl += lanes_below(b);
+      wt += (uint32_t)__popcll(b);
+    }
+    below[q] = bl;
+    if (lane == 0) wsum[q * NW + wave] = wt;
+  }
+  __syncthreads();
+  uint32_t run = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    uint32_t tq = 0, pw = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = wsum[q * NW + w];
+      pw += w < wave ? x : 0u;
+      tq += x;
+    }
+    pos[q] = run + pw + below[q];
+    run += tq;
+  }
+  __syncthreads();
+  return run;
+}
+
+// ------------------------------------------------------------------------------------------
+// hist: first-digit histogram of one segment, added into the row's
+// ------------------------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(kCT) k_topk_hist(TopkLaunch a) {
+  __shared__ uint32_t lh[kTkBins];
+  const int t = blockIdx.y;
+  const int n = row_n(a, t);
+  const int c0 = blockIdx.x * kTkSeg;
+  if (n <= a.k || c0 >= n) return;
+  const float* row = a.scores + (size_t)t * a.ld;
+  uint32_t key[kCQ][4];
+  const uint32_t mask = load_slices<kCQ, kCT>(row, n, c0, key);
+  for (int i = threadIdx.x; i < kTkBins; i += kCT) lh[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kCQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((mask >> (4 * q + e)) & 1u) atomicAdd(&lh[key[q][e] >> kTkShift0], 1u);
+  __syncthreads();
+  uint32_t* gh = tk_hist(a.ws, t);
+  for (int i = threadIdx.x; i < kTkBins; i += kCT)
+    if (lh[i]) atomicAdd(&gh[i], lh[i]);
+}
+
+// ------------------------------------------------------------------------------------------
+// collect: the keys of one segment whose first digit is >= b0, in column order
+// ------------------------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(kCT) k_topk_collect(TopkLaunch a) {
+  __shared__ uint32_t hist[kTkBins];
+  __shared__ uint32_t sbuf[32];
+  __shared__ uint32_t wsum[kCQ * (kCT / 64)];
+  __shared__ uint32_t base;
+  const int t = blockIdx.y;
+  const int n = row_n(a, t);
+  const int seg = blockIdx.x;
+  const int c0 = seg * kTkSeg;
+  if (n <= a.k || a.k > kTkFastK || c0 >= n) return;
+  const float* row = a.scores + (size_t)t * a.ld;
+  uint32_t* rw = tk_row(a.ws, t);
+  uint32_t key[kCQ][4];
+  const uint32_t mask = load_slices<kCQ, kCT>(row, n, c0, key);
+  const uint4* gh = reinterpret_cast<const uint4*>(rw);
+#pragma unroll
+  for (int j = 0; j < kTkBins / (4 * kCT); ++j) {
+    const uint4 h = gh[threadIdx.x + kCT * j];
+    uint32_t* d = hist + 4 * (threadIdx.x + kCT * j);
+    d[0] = h.x; d[1] = h.y; d[2] = h.z; d[3] = h.w;
+  }
+  __syncthreads();
+  int b0;
+  uint32_t need0;
+  tk_find_bin(hist, kTkBins, (uint32_t)a.k, sbuf, &b0, &need0);
+  uint32_t fl[kCQ];
+#pragma unroll
+  for (int q = 0; q < kCQ; ++q) {
+    fl[q] = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      fl[q] |= (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> kTkShift0) >= (uint32_t)b0 ? 1u : 0u) << e;
+  }
+  uint32_t pos[kCQ];
+  const uint32_t total = ordered_slots<kCQ, kCT>(fl, pos, wsum);
   if (threadIdx.x == 0) {
-    r.gt[seg] = tot;
-    r.eq[seg] = 0;
-    if (seg == 0) { r.ctrl[1] = b0; r.ctrl[2] = s_need; }
+    const uint32_t st = atomicAdd(&rw[kTkOffCtr], total);
+    base = st;
+    *reinterpret_cast<uint2*>(rw + kTkOffTable + 2 * seg) = make_uint2(st, total);
+  }
+  __syncthreads();
+  const uint32_t st = base;
+  if (st + total > (uint32_t)kTkItemCap) return;   // the row overflows: resolve streams it
+  uint2* items = reinterpret_cast<uint2*>(rw + kTkOffItems);
+#pragma unroll
+  for (int q = 0; q < kCQ; ++q) {
+    uint32_t p = st + pos[q];
+    const uint32_t cq = (uint32_t)(c0 + 4 * kCT * q + 4 * (int)threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((fl[q] >> e) & 1u) items[p++] = make_uint2(key[q][e], cq + e);
   }
 }
 
-// Radix step over keys held in LDS: among keys whose bits above `shift+bits` equal `prefix`,
-// histogram the `bits`-wide digit at `shift`, and find the digit holding the need-th largest.
-__device__ void lds_radix_step(const uint32_t* keys, int cnt, uint32_t prefix, int hi_shift, int shift, int bits,
-                               uint32_t* hist, uint32_t* sbuf, uint32_t need, int* digit, uint32_t* need_out) {
+// ------------------------------------------------------------------------------------------
+// resolve: one workgroup per row
+// ------------------------------------------------------------------------------------------
+
+struct ResolveSmem {
+  uint32_t key[kTkItemCap];
+  uint32_t col[kTkItemCap];
+  uint32_t hist[kTkBins];
+  uint32_t tst[kTkMaxSeg];    // per segment: first item in the workspace
+  uint32_t tpre[kTkMaxSeg];   // per segment: first item in column order
+  uint32_t sbuf[32];
+  uint32_t wsum[kSQ * (kRT / 64)];
+};
+
+// Among keys[0..cnt) whose bits above shift + bits equal prefix: the bits-wide digit at shift
+// that holds the need-th largest key, and the count still needed inside it.
+__device__ void lds_digit(const uint32_t* keys, int cnt, uint32_t prefix, int shift, int bits, uint32_t need,
+                          ResolveSmem& sm, int* digit, uint32_t* need_out) {
   const int nb = 1 << bits;
-  for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
+  for (int i = threadIdx.x; i < nb; i += kRT) sm.hist[i] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+  const int hs = shift + bits;
+  for (int i = threadIdx.x; i < cnt; i += kRT) {
     const uint32_t k = keys[i];
-    if ((k >> hi_shift) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+    if ((k >> hs) == prefix) atomicAdd(&sm.hist[(k >> shift) & (nb - 1)], 1u);
   }
   __syncthreads();
-  __shared__ int s_d;
-  __shared__ uint32_t s_n;
-  int d = -1; uint32_t nn = 0;
-  find_bin(hist, nb, need, sbuf, &d, &nn);
-  if (d >= 0) { s_d = d; s_n = nn; }
-  __syncthreads();
-  *digit = s_d;
-  *need_out = s_n;
-  __syncthreads();
+  tk_find_bin(sm.hist, nb, need, sm.sbuf, digit, need_out);
 }
 
-// Same as lds_radix_step but streaming the whole row from global memory.
-__device__ void row_radix_step(const float* row, int n, uint32_t prefix, int hi_shift, int shift, int bits,
-                               uint32_t* hist, uint32_t* sbuf, uint32_t need, int* digit, uint32_t* need_out) {
+// The same over the row in memory (streaming finish).
+__device__ void row_digit(const float* row, int n, uint32_t prefix, int shift, int bits, uint32_t need,
+                          ResolveSmem& sm, int* digit, uint32_t* need_out) {
   const int nb = 1 << bits;
-  for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
+  for (int i = threadIdx.x; i < nb; i += kRT) sm.hist[i] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const uint32_t k = score_key(row[i]);
-    if ((k >> hi_shift) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+  const int hs = shift + bits;
+  for (int c0 = 0; c0 < n; c0 += 4 * kRT * kSQ) {
+    uint32_t key[kSQ][4];
+    const uint32_t mask = load_slices<kSQ, kRT>(row, n, c0, key);
+#pragma unroll
+    for (int q = 0; q < kSQ; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> hs) == prefix)
+          atomicAdd(&sm.hist[(key[q][e] >> shift) & (nb - 1)], 1u);
   }
   __syncthreads();
-  __shared__ int s_d;
-  __shared__ uint32_t s_n;
-  int d = -1; uint32_t nn = 0;
-  find_bin(hist, nb, need, sbuf, &d, &nn);
-  if (d >= 0) { s_d = d; s_n = nn; }
-  __syncthreads();
-  *digit = s_d;
-  *need_out = s_n;
-  __syncthreads();
+  tk_find_bin(sm.hist, nb, need, sm.sbuf, digit, need_out);
 }
 
-__global__ void __launch_bounds__(kResolveThreads) k_topk_resolve(TopkLaunch a) {
-  __shared__ uint32_t skey[kCap];
-  __shared__ uint32_t sidx[kCap];
-  __shared__ uint32_t hist[8 * kResolveThreads];
-  __shared__ uint32_t sbuf[24];
-  const int t = blockIdx.x;
-  const int n = row_n(a, t);
-  if (n <= a.k) return;
-  RowWs r = row_ws(a.ws, a.ld, t);
-  const uint32_t cnt = r.ctrl[0];
-  const uint32_t b0 = r.ctrl[1];
-  const uint32_t need0 = r.ctrl[2];
-  const int ns = (int)((n + kSeg - 1) / kSeg);
+// Streaming finish: the exact k-th key from two passes over the row, then one ordered pass that
+// emits every key above it and the lowest columns among the keys equal to it.
+__device__ void finish_streaming(const TopkLaunch& a, int t, int n, uint32_t b0, uint32_t need0, ResolveSmem& sm) {
+  const float* row = a.scores + (size_t)t * a.ld;
   int d1, d2;
   uint32_t need1, need2;
-  uint32_t thr;
-  uint32_t* gtc = hist;                // reused after the radix steps: [ns] gt counts
-  uint32_t* eqc = hist + kTopkMaxSegs; // [ns] eq counts (hist holds 8192 words; ns <= 1024)
-  if (cnt <= (uint32_t)kCap) {
-    for (uint32_t i = threadIdx.x; i < cnt; i += kResolveThreads) { skey[i] = r.ckey[i]; sidx[i] = r.cidx[i]; }
-    __syncthreads();
-    lds_radix_step(skey, (int)cnt, b0, 21, 10, 11, hist, sbuf, need0, &d1, &need1);
-    lds_radix_step(skey, (int)cnt, (b0 << 11) | (uint32_t)d1, 10, 0, 10, hist, sbuf, need1, &d2, &need2);
-    thr = (b0 << 21) | ((uint32_t)d1 << 10) | (uint32_t)d2;
-    for (int i = threadIdx.x; i < 2 * kTopkMaxSegs; i += kResolveThreads) hist[i] = 0;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < cnt; i += kResolveThreads) {
-      const uint32_t k = skey[i];
-      const int s = (int)(sidx[i] / kSeg);
-      if (k > thr) atomicAdd(&gtc[s], 1u);
-      else if (k == thr) atomicAdd(&eqc[s], 1u);
+  row_digit(row, n, b0, 10, 10, need0, sm, &d1, &need1);
+  row_digit(row, n, (b0 << 10) | (uint32_t)d1, 0, 10, need1, sm, &d2, &need2);
+  const uint32_t thr = (b0 << 20) | ((uint32_t)d1 << 10) | (uint32_t)d2;
+  int32_t* out = a.idx + (size_t)t * a.k;
+  uint32_t base = 0, eq_seen = 0;
+  for (int c0 = 0; c0 < n; c0 += 4 * kRT * kSQ) {
+    uint32_t key[kSQ][4];
+    const uint32_t mask = load_slices<kSQ, kRT>(row, n, c0, key);
+    uint32_t gt[kSQ], eq[kSQ], epos[kSQ], spos[kSQ];
+#pragma unroll
+    for (int q = 0; q < kSQ; ++q) {
+      gt[q] = eq[q] = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = (mask >> (4 * q + e)) & 1u;
+        gt[q] |= (in && key[q][e] > thr ? 1u : 0u) << e;
+        eq[q] |= (in && key[q][e] == thr ? 1u : 0u) << e;
+      }
     }
-    __syncthreads();
-    for (int s = threadIdx.x; s < ns; s += kResolveThreads) { r.gt[s] += gtc[s]; r.eq[s] = eqc[s]; }
-  } else {
-    const float* row = a.scores + (size_t)t * a.ld;
-    row_radix_step(row, n, b0, 21, 10, 11, hist, sbuf, need0, &d1, &need1);
-    row_radix_step(row, n, (b0 << 11) | (uint32_t)d1, 10, 0, 10, hist, sbuf, need1, &d2, &need2);
-    thr = (b0 << 21) | ((uint32_t)d1 << 10) | (uint32_t)d2;
-    for (int i = threadIdx.x; i < 2 * kTopkMaxSegs; i += kResolveThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kResolveThreads) {
-      const uint32_t k = score_key(row[i]);
-      if (k > thr) atomicAdd(&gtc[i / kSeg], 1u);
-      else if (k == thr) atomicAdd(&eqc[i / kSeg], 1u);
+    const uint32_t eq_tot = ordered_slots<kSQ, kRT>(eq, epos, sm.wsum);
+#pragma unroll
+    for (int q = 0; q < kSQ; ++q) {
+      uint32_t r = eq_seen + epos[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((eq[q] >> e) & 1u) {
+          if (r < need2) gt[q] |= 1u << e;
+          ++r;
+        }
     }
-    __syncthreads();
-    for (int s = threadIdx.x; s < ns; s += kResolveThreads) { r.gt[s] = gtc[s]; r.eq[s] = eqc[s]; }
+    const uint32_t sel_tot = ordered_slots<kSQ, kRT>(gt, spos, sm.wsum);
+#pragma unroll
+    for (int q = 0; q < kSQ; ++q) {
+      uint32_t p = base + spos[q];
+      const int cq = c0 + 4 * kRT * q + 4 * (int)threadIdx.x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((gt[q] >> e) & 1u) {
+          if (p < (uint32_t)a.k) out[p] = cq + e;
+          ++p;
+        }
+    }
+    base += sel_tot;
+    eq_seen += eq_tot;
   }
-  if (threadIdx.x == 0) { r.ctrl[3] = thr; r.ctrl[4] = need2; }
 }
 
-__global__ void __launch_bounds__(kT) k_topk_emit(TopkLaunch a) {
-  __shared__ uint32_t sbuf[24];
-  __shared__ uint32_t s_base, s_eqb;
-  const int t = blockIdx.y, seg = blockIdx.x;
+__global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
+  __shared__ ResolveSmem sm;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
   const int n = row_n(a, t);
   int32_t* out = a.idx + (size_t)t * a.k;
-  const int s0 = seg * kSeg;
-  if (n <= a.k) {
-    for (int i = s0 + threadIdx.x; i < min(n, s0 + kSeg); i += kT) out[i] = i;
-    if (seg == 0) {
-      for (int i = n + threadIdx.x; i < a.k; i += kT) out[i] = -1;
-      if (threadIdx.x == 0 && a.len) a.len[t] = n;
-    }
+  if (n <= a.k) {   // every visible column, then padding
+    for (int i = tid; i < a.k; i += kRT) out[i] = i < n ? i : -1;
+    if (tid == 0 && a.len) a.len[t] = n;
     return;
   }
-  if (s0 >= n) return;
-  RowWs r = row_ws(a.ws, a.ld, t);
-  const uint32_t thr = r.ctrl[3];
-  const uint32_t need_eq = r.ctrl[4];
-  // Offsets of this segment: eq keys are taken lowest column first, so segment s keeps
-  // min(eq_s, need_eq - eq_before_s) of its eq keys.
+  uint32_t* rw = tk_row(a.ws, t);
+
+  // the row's histogram and item count into LDS, then both zeroed for the next call
   {
-    uint32_t eqb = 0, base = 0;
-    // each thread sums a contiguous run of the earlier segments; two block scans merge them
-    const int per = (seg + kT - 1) / kT;
-    const int lo = threadIdx.x * per, hi = min(seg, lo + per);
-    uint32_t e_local = 0;
-    for (int s = lo; s < hi; ++s) e_local += r.eq[s];
-    uint32_t e_tot;
-    const uint32_t e_before = block_excl_scan(e_local, &e_tot, sbuf);
-    uint32_t sel_local = 0, run = e_before;
-    for (int s = lo; s < hi; ++s) {
-      const uint32_t e = r.eq[s];
-      const uint32_t rem = need_eq > run ? need_eq - run : 0u;
-      sel_local += r.gt[s] + (e < rem ? e : rem);
-      run += e;
-    }
-    uint32_t sel_tot;
-    block_excl_scan(sel_local, &sel_tot, sbuf);
-    eqb = e_tot;
-    base = sel_tot;
-    if (threadIdx.x == 0) { s_base = base; s_eqb = eqb; }
+    const uint4 h = reinterpret_cast<const uint4*>(rw)[tid];
+    sm.hist[4 * tid] = h.x; sm.hist[4 * tid + 1] = h.y; sm.hist[4 * tid + 2] = h.z; sm.hist[4 * tid + 3] = h.w;
+    if (tid == 0) sm.sbuf[24] = rw[kTkOffCtr];
     __syncthreads();
+    reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) rw[kTkOffCtr] = 0u;
   }
-  const uint32_t base = s_base, eqb = s_eqb;
-  // This thread's 16 contiguous scores.
-  const float* row = a.scores + (size_t)t * a.ld;
-  const int c0 = s0 + 16 * threadIdx.x;
-  uint32_t key[16];
-  bool ok[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    ok[i] = c0 + i < n;
-    key[i] = ok[i] ? score_key(row[c0 + i]) : 0u;
+  const uint32_t total = sm.sbuf[24];
+  int b0;
+  uint32_t need0;
+  tk_find_bin(sm.hist, kTkBins, (uint32_t)a.k, sm.sbuf, &b0, &need0);
+  if (a.k > kTkFastK || total > (uint32_t)kTkItemCap) {
+    finish_streaming(a, t, n, (uint32_t)b0, need0, sm);
+    if (tid == 0 && a.len) a.len[t] = a.k;
+    return;
   }
+
+  // items into LDS in column order: segment s holds items tpre[s].. of the row, stored from tst[s]
+  const int S = (n + kTkSeg - 1) / kTkSeg;
+  uint32_t cnt_s = 0;
+  if (tid < S) {
+    const uint2 e = reinterpret_cast<const uint2*>(rw + kTkOffTable)[tid];
+    sm.tst[tid] = e.x;
+    cnt_s = e.y;
+  }
+  const uint32_t pre = tk_excl_scan(cnt_s, nullptr, sm.sbuf);
+  if (tid < S) sm.tpre[tid] = pre;
+  __syncthreads();
+  const uint2* items = reinterpret_cast<const uint2*>(rw + kTkOffItems);
+  for (uint32_t i = tid; i < total; i += kRT) {
+    int lo = 0, hi = S - 1;   // the last segment starting at or before i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm.tpre[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const uint2 it = items[sm.tst[lo] + (i - sm.tpre[lo])];
+    sm.key[i] = it.x;
+    sm.col[i] = it.y;
+  }
+  __syncthreads();
+
+  // the exact k-th key among the candidates (the items inside b0)
+  int d1, d2;
+  uint32_t need1, need2;
+  lds_digit(sm.key, (int)total, (uint32_t)b0, 10, 10, need0, sm, &d1, &need1);
+  lds_digit(sm.key, (int)total, ((uint32_t)b0 << 10) | (uint32_t)d1, 0, 10, need1, sm, &d2, &need2);
+  const uint32_t thr = ((uint32_t)b0 << 20) | ((uint32_t)d1 << 10) | (uint32_t)d2;
+
+  // one ordered pass: keys above thr, and the need2 lowest columns among keys equal to it
+  const uint32_t per = (total + kRT - 1) / kRT;
+  const uint32_t i0 = min(total, per * tid), i1 = min(total, i0 + per);
   uint32_t neq = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) neq += (ok[i] && key[i] == thr) ? 1u : 0u;
-  uint32_t tmp;
-  uint32_t eq_rank = eqb + block_excl_scan(neq, &tmp, sbuf);
-  uint32_t sel_mask = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    bool sel = false;
-    if (ok[i]) {
-      if (key[i] > thr) sel = true;
-      else if (key[i] == thr) { sel = eq_rank < need_eq; ++eq_rank; }
+  for (uint32_t i = i0; i < i1; ++i) neq += sm.key[i] == thr ? 1u : 0u;
+  const uint32_t eq0 = tk_excl_scan(neq, nullptr, sm.sbuf);
+  uint32_t nkeep = 0;
+  {
+    uint32_t r = eq0;
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t k = sm.key[i];
+      const bool eqk = k == thr;
+      nkeep += (k > thr || (eqk && r < need2)) ? 1u : 0u;
+      r += eqk ? 1u : 0u;
     }
-    sel_mask |= sel ? (1u << i) : 0u;
   }
-  uint32_t pos = base + block_excl_scan((uint32_t)__popc(sel_mask), &tmp, sbuf);
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (sel_mask & (1u << i)) {
-      if (pos < (uint32_t)a.k) out[pos] = c0 + i;   // always true when the counts are consistent
-      ++pos;
+  uint32_t p = tk_excl_scan(nkeep, nullptr, sm.sbuf);
+  {
+    uint32_t r = eq0;
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t k = sm.key[i];
+      const bool eqk = k == thr;
+      if (k > thr || (eqk && r < need2)) {
+        if (p < (uint32_t)a.k) out[p] = (int32_t)sm.col[i];
+        ++p;
+      }
+      r += eqk ? 1u : 0u;
     }
-  if (seg == 0 && threadIdx.x == 0 && a.len) a.len[t] = a.k;
+  }
+  if (tid == 0 && a.len) a.len[t] = a.k;
 }
 
 }  // namespace
 
-size_t topk_row_bytes(int64_t ld) { return row_words(ld) * sizeof(uint32_t); }
+size_t topk_ws_bytes(int T) { return tk_total_words(T) * sizeof(uint32_t); }
 
-hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
+hipError_t launch_topk(const TopkLaunch& a, bool hist_given, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const int ns = (int)nseg_of(a.ld);
-  hipLaunchKernelGGL(k_topk_init, dim3(a.T), dim3(kT), 0, s, a);
-  hipLaunchKernelGGL(k_topk_hist, dim3(ns, a.T), dim3(kT), 0, s, a);
-  hipLaunchKernelGGL(k_topk_collect, dim3(ns, a.T), dim3(kT), 0, s, a);
-  hipLaunchKernelGGL(k_topk_resolve, dim3(a.T), dim3(kResolveThreads), 0, s, a);
-  hipLaunchKernelGGL(k_topk_emit, dim3(ns, a.T), dim3(kT), 0, s, a);
+  const int64_t cols = a.ld < a.ncap ? a.ld : a.ncap;
+  const dim3 seg_grid((unsigned)((cols + kTkSeg - 1) / kTkSeg), (unsigned)a.T);
+  if (!hist_given) hipLaunchKernelGGL(k_topk_hist, seg_grid, dim3(kCT), 0, s, a);
+  if (a.k <= kTkFastK) hipLaunchKernelGGL(k_topk_collect, seg_grid, dim3(kCT), 0, s, a);
+  hipLaunchKernelGGL(k_topk_resolve, dim3(a.T), dim3(kRT), 0, s, a);
   return hipGetLastError();
 }
 

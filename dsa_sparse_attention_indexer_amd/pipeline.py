@@ -13,9 +13,9 @@ from typing import Optional
 
 import torch
 
-from . import (dsa_block_select, dsa_block_select_workspace_size, dsa_indexer_scores,
+from . import (dsa_block_select, dsa_block_select_workspace_size, dsa_indexer_scores, dsa_indexer_topk,
                dsa_indexer_workspace_size, dsa_sparse_mla_decode, dsa_sparse_mla_prefill,
-               dsa_sparse_mla_workspace_size, dsa_topk, dsa_topk_workspace_size, indexer_desc, mla_desc)
+               dsa_sparse_mla_workspace_size, dsa_topk, indexer_desc, mla_desc, topk_workspace)
 
 
 @dataclasses.dataclass
@@ -46,7 +46,7 @@ def alloc_buffers(wl, *, prefill: bool = False, block_sparse: bool = False, num_
     lse = torch.empty(T, wl.mla_heads, dtype=torch.float32, device=dev)
     ws_index = torch.empty(max(16, dsa_indexer_workspace_size(indexer_desc(wl.index_q, wl.index_k, wl.inv_freq))),
                            dtype=torch.uint8, device=dev)
-    ws_topk = torch.empty(max(16, dsa_topk_workspace_size(T, ld, k)), dtype=torch.uint8, device=dev)
+    ws_topk = topk_workspace(T, ld, k, dev)
     ws_block = None
     if block_sparse:
         ws_block = torch.empty(max(16, dsa_block_select_workspace_size(T, ld, 128)), dtype=torch.uint8, device=dev)
@@ -83,12 +83,24 @@ def attend(wl, buf: StepBuffers, *, prefill: bool = False, num_splits: int = 0, 
                                  stream=stream)
 
 
+def index_and_select(wl, buf: StepBuffers, stream=None):
+    """Scores and top-k in one call (histogram of the first radix digit fused into the scores)."""
+    return dsa_indexer_topk(wl.index_q, wl.index_w, wl.q_seq, wl.q_pos, wl.index_k, buf.scores, wl.topk, buf.idx,
+                            buf.length, k_scale=wl.index_k_scale, ssmax_s=wl.ssmax_s, ssmax_b=wl.ssmax_b,
+                            inv_freq=wl.inv_freq, ws=buf.ws_index, topk_ws=buf.ws_topk, stream=stream)
+
+
 def layer_step(wl, buf: StepBuffers, *, prefill: bool = False, block_sparse: bool = False,
-               shared_from: Optional[StepBuffers] = None, num_splits: int = 0, stream=None):
-    """Scores -> selection -> sparse MLA; with shared_from, only the MLA over that selection."""
+               shared_from: Optional[StepBuffers] = None, num_splits: int = 0, fused: bool = True, stream=None):
+    """Scores -> selection -> sparse MLA; with shared_from, only the MLA over that selection.
+
+    fused: scores and top-k through dsa_indexer_topk (else the two separate calls)."""
     if shared_from is not None:
         return attend(wl, buf, prefill=prefill, num_splits=num_splits, idx=shared_from.idx,
                       length=shared_from.length, stream=stream)
-    index_scores(wl, buf, stream)
-    select(wl, buf, block_sparse=block_sparse, stream=stream)
+    if fused and not block_sparse:
+        index_and_select(wl, buf, stream)
+    else:
+        index_scores(wl, buf, stream)
+        select(wl, buf, block_sparse=block_sparse, stream=stream)
     return attend(wl, buf, prefill=prefill, num_splits=num_splits, stream=stream)

@@ -126,12 +126,29 @@ dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* desc, const void* q, c
  * Arguments
  *   scores   [num_q][ld_scores] f32;  q_pos [num_q] i32 (n = q_pos + 1, clamped to ld_scores)
  *   idx      [num_q][k] i32;          len [num_q] i32 (may be NULL)
- *   ws       device workspace of at least dsa_topk_workspace_size(num_q, ld_scores, k) bytes
- * Supported: 1 <= k <= 65536; ld_scores <= 2^30.
+ *   ws       device workspace of at least dsa_topk_workspace_size(num_q, ld_scores, k) bytes,
+ *            16-byte aligned (about 148 KiB per query: the row's first-digit histogram and the
+ *            keys that survive it).  It must be zero-filled once before its first use (hipMemset);
+ *            every completed call leaves its bookkeeping zeroed again, so no clearing is needed
+ *            between calls, whatever num_q, ld_scores and k they use.  Calls that overlap in time
+ *            must not share a workspace.
+ * Supported: 1 <= k <= 65536; ld_scores <= 4194304 and a multiple of 4; scores 16-byte aligned.
  * ==========================================================================================*/
-size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k);
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t num_q,
                       int32_t k, int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream);
+
+/* Scores and top-k in one call: dsa_indexer_scores followed by dsa_topk, with the first radix
+ * digit's histogram built inside the fp8 score kernel (the scores are still written to `scores`).
+ * Same arguments, conventions and results as the two calls made in sequence, except that a row
+ * holds min(q_pos + 1, max_ctx) scores (the score kernel's clamp).  `topk_ws` follows dsa_topk's
+ * workspace rules. */
+size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k);
+dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* desc, const void* q, const float* w,
+                              const int32_t* q_seq, const int32_t* q_pos,
+                              const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                              const void* k_cache, const float* k_scale,
+                              float* scores, int64_t ld_scores, int32_t k, int32_t* idx, int32_t* len,
+                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream);
 
 /* ============================================================================================
  * 2b. Block-sparse selection

@@ -45,8 +45,17 @@ def test_topk_rejects_bad_arguments_listing_every_reason(dsa):
     st = L.dsa_topk(None, 6, None, 3, 0, None, None, None, 0, None)
     assert st == dsa.DSA_ERR_ARG
     msg = L.dsa_last_error().decode()
-    for frag in ("multiple of 4", "k must be", "non-NULL", "workspace"):
+    for frag in ("multiple of 4", "k must be", "non-NULL", "top-k workspace"):
         assert frag in msg, msg
+
+
+def test_indexer_topk_requires_its_workspace(dsa):
+    L = dsa.lib()
+    d = dsa.IndexerDesc(2, 64, 128, 64, 1, 100, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN)
+    st = L.dsa_indexer_topk(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 100, 2048,
+                            None, None, None, 0, None, 0, None)
+    msg = L.dsa_last_error().decode()
+    assert st == dsa.DSA_ERR_ARG and "top-k workspace" in msg and "non-NULL" in msg, msg
 
 
 def test_indexer_rejects_unsupported_shapes(dsa):
@@ -77,7 +86,7 @@ def test_mla_rejects_bad_dtype_combinations(dsa):
 
 
 def test_workspace_queries(dsa):
-    assert dsa.dsa_topk_workspace_size(16, 131072, 2048) > 0
+    assert dsa.dsa_topk_workspace_size(16, 131072, 2048) == 16 * (4096 + 4 + 2 * 512 + 2 * 16384) * 4
     assert dsa.dsa_topk_workspace_size(0, 131072, 2048) == 0
     assert dsa.dsa_block_select_workspace_size(4, 524288, 128) == 4 * 4096 * 4
     d = dsa.MlaDesc(16, 64, 512, 64, 16, 131072, 2048, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN, 64, 0.07, 0)

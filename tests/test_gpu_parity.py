@@ -333,3 +333,60 @@ def test_repeat_runs_are_bit_identical(dsa):
     for r in res[1:]:
         for x, y in zip(res[0], r):
             assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------------------------------------
+# fused scores + top-k: identical to the two separate calls; one workspace serves every call
+# ---------------------------------------------------------------------------------------------
+
+FUSED_CASES = [
+    ("ragged", dict(seq_lens=[9000, 2048, 2049, 1, 4097], max_ctx=9000), False),
+    ("prefill_positions", dict(seq_lens=[7000], max_ctx=7000, q_positions=[0, 2047, 2048, 5000, 6999]), False),
+    ("constant_keys", dict(seq_lens=[6000, 3000], max_ctx=6000), True),   # every score ties
+]
+
+
+@pytest.mark.parametrize("name,kw,constant", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_index_topk_equals_separate_calls(dsa, name, kw, constant):
+    wl = workloads.make_workload(name=name, seed=808, **kw)
+    g = wl.to("cuda")
+    if constant:
+        g.index_k[:] = g.index_k[0, 0]
+        g.index_k_scale[:] = g.index_k_scale[0, 0]
+    P = _pipe()
+    sep, fus = P.alloc_buffers(g), P.alloc_buffers(g)
+    P.index_scores(g, sep)
+    P.select(g, sep)
+    P.index_and_select(g, fus)
+    torch.cuda.synchronize()
+    for t in range(wl.num_q):
+        n = int(wl.q_pos[t]) + 1
+        assert torch.equal(sep.scores[t, :n], fus.scores[t, :n]), f"{name} q{t}: scores differ"
+    assert torch.equal(sep.idx, fus.idx) and torch.equal(sep.length, fus.length), f"{name}: selections differ"
+    if constant:   # all scores equal: the lowest k columns win
+        idx = fus.idx.cpu().numpy()
+        for t in range(wl.num_q):
+            n = int(wl.q_pos[t]) + 1
+            assert np.array_equal(idx[t], np.arange(wl.topk)) if n > wl.topk else idx[t, 0] == 0
+
+
+def test_fused_workspace_reused_across_shapes(dsa):
+    P = _pipe()
+    big = workloads.make_workload(name="big", seed=909, seq_lens=[12000, 8000, 5000], max_ctx=12000).to("cuda")
+    small = workloads.make_workload(name="small", seed=910, seq_lens=[3000], max_ctx=3000).to("cuda")
+    bb, bs = P.alloc_buffers(big), P.alloc_buffers(small)
+    shared_ws = bb.ws_topk
+    for i, (wl, buf) in enumerate(((big, bb), (small, bs), (big, bb), (small, bs))):
+        buf.ws_topk = shared_ws
+        if i % 2:   # the separate top-k call shares the same workspace
+            P.index_scores(wl, buf)
+            P.select(wl, buf)
+        else:
+            P.index_and_select(wl, buf)
+        torch.cuda.synchronize()
+        idx, ln = buf.idx.cpu().numpy(), buf.length.cpu().numpy()
+        sc = buf.scores.cpu().numpy()
+        for t in range(wl.num_q):
+            n = int(wl.q_pos[t]) + 1
+            ref, rl = O.topk_row(sc[t, :n].astype(np.float64), wl.topk)
+            assert ln[t] == rl and np.array_equal(idx[t], ref), f"call {i} q{t}: selection differs"
