@@ -4,15 +4,16 @@
 Workload (the headline): batch 16, context 131072 per sequence, RoPE layer, fp8 E4M3FN index keys
 (one fp32 scale per token) and fp8 latent cache (one fp32 scale per 64 elements), bf16 queries.
 One step = lightning-indexer scores over every cached key -> exact top-2048 -> sparse MLA decode
-(64 heads, 512 + 64 dims).  The NoPE-layer and shared-indexer variants are timed the same way and
-reported beside it.  All inputs are seeded synthetic tensors generated on the GPU and resident in
-HBM before timing starts.
+(64 heads, 512 + 64 dims).  The NoPE-layer and shared-indexer variants of the same shape, the
+4096-token chunked prefill on a 61440-token prefix, the 512K block-sparse decode and the batch-64
+16K-32K decode are timed the same way and reported beside it.  All inputs are seeded synthetic
+tensors generated on the GPU and resident in HBM before timing starts.
 
 Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 """
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -25,31 +26,41 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 INDEX_BYTES_PER_KEY = 128 + 4 + 4      # fp8 key row + fp32 scale read, fp32 score written
 LATENT_BYTES_PER_KEY = 576 + 9 * 4     # fp8 latent row + 9 fp32 scales
+MLA_FLOP_PER_KEY_HEAD = 2 * (576 + 512)   # QK^T over 576 dims and PV over 512, per selected key and head
+INDEX_COUNTERS = os.path.join(ROOT, "profiles", "index_scores_fp8_b16_ctx128k_counters.txt")
+INDEX_SOURCES = ["dsa_sparse_attention_indexer_amd/csrc/indexer.hip",
+                 "dsa_sparse_attention_indexer_amd/csrc/dsa_internal.h"]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_slice(wl, t):
-    """CPU copy of query t and its sequence only (B = 1), for timing the oracle."""
-    import torch
-    from workloads import Workload
-    b = int(wl.q_seq[t])
-    sl = lambda x: None if x is None else x[b:b + 1].cpu()
-    return Workload(name=wl.name + f"[q{t}]", num_heads=wl.num_heads, rope_dim=wl.rope_dim,
-                    softmax_scale=wl.softmax_scale, topk=wl.topk, q_seq=torch.zeros(1, dtype=torch.int32),
-                    q_pos=wl.q_pos[t:t + 1].cpu(), seq_len=wl.seq_len[b:b + 1].cpu(), max_ctx=wl.max_ctx,
-                    index_q=wl.index_q[t:t + 1].cpu(), index_w=wl.index_w[t:t + 1].cpu(),
-                    ssmax_s=None if wl.ssmax_s is None else wl.ssmax_s.cpu(),
-                    ssmax_b=None if wl.ssmax_b is None else wl.ssmax_b.cpu(),
-                    inv_freq=None if wl.inv_freq is None else wl.inv_freq.cpu(),
-                    index_k=sl(wl.index_k), index_k_scale=sl(wl.index_k_scale), mla_q=wl.mla_q[t:t + 1].cpu(),
-                    kv=sl(wl.kv), kv_scale=sl(wl.kv_scale), mla_heads=wl.mla_heads)
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per index-score launch from the committed rocprofv3 counter summary, or None if
+    it is missing or was taken on a different version of the kernel's source."""
+    try:
+        with open(INDEX_COUNTERS) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("source_digest") != source_digest(INDEX_SOURCES):
+            return None
+        return float(kv["traffic_bytes_per_dispatch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, seconds):
     """The float64 oracle on whole queries of the same workload, on this host's cores."""
+    import workloads
     from oracle import dsa_oracle as O
     threads = None
     try:
@@ -60,7 +71,7 @@ def cpu_baseline(wl, seconds):
         pass
     done, elapsed, t = 0, 0.0, 0
     while done == 0 or (elapsed < seconds and done < wl.num_q):
-        sub = cpu_slice(wl, t)
+        sub = workloads.slice_query(wl, t)
         t0 = time.perf_counter()
         O.decode_layer(sub, [0])
         elapsed += time.perf_counter() - t0
@@ -103,22 +114,17 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "dispatches": 5}))
         return
 
-    log("generating config 2 (a: RoPE layer) on the GPU ...")
+    log("generating the 128K decode workload (RoPE layer) on the GPU ...")
     wa = workloads.config2("a", device=dev)
     T = wa.num_q
     buf_a = pipeline.alloc_buffers(wa)
-    wb = bb = None
-    if not args.no_variants:
-        log("generating config 2 (b: NoPE layer) ...")
-        wb = workloads.config2("b", device=dev)
-        bb = pipeline.alloc_buffers(wb)
-        buf_c = pipeline.alloc_buffers(wa)   # shared-indexer layer: its own outputs, a's selection
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
 
     def step_a():
         pipeline.layer_step(wa, buf_a)
 
-    # ---- headline: K timed layer steps (variant a) -------------------------------------------
+    # ---- headline: K timed layer steps --------------------------------------------------------
     for _ in range(args.warmup):
         step_a()
     torch.cuda.synchronize()
@@ -128,34 +134,32 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
-    log(f"layer step (a): {ms_per_step * 1e3:.1f} us")
+    log(f"layer step: {ms_per_step * 1e3:.1f} us")
 
-    # ---- per-stage durations with events on the launch stream --------------------------------
-    # (the index-score call is one kernel; scores + top-k is also timed as the fused call the
-    # layer step uses)
-    stream = torch.cuda.current_stream()
-    E = lambda: torch.cuda.Event(enable_timing=True)
-    ev = [[E() for _ in range(5)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        pipeline.index_scores(wa, buf_a)
-        ev[i][1].record(stream)
-        pipeline.select(wa, buf_a)
-        ev[i][2].record(stream)
-        pipeline.attend(wa, buf_a)
-        ev[i][3].record(stream)
-        pipeline.index_and_select(wa, buf_a)
-        ev[i][4].record(stream)
-    torch.cuda.synchronize()
-    st = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps * 1e3 for j in range(4)]
-    t_idx, t_topk, t_mla, t_fused = st
+    # ---- per-stage durations: K back-to-back calls between two events on the launch stream -------
+    def per_call_us(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    t_idx = per_call_us(lambda: pipeline.index_scores(wa, buf_a))
+    t_topk = per_call_us(lambda: pipeline.select(wa, buf_a))
+    t_fused = per_call_us(lambda: pipeline.index_and_select(wa, buf_a))
+    t_mla = per_call_us(lambda: pipeline.attend(wa, buf_a))
     keys = int((wa.q_pos.long() + 1).sum())
     idx_bytes = keys * INDEX_BYTES_PER_KEY
     achieved = idx_bytes / (t_idx * 1e-6) / 1e9
     sel = int(buf_a.length.long().sum())
-    mla_flops = sel * wa.mla_heads * (576 + 512) * 2
+    mla_flops = sel * wa.mla_heads * MLA_FLOP_PER_KEY_HEAD
     mla_tflops = mla_flops / (t_mla * 1e-6) / 1e12
     mla_gbs = sel * LATENT_BYTES_PER_KEY / (t_mla * 1e-6) / 1e9
+    log(f"index {t_idx:.1f} us, top-k {t_topk:.1f} us, fused index+top-k {t_fused:.1f} us, MLA {t_mla:.1f} us")
 
     variants = {}
     if not args.no_variants:
@@ -168,11 +172,36 @@ def main():
                 fn()
             torch.cuda.synchronize()
             return (time.perf_counter() - s0) / args.steps
-        tb = timed(lambda: pipeline.layer_step(wb, bb))
+
+        buf_c = pipeline.alloc_buffers(wa)   # shared-indexer layer: its own outputs, a's selection
         tc = timed(lambda: pipeline.layer_step(wa, buf_c, shared_from=buf_a))
-        variants = {"nope_layer": {"us_per_step": tb * 1e6, "tok_per_s": T / tb},
-                    "shared_indexer_layer": {"us_per_step": tc * 1e6, "tok_per_s": T / tc}}
-        log(f"NoPE layer {tb * 1e6:.1f} us, shared-indexer layer {tc * 1e6:.1f} us")
+        variants["shared_indexer_layer_b16_ctx128k"] = {"us_per_step": tc * 1e6, "tok_per_s": T / tc}
+        del buf_c
+        log("generating the NoPE-layer workload ...")
+        wb = workloads.config2("b", device=dev)
+        bb = pipeline.alloc_buffers(wb)
+        tb = timed(lambda: pipeline.layer_step(wb, bb))
+        variants["nope_layer_b16_ctx128k"] = {"us_per_step": tb * 1e6, "tok_per_s": wb.num_q / tb}
+        del wb, bb
+        log("generating the 4096-on-61440 chunked prefill ...")
+        w3 = workloads.config3(device=dev)
+        b3 = pipeline.alloc_buffers(w3, prefill=True)
+        t3 = timed(lambda: pipeline.layer_step(w3, b3, prefill=True))
+        variants["chunked_prefill_4096_on_61440"] = {"us_per_step": t3 * 1e6, "tok_per_s": w3.num_q / t3}
+        del w3, b3
+        log("generating the 512K block-sparse decode ...")
+        w4 = workloads.config4(device=dev)
+        b4 = pipeline.alloc_buffers(w4, block_sparse=True)
+        t4 = timed(lambda: pipeline.layer_step(w4, b4, block_sparse=True))
+        variants["block_sparse_b4_ctx512k"] = {"us_per_step": t4 * 1e6, "tok_per_s": w4.num_q / t4}
+        del w4, b4
+        log("generating the batch-64 16K-32K decode ...")
+        w1 = workloads.config1(device=dev)
+        b1 = pipeline.alloc_buffers(w1)
+        t1 = timed(lambda: pipeline.layer_step(w1, b1))
+        variants["decode_b64_ctx16k_32k"] = {"us_per_step": t1 * 1e6, "tok_per_s": w1.num_q / t1}
+        del w1, b1
+        log("variants: " + ", ".join(f"{k} {v['us_per_step']:.1f} us" for k, v in variants.items()))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -197,8 +226,8 @@ def main():
                    "topk": wa.topk, "kv_cache": "fp8 e4m3fn + fp32 scales"},
         "roofline": {"bound": "hbm", "kernel": "index scores (fp8 keys)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": idx_bytes},
-        "stages_us": {"index_scores": t_idx, "topk": t_topk, "sparse_mla": t_mla, "index_topk_fused": t_fused},
+                     "traffic": counter_traffic(), "bytes_per_launch": idx_bytes},
+        "stages_us": {"index_scores": t_idx, "topk": t_topk, "index_topk_fused": t_fused, "sparse_mla": t_mla},
         "keys_scored_per_s": keys / (t_idx * 1e-6),
         "sparse_mla": {"tflops": mla_tflops, "frac_bf16_peak": mla_tflops / BF16_PEAK_TFLOPS,
                        "gather_gbs": mla_gbs, "frac_hbm_peak": mla_gbs / HBM_PEAK_GBS},

@@ -38,6 +38,7 @@ constexpr int kHPad = 32;        // heads padded to the MFMA M dimension
 constexpr int kThreads = 256;    // 4 waves
 constexpr int kTile = 32;        // keys per MFMA N tile
 constexpr int kQsStride = kD + 1;  // double row stride in LDS (odd: per-head reductions avoid conflicts)
+constexpr int kDepth = 3;        // key tiles in flight per wave in the fp8 stream
 
 struct PrepSmem {
   double qs[kHPad][kQsStride];   // q' (rotated, SSMax-scaled), float64
@@ -324,14 +325,14 @@ k_index_scores_fp8(IndexerLaunch a) {
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(srow, nrow * 4u);
   constexpr uint32_t kStride = 4 * kTile;   // the 4 waves interleave 32-key tiles
 
-  // Three key tiles go out first; the query prep (float64 RoPE and SSMax, power-of-two scaling,
+  // The first key tiles go out first; the query prep (float64 RoPE and SSMax, power-of-two scaling,
   // hi/lo fp16 split) runs in LDS while they are in flight.
   const PrepIn pin = prep_load<BF16Q>(a, t);
   __builtin_amdgcn_sched_barrier(0);
   uint32_t rel = wave * kTile;
-  KeyTile tb[3];
+  KeyTile tb[kDepth];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) load_tile(tb[i], krs, srs, rel + i * kStride + col, g);
+  for (int i = 0; i < kDepth; ++i) load_tile(tb[i], krs, srs, rel + i * kStride + col, g);
   __builtin_amdgcn_sched_barrier(0);
   prep_compute<BF16Q>(sm, pin, a, p);
   build_fp8_operands(sm, &qa, a, t);
@@ -353,16 +354,16 @@ k_index_scores_fp8(IndexerLaunch a) {
     __syncthreads();
   }
 
-  // Fully unrolled: straight-line code gives the compiler exact wait counts, so two tiles stay in
-  // flight behind the one being multiplied.  Past the chunk the loads read zeros and the stores
+  // Fully unrolled: straight-line code gives the compiler exact wait counts, so kDepth - 1 tiles
+  // stay in flight behind the one being multiplied.  Past the chunk the loads read zeros and the stores
   // are dropped, so there is no per-tile guard.
 #pragma unroll
   for (int it = 0; it < TPW; ++it) {
-    KeyTile& cur = tb[it % 3];
+    KeyTile& cur = tb[it % kDepth];
     const float sc = tile_scores(cur, ahi, alo, cf);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
     if (hist && g == 0 && rel + col < nrow) atomicAdd(&lh[score_key(sc) >> kTkShift0], 1u);
-    if (it + 3 < TPW) load_tile(cur, krs, srs, rel + 3 * kStride + col, g);
+    if (it + kDepth < TPW) load_tile(cur, krs, srs, rel + kDepth * kStride + col, g);
     rel += kStride;
   }
   if (hist) {   // this chunk's counts into the row's histogram (read by the next kernel)

@@ -55,3 +55,36 @@ def check_attention(out, lse, ref_out, ref_lse, fp8, where=""):
             dl = np.abs(lse[fin] - ref_lse[fin])
             assert dl.max() <= lim_lse * max(1.0, np.abs(ref_lse[fin]).max()), f"{where}: lse err {dl.max():.3g}"
     return rel
+
+
+def check_block_selection(gpu_idx, gpu_len, scores, pos, block=128, nblocks=16, where=""):
+    """Block-sparse selection vs the oracle's scores: the block holding `pos` is kept, the other
+    kept blocks may differ from the oracle's only where block maxima lie inside the tie band, and
+    the list is every visible key of the kept blocks, ascending, -1 padded."""
+    s = np.asarray(scores, dtype=np.float64)[: pos + 1]
+    n = pos + 1
+    nb = (n + block - 1) // block
+    bmax = np.array([s[j * block: min(n, (j + 1) * block)].max() for j in range(nb)])
+    gi = np.asarray(gpu_idx)
+    gl = int(gpu_len)
+    assert np.all(gi[gl:] == -1), f"{where}: padding is not -1"
+    chosen = sorted(set(int(x) // block for x in gi[:gl]))
+    want = [t for j in chosen for t in range(j * block, min(n, (j + 1) * block))]
+    assert gl == len(want) and np.array_equal(gi[:gl], want), f"{where}: not the full ascending key list of its blocks"
+    recent = pos // block
+    assert recent in chosen, f"{where}: most recent block missing"
+    assert len(chosen) == min(nb, nblocks), f"{where}: {len(chosen)} blocks kept"
+    if nb <= nblocks:
+        return 0
+    others = np.array([j for j in range(nb) if j != recent])
+    vals = np.sort(bmax[others])[::-1]
+    kth = vals[nblocks - 2]
+    rms = math.sqrt(float(np.mean(s * s)))
+    band = SELECT_BAND * max(abs(kth), rms)
+    picked = [j for j in chosen if j != recent]
+    bad = [j for j in picked if bmax[j] < kth - band]
+    bad += [int(j) for j in others if j not in picked and bmax[j] > kth + band]
+    assert not bad, f"{where}: blocks {bad[:5]} disagree with the oracle outside the band"
+    from oracle import dsa_oracle as O
+    ref, rl = O.block_select_row(s, pos, block, nblocks, topk=len(gi))
+    return len(set(chosen) ^ set(int(x) // block for x in ref[:rl]))

@@ -230,3 +230,18 @@ def config4(device="cpu", seed=4, batch=4, ctx=524288):
     """Block-sparse long-context decode: 4 index heads, 128-token blocks, top-16 blocks."""
     return make_workload(name=f"blocksparse_b{batch}_ctx{ctx}_fp8", seed=seed, seq_lens=[ctx] * batch,
                          max_ctx=ctx, num_heads=4, device=device)
+
+
+def slice_query(wl: Workload, t: int) -> Workload:
+    """Query t and its own sequence only (B = 1), copied to the CPU: what the oracle needs to
+    recompute one query of a large workload."""
+    b = int(wl.q_seq[t])
+    sl = lambda x: None if x is None else x[b:b + 1].cpu()
+    cpu = lambda x: None if x is None else x.cpu()
+    return Workload(name=f"{wl.name}[q{t}]", num_heads=wl.num_heads, rope_dim=wl.rope_dim,
+                    softmax_scale=wl.softmax_scale, topk=wl.topk, q_seq=torch.zeros(1, dtype=torch.int32),
+                    q_pos=wl.q_pos[t:t + 1].cpu(), seq_len=wl.seq_len[b:b + 1].cpu(), max_ctx=wl.max_ctx,
+                    index_q=wl.index_q[t:t + 1].cpu(), index_w=wl.index_w[t:t + 1].cpu(),
+                    ssmax_s=cpu(wl.ssmax_s), ssmax_b=cpu(wl.ssmax_b), inv_freq=cpu(wl.inv_freq),
+                    index_k=sl(wl.index_k), index_k_scale=sl(wl.index_k_scale), mla_q=wl.mla_q[t:t + 1].cpu(),
+                    kv=sl(wl.kv), kv_scale=sl(wl.kv_scale), mla_heads=wl.mla_heads)
