@@ -39,6 +39,9 @@ constexpr int kRow = 576;                 // latent row: 512 + 64
 constexpr int kLora = 512;
 constexpr int kBlocks = kRow / 64;        // scales per row
 constexpr int kKsStride = kRow + 8;       // bf16 per key-major row (1168 B: rows shift by 4 banks)
+constexpr int kRing = 4;                  // key tiles gathered ahead (fp8 path)
+constexpr int kRowsChunk = 2048;          // selection slots staged in LDS at a time (fp8 path)
+constexpr float kLazyLog2 = 8.f;          // the running maximum lags the true one by at most this (log2)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -97,171 +100,271 @@ __device__ __forceinline__ void dequant16(const u32x4 raw, float s, u32x4& lo, u
   }
 }
 
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt in 6:4 and lgkmcnt in 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Gathers straight into LDS: lane l's 16 (4) bytes from global address g land at LDS byte
+// lds + 16*l (4*l); lds must be the same in every lane.  Written as inline assembly so that the
+// compiler does not track these loads as LDS writes -- it would otherwise make later LDS accesses
+// wait for every gather in flight.  The callers wait for them explicitly (wait_vmcnt) before a
+// barrier, and vmcnt counts them like any other vector-memory load.
+__device__ __forceinline__ void gather16_to_lds(const void* g, void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void gather4_to_lds(const void* g, void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+}
+
+// Workgroup barrier for hand-offs through LDS: this wave's LDS operations are complete before it,
+// but global loads in flight (the gathers of later tiles) are not waited for, as __syncthreads
+// would.  The empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kMlaThreads = 512;   // fp8 path: 8 waves = 4 head groups x 2 halves
+
 template <int ROPE>
-__global__ void __launch_bounds__(kThreads)
+struct MlaFp8 {
+  static constexpr int DQ = kLora + ROPE;               // bytes of a latent row that are used
+  static constexpr int KSTEPS = DQ / 32;
+  static constexpr int CHUNKS = DQ / 16;                // 16-byte chunks per used row
+  static constexpr int NSC = DQ / 64;                   // scales per used row
+  static constexpr int WROWS = kTileK / 8;              // rows of a tile each wave gathers
+  static constexpr int WCH = WROWS * CHUNKS;            // chunks per wave and tile
+  static constexpr int WCHI = (WCH + 63) / 64;          // chunk loads per wave and tile
+  static constexpr int WSC = WROWS * NSC;               // scale words per wave and tile
+  static constexpr int WSCI = (WSC + 63) / 64;          // scale loads per wave and tile
+  static constexpr int LPT = WCHI + WSCI;               // LDS-direct loads per wave and tile
+  static constexpr int NCH = kTileK * CHUNKS;
+  static constexpr int PER = (NCH + kMlaThreads - 1) / kMlaThreads;
+  static constexpr int ODIM = kLora / 2;                // output dims per wave
+};
+
+// Wave w = 4 * half + hg owns heads 16hg..16hg+15.  For each 32-key tile it computes the partial
+// S^T over its half of the query dims (K-steps KH*half..KH*half+KH-1) for all 32 keys, adds the
+// other half's partial through LDS, and accumulates O^T for output dims 256*half..256*half+255.
+// Per lane: the query slice (KH operands) and 64 accumulator registers.
+template <int ROPE>
+__global__ void __launch_bounds__(kMlaThreads)
 k_mla_fp8(MlaLaunch a) {
-  constexpr int DQ = kLora + ROPE;
-  constexpr int KSTEPS = DQ / 32;
-  constexpr int CHUNKS = DQ / 16;                     // 16-byte chunks of a row that are used
-  constexpr int NCH = kTileK * CHUNKS;
-  constexpr int PER = (NCH + kThreads - 1) / kThreads;
-  __shared__ uint16_t ks[kTileK][kKsStride];
-  __shared__ int srow[2][kTileK];
-  __shared__ int svalid[2][kTileK];
+  using C = MlaFp8<ROPE>;
+  constexpr int DQ = C::DQ, KSTEPS = C::KSTEPS, CHUNKS = C::CHUNKS, NSC = C::NSC, WROWS = C::WROWS;
+  constexpr int LPT = C::LPT, NCH = C::NCH, PER = C::PER;
+  constexpr int MD = C::ODIM / 16;                      // 16-dim output tiles per wave
+  static_assert(kRing == 4, "four ring slots, each its own LDS object");
+  // Raw fp8 rows and scales of up to four tiles in flight, gathered straight into LDS.
+  struct Slot {
+    uint8_t raw[kTileK * DQ];
+    float sc[kTileK * NSC];
+  };
+  __shared__ __attribute__((aligned(16))) Slot sl0, sl1, sl2, sl3;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kTileK][kKsStride];
+  __shared__ __attribute__((aligned(16))) float4v xz[2][4][2][64];   // partial scores swapped between halves
+  __shared__ int rows[kRowsChunk];                      // row of every slot of the current chunk, -1 if none
   const int t = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hg = wave & 3, half = wave >> 2;
   const int c = lane & 15, g = lane >> 4;
   const int b = clampi(a.q_seq[t], 0, a.B - 1);
   const int L = a.len ? clampi(a.len[t], 0, a.topk) : a.topk;
   const int slot0 = split * a.per_split;
   const int slot1 = min(L, slot0 + a.per_split);
-  const bool active = 16 * wave < a.H;
-  const int head = 16 * wave + c;
+  const bool active = 16 * hg < a.H;
+  const int head = 16 * hg + c;
   const float zscale = a.softmax_scale * kLog2e;
   const int32_t* irow = a.idx + (size_t)t * a.topk;
   const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(a.kv) + (size_t)b * a.max_ctx * kRow;
   const float* scseq = a.kv_scale + (size_t)b * a.max_ctx * kBlocks;
 
-  auto fetch_idx = [&](int tile_base) -> int {   // row of slot tile_base + tid (tid < 32), -1 if none
-    const int slot = tile_base + tid;
-    const int r = slot < slot1 ? irow[slot] : -1;
-    return (r >= 0 && r < a.max_ctx) ? r : -1;
-  };
-  u32x4 raw[PER];
-  float rsc[PER];
-  auto issue_loads = [&](int buf) {
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int ch = tid + kThreads * m;
-      if (ch < NCH) {
-        const int r = ch / CHUNKS, cc = ch % CHUNKS;
-        const int row = srow[buf][r];
-        raw[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kvseq + (size_t)row * kRow) + cc);
-        rsc[m] = scseq[(size_t)row * kBlocks + (cc >> 2)];
-      }
-    }
-  };
-
-  bf16x8 qreg[KSTEPS];
+  constexpr int KH = KSTEPS / 2;                        // K-steps per half
+  static_assert(KSTEPS % 2 == 0, "query dims split in two halves");
+  bf16x8 qreg[KH];
   if (active) {
-    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + head) * DQ;
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + head) * DQ + 32 * KH * half;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
+    for (int s = 0; s < KH; ++s)
       qreg[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 32 * s + 8 * g));
   }
   float m_run = -INFINITY, l_run = 0.f;
-  float4v oacc[kLora / 16];
+  float4v oacc[MD];
 #pragma unroll
-  for (int md = 0; md < kLora / 16; ++md) oacc[md] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int md = 0; md < MD; ++md) oacc[md] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: rows of tile 0 -> LDS, its data in flight, rows of tile 1 in a register
-  if (slot0 < slot1) {
-    if (tid < kTileK) {
-      const int r = fetch_idx(slot0);
-      srow[0][tid] = r < 0 ? 0 : r;
-      svalid[0][tid] = r >= 0;
+  // Wave w gathers rows WROWS*w.. of tile tau: their chunks and scales are contiguous in the slot,
+  // and lane l of a load lands at 16*l (4*l) bytes from the load's base.
+  auto issue = [&](Slot& sl, int tau) {
+    const int* tr = rows + kTileK * tau + WROWS * wave;
+#pragma unroll
+    for (int j = 0; j < C::WCHI; ++j) {
+      const int i = 64 * j + lane;
+      const int r = i < C::WCH ? i / CHUNKS : 0, cc = i % CHUNKS;
+      const int row = max(tr[r], 0);
+      if (i < C::WCH) gather16_to_lds(kvseq + (size_t)row * kRow + 16 * cc, sl.raw + WROWS * wave * DQ + 1024 * j);
     }
-    __syncthreads();
-    issue_loads(0);
-  }
-  int next_row = -1;
-  if (tid < kTileK && slot0 + kTileK < slot1) next_row = fetch_idx(slot0 + kTileK);
+#pragma unroll
+    for (int j = 0; j < C::WSCI; ++j) {
+      const int i = 64 * j + lane;
+      const int r = i < C::WSC ? i / NSC : 0, sc = i % NSC;
+      const int row = max(tr[r], 0);
+      if (i < C::WSC) gather4_to_lds(scseq + (size_t)row * kBlocks + sc, sl.sc + WROWS * wave * NSC + 64 * j);
+    }
+  };
 
-  int cur = 0;
-  for (int tb = slot0; tb < slot1; tb += kTileK, cur ^= 1) {
-    __syncthreads();                       // the previous tile's readers of ks are done
+  // One tile: wait for its gathers, dequantise to bf16 in ks, refill the slot, then QK^T, online
+  // softmax and PV on the matrix cores.
+  auto step = [&](Slot& sl, int tau, int ntiles) {
+    const int later = min(ntiles, tau + kRing) - tau - 1;   // tiles whose gathers were issued after tau's
+    if (later >= 3) wait_vmcnt<3 * LPT>();
+    else if (later == 2) wait_vmcnt<2 * LPT>();
+    else if (later == 1) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    lds_barrier();                         // every wave's gathers of tile tau are in LDS; ks is free
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int ch = tid + kThreads * m;
+      const int ch = tid + kMlaThreads * m;
       if (ch < NCH) {
         const int r = ch / CHUNKS, cc = ch % CHUNKS;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sl.raw + 16 * ch);
         u32x4 lo, hi;
-        dequant16(raw[m], rsc[m], lo, hi);
-        uint16_t* dst = &ks[ks_row_of_key(r)][16 * cc];
-        *reinterpret_cast<u32x4*>(dst) = lo;
-        *reinterpret_cast<u32x4*>(dst + 8) = hi;
+        dequant16(v, sl.sc[r * NSC + (cc >> 2)], lo, hi);
+        u32x4* dst = reinterpret_cast<u32x4*>(&ks[ks_row_of_key(r)][16 * cc]);
+        dst[0] = lo;
+        dst[1] = hi;
       }
     }
-    const bool more = tb + kTileK < slot1;
-    if (tid < kTileK && more) {
-      srow[cur ^ 1][tid] = next_row < 0 ? 0 : next_row;
-      svalid[cur ^ 1][tid] = next_row >= 0;
-    }
-    __syncthreads();                       // ks and the next tile's rows are ready
-    if (more) {
-      issue_loads(cur ^ 1);
-      if (tid < kTileK) next_row = tb + 2 * kTileK < slot1 ? fetch_idx(tb + 2 * kTileK) : -1;
-    }
+    // validity of this lane's 8 keys (8g + e) of tile tau
+    uint32_t vmask = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vmask |= (rows[kTileK * tau + 8 * g + e] >= 0 ? 1u : 0u) << e;
+    lds_barrier();                         // ks is complete and the slot has been read
+    if (tau + kRing < ntiles) issue(sl, tau + kRing);
+    // partial S^T over this half's query dims: lane (c, g) gets keys 8g + 4mb + i of head c
+    float4v sacc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
     if (active) {
-      float4v sacc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
+      constexpr int KB = 3;   // K operands read a batch ahead of their MFMAs
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
+      for (int s0 = 0; s0 < KH; s0 += KB) {
+        bf16x8 kop[2][KB];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&ks[16 * mb + c][32 * s + 8 * g]));
-          sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[s], sacc[mb], 0, 0, 0);
-        }
+        for (int j = 0; j < KB; ++j)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            if (s0 + j < KH)
+              kop[mb][j] = __builtin_bit_cast(
+                  bf16x8, *reinterpret_cast<const u32x4*>(&ks[16 * mb + c][32 * (KH * half + s0 + j) + 8 * g]));
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            if (s0 + j < KH) sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[mb][j], qreg[s0 + j], sacc[mb], 0, 0, 0);
       }
-      // this lane: head c, keys 8g + 4mb + i
-      float z[8];
-      float tmax = -INFINITY;
+    }
+    xz[half][hg][0][lane] = sacc[0];
+    xz[half][hg][1][lane] = sacc[1];
+    lds_barrier();                         // both halves' partial scores are in LDS
+    if (!active) return;
+    float z[8];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb) {
+      const float4v other = xz[half ^ 1][hg][mb][lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kappa = 8 * g + 4 * mb + i;
-          const float v = svalid[cur][kappa] ? sacc[mb][i] * zscale : -INFINITY;
-          z[4 * mb + i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      float alpha = 1.f;
-      float p[8];
-      if (m_new == -INFINITY) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = 0.f;
-      } else {
-        alpha = exp2f(m_run - m_new);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = exp2f(z[e] - m_new);
+      for (int i = 0; i < 4; ++i) {
+        const float dot = sacc[mb][i] + other[i];   // the same sum in both halves (addition commutes)
+        z[4 * mb + i] = ((vmask >> (4 * mb + i)) & 1u) ? dot * zscale : -INFINITY;
       }
-      float psum = 0.f;
+    }
+    float tmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) psum += p[e];
-      l_run = l_run * alpha + psum;
+    for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, z[e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // Lazy rescaling: the reference maximum m_run only moves when the tile's maximum exceeds it by
+    // more than 2^kLazyLog2 (or on the first keys), so probabilities stay below 2^kLazyLog2 and the
+    // accumulators are rescaled rarely instead of on every tile.  O and l share m_run, so the
+    // normalised result is the same softmax.
+    const bool bump = tmax > m_run + kLazyLog2;
+    if (__ballot(bump)) {
+      const float m_new = bump ? tmax : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
       m_run = m_new;
-      if (__ballot(alpha != 1.f)) {
+    }
+    float p[8];
 #pragma unroll
-        for (int md = 0; md < kLora / 16; ++md) oacc[md] *= alpha;
+    for (int e = 0; e < 8; ++e) p[e] = m_run == -INFINITY ? 0.f : exp2f(z[e] - m_run);
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) psum += p[e];
+    l_run += psum;
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = cvt2_bf16(float2v{p[2 * e], p[2 * e + 1]});
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, pk);
+    // V^T operand rows: LDS rows 16h + 4g + j/4 hold keys 8g + 4h + j/4
+    const int trow = 4 * g + (c >> 2), tcol = 4 * (c & 3) + C::ODIM * half;
+    typedef __attribute__((address_space(3))) short4v* lds_s4p;
+    constexpr int VB = 4;   // V^T operands read a batch ahead of their MFMAs
+#pragma unroll
+    for (int md0 = 0; md0 < MD; md0 += VB) {
+      short8v vv[VB];
+#pragma unroll
+      for (int j = 0; j < VB; ++j) {
+        const short4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(&ks[trow][16 * (md0 + j) + tcol]));
+        const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(&ks[16 + trow][16 * (md0 + j) + tcol]));
+        vv[j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      u32x4 pk;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pk[e] = cvt2_bf16(float2v{p[2 * e], p[2 * e + 1]});
-      const bf16x8 pop = __builtin_bit_cast(bf16x8, pk);
-      // V^T operand rows: LDS rows 16h + 4g + j/4 hold keys 8g + 4h + j/4
-      const int trow = 4 * g + (c >> 2), tcol = 4 * (c & 3);
-#pragma unroll
-      for (int md = 0; md < kLora / 16; ++md) {
-        typedef __attribute__((address_space(3))) short4v* lds_s4p;
-        const short4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(&ks[trow][16 * md + tcol]));
-        const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(&ks[16 + trow][16 * md + tcol]));
-        const short8v vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pop, oacc[md], 0, 0, 0);
-      }
+      for (int j = 0; j < VB; ++j)
+        oacc[md0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv[j]), pop, oacc[md0 + j], 0, 0, 0);
+    }
+  };
+
+  for (int cb = slot0; cb < slot1; cb += kRowsChunk) {   // chunks of the split's slots (one, normally)
+    const int nslot = min(kRowsChunk, slot1 - cb);
+    const int ntiles = (nslot + kTileK - 1) / kTileK;
+    __syncthreads();                       // the previous chunk is completely consumed
+    for (int i = tid; i < ntiles * kTileK; i += kMlaThreads) {
+      const int r = i < nslot ? irow[cb + i] : -1;
+      rows[i] = (r >= 0 && r < a.max_ctx) ? r : -1;
+    }
+    __syncthreads();
+    wait_vmcnt<0>();   // the query loads are done (tells the compiler too: no waits for them below)
+    issue(sl0, 0);
+    if (1 < ntiles) issue(sl1, 1);
+    if (2 < ntiles) issue(sl2, 2);
+    if (3 < ntiles) issue(sl3, 3);
+    for (int tau = 0; tau < ntiles; tau += kRing) {
+      step(sl0, tau, ntiles);
+      if (tau + 1 < ntiles) step(sl1, tau + 1, ntiles);
+      if (tau + 2 < ntiles) step(sl2, tau + 2, ntiles);
+      if (tau + 3 < ntiles) step(sl3, tau + 3, ntiles);
     }
   }
   if (!active) return;
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  // oacc[md][i] = O^T[dim 16md + 4g + i][head c]
+  // oacc[md][i] = O^T[dim ODIM*half + 16md + 4g + i][head c]
 #pragma unroll
-  for (int md = 0; md < kLora / 16; ++md) {
+  for (int md = 0; md < MD; ++md) {
     float o[4] = {oacc[md][0], oacc[md][1], oacc[md][2], oacc[md][3]};
-    write_partial_or_final(a, t, split, head, m_run, l_tot, o, 16 * md + 4 * g, 4);
+    write_partial_or_final(a, t, split, head, m_run, l_tot, o, C::ODIM * half + 16 * md + 4 * g, 4);
   }
-  if (g == 0) write_stats(a, t, split, head, m_run, l_tot);
+  if (g == 0 && half == 0) write_stats(a, t, split, head, m_run, l_tot);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -366,49 +469,49 @@ k_mla_f32(MlaLaunch a) {
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s;  lse = ln2 (M + log2 L).
-// One workgroup per (query, 4 heads).
-constexpr int kCombineHeads = 4;
+// One workgroup per (query, head): 128 threads, one float4 of the 512-dim output each, with the
+// partials of up to 16 splits in flight per thread.
+constexpr int kCombineThreads = 128;
 
-__global__ void __launch_bounds__(kThreads) k_mla_combine(MlaLaunch a) {
-  __shared__ float sm_m[kCombineHeads][64], sm_l[kCombineHeads][64];
-  __shared__ float wts[kCombineHeads][64];
-  const int t = blockIdx.y, h0 = blockIdx.x * kCombineHeads;
-  const int nh = min(kCombineHeads, a.H - h0);
+__global__ void __launch_bounds__(kCombineThreads) k_mla_combine(MlaLaunch a) {
+  __shared__ float wts[64];
+  const int t = blockIdx.y, h = blockIdx.x;
   const float* stats = a.ws + (size_t)a.T * a.splits * a.H * a.kv_lora;
-  // all (head, split) statistics in one parallel load
-  for (int e = threadIdx.x; e < nh * a.splits; e += kThreads) {
-    const int hl = e / a.splits, s = e % a.splits;
-    const size_t i = ((size_t)t * a.splits + s) * a.H + h0 + hl;
-    sm_m[hl][s] = stats[2 * i];
-    sm_l[hl][s] = stats[2 * i + 1];
+  // split statistics: one thread per split, max and sum by wave reduction (splits <= 64)
+  const int tid = threadIdx.x;
+  float m = -INFINITY, l = 0.f;
+  if (tid < a.splits) {
+    const size_t i = ((size_t)t * a.splits + tid) * a.H + h;
+    m = stats[2 * i];
+    l = stats[2 * i + 1];
   }
+  float M = m;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float w = (M == -INFINITY || tid >= a.splits) ? 0.f : exp2f(m - M);
+  float Ls = w * l;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
+  if (tid < 64) wts[tid] = Ls > 0.f ? w / Ls : 0.f;
+  if (tid == 0 && a.lse) a.lse[(size_t)t * a.H + h] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
   __syncthreads();
-  if (threadIdx.x < nh) {
-    const int hl = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, sm_m[hl][s]);
-    float Ls = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float w = (M == -INFINITY) ? 0.f : exp2f(sm_m[hl][s] - M);
-      wts[hl][s] = w;
-      Ls += w * sm_l[hl][s];
-    }
-    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    for (int s = 0; s < a.splits; ++s) wts[hl][s] *= inv;
-    if (a.lse) a.lse[(size_t)t * a.H + h0 + hl] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-  const int n4 = nh * a.kv_lora / 4;
-  for (int e = threadIdx.x; e < n4; e += kThreads) {
-    const int hl = (4 * e) / a.kv_lora;
+  const float4* part = reinterpret_cast<const float4*>(a.ws + ((size_t)t * a.splits * a.H + h) * a.kv_lora);
+  const size_t sstride = (size_t)a.H * a.kv_lora / 4;   // float4s between consecutive splits
+  for (int e = tid; e < a.kv_lora / 4; e += kCombineThreads) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < a.splits; ++s) {
-      const float w = wts[hl][s];
-      const float4 v = reinterpret_cast<const float4*>(a.ws + (((size_t)t * a.splits + s) * a.H + h0) * a.kv_lora)[e];
-      acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+    for (int s0 = 0; s0 < a.splits; s0 += 16) {
+      float4 v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        v[j] = s0 + j < a.splits ? part[(size_t)(s0 + j) * sstride + e] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float wj = s0 + j < a.splits ? wts[s0 + j] : 0.f;
+        acc.x = fmaf(wj, v[j].x, acc.x); acc.y = fmaf(wj, v[j].y, acc.y);
+        acc.z = fmaf(wj, v[j].z, acc.z); acc.w = fmaf(wj, v[j].w, acc.w);
+      }
     }
-    reinterpret_cast<float4*>(a.out + ((size_t)t * a.H + h0) * a.kv_lora)[e] = acc;
+    reinterpret_cast<float4*>(a.out + ((size_t)t * a.H + h) * a.kv_lora)[e] = acc;
   }
 }
 
@@ -418,14 +521,14 @@ hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   dim3 grid(a.splits, a.T);
   if (a.kv_dtype == DSA_FP8_E4M3FN) {
-    if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_fp8<64>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_mla_fp8<0>, grid, dim3(kThreads), 0, s, a);
+    if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_fp8<64>, grid, dim3(kMlaThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_mla_fp8<0>, grid, dim3(kMlaThreads), 0, s, a);
   } else {
     if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_f32<64>, grid, dim3(kF32Threads), 0, s, a);
     else hipLaunchKernelGGL(k_mla_f32<0>, grid, dim3(kF32Threads), 0, s, a);
   }
   if (a.splits > 1)
-    hipLaunchKernelGGL(k_mla_combine, dim3((a.H + kCombineHeads - 1) / kCombineHeads, a.T), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(k_mla_combine, dim3(a.H, a.T), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 
