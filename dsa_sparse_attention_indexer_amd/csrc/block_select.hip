@@ -7,8 +7,9 @@
 //   1. block_max  one wave per block reduces its visible scores (block maxima -> workspace)
 //   2. select     one workgroup per query: the block holding the query position is forced in, the
 //                 other nblocks-1 are taken by repeated block-wide argmax over (score, -block)
-//                 packed into one u64 (so equal scores go to the lower block), then the kept
-//                 blocks are expanded into ascending key indices with -1 padding.
+//                 packed into one u64 (so equal scores go to the lower block), with the maxima
+//                 held in registers; the kept blocks are then ranked and expanded into ascending
+//                 key indices with -1 padding.
 
 #include "dsa_internal.h"
 
@@ -43,6 +44,10 @@ __global__ void __launch_bounds__(kT) k_block_max(BlockSelectLaunch a) {
   if (lane == 0) reinterpret_cast<uint32_t*>(a.ws)[(size_t)t * nblk_of(a.ld, a.block) + j] = best;
 }
 
+constexpr int kPT = 1024;       // pick threads: 16 waves
+constexpr int kPickPer = 16;    // block maxima per thread kept in registers (nb <= 16384)
+
+// Block-wide maximum of one u64 per thread; every thread gets the result.
 __device__ uint64_t block_max_u64(uint64_t v, uint64_t* sbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -53,74 +58,109 @@ __device__ uint64_t block_max_u64(uint64_t v, uint64_t* sbuf) {
   if (lane == 0) sbuf[wave] = v;
   __syncthreads();
   uint64_t r = sbuf[0];
-  for (int w = 1; w < kT / 64; ++w) r = sbuf[w] > r ? sbuf[w] : r;
+#pragma unroll
+  for (int w = 1; w < kPT / 64; ++w) r = sbuf[w] > r ? sbuf[w] : r;
   __syncthreads();
   return r;
 }
 
-__global__ void __launch_bounds__(kT) k_block_pick(BlockSelectLaunch a) {
-  __shared__ uint64_t sbuf[kT / 64];
+// Higher score first, then lower block: the score key above the inverted block id.  Every non-NaN
+// score key is >= 1, so 0 marks "not a candidate".
+__device__ inline uint64_t pack_block(uint32_t key, int64_t j) {
+  return (uint64_t)key << 32 | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+__global__ void __launch_bounds__(kPT) k_block_pick(BlockSelectLaunch a) {
+  __shared__ uint64_t sbuf[kPT / 64];
   __shared__ int chosen[kMaxBlocksKept];
-  __shared__ int nchosen;
+  __shared__ int sorted[kMaxBlocksKept];
   __shared__ int offs[kMaxBlocksKept + 1];
   const int t = blockIdx.x;
+  const int tid = threadIdx.x;
   int64_t n = (int64_t)a.q_pos[t] + 1;
   n = n < 0 ? 0 : (n > a.ld ? a.ld : n);
   const int64_t nb = (n + a.block - 1) / a.block;
   const uint32_t* bmax = reinterpret_cast<const uint32_t*>(a.ws) + (size_t)t * nblk_of(a.ld, a.block);
-  if (threadIdx.x == 0) nchosen = 0;
-  __syncthreads();
+  int m;
   if (nb <= a.nblocks) {
-    if (threadIdx.x < nb) chosen[threadIdx.x] = (int)threadIdx.x;
-    if (threadIdx.x == 0) nchosen = (int)nb;
+    m = (int)nb;
+    if (tid < m) chosen[tid] = tid;
   } else {
+    m = a.nblocks;
     const int recent = (int)((n - 1) / a.block);
-    if (threadIdx.x == 0) { chosen[0] = recent; nchosen = 1; }
-    __syncthreads();
-    for (int r = 1; r < a.nblocks; ++r) {
-      uint64_t best = 0;
-      for (int64_t j = threadIdx.x; j < nb; j += kT) {
-        bool taken = false;
-        for (int c = 0; c < r; ++c) taken |= (chosen[c] == (int)j);
-        if (taken) continue;
-        // higher score first, then lower block: the score key above the inverted block id
-        // (every non-NaN score key is >= 1, so 0 never wins)
-        const uint64_t v = (uint64_t)bmax[j] << 32 | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-        best = v > best ? v : best;
+    if (tid == 0) chosen[0] = recent;
+    if (nb <= (int64_t)kPT * kPickPer) {
+      // all candidates in registers; nblocks-1 rounds of block-wide argmax
+      uint64_t v[kPickPer];
+#pragma unroll
+      for (int i = 0; i < kPickPer; ++i) {
+        const int64_t j = tid + (int64_t)kPT * i;
+        v[i] = (j < nb && j != recent) ? pack_block(bmax[j], j) : 0ull;
       }
-      best = block_max_u64(best, sbuf);
-      if (threadIdx.x == 0) { chosen[r] = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull)); nchosen = r + 1; }
-      __syncthreads();
+      for (int r = 1; r < m; ++r) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < kPickPer; ++i) best = v[i] > best ? v[i] : best;
+        best = block_max_u64(best, sbuf);
+        const int j = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+        if (tid == 0) chosen[r] = j;
+        if (j % kPT == tid) {
+#pragma unroll
+          for (int i = 0; i < kPickPer; ++i)
+            if (i == j / kPT) v[i] = 0ull;
+        }
+      }
+    } else {
+      // very many blocks: rescan the maxima from memory each round
+      for (int r = 1; r < m; ++r) {
+        __syncthreads();
+        uint64_t best = 0;
+        for (int64_t j = tid; j < nb; j += kPT) {
+          bool taken = j == recent;
+          for (int c = 1; c < r; ++c) taken |= (chosen[c] == (int)j);
+          if (taken) continue;
+          const uint64_t v = pack_block(bmax[j], j);
+          best = v > best ? v : best;
+        }
+        best = block_max_u64(best, sbuf);
+        if (tid == 0) chosen[r] = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+      }
     }
   }
   __syncthreads();
-  const int m = nchosen;
-  if (threadIdx.x == 0) {
-    // ascending order (m <= 64: insertion sort), then output offsets
-    for (int i = 1; i < m; ++i) {
-      const int v = chosen[i];
-      int j = i - 1;
-      while (j >= 0 && chosen[j] > v) { chosen[j + 1] = chosen[j]; --j; }
-      chosen[j + 1] = v;
-    }
+  // ascending: each chosen block's rank among the chosen ones (distinct ids)
+  if (tid < m) {
+    const int v = chosen[tid];
+    int rank = 0;
+    for (int i = 0; i < m; ++i) rank += chosen[i] < v ? 1 : 0;
+    sorted[rank] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
     int run = 0;
     for (int i = 0; i < m; ++i) {
       offs[i] = run;
-      const int64_t lo = (int64_t)chosen[i] * a.block;
-      const int64_t cnt = (lo + a.block <= n) ? a.block : (n - lo);
-      run += (int)cnt;
+      const int64_t lo = (int64_t)sorted[i] * a.block;
+      run += (int)((lo + a.block <= n) ? a.block : (n - lo));
     }
     offs[m] = run;
   }
   __syncthreads();
   int32_t* out = a.idx + (size_t)t * a.topk;
-  for (int i = 0; i < m; ++i) {
-    const int64_t lo = (int64_t)chosen[i] * a.block;
-    const int cnt = offs[i + 1] - offs[i];
-    for (int e = threadIdx.x; e < cnt; e += kT) out[offs[i] + e] = (int32_t)(lo + e);
+  const int total = offs[m];
+  for (int e = tid; e < a.topk; e += kPT) {
+    int32_t val = -1;
+    if (e < total) {
+      int lo = 0, hi = m - 1;   // the last kept block whose first slot is <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offs[mid] <= e) lo = mid; else hi = mid - 1;
+      }
+      val = (int32_t)((int64_t)sorted[lo] * a.block + (e - offs[lo]));
+    }
+    out[e] = val;
   }
-  for (int e = offs[m] + threadIdx.x; e < a.topk; e += kT) out[e] = -1;
-  if (threadIdx.x == 0 && a.len) a.len[t] = offs[m];
+  if (tid == 0 && a.len) a.len[t] = total;
 }
 
 }  // namespace
@@ -134,7 +174,7 @@ hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s) {
   const int64_t nb = nblk_of(a.ld, a.block);
   dim3 g1((unsigned)((nb + 3) / 4), a.T);
   hipLaunchKernelGGL(k_block_max, g1, dim3(kT), 0, s, a);
-  hipLaunchKernelGGL(k_block_pick, dim3(a.T), dim3(kT), 0, s, a);
+  hipLaunchKernelGGL(k_block_pick, dim3(a.T), dim3(kPT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ def index_and_select(wl, buf: StepBuffers, stream=None):
 
 
 def layer_step(wl, buf: StepBuffers, *, prefill: bool = False, block_sparse: bool = False,
-               shared_from: Optional[StepBuffers] = None, num_splits: int = 0, fused: bool = True, stream=None):
+               shared_from: Optional[StepBuffers] = None, num_splits: int = 0, fused: bool = False, stream=None):
     """Scores -> selection -> sparse MLA; with shared_from, only the MLA over that selection.
 
     fused: scores and top-k through dsa_indexer_topk (else the two separate calls)."""
