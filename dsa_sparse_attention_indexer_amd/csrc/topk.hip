@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(kCT) k_topk_hist(TopkLaunch a) {
 // ------------------------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(kCT) k_topk_collect(TopkLaunch a) {
-  __shared__ uint32_t hist[kTkBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kTkBins];
   __shared__ uint32_t sbuf[32];
   __shared__ uint32_t wsum[kCQ * (kCT / 64)];
   __shared__ uint32_t base;
@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(kCT) k_topk_collect(TopkLaunch a) {
   __syncthreads();
   int b0;
   uint32_t need0;
-  tk_find_bin(hist, kTkBins, (uint32_t)a.k, sbuf, &b0, &need0);
+  tk_find_bin<kTkBins, kCT>(hist, (uint32_t)a.k, sbuf, &b0, &need0);
   uint32_t fl[kCQ];
 #pragma unroll
   for (int q = 0; q < kCQ; ++q) {
@@ -212,9 +212,11 @@ struct ResolveSmem {
 
 // Among keys[0..cnt) whose bits above shift + bits equal prefix: the bits-wide digit at shift
 // that holds the need-th largest key, and the count still needed inside it.
-__device__ void lds_digit(const uint32_t* keys, int cnt, uint32_t prefix, int shift, int bits, uint32_t need,
+template <int BITS>
+__device__ void lds_digit(const uint32_t* keys, int cnt, uint32_t prefix, int shift, uint32_t need,
                           ResolveSmem& sm, int* digit, uint32_t* need_out) {
-  const int nb = 1 << bits;
+  constexpr int nb = 1 << BITS;
+  constexpr int bits = BITS;
   for (int i = threadIdx.x; i < nb; i += kRT) sm.hist[i] = 0;
   __syncthreads();
   const int hs = shift + bits;
@@ -223,13 +225,15 @@ __device__ void lds_digit(const uint32_t* keys, int cnt, uint32_t prefix, int sh
     if ((k >> hs) == prefix) atomicAdd(&sm.hist[(k >> shift) & (nb - 1)], 1u);
   }
   __syncthreads();
-  tk_find_bin(sm.hist, nb, need, sm.sbuf, digit, need_out);
+  tk_find_bin<nb, kRT>(sm.hist, need, sm.sbuf, digit, need_out);
 }
 
 // The same over the row in memory (streaming finish).
-__device__ void row_digit(const float* row, int n, uint32_t prefix, int shift, int bits, uint32_t need,
+template <int BITS>
+__device__ void row_digit(const float* row, int n, uint32_t prefix, int shift, uint32_t need,
                           ResolveSmem& sm, int* digit, uint32_t* need_out) {
-  const int nb = 1 << bits;
+  constexpr int nb = 1 << BITS;
+  constexpr int bits = BITS;
   for (int i = threadIdx.x; i < nb; i += kRT) sm.hist[i] = 0;
   __syncthreads();
   const int hs = shift + bits;
@@ -244,7 +248,7 @@ __device__ void row_digit(const float* row, int n, uint32_t prefix, int shift, i
           atomicAdd(&sm.hist[(key[q][e] >> shift) & (nb - 1)], 1u);
   }
   __syncthreads();
-  tk_find_bin(sm.hist, nb, need, sm.sbuf, digit, need_out);
+  tk_find_bin<nb, kRT>(sm.hist, need, sm.sbuf, digit, need_out);
 }
 
 // Streaming finish: the exact k-th key from two passes over the row, then one ordered pass that
@@ -253,8 +257,8 @@ __device__ void finish_streaming(const TopkLaunch& a, int t, int n, uint32_t b0,
   const float* row = a.scores + (size_t)t * a.ld;
   int d1, d2;
   uint32_t need1, need2;
-  row_digit(row, n, b0, 10, 10, need0, sm, &d1, &need1);
-  row_digit(row, n, (b0 << 10) | (uint32_t)d1, 0, 10, need1, sm, &d2, &need2);
+  row_digit<10>(row, n, b0, 10, need0, sm, &d1, &need1);
+  row_digit<10>(row, n, (b0 << 10) | (uint32_t)d1, 0, need1, sm, &d2, &need2);
   const uint32_t thr = (b0 << 20) | ((uint32_t)d1 << 10) | (uint32_t)d2;
   int32_t* out = a.idx + (size_t)t * a.k;
   uint32_t base = 0, eq_seen = 0;
@@ -301,7 +305,7 @@ __device__ void finish_streaming(const TopkLaunch& a, int t, int n, uint32_t b0,
 }
 
 __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
-  __shared__ ResolveSmem sm;
+  __shared__ __attribute__((aligned(16))) ResolveSmem sm;
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = row_n(a, t);
@@ -313,11 +317,18 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   }
   uint32_t* rw = tk_row(a.ws, t);
 
-  // the row's histogram and item count into LDS, then both zeroed for the next call
+  // the row's histogram, item count and segment table in one round of loads; the histogram and
+  // the count are then zeroed for the next call
+  const int S = (n + kTkSeg - 1) / kTkSeg;
+  uint32_t cnt_s = 0;
   {
     const uint4 h = reinterpret_cast<const uint4*>(rw)[tid];
-    sm.hist[4 * tid] = h.x; sm.hist[4 * tid + 1] = h.y; sm.hist[4 * tid + 2] = h.z; sm.hist[4 * tid + 3] = h.w;
+    uint2 te = make_uint2(0u, 0u);
+    if (tid < S) te = reinterpret_cast<const uint2*>(rw + kTkOffTable)[tid];
     if (tid == 0) sm.sbuf[24] = rw[kTkOffCtr];
+    sm.hist[4 * tid] = h.x; sm.hist[4 * tid + 1] = h.y; sm.hist[4 * tid + 2] = h.z; sm.hist[4 * tid + 3] = h.w;
+    if (tid < S) sm.tst[tid] = te.x;
+    cnt_s = te.y;
     __syncthreads();
     reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) rw[kTkOffCtr] = 0u;
@@ -325,7 +336,7 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   const uint32_t total = sm.sbuf[24];
   int b0;
   uint32_t need0;
-  tk_find_bin(sm.hist, kTkBins, (uint32_t)a.k, sm.sbuf, &b0, &need0);
+  tk_find_bin<kTkBins, kRT>(sm.hist, (uint32_t)a.k, sm.sbuf, &b0, &need0);
   if (a.k > kTkFastK || total > (uint32_t)kTkItemCap) {
     finish_streaming(a, t, n, (uint32_t)b0, need0, sm);
     if (tid == 0 && a.len) a.len[t] = a.k;
@@ -333,14 +344,7 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   }
 
   // items into LDS in column order: segment s holds items tpre[s].. of the row, stored from tst[s]
-  const int S = (n + kTkSeg - 1) / kTkSeg;
-  uint32_t cnt_s = 0;
-  if (tid < S) {
-    const uint2 e = reinterpret_cast<const uint2*>(rw + kTkOffTable)[tid];
-    sm.tst[tid] = e.x;
-    cnt_s = e.y;
-  }
-  const uint32_t pre = tk_excl_scan(cnt_s, nullptr, sm.sbuf);
+  const uint32_t pre = tk_excl_scan<kRT>(cnt_s, nullptr, sm.sbuf);
   if (tid < S) sm.tpre[tid] = pre;
   __syncthreads();
   const uint2* items = reinterpret_cast<const uint2*>(rw + kTkOffItems);
@@ -356,40 +360,65 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   }
   __syncthreads();
 
-  // the exact k-th key among the candidates (the items inside b0)
-  int d1, d2;
-  uint32_t need1, need2;
-  lds_digit(sm.key, (int)total, (uint32_t)b0, 10, 10, need0, sm, &d1, &need1);
-  lds_digit(sm.key, (int)total, ((uint32_t)b0 << 10) | (uint32_t)d1, 0, 10, need1, sm, &d2, &need2);
-  const uint32_t thr = ((uint32_t)b0 << 20) | ((uint32_t)d1 << 10) | (uint32_t)d2;
+  // the exact k-th key among the candidates (the items inside b0): bits 19..10 first
+  int d1;
+  uint32_t need1;
+  lds_digit<10>(sm.key, (int)total, (uint32_t)b0, 10, need0, sm, &d1, &need1);
+  const uint32_t pre22 = ((uint32_t)b0 << 10) | (uint32_t)d1;
+  uint32_t thr, need2;
+  const uint32_t c1 = sm.hist[d1];   // keys sharing the top 22 bits of the k-th key
+  __syncthreads();                   // read before the histogram is reused below
+  if (c1 <= 64u) {
+    // typically a handful of keys share the top 22 bits: collect them and rank them in one wave
+    if (tid == 0) sm.sbuf[25] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < total; i += kRT) {
+      const uint32_t k = sm.key[i];
+      if ((k >> 10) == pre22) sm.wsum[atomicAdd(&sm.sbuf[25], 1u)] = k;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t c = sm.sbuf[25];
+      const uint32_t mine = tid < (int)c ? sm.wsum[tid] : 0u;
+      uint32_t above = 0, same = 0;
+      for (uint32_t j = 0; j < c; ++j) {
+        const uint32_t o = sm.wsum[j];
+        above += o > mine ? 1u : 0u;
+        same += o == mine ? 1u : 0u;
+      }
+      if (tid < (int)c && above < need1 && need1 <= above + same) { sm.sbuf[26] = mine; sm.sbuf[27] = need1 - above; }
+    }
+    __syncthreads();
+    thr = sm.sbuf[26];
+    need2 = sm.sbuf[27];
+  } else {
+    int d2;
+    lds_digit<10>(sm.key, (int)total, pre22, 0, need1, sm, &d2, &need2);
+    thr = (pre22 << 10) | (uint32_t)d2;
+  }
 
-  // one ordered pass: keys above thr, and the need2 lowest columns among keys equal to it
+  // One ordered pass: keys above thr, and the need2 lowest columns among the keys equal to it.
+  // Item i goes to slot (#keys above thr before i) + min(#keys equal to thr before i, need2); both
+  // counts come from one scan of a packed pair (each at most 16384, so no carry crosses).
   const uint32_t per = (total + kRT - 1) / kRT;
   const uint32_t i0 = min(total, per * tid), i1 = min(total, i0 + per);
-  uint32_t neq = 0;
-  for (uint32_t i = i0; i < i1; ++i) neq += sm.key[i] == thr ? 1u : 0u;
-  const uint32_t eq0 = tk_excl_scan(neq, nullptr, sm.sbuf);
-  uint32_t nkeep = 0;
-  {
-    uint32_t r = eq0;
-    for (uint32_t i = i0; i < i1; ++i) {
-      const uint32_t k = sm.key[i];
-      const bool eqk = k == thr;
-      nkeep += (k > thr || (eqk && r < need2)) ? 1u : 0u;
-      r += eqk ? 1u : 0u;
-    }
+  uint32_t ngt = 0, neq = 0;
+  for (uint32_t i = i0; i < i1; ++i) {
+    const uint32_t k = sm.key[i];
+    ngt += k > thr ? 1u : 0u;
+    neq += k == thr ? 1u : 0u;
   }
-  uint32_t p = tk_excl_scan(nkeep, nullptr, sm.sbuf);
-  {
-    uint32_t r = eq0;
-    for (uint32_t i = i0; i < i1; ++i) {
-      const uint32_t k = sm.key[i];
-      const bool eqk = k == thr;
-      if (k > thr || (eqk && r < need2)) {
-        if (p < (uint32_t)a.k) out[p] = (int32_t)sm.col[i];
-        ++p;
-      }
-      r += eqk ? 1u : 0u;
+  const uint32_t pk = tk_excl_scan<kRT>((neq << 16) | ngt, nullptr, sm.sbuf);
+  uint32_t gt = pk & 0xFFFFu, eq = pk >> 16;
+  for (uint32_t i = i0; i < i1; ++i) {
+    const uint32_t k = sm.key[i];
+    if (k > thr) {
+      const uint32_t p = gt + min(eq, need2);
+      if (p < (uint32_t)a.k) out[p] = (int32_t)sm.col[i];
+      ++gt;
+    } else if (k == thr) {
+      if (eq < need2 && gt + eq < (uint32_t)a.k) out[gt + eq] = (int32_t)sm.col[i];
+      ++eq;
     }
   }
   if (tid == 0 && a.len) a.len[t] = a.k;

@@ -31,9 +31,12 @@ __host__ __device__ inline size_t tk_total_words(int T) { return (size_t)T * kTk
 __device__ inline uint32_t* tk_row(void* ws, int t) { return reinterpret_cast<uint32_t*>(ws) + (size_t)t * kTkRowWords; }
 __device__ inline uint32_t* tk_hist(void* ws, int t) { return tk_row(ws, t); }
 
-// Block-wide exclusive prefix sum (blockDim.x a multiple of 64, at most 1024 threads).
-__device__ inline uint32_t tk_excl_scan(uint32_t v, uint32_t* total, uint32_t* sbuf /* >= 17 words */) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+// Block-wide exclusive prefix sum over NT threads (a multiple of 64, at most 1024); *total, if
+// given, gets the sum.  sbuf: at least NT/64 words.
+template <int NT>
+__device__ inline uint32_t tk_excl_scan(uint32_t v, uint32_t* total, uint32_t* sbuf) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -42,32 +45,46 @@ __device__ inline uint32_t tk_excl_scan(uint32_t v, uint32_t* total, uint32_t* s
   }
   if (lane == 63) sbuf[wave] = x;
   __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < nw; ++w) { const uint32_t s = sbuf[w]; sbuf[w] = run; run += s; }
-    sbuf[16] = run;
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t s = sbuf[w];
+    off += w < wave ? s : 0u;
+    tot += s;
   }
   __syncthreads();
-  const uint32_t r = sbuf[wave] + x - v;
-  if (total) *total = sbuf[16];
-  __syncthreads();
-  return r;
+  if (total) *total = tot;
+  return off + x - v;
 }
 
-// The bin of an nb-bin histogram (nb a multiple of blockDim.x) holding the need-th largest key:
-// returns it and the count still needed inside it, identically in every thread.
-__device__ inline void tk_find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* sbuf, int* bin_out,
+// The bin of an NB-bin histogram (16-byte aligned) that holds the need-th largest key: returns it
+// and the count still needed inside it, identically in every thread.  Thread i owns NB/NT
+// consecutive bins counted from the top.  sbuf: at least 22 words.
+template <int NB, int NT>
+__device__ inline void tk_find_bin(const uint32_t* h, uint32_t need, uint32_t* sbuf, int* bin_out,
                                    uint32_t* need_out) {
-  const int tid = threadIdx.x;
-  const int per = nb / (int)blockDim.x;
-  const int hi = nb - per * tid;   // thread 0 owns the top bins
+  static_assert(NB % NT == 0, "bins per thread");
+  constexpr int PER = NB / NT;
+  const int lo = NB - PER * ((int)threadIdx.x + 1);
+  uint32_t c[PER];
+  if constexpr (PER % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const uint4 x = *reinterpret_cast<const uint4*>(h + lo + 4 * q);
+      c[4 * q] = x.x; c[4 * q + 1] = x.y; c[4 * q + 2] = x.z; c[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) c[i] = h[lo + i];
+  }
   uint32_t local = 0;
-  for (int i = 1; i <= per; ++i) local += h[hi - i];
-  uint32_t above = tk_excl_scan(local, nullptr, sbuf);
-  for (int i = 1; i <= per; ++i) {
-    const uint32_t c = h[hi - i];
-    if (above < need && need <= above + c) { sbuf[20] = (uint32_t)(hi - i); sbuf[21] = need - above; }
-    above += c;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) local += c[i];
+  uint32_t above = tk_excl_scan<NT>(local, nullptr, sbuf);
+#pragma unroll
+  for (int i = PER - 1; i >= 0; --i) {
+    if (above < need && need <= above + c[i]) { sbuf[20] = (uint32_t)(lo + i); sbuf[21] = need - above; }
+    above += c[i];
   }
   __syncthreads();
   *bin_out = (int)sbuf[20];
