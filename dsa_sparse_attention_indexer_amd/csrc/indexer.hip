@@ -38,7 +38,7 @@ constexpr int kHPad = 32;        // heads padded to the MFMA M dimension
 constexpr int kThreads = 256;    // 4 waves
 constexpr int kTile = 32;        // keys per MFMA N tile
 constexpr int kQsStride = kD + 1;  // double row stride in LDS (odd: per-head reductions avoid conflicts)
-constexpr int kDepth = 3;        // key tiles in flight per wave in the fp8 stream
+constexpr int kDepth = 5;        // key tiles in flight per wave in the fp8 stream
 
 struct PrepSmem {
   double qs[kHPad][kQsStride];   // q' (rotated, SSMax-scaled), float64
