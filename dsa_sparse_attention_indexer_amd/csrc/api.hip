@@ -150,7 +150,7 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const 
   if (st != DSA_OK || d->num_q == 0) return st;
   dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
                                         ld_scores);
-  const bool fused = d->k_dtype == DSA_FP8_E4M3FN;
+  const bool fused = d->k_dtype == DSA_FP8_E4M3FN && !dsa::indexer_grouped(d->num_q, d->k_dtype);
   if (fused) { a.topk_ws = topk_ws; a.topk_k = k; }
   hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status("dsa_indexer_topk", e);

@@ -73,6 +73,7 @@ constexpr int64_t kTopkMaxCols = int64_t(1) << 22;   // columns a top-k row may 
 
 size_t topk_ws_bytes(int T);
 size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype);
+bool indexer_grouped(int T, dsa_dtype_t k_dtype);   // many-query path: no fused first top-k digit
 size_t block_select_ws_bytes(int T, int64_t ld, int block);
 
 // ---- launchers (return the HIP status of the last launch) -----------------------------------

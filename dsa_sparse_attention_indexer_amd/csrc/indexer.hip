@@ -228,6 +228,16 @@ __device__ void build_fp8_operands(PrepSmem& sm, QPrepFp8* o, const IndexerLaunc
   __syncthreads();
 }
 
+// Many queries (prefill): each query's MFMA operands prepared once, one workgroup per query, into
+// the workspace; the grouped stream kernel below loads them.
+__global__ void __launch_bounds__(kThreads) k_index_qprep_fp8(IndexerLaunch a, void* ws) {
+  __shared__ PrepSmem sm;
+  const int t = blockIdx.x;
+  const int p = clampi(a.q_pos[t], -1, a.max_ctx - 1);
+  prep_query(sm, a, t, p < 0 ? 0 : p);
+  build_fp8_operands(sm, reinterpret_cast<QPrepFp8*>(reinterpret_cast<uint8_t*>(ws) + (size_t)t * kQPrepBytes), a, t);
+}
+
 // fp32 keys: q' as fp32 and the head weights, one workgroup per query, to the workspace.
 __global__ void __launch_bounds__(kThreads) k_index_qprep(IndexerLaunch a, void* ws) {
   __shared__ PrepSmem sm;
@@ -295,6 +305,35 @@ __device__ __forceinline__ float tile_scores(const KeyTile& kt, const half8* ahi
   // lanes l and l^32 hold the two halves of key column l&31's head sum
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
   return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * kt.sc;
+}
+
+// Two tiles at once with independent accumulators (the MFMA chains interleave; used where the
+// matrix cores, not memory, bound the stream).
+__device__ __forceinline__ void tile_scores2(const KeyTile& k0, const KeyTile& k1, const half8* ahi, const half8* alo,
+                                             const float* cf, float& s0, float& s1) {
+  float16v a0 = {}, a1 = {};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const half8 x0 = fp8x8_to_half8(k0.x[c][2 * h], k0.x[c][2 * h + 1]);
+      const half8 x1 = fp8x8_to_half8(k1.x[c][2 * h], k1.x[c][2 * h + 1]);
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[2 * c + h], x0, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[2 * c + h], x1, a1, 0, 0, 0);
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[2 * c + h], x0, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[2 * c + h], x1, a1, 0, 0, 0);
+    }
+  }
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    p0 = fmaf(cf[r], fmaxf(a0[r], 0.f), p0);
+    p1 = fmaf(cf[r], fmaxf(a1[r], 0.f), p1);
+  }
+  const auto w0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p0), false, false);
+  const auto w1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p1), false, false);
+  s0 = (__uint_as_float(w0[0]) + __uint_as_float(w0[1])) * k0.sc;
+  s1 = (__uint_as_float(w1[0]) + __uint_as_float(w1[1])) * k1.sc;
 }
 
 // TPW: 32-key tiles per wave (a workgroup covers 4 * 32 * TPW keys).  HIST: also histogram the
@@ -374,6 +413,192 @@ k_index_scores_fp8(IndexerLaunch a) {
   }
 }
 
+// Grouped variant for many queries (prefill).  Workgroup (x, y) scores key chunk x for the four
+// queries 4y..4y+3, one per wave, with operands prepared once per query in the workspace.  When the
+// four queries read the same sequence (consecutive queries of a chunked prefill), each 32-key tile
+// is gathered once into an LDS ring (global_load_lds, one 16-byte chunk per lane) and all four waves
+// read their MFMA B operands from it, so the key stream is read from memory once per four queries.
+// Otherwise every wave streams its own keys from memory as the decode kernel does.
+constexpr int kGroup = 4;
+constexpr int kRingTiles = 8;                    // key tiles in flight per workgroup
+constexpr int kTileBytes = kTile * kD;           // 4 KiB
+
+typedef __attribute__((address_space(3))) void* lds_vp;
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_vp)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_vp)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Barrier for LDS hand-offs that does not wait for global loads in flight.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16-byte slot of (row r, chunk k) of a tile in LDS: chunks are XOR-swizzled by row pair so that the
+// 16 lanes of a ds_read_b128 quarter (rows col..col+15, one chunk) hit 16 different bank groups.
+__device__ __forceinline__ int tile_slot(int r, int k) { return 8 * r + (k ^ ((r >> 1) & 7)); }
+
+struct SharedTiles {
+  u32x4 key[kRingTiles][kTile * kD / 16];
+  float sc[kRingTiles][kTile];
+};
+
+// Waves of mismatched sequences: each streams its own keys (as the decode kernel does).
+template <int TPW>
+__device__ void grouped_private_stream(const IndexerLaunch& a, int t, int c0, const half8* ahi, const half8* alo,
+                                       const float* cf) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
+  const int b = clampi(a.q_seq[t], 0, a.B - 1);
+  const int n = clampi(a.q_pos[t], -1, a.max_ctx - 1) + 1;
+  if (c0 >= n) return;
+  const uint32_t nrow = (uint32_t)(min(n, c0 + kTile * TPW) - c0);
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(reinterpret_cast<const uint8_t*>(a.k_cache) + ((size_t)b * a.max_ctx + c0) * kD, nrow * kD);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.k_scale + (size_t)b * a.max_ctx + c0, nrow * 4u);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.scores + (size_t)t * a.ld + c0, nrow * 4u);
+  const uint32_t out_off = g == 0 ? 4u * col : 0x80000000u;
+  KeyTile tb[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i) load_tile(tb[i], krs, srs, i * kTile + col, g);
+  uint32_t rel = 0;
+#pragma unroll
+  for (int it = 0; it < TPW; ++it) {
+    KeyTile& cur = tb[it % kDepth];
+    const float sc = tile_scores(cur, ahi, alo, cf);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
+    if (it + kDepth < TPW) load_tile(cur, krs, srs, rel + kDepth * kTile + col, g);
+    rel += kTile;
+  }
+}
+
+template <int TPW>
+__global__ void __launch_bounds__(kThreads)
+k_index_scores_fp8_grouped(IndexerLaunch a, const void* ws) {
+  static_assert(TPW >= kRingTiles, "ring shorter than the chunk");
+  __shared__ __attribute__((aligned(16))) SharedTiles st;
+  __shared__ int sseq[kGroup], sn[kGroup];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, col = lane & 31;
+  const int t = kGroup * blockIdx.y + wave;
+  const bool live = t < a.T;
+  const int c0 = blockIdx.x * kTile * TPW;
+  if (lane == 0) {
+    sseq[wave] = live ? clampi(a.q_seq[t], 0, a.B - 1) : -1;
+    sn[wave] = live ? clampi(a.q_pos[t], -1, a.max_ctx - 1) + 1 : 0;
+  }
+  __syncthreads();
+  int b = -1, nmax = 0;
+  bool uniform = true;
+#pragma unroll
+  for (int w = 0; w < kGroup; ++w) {
+    const int sw = sseq[w];
+    if (sw >= 0) {
+      uniform = uniform && (b < 0 || sw == b);
+      b = b < 0 ? sw : b;
+      nmax = max(nmax, sn[w]);
+    }
+  }
+  if (c0 >= nmax) return;   // every query of the group has fewer keys than the chunk start
+
+  half8 ahi[8], alo[8];
+  float cf[16];
+  auto load_operands = [&]() {
+    if (!live) return;
+    const QPrepFp8* qp = reinterpret_cast<const QPrepFp8*>(reinterpret_cast<const uint8_t*>(ws) + (size_t)t * kQPrepBytes);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      ahi[s] = __builtin_bit_cast(half8, qp->a[2 * s][lane]);
+      alo[s] = __builtin_bit_cast(half8, qp->a[2 * s + 1][lane]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cf[r] = qp->cf[r][lane];
+  };
+  if (!uniform) {
+    load_operands();
+    if (live) grouped_private_stream<TPW>(a, t, c0, ahi, alo, cf);
+    return;
+  }
+
+  // shared stream: rows c0.. of sequence b, up to the longest query of the group
+  const int rows = min(nmax - c0, kTile * TPW);
+  const int ntiles = (rows + kTile - 1) / kTile;
+  const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.k_cache) + ((size_t)b * a.max_ctx + c0) * kD;
+  const float* sseqp = a.k_scale + (size_t)b * a.max_ctx + c0;
+  const int n = live ? sn[wave] : 0;
+  const uint32_t nrow = (uint32_t)max(0, min(n - c0, kTile * TPW));
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.scores + (size_t)(live ? t : 0) * a.ld + c0, nrow * 4u);
+  const uint32_t out_off = g == 0 ? 4u * col : 0x80000000u;
+  // this lane's slot q = 64 * wave + lane of each tile holds row q/8's chunk (q%8) ^ swizzle
+  const int q = 64 * wave + lane;
+  const int qr = q >> 3, qk = (q & 7) ^ ((qr >> 1) & 7);
+  auto issue = [&](int tau) {
+    const int slot = tau % kRingTiles;
+    const int r = min(kTile * tau + qr, rows - 1);   // rows past the group's range read a valid row
+    dma16(kseq + (size_t)r * kD + 16 * qk, &st.key[slot][64 * wave]);
+    if (lane < kTile / kGroup) dma4(sseqp + min(kTile * tau + (kTile / kGroup) * wave + lane, rows - 1),
+                                    &st.sc[slot][(kTile / kGroup) * wave]);
+  };
+  constexpr int LPT = 2;   // LDS-direct loads per wave and tile
+#pragma unroll
+  for (int i = 0; i < kRingTiles; ++i)
+    if (i < ntiles) issue(i);
+  load_operands();
+  wait_vm<0>();   // operands and the first tiles are in (tells the compiler too: no waits below)
+  // Two tiles per step: one barrier per pair, and their MFMA chains interleave.
+  for (int tau = 0; tau < ntiles; tau += 2) {
+    // gathers issued so far: the first ring's worth, then two per step from step 1 on (after the
+    // wait); tiles tau and tau + 1 have landed once at most the later ones are outstanding
+    const int step = tau >> 1;
+    const int issued = min(ntiles, kRingTiles + 2 * max(step - 1, 0));
+    const int later = issued - min(tau + 1, ntiles - 1) - 1;
+    switch (later) {
+      case 7: wait_vm<7 * LPT>(); break;
+      case 6: wait_vm<6 * LPT>(); break;
+      case 5: wait_vm<5 * LPT>(); break;
+      case 4: wait_vm<4 * LPT>(); break;
+      case 3: wait_vm<3 * LPT>(); break;
+      case 2: wait_vm<2 * LPT>(); break;
+      case 1: wait_vm<LPT>(); break;
+      default: wait_vm<0>(); break;
+    }
+    lds_sync();   // tiles tau, tau + 1 are in LDS for every wave; every wave is done with the last pair
+    if (step >= 1) {
+      if (tau - 2 + kRingTiles < ntiles) issue(tau - 2 + kRingTiles);
+      if (tau - 1 + kRingTiles < ntiles) issue(tau - 1 + kRingTiles);
+    }
+    const uint32_t rel = (uint32_t)(kTile * tau);
+    if (rel < nrow) {
+      KeyTile k0, k1;
+      const int s0 = tau % kRingTiles, s1 = (tau + 1) % kRingTiles;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        k0.x[c] = st.key[s0][tile_slot(col, 2 * c + g)];
+        k1.x[c] = st.key[s1][tile_slot(col, 2 * c + g)];
+      }
+      k0.sc = st.sc[s0][col];
+      k1.sc = st.sc[s1][col];
+      float r0, r1;
+      tile_scores2(k0, k1, ahi, alo, cf, r0, r1);   // past the last tile, k1 holds stale data: not stored
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r0), ors, out_off + 4u * rel, 0, 0);
+      if (tau + 1 < ntiles)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r1), ors, out_off + 4u * (rel + kTile), 0, 0);
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // fp32 keys: vector FMAs
 // ------------------------------------------------------------------------------------------
@@ -418,11 +643,23 @@ k_index_scores_f32(IndexerLaunch a, const void* ws) {
 
 }  // namespace
 
-size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype) { return k_dtype == DSA_FP8_E4M3FN ? 0 : (size_t)T * kQPrepBytes; }
+// fp8 keys take the grouped path (queries prepared once into the workspace) from this many queries on
+constexpr int kGroupedMinQueries = 256;
+
+size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype) {
+  if (k_dtype == DSA_FP8_E4M3FN && T < kGroupedMinQueries) return 0;
+  return (size_t)T * kQPrepBytes;
+}
+
+bool indexer_grouped(int T, dsa_dtype_t k_dtype) { return k_dtype == DSA_FP8_E4M3FN && T >= kGroupedMinQueries; }
 
 hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
   if (a.T == 0 || a.max_ctx == 0) return hipSuccess;
-  if (a.k_dtype == DSA_FP8_E4M3FN) {
+  if (indexer_grouped(a.T, a.k_dtype)) {
+    hipLaunchKernelGGL(k_index_qprep_fp8, dim3(a.T), dim3(kThreads), 0, s, a, ws);
+    dim3 grid((a.max_ctx + kTile * 32 - 1) / (kTile * 32), (a.T + kGroup - 1) / kGroup);
+    hipLaunchKernelGGL(k_index_scores_fp8_grouped<32>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
+  } else if (a.k_dtype == DSA_FP8_E4M3FN) {
     // 4096-key chunks (32 tiles per wave) when that still gives >= 512 workgroups, else 1024.
     const int64_t big = (int64_t)a.T * ((a.max_ctx + 4095) / 4096);
     const bool hist = a.topk_ws != nullptr;

@@ -46,6 +46,11 @@ SCORE_CASES = [
     ("fp8_h4", dict(seq_lens=[5000, 333], max_ctx=5000, num_heads=4)),
     ("fp8_f32q_nossmax", dict(seq_lens=[1025], max_ctx=1028, q_dtype=torch.float32, ssmax=False)),
     ("f32_bf16q_h7", dict(seq_lens=[900], max_ctx=900, fp8=False, num_heads=7)),
+    # >= 256 queries take the grouped many-query path (queries prepared once, 4 per workgroup)
+    ("fp8_prefill_grouped", dict(seq_lens=[6000], max_ctx=6000, q_positions=list(range(5699, 6000)))),
+    ("fp8_grouped_mixed_seqs", dict(seq_lens=[3000, 2500, 1200], max_ctx=3000,
+                                    q_positions=[(37 * i) % 1100 + 50 for i in range(258)],
+                                    q_seqs=[i % 3 for i in range(258)])),
 ]
 
 
