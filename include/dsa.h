@@ -84,8 +84,11 @@ int32_t dsa_abi_version(void);
  *   k_scale  [num_seqs][max_ctx] f32       per-token key scale (FP8 keys; NULL for F32 keys)
  *   scores   [num_q][ld_scores] f32        row t gets S(0..p); entries past p are not written
  *   ld_scores >= max_ctx
- *   ws       device workspace of at least dsa_indexer_workspace_size(desc) bytes (the prepared
- *            queries: one small kernel forms q' once per query before the key stream starts)
+ *   ws       device workspace of at least dsa_indexer_workspace_size(desc) bytes, 16-byte
+ *            aligned: the queries prepared once each (about 20 KiB per query) on the fp32-key
+ *            path and, from 256 queries on (prefill), on the fp8 path; 0 bytes otherwise (the fp8
+ *            decode kernel prepares its query while its first key tiles are in flight), and then
+ *            ws may be NULL.
  *
  * Supported: head_dim == 128; 1 <= num_heads <= 32; rope_dim in {0, 64}; q_dtype F32 or BF16;
  * k_dtype F32 (fp32 vector path) or FP8_E4M3FN (matrix-core path).  The FP8 path computes q'
