@@ -54,15 +54,32 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
 }
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt2_bf16(float2v v) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Split partials: the fp32 path keeps them unnormalised in fp32; the fp8 path (whose error budget
+// is set by its bf16 operands) stores them normalised by their own sum, as bf16, which halves the
+// partial traffic; the combine knows the format from the cache dtype.
+__device__ __forceinline__ bool bf16_partials(const MlaLaunch& a) { return a.kv_dtype == DSA_FP8_E4M3FN; }
+
 __device__ __forceinline__ void write_partial_or_final(const MlaLaunch& a, int t, int split, int head,
                                                        float m_log2, float l_tot, const float* o, int d0,
                                                        int ndim) {
   // o: ndim consecutive output dims starting at d0 for this head (unnormalised)
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (a.splits == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* dst = a.out + ((size_t)t * a.H + head) * a.kv_lora + d0;
     for (int i = 0; i < ndim; i += 4)
       *reinterpret_cast<float4*>(dst + i) = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
+  } else if (bf16_partials(a)) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.ws) + (((size_t)t * a.splits + split) * a.H + head) * a.kv_lora + d0;
+    for (int i = 0; i < ndim; i += 4)
+      *reinterpret_cast<uint2*>(dst + i) = make_uint2(cvt2_bf16(float2v{o[i] * inv, o[i + 1] * inv}),
+                                                      cvt2_bf16(float2v{o[i + 2] * inv, o[i + 3] * inv}));
   } else {
     float* dst = a.ws + (((size_t)t * a.splits + split) * a.H + head) * a.kv_lora + d0;
     for (int i = 0; i < ndim; i += 4)
@@ -82,12 +99,6 @@ __device__ __forceinline__ void write_stats(const MlaLaunch& a, int t, int split
 }
 
 typedef short short4v __attribute__((ext_vector_type(4)));
-typedef float float2v __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t cvt2_bf16(float2v v) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // 16 fp8 codes times one scale -> 16 bf16 (8 dwords), nearest even.
 __device__ __forceinline__ void dequant16(const u32x4 raw, float s, u32x4& lo, u32x4& hi) {
@@ -492,18 +503,31 @@ __global__ void __launch_bounds__(kCombineThreads) k_mla_combine(MlaLaunch a) {
   float Ls = w * l;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
-  if (tid < 64) wts[tid] = Ls > 0.f ? w / Ls : 0.f;
+  const bool norm = bf16_partials(a);   // normalised partials carry their own sum l
+  if (tid < 64) wts[tid] = Ls > 0.f ? (norm ? w * l : w) / Ls : 0.f;
   if (tid == 0 && a.lse) a.lse[(size_t)t * a.H + h] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
   __syncthreads();
-  const float4* part = reinterpret_cast<const float4*>(a.ws + ((size_t)t * a.splits * a.H + h) * a.kv_lora);
-  const size_t sstride = (size_t)a.H * a.kv_lora / 4;   // float4s between consecutive splits
+  float4* outp = reinterpret_cast<float4*>(a.out + ((size_t)t * a.H + h) * a.kv_lora);
+  const size_t base = ((size_t)t * a.splits * a.H + h) * a.kv_lora;   // element offset of split 0
+  const size_t sstride = (size_t)a.H * a.kv_lora;                    // elements between splits
   for (int e = tid; e < a.kv_lora / 4; e += kCombineThreads) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < a.splits; s0 += 16) {
       float4 v[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        v[j] = s0 + j < a.splits ? part[(size_t)(s0 + j) * sstride + e] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < 16; ++j) {
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (s0 + j < a.splits) {
+          const size_t off = base + (size_t)(s0 + j) * sstride + 4 * e;
+          if (norm) {
+            const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.ws) + off);
+            v[j] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+          } else {
+            v[j] = *reinterpret_cast<const float4*>(a.ws + off);
+          }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float wj = s0 + j < a.splits ? wts[s0 + j] : 0.f;
@@ -511,7 +535,7 @@ __global__ void __launch_bounds__(kCombineThreads) k_mla_combine(MlaLaunch a) {
         acc.z = fmaf(wj, v[j].z, acc.z); acc.w = fmaf(wj, v[j].w, acc.w);
       }
     }
-    reinterpret_cast<float4*>(a.out + ((size_t)t * a.H + h) * a.kv_lora)[e] = acc;
+    outp[e] = acc;
   }
 }
 
