@@ -132,6 +132,7 @@ TOPK_CASES = [
     ("small_k", 16, [15, 16, 17, 100, 4095, 4096, 4097, 9000]),
     ("k1", 1, [1, 2, 5000]),
     ("big_row", 2048, [131072]),
+    ("k_above_lds_resolve", 5000, [4999, 5000, 5001, 20000]),   # k > 4096: the streaming finish
 ]
 
 
@@ -203,6 +204,23 @@ def test_block_select_bit_exact(dsa):
         assert gl[t] == rl and np.array_equal(gi[t], ref), f"row {t}"
 
 
+def test_block_select_many_blocks(dsa):
+    """More block maxima than the picker keeps in registers (1-key blocks over 20000 keys)."""
+    rng = np.random.default_rng(23)
+    n = 20000
+    sc = rng.standard_normal((2, n)).astype(np.float32)
+    sc[1, :] = np.round(sc[1, :] * 4)                 # ties between single-key blocks
+    qp = torch.as_tensor([n - 1, 17000], dtype=torch.int32).cuda()
+    idx = torch.empty(2, 2048, dtype=torch.int32, device="cuda")
+    ln = torch.empty(2, dtype=torch.int32, device="cuda")
+    dsa.dsa_block_select(torch.from_numpy(sc).cuda(), qp, idx, ln, block=1, nblocks=16)
+    torch.cuda.synchronize()
+    gi, gl = idx.cpu().numpy(), ln.cpu().numpy()
+    for t, p in enumerate([n - 1, 17000]):
+        ref, rl = O.block_select_row(sc[t, :p + 1].astype(np.float64), p, block=1, nblocks=16)
+        assert gl[t] == rl and np.array_equal(gi[t], ref), f"row {t}"
+
+
 # ---------------------------------------------------------------------------------------------
 # sparse MLA on a given selection
 # ---------------------------------------------------------------------------------------------
@@ -215,6 +233,9 @@ MLA_CASES = [
     ("f32_rope_decode", dict(seq_lens=[2500, 3000], max_ctx=3000, fp8=False, q_dtype=torch.float32), False, 0),
     ("f32_nope_prefill", dict(seq_lens=[2200], max_ctx=2200, fp8=False, q_dtype=torch.float32, rope=False,
                               q_positions=[2199, 50]), True, 0),
+    # selections wider than the 2048 slots staged in LDS at a time (and top-k above 4096)
+    ("fp8_topk4100_prefill", dict(seq_lens=[6000], max_ctx=6000, q_positions=[5999, 4500, 3000], topk=4100), True, 0),
+    ("fp8_topk4100_decode", dict(seq_lens=[6000, 5000], max_ctx=6000, topk=4100), False, 0),
 ]
 
 
