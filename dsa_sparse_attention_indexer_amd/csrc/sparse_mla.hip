@@ -39,9 +39,9 @@ constexpr int kRow = 576;                 // latent row: 512 + 64
 constexpr int kLora = 512;
 constexpr int kBlocks = kRow / 64;        // scales per row
 constexpr int kKsStride = kRow + 8;       // bf16 per key-major row (1168 B: rows shift by 4 banks)
-constexpr int kRing = 4;                  // key tiles gathered ahead (fp8 path)
 constexpr int kRowsChunk = 2048;          // selection slots staged in LDS at a time (fp8 path)
 constexpr float kLazyLog2 = 8.f;          // the running maximum lags the true one by at most this (log2)
+constexpr float kNoMax = -1.0e30f;        // running maximum before the first valid key (fp8 path)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -135,6 +135,17 @@ __device__ __forceinline__ void gather4_to_lds(const void* g, void* lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
 
+// Maximum over lanes l and l ^ 16 (ds_swizzle swap of 16-lane halves) and over l and l ^ 32
+// (v_permlane32_swap), without the address arithmetic of a bpermute shuffle.
+__device__ __forceinline__ float max_xor16(float x) {
+  return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 // Workgroup barrier for hand-offs through LDS: this wave's LDS operations are complete before it,
 // but global loads in flight (the gathers of later tiles) are not waited for, as __syncthreads
 // would.  The empty asm statements keep the compiler from moving memory accesses across it.
@@ -146,6 +157,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 constexpr int kMlaThreads = 512;   // fp8 path: 8 waves = 4 head groups x 2 halves
+constexpr int kSlots = 3;          // raw tiles in LDS: the next one to dequantise plus two in flight
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 template <int ROPE>
 struct MlaFp8 {
@@ -160,7 +177,9 @@ struct MlaFp8 {
   static constexpr int WSCI = (WSC + 63) / 64;          // scale loads per wave and tile
   static constexpr int LPT = WCHI + WSCI;               // LDS-direct loads per wave and tile
   static constexpr int NCH = kTileK * CHUNKS;
-  static constexpr int PER = (NCH + kMlaThreads - 1) / kMlaThreads;
+  static constexpr int FULL = NCH / kMlaThreads;        // whole chunks each thread dequantises
+  static constexpr int REM = NCH - FULL * kMlaThreads;  // the rest, split into 4-byte quarters
+  static_assert(4 * REM <= kMlaThreads, "at most one quarter chunk per thread");
   static constexpr int ODIM = kLora / 2;                // output dims per wave
 };
 
@@ -168,125 +187,156 @@ struct MlaFp8 {
 // S^T over its half of the query dims (K-steps KH*half..KH*half+KH-1) for all 32 keys, adds the
 // other half's partial through LDS, and accumulates O^T for output dims 256*half..256*half+255.
 // Per lane: the query slice (KH operands) and 64 accumulator registers.
+//
+// Tiles are software-pipelined over two bf16 buffers (ks0, ks1) and kSlots raw slots, two
+// barriers per tile tau:
+//   B0  ks[tau & 1] holds tile tau, tile tau+1's gathers are in their slot, the other bf16 buffer
+//       and tile tau's slot are free;
+//   phase 1: gathers of tile tau+3 into tile tau's slot; the partial QK^T of tile tau on the
+//       matrix cores while the same waves dequantise tile tau+1 into the other buffer (independent
+//       instruction streams the compiler interleaves); partial scores to LDS;
+//   B1  both halves' partial scores are in LDS;
+//   phase 2: online softmax and PV of tile tau.
 template <int ROPE>
 __global__ void __launch_bounds__(kMlaThreads)
 k_mla_fp8(MlaLaunch a) {
   using C = MlaFp8<ROPE>;
   constexpr int DQ = C::DQ, KSTEPS = C::KSTEPS, CHUNKS = C::CHUNKS, NSC = C::NSC, WROWS = C::WROWS;
-  constexpr int LPT = C::LPT, NCH = C::NCH, PER = C::PER;
+  constexpr int LPT = C::LPT;
   constexpr int MD = C::ODIM / 16;                      // 16-dim output tiles per wave
-  static_assert(kRing == 4, "four ring slots, each its own LDS object");
-  // Raw fp8 rows and scales of up to four tiles in flight, gathered straight into LDS.
+  // Raw fp8 rows and scales of a tile, gathered straight into LDS.
   struct Slot {
     uint8_t raw[kTileK * DQ];
     float sc[kTileK * NSC];
   };
-  __shared__ __attribute__((aligned(16))) Slot sl0, sl1, sl2, sl3;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kTileK][kKsStride];
+  typedef uint16_t KsTile[kTileK][kKsStride];
+  __shared__ __attribute__((aligned(16))) Slot sl[kSlots];
+  __shared__ __attribute__((aligned(16))) KsTile ks0, ks1;
   __shared__ __attribute__((aligned(16))) float4v xz[2][4][2][64];   // partial scores swapped between halves
   __shared__ int rows[kRowsChunk];                      // row of every slot of the current chunk, -1 if none
   const int t = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hg = wave & 3, half = wave >> 2;
   const int c = lane & 15, g = lane >> 4;
-  const int b = clampi(a.q_seq[t], 0, a.B - 1);
-  const int L = a.len ? clampi(a.len[t], 0, a.topk) : a.topk;
   const int slot0 = split * a.per_split;
-  const int slot1 = min(L, slot0 + a.per_split);
   const bool active = 16 * hg < a.H;
   const int head = 16 * hg + c;
   const float zscale = a.softmax_scale * kLog2e;
   const int32_t* irow = a.idx + (size_t)t * a.topk;
-  const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(a.kv) + (size_t)b * a.max_ctx * kRow;
-  const float* scseq = a.kv_scale + (size_t)b * a.max_ctx * kBlocks;
 
+  // The first chunk's row indices and the query are loaded before the selection length and the
+  // sequence are known, so that all of these loads are in flight together.
+  const int slot_end = min(slot0 + a.per_split, a.topk);   // this split's slots before the length cut
+  constexpr int RPT = kRowsChunk / kMlaThreads;
+  int rv[RPT];
+  auto load_rows = [&](int cb) {
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int i = tid + kMlaThreads * u;
+      rv[u] = cb + i < slot_end ? irow[cb + i] : -1;
+    }
+  };
+  load_rows(slot0);
   constexpr int KH = KSTEPS / 2;                        // K-steps per half
   static_assert(KSTEPS % 2 == 0, "query dims split in two halves");
-  bf16x8 qreg[KH];
+  bf16x8 qreg[KH];                                      // zero in waves without heads
+#pragma unroll
+  for (int s = 0; s < KH; ++s) qreg[s] = bf16x8{};
   if (active) {
     const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + head) * DQ + 32 * KH * half;
 #pragma unroll
     for (int s = 0; s < KH; ++s)
       qreg[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 32 * s + 8 * g));
   }
-  float m_run = -INFINITY, l_run = 0.f;
+  const int b = clampi(a.q_seq[t], 0, a.B - 1);
+  const int L = a.len ? clampi(a.len[t], 0, a.topk) : a.topk;
+  const int slot1 = min(L, slot0 + a.per_split);
+  const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(a.kv) + (size_t)b * a.max_ctx * kRow;
+  const float* scseq = a.kv_scale + (size_t)b * a.max_ctx * kBlocks;
+
+  float m_run = kNoMax, l_run = 0.f;
   float4v oacc[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) oacc[md] = float4v{0.f, 0.f, 0.f, 0.f};
 
   // Wave w gathers rows WROWS*w.. of tile tau: their chunks and scales are contiguous in the slot,
   // and lane l of a load lands at 16*l (4*l) bytes from the load's base.
-  auto issue = [&](Slot& sl, int tau) {
+  auto issue = [&](Slot& s, int tau) {
     const int* tr = rows + kTileK * tau + WROWS * wave;
+    // every row index first: the gathers are opaque to the compiler, which keeps LDS reads after them
+    int rc[C::WCHI], rs[C::WSCI];
 #pragma unroll
     for (int j = 0; j < C::WCHI; ++j) {
       const int i = 64 * j + lane;
-      const int r = i < C::WCH ? i / CHUNKS : 0, cc = i % CHUNKS;
-      const int row = max(tr[r], 0);
-      if (i < C::WCH) gather16_to_lds(kvseq + (size_t)row * kRow + 16 * cc, sl.raw + WROWS * wave * DQ + 1024 * j);
+      rc[j] = max(tr[i < C::WCH ? i / CHUNKS : 0], 0);
     }
 #pragma unroll
     for (int j = 0; j < C::WSCI; ++j) {
       const int i = 64 * j + lane;
-      const int r = i < C::WSC ? i / NSC : 0, sc = i % NSC;
-      const int row = max(tr[r], 0);
-      if (i < C::WSC) gather4_to_lds(scseq + (size_t)row * kBlocks + sc, sl.sc + WROWS * wave * NSC + 64 * j);
+      rs[j] = max(tr[i < C::WSC ? i / NSC : 0], 0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::WCHI; ++j) {
+      const int i = 64 * j + lane;
+      if (i < C::WCH)
+        gather16_to_lds(kvseq + (size_t)rc[j] * kRow + 16 * (i % CHUNKS), s.raw + WROWS * wave * DQ + 1024 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < C::WSCI; ++j) {
+      const int i = 64 * j + lane;
+      if (i < C::WSC)
+        gather4_to_lds(scseq + (size_t)rs[j] * kBlocks + i % NSC, s.sc + WROWS * wave * NSC + 64 * j);
     }
   };
 
-  // One tile: wait for its gathers, dequantise to bf16 in ks, refill the slot, then QK^T, online
-  // softmax and PV on the matrix cores.
-  auto step = [&](Slot& sl, int tau, int ntiles) {
-    const int later = min(ntiles, tau + kRing) - tau - 1;   // tiles whose gathers were issued after tau's
-    if (later >= 3) wait_vmcnt<3 * LPT>();
-    else if (later == 2) wait_vmcnt<2 * LPT>();
-    else if (later == 1) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
-    lds_barrier();                         // every wave's gathers of tile tau are in LDS; ks is free
+  // fp8 tile -> bf16 key-major tile (code * scale, nearest even); the same share for every thread:
+  // FULL 16-byte chunks, then one 4-byte quarter of the rest.
+  auto dequant = [&](const Slot& s, KsTile& ks) {
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
+    for (int m = 0; m < C::FULL; ++m) {
       const int ch = tid + kMlaThreads * m;
-      if (ch < NCH) {
-        const int r = ch / CHUNKS, cc = ch % CHUNKS;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sl.raw + 16 * ch);
-        u32x4 lo, hi;
-        dequant16(v, sl.sc[r * NSC + (cc >> 2)], lo, hi);
-        u32x4* dst = reinterpret_cast<u32x4*>(&ks[ks_row_of_key(r)][16 * cc]);
-        dst[0] = lo;
-        dst[1] = hi;
-      }
+      const int r = ch / CHUNKS, cc = ch % CHUNKS;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(s.raw + 16 * ch);
+      u32x4 lo, hi;
+      dequant16(v, s.sc[r * NSC + (cc >> 2)], lo, hi);
+      u32x4* dst = reinterpret_cast<u32x4*>(&ks[ks_row_of_key(r)][16 * cc]);
+      dst[0] = lo;
+      dst[1] = hi;
     }
-    // validity of this lane's 8 keys (8g + e) of tile tau
-    uint32_t vmask = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vmask |= (rows[kTileK * tau + 8 * g + e] >= 0 ? 1u : 0u) << e;
-    lds_barrier();                         // ks is complete and the slot has been read
-    if (tau + kRing < ntiles) issue(sl, tau + kRing);
-    // partial S^T over this half's query dims: lane (c, g) gets keys 8g + 4mb + i of head c
-    float4v sacc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
-    if (active) {
-      constexpr int KB = 3;   // K operands read a batch ahead of their MFMAs
-#pragma unroll
-      for (int s0 = 0; s0 < KH; s0 += KB) {
-        bf16x8 kop[2][KB];
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            if (s0 + j < KH)
-              kop[mb][j] = __builtin_bit_cast(
-                  bf16x8, *reinterpret_cast<const u32x4*>(&ks[16 * mb + c][32 * (KH * half + s0 + j) + 8 * g]));
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            if (s0 + j < KH) sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[mb][j], qreg[s0 + j], sacc[mb], 0, 0, 0);
-      }
+    if (C::REM > 0 && tid < 4 * C::REM) {
+      const int ch = C::FULL * kMlaThreads + (tid >> 2), qd = tid & 3;
+      const int r = ch / CHUNKS, cc = ch % CHUNKS;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(s.raw + 16 * ch + 4 * qd);
+      const float sc = s.sc[r * NSC + (cc >> 2)];
+      const float2v lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false) * sc;
+      const float2v hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true) * sc;
+      *reinterpret_cast<uint2*>(&ks[ks_row_of_key(r)][16 * cc + 4 * qd]) = make_uint2(cvt2_bf16(lo), cvt2_bf16(hi));
     }
-    xz[half][hg][0][lane] = sacc[0];
-    xz[half][hg][1][lane] = sacc[1];
-    lds_barrier();                         // both halves' partial scores are in LDS
-    if (!active) return;
+  };
+
+  // partial S^T over this half's query dims: lane (c, g) gets keys 8g + 4mb + i of head c
+  auto qk = [&](const KsTile& ks, float4v* sacc) {
+    constexpr int KB = 3;   // K operands read a batch ahead of their MFMAs
+#pragma unroll
+    for (int s0 = 0; s0 < KH; s0 += KB) {
+      bf16x8 kop[2][KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          if (s0 + j < KH)
+            kop[mb][j] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(&ks[16 * mb + c][32 * (KH * half + s0 + j) + 8 * g]));
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          if (s0 + j < KH) sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[mb][j], qreg[s0 + j], sacc[mb], 0, 0, 0);
+    }
+  };
+
+  // online softmax of tile tau's scores and O^T += V^T P^T
+  auto attend = [&](const KsTile& ks, const float4v* sacc, uint32_t vmask) {
     float z[8];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -300,24 +350,27 @@ k_mla_fp8(MlaLaunch a) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, z[e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_xor16(tmax);
+    tmax = max_xor32(tmax);
     // Lazy rescaling: the reference maximum m_run only moves when the tile's maximum exceeds it by
     // more than 2^kLazyLog2 (or on the first keys), so probabilities stay below 2^kLazyLog2 and the
     // accumulators are rescaled rarely instead of on every tile.  O and l share m_run, so the
-    // normalised result is the same softmax.
+    // normalised result is the same softmax.  Before the first valid key m_run is kNoMax (finite),
+    // so every exponent below is a plain hardware exp2 of a non-NaN argument.
     const bool bump = tmax > m_run + kLazyLog2;
     if (__ballot(bump)) {
       const float m_new = bump ? tmax : m_run;
-      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run is kNoMax
       l_run *= alpha;
+      if (__ballot(bump && m_run != kNoMax)) {   // the accumulators hold keys to rescale
 #pragma unroll
-      for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+        for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+      }
       m_run = m_new;
     }
     float p[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = m_run == -INFINITY ? 0.f : exp2f(z[e] - m_run);
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(z[e] - m_run);
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) psum += p[e];
@@ -345,25 +398,57 @@ k_mla_fp8(MlaLaunch a) {
     }
   };
 
+  // One tile; KBC selects the bf16 buffer of tile tau (the other one receives tile tau+1), st is
+  // tile tau's slot.
+  auto step = [&](auto KBC, int tau, int ntiles, int st) {
+    KsTile& kcur = decltype(KBC)::value ? ks1 : ks0;
+    KsTile& knext = decltype(KBC)::value ? ks0 : ks1;
+    if (tau + 2 < ntiles) wait_vmcnt<LPT>();   // tile tau+1's gathers are done, tile tau+2's may not be
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (tau + 3 < ntiles) issue(sl[st], tau + 3);
+    // validity of this lane's 8 keys (8g + e) of tile tau
+    uint32_t vmask = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vmask |= (rows[kTileK * tau + 8 * g + e] >= 0 ? 1u : 0u) << e;
+    float4v sacc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
+    qk(kcur, sacc);
+    // the next tile (after the last one: stale slot contents into a buffer nobody reads)
+    dequant(sl[st == kSlots - 1 ? 0 : st + 1], knext);
+    xz[half][hg][0][lane] = sacc[0];
+    xz[half][hg][1][lane] = sacc[1];
+    lds_barrier();                         // both halves' partial scores are in LDS
+    if (active) attend(kcur, sacc, vmask);
+  };
+
   for (int cb = slot0; cb < slot1; cb += kRowsChunk) {   // chunks of the split's slots (one, normally)
+    if (cb != slot0) load_rows(cb);
     const int nslot = min(kRowsChunk, slot1 - cb);
     const int ntiles = (nslot + kTileK - 1) / kTileK;
     __syncthreads();                       // the previous chunk is completely consumed
-    for (int i = tid; i < ntiles * kTileK; i += kMlaThreads) {
-      const int r = i < nslot ? irow[cb + i] : -1;
-      rows[i] = (r >= 0 && r < a.max_ctx) ? r : -1;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int i = tid + kMlaThreads * u;
+      if (i < ntiles * kTileK) rows[i] = (i < nslot && rv[u] >= 0 && rv[u] < a.max_ctx) ? rv[u] : -1;
     }
     __syncthreads();
     wait_vmcnt<0>();   // the query loads are done (tells the compiler too: no waits for them below)
-    issue(sl0, 0);
-    if (1 < ntiles) issue(sl1, 1);
-    if (2 < ntiles) issue(sl2, 2);
-    if (3 < ntiles) issue(sl3, 3);
-    for (int tau = 0; tau < ntiles; tau += kRing) {
-      step(sl0, tau, ntiles);
-      if (tau + 1 < ntiles) step(sl1, tau + 1, ntiles);
-      if (tau + 2 < ntiles) step(sl2, tau + 2, ntiles);
-      if (tau + 3 < ntiles) step(sl3, tau + 3, ntiles);
+    issue(sl[0], 0);
+    if (1 < ntiles) issue(sl[1], 1);
+    if (2 < ntiles) issue(sl[2], 2);
+    if (ntiles > 2) wait_vmcnt<2 * LPT>();
+    else if (ntiles > 1) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    lds_barrier();                         // tile 0 is in its slot
+    dequant(sl[0], ks0);
+    int st = 0;
+    for (int tau = 0; tau < ntiles; tau += 2) {
+      step(IntC<0>(), tau, ntiles, st);
+      st = st == kSlots - 1 ? 0 : st + 1;
+      if (tau + 1 < ntiles) {
+        step(IntC<1>(), tau + 1, ntiles, st);
+        st = st == kSlots - 1 ? 0 : st + 1;
+      }
     }
   }
   if (!active) return;

@@ -170,6 +170,29 @@ def test_topk_heavy_threshold_bin_overflow(dsa):
     assert np.array_equal(idx[0], ref)
 
 
+@pytest.mark.parametrize("dist", ["normal", "ties3", "heavy_bin"])
+def test_topk_many_rows(dsa, dist):
+    """Hundreds of rows of mixed lengths in one call, including rows whose threshold bin holds more
+    keys than the candidate buffer (the streaming finish)."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 40000, 300).tolist() + [40000, 2048, 2049, 16384, 16385, 32769]
+    rows = []
+    for n in lens:
+        if dist == "normal":
+            r = rng.standard_normal(n).astype(np.float32)
+        elif dist == "ties3":
+            r = rng.choice(np.array([-1.5, 0.25, 3.0], np.float32), n)
+        else:   # more than the candidate buffer's worth of keys in the threshold's top bits
+            r = (1.0 + rng.integers(0, 4, n) * 2.0 ** -20).astype(np.float32)
+            r[rng.choice(n, min(n, 100), replace=False)] = 7.0
+        rows.append(r)
+    idx, ln = _run_topk(dsa, rows, [n - 1 for n in lens], 2048)
+    for t, r in enumerate(rows):
+        ref, rl = O.topk_row(r.astype(np.float64), 2048)
+        assert ln[t] == rl, f"{dist} row {t}: len {ln[t]} != {rl}"
+        assert np.array_equal(idx[t], ref), f"{dist} row {t} (n={len(r)}): selections differ"
+
+
 def test_topk_row_shorter_than_ld_and_deterministic(dsa):
     rng = np.random.default_rng(11)
     rows = [rng.standard_normal(9000).astype(np.float32) for _ in range(3)]
