@@ -64,7 +64,7 @@ struct MlaLaunch {
   const int32_t* len;
   float* out;
   float* lse;
-  float* ws;  // split partials: [T][splits][H][kv_lora] O, then [T][splits][H] m and l
+  float* ws;  // split partials: [T][H][splits][kv_lora] O, then [T][H][splits] m and l
 };
 
 // ---- sizes shared between validation and the kernels ----------------------------------------

@@ -76,12 +76,12 @@ __device__ __forceinline__ void write_partial_or_final(const MlaLaunch& a, int t
     for (int i = 0; i < ndim; i += 4)
       *reinterpret_cast<float4*>(dst + i) = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
   } else if (bf16_partials(a)) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(a.ws) + (((size_t)t * a.splits + split) * a.H + head) * a.kv_lora + d0;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.ws) + (((size_t)t * a.H + head) * a.splits + split) * a.kv_lora + d0;
     for (int i = 0; i < ndim; i += 4)
       *reinterpret_cast<uint2*>(dst + i) = make_uint2(cvt2_bf16(float2v{o[i] * inv, o[i + 1] * inv}),
                                                       cvt2_bf16(float2v{o[i + 2] * inv, o[i + 3] * inv}));
   } else {
-    float* dst = a.ws + (((size_t)t * a.splits + split) * a.H + head) * a.kv_lora + d0;
+    float* dst = a.ws + (((size_t)t * a.H + head) * a.splits + split) * a.kv_lora + d0;
     for (int i = 0; i < ndim; i += 4)
       *reinterpret_cast<float4*>(dst + i) = make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
   }
@@ -92,7 +92,7 @@ __device__ __forceinline__ void write_stats(const MlaLaunch& a, int t, int split
     if (a.lse) a.lse[(size_t)t * a.H + head] = l_tot > 0.f ? (m_log2 + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     float* stats = a.ws + (size_t)a.T * a.splits * a.H * a.kv_lora;
-    const size_t i = ((size_t)t * a.splits + split) * a.H + head;
+    const size_t i = ((size_t)t * a.H + head) * a.splits + split;
     stats[2 * i] = m_log2;
     stats[2 * i + 1] = l_tot;
   }
@@ -156,6 +156,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id.  A 1-D grid of
+// 8 * inner * ceil(T / 8) workgroups is mapped so that every workgroup of query t runs on XCD t % 8:
+// the splits of a query share one L2 for the query and the row indices, and the combine that reads
+// their partials runs on the XCD whose L2 they were written to.  Returns false for the padding.
+__device__ __forceinline__ bool xcd_query_map(int inner, int T, int* t, int* j) {
+  const int id = blockIdx.x, x = id & 7, r = id >> 3;
+  *j = r % inner;
+  *t = 8 * (r / inner) + x;
+  return *t < T;
+}
+inline unsigned xcd_grid(int inner, int T) { return (unsigned)(8 * inner * ((T + 7) / 8)); }
+
 constexpr int kMlaThreads = 512;   // fp8 path: 8 waves = 4 head groups x 2 halves
 constexpr int kSlots = 3;          // raw tiles in LDS: the next one to dequantise plus two in flight
 
@@ -200,6 +212,8 @@ struct MlaFp8 {
 template <int ROPE>
 __global__ void __launch_bounds__(kMlaThreads)
 k_mla_fp8(MlaLaunch a) {
+  int t, split;
+  if (!xcd_query_map(a.splits, a.T, &t, &split)) return;
   using C = MlaFp8<ROPE>;
   constexpr int DQ = C::DQ, KSTEPS = C::KSTEPS, CHUNKS = C::CHUNKS, NSC = C::NSC, WROWS = C::WROWS;
   constexpr int LPT = C::LPT;
@@ -214,7 +228,6 @@ k_mla_fp8(MlaLaunch a) {
   __shared__ __attribute__((aligned(16))) KsTile ks0, ks1;
   __shared__ __attribute__((aligned(16))) float4v xz[2][4][2][64];   // partial scores swapped between halves
   __shared__ int rows[kRowsChunk];                      // row of every slot of the current chunk, -1 if none
-  const int t = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hg = wave & 3, half = wave >> 2;
   const int c = lane & 15, g = lane >> 4;
@@ -565,63 +578,80 @@ k_mla_f32(MlaLaunch a) {
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s;  lse = ln2 (M + log2 L).
-// One workgroup per (query, head): 128 threads, one float4 of the 512-dim output each, with the
-// partials of up to 16 splits in flight per thread.
-constexpr int kCombineThreads = 128;
+// One wave per (query, head), 8 of the 512 output dims per lane.  The first batch of partials is
+// loaded before the split statistics are reduced, so both sets of loads are in flight together;
+// split s's weight is then read from lane s.
+constexpr int kCombineHeads = 4;                      // waves (heads) per workgroup
+constexpr int kCombineThreads = 64 * kCombineHeads;
 
+template <bool BF16>
 __global__ void __launch_bounds__(kCombineThreads) k_mla_combine(MlaLaunch a) {
-  __shared__ float wts[64];
-  const int t = blockIdx.y, h = blockIdx.x;
+  constexpr int SB = BF16 ? 16 : 8;                   // splits per batch of loads
+  int t, hq;
+  if (!xcd_query_map((a.H + kCombineHeads - 1) / kCombineHeads, a.T, &t, &hq)) return;
+  const int lane = threadIdx.x & 63;
+  const int h = hq * kCombineHeads + (threadIdx.x >> 6);
+  if (h >= a.H) return;                               // whole waves; the kernel has no barriers
   const float* stats = a.ws + (size_t)a.T * a.splits * a.H * a.kv_lora;
-  // split statistics: one thread per split, max and sum by wave reduction (splits <= 64)
-  const int tid = threadIdx.x;
+  const size_t base = ((size_t)t * a.H + h) * a.splits * a.kv_lora + 8 * lane;   // split 0, this lane's dims
+  const size_t sstride = (size_t)a.kv_lora;                                      // elements between splits
+  // split statistics: lane s holds split s (splits <= 64)
   float m = -INFINITY, l = 0.f;
-  if (tid < a.splits) {
-    const size_t i = ((size_t)t * a.splits + tid) * a.H + h;
+  if (lane < a.splits) {
+    const size_t i = ((size_t)t * a.H + h) * a.splits + lane;
     m = stats[2 * i];
     l = stats[2 * i + 1];
   }
+  float v[SB][8];
+  auto load = [&](int s0) {
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      if (s0 + j < a.splits) {
+        const size_t off = base + (size_t)(s0 + j) * sstride;
+        if (BF16) {
+          const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.ws) + off);
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[j][2 * e] = __uint_as_float(w4[e] << 16);
+            v[j][2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+          }
+        } else {
+          const float4 x = *reinterpret_cast<const float4*>(a.ws + off);
+          const float4 y = *reinterpret_cast<const float4*>(a.ws + off + 4);
+          v[j][0] = x.x; v[j][1] = x.y; v[j][2] = x.z; v[j][3] = x.w;
+          v[j][4] = y.x; v[j][5] = y.y; v[j][6] = y.z; v[j][7] = y.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+      }
+    }
+  };
+  load(0);
   float M = m;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  const float w = (M == -INFINITY || tid >= a.splits) ? 0.f : exp2f(m - M);
+  const float w = (M == -INFINITY || lane >= a.splits) ? 0.f : exp2f(m - M);
   float Ls = w * l;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
-  const bool norm = bf16_partials(a);   // normalised partials carry their own sum l
-  if (tid < 64) wts[tid] = Ls > 0.f ? (norm ? w * l : w) / Ls : 0.f;
-  if (tid == 0 && a.lse) a.lse[(size_t)t * a.H + h] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
-  __syncthreads();
-  float4* outp = reinterpret_cast<float4*>(a.out + ((size_t)t * a.H + h) * a.kv_lora);
-  const size_t base = ((size_t)t * a.splits * a.H + h) * a.kv_lora;   // element offset of split 0
-  const size_t sstride = (size_t)a.H * a.kv_lora;                    // elements between splits
-  for (int e = tid; e < a.kv_lora / 4; e += kCombineThreads) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < a.splits; s0 += 16) {
-      float4 v[16];
+  // normalised (bf16) partials carry their own sum l
+  const float wt = Ls > 0.f ? (BF16 ? w * l : w) / Ls : 0.f;
+  if (lane == 0 && a.lse) a.lse[(size_t)t * a.H + h] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < a.splits; s0 += SB) {
+    if (s0 > 0) load(s0);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (s0 + j < a.splits) {
-          const size_t off = base + (size_t)(s0 + j) * sstride + 4 * e;
-          if (norm) {
-            const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.ws) + off);
-            v[j] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
-          } else {
-            v[j] = *reinterpret_cast<const float4*>(a.ws + off);
-          }
-        }
-      }
+    for (int j = 0; j < SB; ++j) {
+      const float wj = __shfl(wt, min(s0 + j, 63));
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float wj = s0 + j < a.splits ? wts[s0 + j] : 0.f;
-        acc.x = fmaf(wj, v[j].x, acc.x); acc.y = fmaf(wj, v[j].y, acc.y);
-        acc.z = fmaf(wj, v[j].z, acc.z); acc.w = fmaf(wj, v[j].w, acc.w);
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj, v[j][e], acc[e]);
     }
-    outp[e] = acc;
   }
+  float* outp = a.out + ((size_t)t * a.H + h) * a.kv_lora + 8 * lane;
+  *reinterpret_cast<float4*>(outp) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(outp + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 }  // namespace
@@ -630,14 +660,18 @@ hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   dim3 grid(a.splits, a.T);
   if (a.kv_dtype == DSA_FP8_E4M3FN) {
-    if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_fp8<64>, grid, dim3(kMlaThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_mla_fp8<0>, grid, dim3(kMlaThreads), 0, s, a);
+    const dim3 xgrid(xcd_grid(a.splits, a.T));
+    if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_fp8<64>, xgrid, dim3(kMlaThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_mla_fp8<0>, xgrid, dim3(kMlaThreads), 0, s, a);
   } else {
     if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_f32<64>, grid, dim3(kF32Threads), 0, s, a);
     else hipLaunchKernelGGL(k_mla_f32<0>, grid, dim3(kF32Threads), 0, s, a);
   }
-  if (a.splits > 1)
-    hipLaunchKernelGGL(k_mla_combine, dim3(a.H, a.T), dim3(kCombineThreads), 0, s, a);
+  if (a.splits > 1) {
+    const dim3 cgrid(xcd_grid((a.H + kCombineHeads - 1) / kCombineHeads, a.T));
+    if (a.kv_dtype == DSA_FP8_E4M3FN) hipLaunchKernelGGL(k_mla_combine<true>, cgrid, dim3(kCombineThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_mla_combine<false>, cgrid, dim3(kCombineThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
