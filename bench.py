@@ -7,11 +7,13 @@ One step = lightning-indexer scores over every cached key -> exact top-2048 -> s
 (64 heads, 512 + 64 dims).  The NoPE-layer and shared-indexer variants of the same shape, the
 4096-token chunked prefill on a 61440-token prefix, the 512K block-sparse decode and the batch-64
 16K-32K decode are timed the same way and reported beside it.  All inputs are seeded synthetic
-tensors generated on the GPU and resident in HBM before timing starts.
+tensors generated on the GPU and resident in HBM before timing starts; every timed loop cycles
+through three copies of its workload's caches, so each call reads HBM as in a multi-layer decode.
 
 Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -28,12 +30,41 @@ INDEX_BYTES_PER_KEY = 128 + 4 + 4      # fp8 key row + fp32 scale read, fp32 sco
 LATENT_BYTES_PER_KEY = 576 + 9 * 4     # fp8 latent row + 9 fp32 scales
 MLA_FLOP_PER_KEY_HEAD = 2 * (576 + 512)   # QK^T over 576 dims and PV over 512, per selected key and head
 INDEX_COUNTERS = os.path.join(ROOT, "profiles", "index_scores_fp8_b16_ctx128k_counters.txt")
-INDEX_SOURCES = ["dsa_sparse_attention_indexer_amd/csrc/indexer.hip",
+INDEX_SOURCES = ["dsa_sparse_attention_indexer_amd/csrc/indexer.hip", "dsa_sparse_attention_indexer_amd/csrc/topk_common.h",
                  "dsa_sparse_attention_indexer_amd/csrc/dsa_internal.h"]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+N_COPIES = 3   # copies of each workload's caches cycled through by the timed loops
+
+
+def cache_copies(wl, n=N_COPIES):
+    """The workload plus n - 1 copies whose caches (index keys, latents and their scales) are clones.
+
+    A decode step of one layer reads that layer's caches once; between two steps of the same layer
+    every other layer streams its own.  Timing back-to-back steps on one copy would instead serve part
+    of the 285 MB index-key stream from the 256 MB last-level cache.  Cycling through copies (4+ GB)
+    makes every timed step read HBM, as in a multi-layer decode."""
+    out = [wl]
+    for _ in range(n - 1):
+        out.append(dataclasses.replace(
+            wl, index_k=wl.index_k.clone(),
+            index_k_scale=None if wl.index_k_scale is None else wl.index_k_scale.clone(),
+            kv=wl.kv.clone(), kv_scale=None if wl.kv_scale is None else wl.kv_scale.clone()))
+    return out
+
+
+def cycling(fn, wls):
+    """fn(workload) over the copies in turn."""
+    i = [0]
+
+    def call():
+        fn(wls[i[0] % len(wls)])
+        i[0] += 1
+    return call
 
 
 def source_digest(paths):
@@ -121,8 +152,8 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step_a():
-        pipeline.layer_step(wa, buf_a)
+    was = cache_copies(wa)
+    step_a = cycling(lambda w: pipeline.layer_step(w, buf_a), was)
 
     # ---- headline: K timed layer steps --------------------------------------------------------
     for _ in range(args.warmup):
@@ -148,23 +179,21 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / args.steps
 
-    # The index kernel streams 285 MB per call, more than the 256 MB last-level cache: its
-    # roofline figure is timed over calls that rotate through three copies of the key cache, so
-    # every call reads HBM (as inside a real decode step), not lines left by the previous call.
-    from dsa_sparse_attention_indexer_amd import dsa_indexer_scores
-    kcopies = [(wa.index_k, wa.index_k_scale)] + [(wa.index_k.clone(), wa.index_k_scale.clone()) for _ in range(2)]
-    rot = [0]
+    # Every stage is timed over calls that cycle through the cache copies, so each call reads HBM
+    # (as inside a real decode step), not lines left in the last-level cache by the previous call.
+    # The score kernel (with the histogram, as in the step) back to back on scratch buffers (their
+    # histogram piles up over the calls and is discarded), then score kernel + top-k pairs: the
+    # top-k's share is the difference.
+    tmp = pipeline.alloc_buffers(wa)
+    t_idx = per_call_us(cycling(lambda w: pipeline.index_scores_hist(w, tmp), was))
+    del tmp
 
-    def index_cold():
-        k, sc = kcopies[rot[0] % 3]
-        rot[0] += 1
-        dsa_indexer_scores(wa.index_q, wa.index_w, wa.q_seq, wa.q_pos, k, buf_a.scores, k_scale=sc,
-                           ssmax_s=wa.ssmax_s, ssmax_b=wa.ssmax_b, inv_freq=wa.inv_freq, ws=buf_a.ws_index)
+    def pair(w):
+        pipeline.index_scores_hist(w, buf_a)
+        pipeline.select_hist(w, buf_a)
 
-    t_idx = per_call_us(index_cold)
-    del kcopies
-    t_topk = per_call_us(lambda: pipeline.select(wa, buf_a))
-    t_mla = per_call_us(lambda: pipeline.attend(wa, buf_a))
+    t_topk = per_call_us(cycling(pair, was)) - t_idx
+    t_mla = per_call_us(cycling(lambda w: pipeline.attend(w, buf_a), was))
     keys = int((wa.q_pos.long() + 1).sum())
     idx_bytes = keys * INDEX_BYTES_PER_KEY
     achieved = idx_bytes / (t_idx * 1e-6) / 1e9
@@ -187,34 +216,35 @@ def main():
             return (time.perf_counter() - s0) / args.steps
 
         buf_c = pipeline.alloc_buffers(wa)   # shared-indexer layer: its own outputs, a's selection
-        tc = timed(lambda: pipeline.layer_step(wa, buf_c, shared_from=buf_a))
+        tc = timed(cycling(lambda w: pipeline.layer_step(w, buf_c, shared_from=buf_a), was))
         variants["shared_indexer_layer_b16_ctx128k"] = {"us_per_step": tc * 1e6, "tok_per_s": T / tc}
-        tf = timed(lambda: pipeline.layer_step(wa, buf_c, fused=True))   # dsa_indexer_topk
-        variants["fused_index_topk_layer_b16_ctx128k"] = {"us_per_step": tf * 1e6, "tok_per_s": T / tf}
+        tf = timed(cycling(lambda w: pipeline.layer_step(w, buf_c, fused=False), was))   # two separate calls
+        variants["separate_index_topk_layer_b16_ctx128k"] = {"us_per_step": tf * 1e6, "tok_per_s": T / tf}
         del buf_c
+        del was
         log("generating the NoPE-layer workload ...")
-        wb = workloads.config2("b", device=dev)
-        bb = pipeline.alloc_buffers(wb)
-        tb = timed(lambda: pipeline.layer_step(wb, bb))
-        variants["nope_layer_b16_ctx128k"] = {"us_per_step": tb * 1e6, "tok_per_s": wb.num_q / tb}
+        wb = cache_copies(workloads.config2("b", device=dev))
+        bb = pipeline.alloc_buffers(wb[0])
+        tb = timed(cycling(lambda w: pipeline.layer_step(w, bb), wb))
+        variants["nope_layer_b16_ctx128k"] = {"us_per_step": tb * 1e6, "tok_per_s": wb[0].num_q / tb}
         del wb, bb
         log("generating the 4096-on-61440 chunked prefill ...")
-        w3 = workloads.config3(device=dev)
-        b3 = pipeline.alloc_buffers(w3, prefill=True)
-        t3 = timed(lambda: pipeline.layer_step(w3, b3, prefill=True))
-        variants["chunked_prefill_4096_on_61440"] = {"us_per_step": t3 * 1e6, "tok_per_s": w3.num_q / t3}
+        w3 = cache_copies(workloads.config3(device=dev))
+        b3 = pipeline.alloc_buffers(w3[0], prefill=True)
+        t3 = timed(cycling(lambda w: pipeline.layer_step(w, b3, prefill=True), w3))
+        variants["chunked_prefill_4096_on_61440"] = {"us_per_step": t3 * 1e6, "tok_per_s": w3[0].num_q / t3}
         del w3, b3
         log("generating the 512K block-sparse decode ...")
-        w4 = workloads.config4(device=dev)
-        b4 = pipeline.alloc_buffers(w4, block_sparse=True)
-        t4 = timed(lambda: pipeline.layer_step(w4, b4, block_sparse=True))
-        variants["block_sparse_b4_ctx512k"] = {"us_per_step": t4 * 1e6, "tok_per_s": w4.num_q / t4}
+        w4 = cache_copies(workloads.config4(device=dev))
+        b4 = pipeline.alloc_buffers(w4[0], block_sparse=True)
+        t4 = timed(cycling(lambda w: pipeline.layer_step(w, b4, block_sparse=True), w4))
+        variants["block_sparse_b4_ctx512k"] = {"us_per_step": t4 * 1e6, "tok_per_s": w4[0].num_q / t4}
         del w4, b4
         log("generating the batch-64 16K-32K decode ...")
-        w1 = workloads.config1(device=dev)
-        b1 = pipeline.alloc_buffers(w1)
-        t1 = timed(lambda: pipeline.layer_step(w1, b1))
-        variants["decode_b64_ctx16k_32k"] = {"us_per_step": t1 * 1e6, "tok_per_s": w1.num_q / t1}
+        w1 = cache_copies(workloads.config1(device=dev))
+        b1 = pipeline.alloc_buffers(w1[0])
+        t1 = timed(cycling(lambda w: pipeline.layer_step(w, b1), w1))
+        variants["decode_b64_ctx16k_32k"] = {"us_per_step": t1 * 1e6, "tok_per_s": w1[0].num_q / t1}
         del w1, b1
         log("variants: " + ", ".join(f"{k} {v['us_per_step']:.1f} us" for k, v in variants.items()))
 
@@ -239,10 +269,10 @@ def main():
         "config": {"workload": "decode layer step (RoPE layer): indexer + top-2048 + sparse MLA",
                    "batch": T, "context": wa.max_ctx, "index_heads": wa.num_heads, "mla_heads": wa.mla_heads,
                    "topk": wa.topk, "kv_cache": "fp8 e4m3fn + fp32 scales"},
-        "roofline": {"bound": "hbm", "kernel": "index scores (fp8 keys)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "index scores + first-digit histogram (fp8 keys)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counter_traffic(), "bytes_per_launch": idx_bytes},
-        "stages_us": {"index_scores": t_idx, "topk": t_topk, "sparse_mla": t_mla},
+        "stages_us": {"index_scores_hist": t_idx, "topk_from_hist": t_topk, "sparse_mla": t_mla},
         "keys_scored_per_s": keys / (t_idx * 1e-6),
         "sparse_mla": {"tflops": mla_tflops, "frac_bf16_peak": mla_tflops / BF16_PEAK_TFLOPS,
                        "gather_gbs": mla_gbs, "frac_hbm_peak": mla_gbs / HBM_PEAK_GBS},

@@ -56,6 +56,9 @@ def _load():
         "dsa_indexer_scores": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, P, SZ, P]),
         "dsa_indexer_topk": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, P, P, P, SZ,
                                    P, SZ, P]),
+        "dsa_indexer_scores_hist": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, P, SZ,
+                                          P, SZ, P]),
+        "dsa_topk_hist": (I32, [ctypes.POINTER(IndexerDesc), P, I64, P, I32, P, P, P, SZ, P]),
         "dsa_topk_workspace_size": (SZ, [I32, I64, I32]),
         "dsa_topk": (I32, [P, I64, P, I32, I32, P, P, P, SZ, P]),
         "dsa_block_select_workspace_size": (SZ, [I32, I64, I32]),
@@ -77,6 +80,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_indexer_topk",
+            "dsa_indexer_scores_hist", "dsa_topk_hist",
             "dsa_topk_workspace_size", "dsa_topk", "dsa_block_select_workspace_size", "dsa_block_select", "dsa_sparse_mla_workspace_size",
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill"]
 
@@ -200,6 +204,51 @@ def dsa_indexer_topk(q, w, q_seq, q_pos, k_cache, scores, k, idx, length=None, k
                                  _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores), ld, k,
                                  _ptr(idx), _ptr(length), _ptr(ws), ws.numel(), _ptr(topk_ws), topk_ws.numel(),
                                  _stream(stream)))
+    return idx, length
+
+
+def dsa_indexer_scores_hist(q, w, q_seq, q_pos, k_cache, scores, k, topk_ws, k_scale=None, ssmax_s=None,
+                            ssmax_b=None, inv_freq=None, ws=None, stream=None):
+    """First half of dsa_indexer_topk: the scores, plus each row's first-digit histogram left in
+    topk_ws for dsa_topk_hist.  Arguments as dsa_indexer_topk (no index outputs)."""
+    T, H, D = q.shape
+    B, max_ctx, _ = k_cache.shape
+    _dev("q", q, (torch.float32, torch.bfloat16))
+    _dev("w", w, torch.float32, (T, H))
+    _dev("q_seq", q_seq, torch.int32, (T,))
+    _dev("q_pos", q_pos, torch.int32, (T,))
+    _dev("k_cache", k_cache, (torch.float32, torch.uint8, torch.float8_e4m3fn))
+    _dev("k_scale", k_scale, torch.float32, (B, max_ctx))
+    _dev("ssmax_s", ssmax_s, torch.float32, (H,))
+    _dev("ssmax_b", ssmax_b, torch.float32, (H,))
+    _dev("inv_freq", inv_freq, torch.float32)
+    _dev("scores", scores, torch.float32)
+    _dev("topk_ws", topk_ws, torch.uint8)
+    if scores.dim() != 2 or scores.shape[0] != T:
+        raise ValueError("scores must be [T][ld]")
+    d = indexer_desc(q, k_cache, inv_freq)
+    if ws is None:
+        ws = torch.empty(max(16, dsa_indexer_workspace_size(d)), dtype=torch.uint8, device=q.device)
+    _dev("ws", ws, torch.uint8)
+    _check(_lib.dsa_indexer_scores_hist(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
+                                        _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores),
+                                        scores.shape[1], k, _ptr(ws), ws.numel(), _ptr(topk_ws), topk_ws.numel(),
+                                        _stream(stream)))
+    return scores
+
+
+def dsa_topk_hist(scores, q_pos, k, idx, length, max_ctx, topk_ws, stream=None):
+    """Second half of dsa_indexer_topk: the top-k of each row from the scores and the histogram a
+    preceding dsa_indexer_scores_hist left in topk_ws (rows hold min(q_pos + 1, max_ctx) scores)."""
+    T = scores.shape[0]
+    _dev("scores", scores, torch.float32)
+    _dev("q_pos", q_pos, torch.int32, (T,))
+    _dev("idx", idx, torch.int32, (T, k))
+    _dev("length", length, torch.int32, (T,))
+    _dev("topk_ws", topk_ws, torch.uint8)
+    d = IndexerDesc(T, 0, 128, 0, 1, max_ctx, DSA_F32, DSA_F32)   # only num_q and max_ctx are read
+    _check(_lib.dsa_topk_hist(ctypes.byref(d), _ptr(scores), scores.shape[1], _ptr(q_pos), k, _ptr(idx),
+                              _ptr(length), _ptr(topk_ws), topk_ws.numel(), _stream(stream)))
     return idx, length
 
 

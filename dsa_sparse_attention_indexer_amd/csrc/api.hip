@@ -86,14 +86,15 @@ void check_indexer(Checker& ck, const dsa_indexer_desc_t* d, const void* q, cons
 }
 
 void check_topk(Checker& ck, int32_t num_q, int64_t ld_scores, int32_t k, const void* scores, const int32_t* q_pos,
-                const int32_t* idx) {
+                const int32_t* idx, bool with_idx = true) {
   ck.need(num_q >= 0 && num_q <= 65535, "num_q must be in [0, 65535]");
   ck.need(ld_scores >= 1, "ld_scores must be >= 1");
   ck.support(ld_scores <= dsa::kTopkMaxCols, "ld_scores must be <= 4194304");
   ck.need(ld_scores % 4 == 0, "ld_scores must be a multiple of 4");
   ck.support(k >= 1 && k <= 65536, "k must be in [1, 65536]");
   if (num_q > 0) {
-    ck.need(scores && q_pos && idx, "scores, q_pos and idx must be non-NULL");
+    ck.need(scores && q_pos && (idx || !with_idx), with_idx ? "scores, q_pos and idx must be non-NULL"
+                                                              : "scores and q_pos must be non-NULL");
     ck.need(aligned(scores, 16), "scores must be 16-byte aligned");
   }
 }
@@ -156,6 +157,45 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const 
   if (e != hipSuccess) return hip_status("dsa_indexer_topk", e);
   dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws};
   return hip_status("dsa_indexer_topk", dsa::launch_topk(tk, fused, (hipStream_t)stream));
+}
+
+dsa_status_t dsa_indexer_scores_hist(const dsa_indexer_desc_t* d, const void* q, const float* w,
+                                     const int32_t* q_seq, const int32_t* q_pos,
+                                     const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                                     const void* k_cache, const float* k_scale,
+                                     float* scores, int64_t ld_scores, int32_t k,
+                                     void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream) {
+  Checker ck;
+  if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_scores_hist"); }
+  check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
+                ws_bytes);
+  check_topk(ck, d->num_q, ld_scores, k, scores, q_pos, nullptr, false);   // no index output in this half
+  check_topk_ws(ck, d->num_q, topk_ws, topk_ws_bytes);
+  dsa_status_t st = ck.finish("dsa_indexer_scores_hist");
+  if (st != DSA_OK || d->num_q == 0) return st;
+  dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
+                                        ld_scores);
+  const bool fused = d->k_dtype == DSA_FP8_E4M3FN && !dsa::indexer_grouped(d->num_q, d->k_dtype);
+  if (fused) { a.topk_ws = topk_ws; a.topk_k = k; }
+  hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
+  if (e != hipSuccess || fused) return hip_status("dsa_indexer_scores_hist", e);
+  dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, nullptr, nullptr, topk_ws};
+  return hip_status("dsa_indexer_scores_hist", dsa::launch_topk_hist(tk, (hipStream_t)stream));
+}
+
+dsa_status_t dsa_topk_hist(const dsa_indexer_desc_t* d, const float* scores, int64_t ld_scores,
+                           const int32_t* q_pos, int32_t k, int32_t* idx, int32_t* len,
+                           void* topk_ws, size_t topk_ws_bytes, void* stream) {
+  Checker ck;
+  if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_topk_hist"); }
+  ck.need(d->max_ctx >= 1 && d->max_ctx <= (1 << 26), "max_ctx must be in [1, 2^26]");
+  ck.need(ld_scores >= d->max_ctx, "ld_scores must be >= max_ctx");
+  check_topk(ck, d->num_q, ld_scores, k, scores, q_pos, idx);
+  check_topk_ws(ck, d->num_q, topk_ws, topk_ws_bytes);
+  dsa_status_t st = ck.finish("dsa_topk_hist");
+  if (st != DSA_OK || d->num_q == 0) return st;
+  dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws};
+  return hip_status("dsa_topk_hist", dsa::launch_topk(tk, true, (hipStream_t)stream));
 }
 
 size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k) {

@@ -80,6 +80,7 @@ size_t block_select_ws_bytes(int T, int64_t ld, int block);
 
 hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s);
 hipError_t launch_topk(const TopkLaunch& a, bool hist_given, hipStream_t s);
+hipError_t launch_topk_hist(const TopkLaunch& a, hipStream_t s);   // the first-digit histogram only
 hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s);
 

@@ -11,13 +11,14 @@
 //    owns the 32 (zero-padded) heads of one query as the A operand of v_mfma_f32_32x32x16_f16 and
 //    streams 32-key tiles as the B operand straight from HBM (16-byte loads per lane, the fp8
 //    bytes converted exactly to fp16 by v_cvt_scalef32_pk_f16_fp8 with unit scale).  q' is formed
-//    in float64, scaled by a power of two per head and split into two fp16 terms (hi + lo) whose
+//    in float32, scaled by a power of two per head and split into two fp16 terms (hi + lo) whose
 //    products accumulate into one fp32 accumulator, so the dot product keeps ~22 bits of q'.
 //    ReLU, the head weights and the per-token scale are applied in registers; the two halves of
 //    the wave are summed with v_permlane32_swap, and lanes 0..31 store 32 consecutive scores.
 //  * fp32 keys (the reference-precision path): one thread per key, fp32 FMAs against q' in LDS.
 //
-// Query prep (RoPE angles formed and evaluated in float64, SSMax in float64): on the fp8 path each
+// Query prep (RoPE angles formed and reduced to [-pi, pi] in float64, then sine, cosine, SSMax and
+// the rotation in float32, about 1e-7 relative): on the fp8 path each
 // workgroup prepares its query in LDS while its first key tiles are in flight; on the fp32 path a
 // small kernel prepares each query once into the caller's workspace.
 
@@ -37,14 +38,14 @@ constexpr int kD = 128;          // index head dim
 constexpr int kHPad = 32;        // heads padded to the MFMA M dimension
 constexpr int kThreads = 256;    // 4 waves
 constexpr int kTile = 32;        // keys per MFMA N tile
-constexpr int kQsStride = kD + 1;  // double row stride in LDS (odd: per-head reductions avoid conflicts)
+constexpr int kQsStride = kD + 1;  // row stride of q' in LDS (odd: per-head reductions avoid conflicts)
 constexpr int kDepth = 5;        // key tiles in flight per wave in the fp8 stream
 
 struct PrepSmem {
-  double qs[kHPad][kQsStride];   // q' (rotated, SSMax-scaled), float64
-  double cs[32], sn[32];         // cos / sin of the 32 rotary angles
-  double mh[kHPad];              // SSMax multipliers
-  double wv[kHPad];              // raw head weights
+  float qs[kHPad][kQsStride];    // q' (rotated, SSMax-scaled)
+  float cs[32], sn[32];          // cos / sin of the 32 rotary angles
+  float mh[kHPad];               // SSMax multipliers
+  float wv[kHPad];               // raw head weights
   float coef[kHPad];             // w_h / (sqrt(H) sqrt(128)) * 2^-e_h   (fp8 path)
   int ex[kHPad];                 // per-head power-of-two exponent e_h   (fp8 path)
 };
@@ -94,16 +95,23 @@ __device__ void prep_compute(PrepSmem& sm, const PrepIn& in, const IndexerLaunch
   const int h = tid >> 3, part = tid & 7;
   const int npairs = a.rope_dim / 2;
   if (tid < npairs) {
-    // p * inv_freq[j] is exact in float64 (24-bit times 31-bit); sin/cos evaluated in float64.
+    // p * inv_freq[j] is exact in float64 (24-bit times 26-bit); it is reduced to [-pi, pi] in
+    // float64 with a two-term 2*pi (error far below float32 resolution up to p = 2^26), and the
+    // sine and cosine of the reduced angle are taken in float32 (about one ulp).
+    constexpr double kInv2Pi = 0.15915494309189535;
+    constexpr double k2PiHi = 6.283185307179586;
+    constexpr double k2PiLo = 2.4492935982947064e-16;
     const double ang = (double)p * (double)in.invf;
-    double sn, cs;
-    sincos(ang, &sn, &cs);
+    const double k = rint(ang * kInv2Pi);
+    const double r = fma(-k, k2PiLo, fma(-k, k2PiHi, ang));
+    float sn, cs;
+    sincosf((float)r, &sn, &cs);
     sm.cs[tid] = cs;
     sm.sn[tid] = sn;
   }
   if (tid < kHPad) {
-    sm.mh[tid] = (a.ssmax_s != nullptr && tid < a.H) ? (double)in.ss * log((double)p + 1.0) + (double)in.sb : 1.0;
-    sm.wv[tid] = tid < a.H ? (double)in.wv : 0.0;
+    sm.mh[tid] = (a.ssmax_s != nullptr && tid < a.H) ? fmaf(in.ss, logf((float)p + 1.f), in.sb) : 1.f;
+    sm.wv[tid] = tid < a.H ? in.wv : 0.f;
   }
   float x[16];
 #pragma unroll
@@ -118,15 +126,15 @@ __device__ void prep_compute(PrepSmem& sm, const PrepIn& in, const IndexerLaunch
     }
   }
   __syncthreads();
-  const double m = h < a.H ? sm.mh[h] : 0.0;
+  const float m = h < a.H ? sm.mh[h] : 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = 8 * part + i;          // pair (2j, 2j + 1)
-    double x0 = (double)x[2 * i], x1 = (double)x[2 * i + 1];
+    float x0 = x[2 * i], x1 = x[2 * i + 1];
     if (j < npairs) {
-      const double c = sm.cs[j], sn = sm.sn[j];
-      const double r0 = x0 * c - x1 * sn;
-      const double r1 = x0 * sn + x1 * c;
+      const float c = sm.cs[j], sn = sm.sn[j];
+      const float r0 = fmaf(x0, c, -x1 * sn);
+      const float r1 = fmaf(x0, sn, x1 * c);
       x0 = r0;
       x1 = r1;
     }
@@ -169,30 +177,51 @@ __device__ __forceinline__ uint32_t pack_half2(_Float16 lo, _Float16 hi) {
 
 // From q' in sm.qs: per-head power-of-two scales, head weights and the hi/lo fp16 MFMA A operands
 // of every lane, written to `o` (LDS or global).  All 256 threads participate.
-__device__ void build_fp8_operands(PrepSmem& sm, QPrepFp8* o, const IndexerLaunch& a, int t) {
+__device__ void prep_scales(PrepSmem& sm, const IndexerLaunch& a) {
   const int tid = threadIdx.x;
-  const double inv_norm = 1.0 / (sqrt((double)a.H) * sqrt((double)kD));
+  const float inv_norm = 1.f / sqrtf((float)(a.H * kD));   // one rounding (exact for H = 32)
   // max|q'_h| * 2^e_h in [2^14, 2^15) keeps both fp16 terms normal
   {
     const int h = tid >> 3, part = tid & 7;   // 32 heads x 8 lanes
-    double mx = 0.0;
-    for (int d = part * 16; d < part * 16 + 16; ++d) mx = fmax(mx, fabs(sm.qs[h][d]));
-    mx = fmax(mx, __shfl_xor(mx, 1));
-    mx = fmax(mx, __shfl_xor(mx, 2));
-    mx = fmax(mx, __shfl_xor(mx, 4));
+    float mx = 0.f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) mx = fmaxf(mx, fabsf(sm.qs[h][16 * part + d]));
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
     if (part == 0) {
       int e = 0;
-      if (mx > 0.0) {
+      if (mx > 0.f) {
         int x;
-        frexp(mx, &x);   // mx = f * 2^x, f in [0.5, 1)
+        frexpf(mx, &x);   // mx = f * 2^x, f in [0.5, 1)
         e = 15 - x;
       }
       sm.ex[h] = e;
-      const double wv = h < a.H ? sm.wv[h] * inv_norm : 0.0;
-      sm.coef[h] = (float)ldexp(wv, -e);
+      const float wv = h < a.H ? sm.wv[h] * inv_norm : 0.f;
+      sm.coef[h] = ldexpf(wv, -e);
     }
   }
   __syncthreads();
+}
+
+// hi/lo fp16 split of q' * 2^e (exact power-of-two scaling; the residual v - hi is exact in fp32).
+__device__ __forceinline__ void split_half8(const float* v, u32x4& h4, u32x4& l4) {
+  _Float16 hi[8], lo[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hi[i] = (_Float16)v[i];                           // |v| < 2^15: normal
+    lo[i] = (_Float16)(v[i] - (float)hi[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h4[i] = pack_half2(hi[2 * i], hi[2 * i + 1]);
+    l4[i] = pack_half2(lo[2 * i], lo[2 * i + 1]);
+  }
+}
+
+__device__ void build_fp8_operands(PrepSmem& sm, QPrepFp8* o, const IndexerLaunch& a, int t) {
+  const int tid = threadIdx.x;
+  prep_scales(sm, a);
   // A operand of lane l (row m = l & 31, half g = l >> 5) for K-step s: q'[m][32(s>>1) + 16g + 8(s&1) + i]
   {
     const int l = tid & 63, sg = tid >> 6;
@@ -202,19 +231,11 @@ __device__ void build_fp8_operands(PrepSmem& sm, QPrepFp8* o, const IndexerLaunc
     for (int ss = 0; ss < 2; ++ss) {
       const int s = 2 * sg + ss;
       const int base = 32 * (s >> 1) + 16 * g + 8 * (s & 1);
-      _Float16 hi[8], lo[8];
+      float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double v = ldexp(sm.qs[m][base + i], e);
-        hi[i] = (_Float16)(float)v;                        // |v| < 2^15: normal, exact residual below
-        lo[i] = (_Float16)(float)(v - (double)(float)hi[i]);
-      }
+      for (int i = 0; i < 8; ++i) v[i] = ldexpf(sm.qs[m][base + i], e);
       u32x4 h4, l4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h4[i] = pack_half2(hi[2 * i], hi[2 * i + 1]);
-        l4[i] = pack_half2(lo[2 * i], lo[2 * i + 1]);
-      }
+      split_half8(v, h4, l4);
       o->a[2 * s][l] = h4;
       o->a[2 * s + 1][l] = l4;
     }
@@ -246,9 +267,9 @@ __global__ void __launch_bounds__(kThreads) k_index_qprep(IndexerLaunch a, void*
   const int p = clampi(a.q_pos[t], -1, a.max_ctx - 1);
   prep_query(sm, a, t, p < 0 ? 0 : p);
   QPrepF32* o = reinterpret_cast<QPrepF32*>(reinterpret_cast<uint8_t*>(ws) + (size_t)t * kQPrepBytes);
-  const double inv_norm = 1.0 / (sqrt((double)a.H) * sqrt((double)kD));
-  for (int e = tid; e < kHPad * kD; e += kThreads) o->q[e / kD][e % kD] = (float)sm.qs[e / kD][e % kD];
-  if (tid < kHPad) o->coef[tid] = tid < a.H ? (float)(sm.wv[tid] * inv_norm) : 0.f;
+  const float inv_norm = 1.f / sqrtf((float)(a.H * kD));   // one rounding (exact for H = 32)
+  for (int e = tid; e < kHPad * kD; e += kThreads) o->q[e / kD][e % kD] = sm.qs[e / kD][e % kD];
+  if (tid < kHPad) o->coef[tid] = tid < a.H ? sm.wv[tid] * inv_norm : 0.f;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -336,15 +357,69 @@ __device__ __forceinline__ void tile_scores2(const KeyTile& k0, const KeyTile& k
   s1 = (__uint_as_float(w1[0]) + __uint_as_float(w1[1])) * k1.sc;
 }
 
+// 16-byte slot of (row r, chunk k) of a 32-row key tile in LDS: chunks are XOR-swizzled by row pair
+// so that the 16 lanes of a ds_read_b128 quarter (rows col..col+15, one chunk) hit 16 different
+// bank groups.
+__device__ __forceinline__ int tile_slot(int r, int k) { return 8 * r + (k ^ ((r >> 1) & 7)); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Raw buffer descriptor words (as make_rsrc builds them) for the inline-assembly loads below.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32) & 0xFFFF),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+typedef __attribute__((address_space(3))) void* lds_vp;
+
+// Streaming buffer loads straight into LDS, non-temporal (the key stream is read once): lane l's 16
+// (4) bytes at byte voff of the buffer land at LDS byte lds + 16*l (4*l); offsets past the buffer
+// read zero.  Inline assembly keeps the compiler from treating them as LDS writes (it would make
+// every later LDS read wait for all of them); callers wait with wait_vm.
+__device__ __forceinline__ void bdma16(i32x4 rs, uint32_t voff, void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_vp)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rs), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void bdma4(i32x4 rs, uint32_t voff, void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_vp)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rs), "s"(base)
+               : "memory", "m0");
+}
+
+constexpr int kRing = 3;   // key tiles in flight per wave (its own LDS ring)
+
+struct WaveRing {
+  u32x4 key[kRing][kTile * kD / 16];
+  float sc[kRing][kTile];
+};
+
 // TPW: 32-key tiles per wave (a workgroup covers 4 * 32 * TPW keys).  HIST: also histogram the
 // first top-k digit of this chunk's scores into the top-k workspace (the fused selection path).
+//
+// Each wave streams its tiles through a private ring of kRing LDS slots: every load instruction
+// reads whole 128-byte key rows (8 lanes per row) with the non-temporal policy, which the memory
+// system serves markedly faster than the per-lane operand pattern; the MFMA operands are then read
+// from LDS (swizzled, conflict-free).  The ring is private, so no barrier is involved: a wave waits
+// for its own loads with vmcnt.
 template <int TPW, bool HIST, bool BF16Q>
 __global__ void __launch_bounds__(kThreads)
 k_index_scores_fp8(IndexerLaunch a) {
   constexpr int chunk = 4 * kTile * TPW;
-  __shared__ PrepSmem sm;
-  __shared__ QPrepFp8 qa;
-  __shared__ uint32_t lh[HIST ? kTkBins : 1];
+  constexpr int kLoadsPerTile = 5;          // four 16-byte row loads and one scale load
+  __shared__ __attribute__((aligned(16))) WaveRing ring[4];
+  // query prep, then (fused path) the chunk's histogram: the histogram reuses the prep's space
+  __shared__ __attribute__((aligned(16))) union PrepOrHist {
+    PrepSmem sm;
+    uint32_t lh[HIST ? kTkBins : 1];
+  } pu;
+  PrepSmem& sm = pu.sm;
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar) loop control
@@ -359,57 +434,102 @@ k_index_scores_fp8(IndexerLaunch a) {
   const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.k_cache) + ((size_t)b * a.max_ctx + c0) * kD;
   const float* sseq = a.k_scale + (size_t)b * a.max_ctx + c0;
   float* srow = a.scores + (size_t)t * a.ld + c0;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kseq, nrow * kD);
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(sseq, nrow * 4u);
+  const i32x4 krs = rsrc_words(kseq, nrow * kD);
+  const i32x4 srs = rsrc_words(sseq, nrow * 4u);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(srow, nrow * 4u);
   constexpr uint32_t kStride = 4 * kTile;   // the 4 waves interleave 32-key tiles
+  WaveRing& wr = ring[wave];
 
-  // The first key tiles go out first; the query prep (float64 RoPE and SSMax, power-of-two scaling,
-  // hi/lo fp16 split) runs in LDS while they are in flight.
+  // tile j of this wave (rows wave*32 + j*128 .. of the chunk) into ring slot j % kRing: load c
+  // brings rows 8c..8c+7, lane l the 16-byte chunk stored at slot position 64c + l
+  const int lr = lane >> 3, lj = lane & 7;
+  auto issue = [&](int j) {
+    const uint32_t row0 = wave * kTile + (uint32_t)j * kStride;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int r = 8 * c + lr;
+      const int k = lj ^ ((r >> 1) & 7);     // the chunk whose swizzled slot is position 64c + l
+      bdma16(krs, (row0 + r) * kD + 16u * k, &wr.key[j % kRing][64 * c]);
+    }
+    if (lane < kTile) bdma4(srs, (row0 + lane) * 4u, &wr.sc[j % kRing][0]);   // 32 scales: lanes 0..31
+  };
+
+  // The first key tiles go out first; the query prep (RoPE and SSMax, power-of-two scaling, hi/lo
+  // fp16 split) runs while they are in flight.
   const PrepIn pin = prep_load<BF16Q>(a, t);
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t rel = wave * kTile;
-  KeyTile tb[kDepth];
 #pragma unroll
-  for (int i = 0; i < kDepth; ++i) load_tile(tb[i], krs, srs, rel + i * kStride + col, g);
+  for (int i = 0; i < kRing; ++i)
+    if (i < TPW) issue(i);
   __builtin_amdgcn_sched_barrier(0);
   prep_compute<BF16Q>(sm, pin, a, p);
-  build_fp8_operands(sm, &qa, a, t);
+  prep_scales(sm, a);
+  // this lane's MFMA A operands (row m = lane & 31, half g) for the 8 K-steps, and its 16
+  // accumulator-row weights (row r of a lane in half g is head 8(r>>2) + 4g + (r&3))
   half8 ahi[8], alo[8];
   float cf[16];
+  {
+    const int m = lane & 31;
+    const int e = sm.ex[m];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    ahi[s] = __builtin_bit_cast(half8, qa.a[2 * s][lane]);
-    alo[s] = __builtin_bit_cast(half8, qa.a[2 * s + 1][lane]);
+    for (int s = 0; s < 8; ++s) {
+      const int base = 32 * (s >> 1) + 16 * g + 8 * (s & 1);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ldexpf(sm.qs[m][base + i], e);
+      u32x4 h4, l4;
+      split_half8(v, h4, l4);
+      ahi[s] = __builtin_bit_cast(half8, h4);
+      alo[s] = __builtin_bit_cast(half8, l4);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cf[r] = sm.coef[8 * (r >> 2) + 4 * g + (r & 3)];
   }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) cf[r] = qa.cf[r][lane];
 
   // only lanes 0..31 store (lanes 32..63 hold the same columns); the others aim past the range
   const uint32_t out_off = g == 0 ? 4u * col : 0x80000000u;
   const bool hist = HIST && n > a.topk_k;
-  if (hist) {
-    for (int i = threadIdx.x; i < kTkBins; i += kThreads) lh[i] = 0;
+  if (HIST) {
+    __syncthreads();   // every wave is done with the prep space
+    if (hist)
+      for (int i = threadIdx.x; i < kTkBins; i += kThreads) pu.lh[i] = 0;
     __syncthreads();
   }
 
-  // Fully unrolled: straight-line code gives the compiler exact wait counts, so kDepth - 1 tiles
-  // stay in flight behind the one being multiplied.  Past the chunk the loads read zeros and the stores
-  // are dropped, so there is no per-tile guard.
+  // Fully unrolled: the vmcnt of every wait is a compile-time count.  Before tile it is read, the
+  // loads issued after its own are those of the later tiles already in the ring and the score
+  // stores of the earlier iterations issued after it.
+  uint32_t rel = wave * kTile;
 #pragma unroll
   for (int it = 0; it < TPW; ++it) {
-    KeyTile& cur = tb[it % kDepth];
+    const int later_tiles = (it + kRing - 1 < TPW ? kRing - 1 : TPW - 1 - it);
+    const int later_stores = it < kRing - 1 ? it : kRing - 1;
+    switch (later_tiles * kLoadsPerTile + later_stores) {
+#define DSA_WAIT_CASE(N) case N: wait_vm<N>(); break;
+      DSA_WAIT_CASE(0) DSA_WAIT_CASE(1) DSA_WAIT_CASE(2) DSA_WAIT_CASE(3) DSA_WAIT_CASE(4) DSA_WAIT_CASE(5)
+      DSA_WAIT_CASE(6) DSA_WAIT_CASE(7) DSA_WAIT_CASE(8) DSA_WAIT_CASE(9) DSA_WAIT_CASE(10) DSA_WAIT_CASE(11)
+      DSA_WAIT_CASE(12)
+#undef DSA_WAIT_CASE
+      default: wait_vm<0>(); break;
+    }
+    asm volatile("" ::: "memory");           // the ring reads below stay after the wait
+    KeyTile cur;
+    const u32x4* slot = wr.key[it % kRing];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cur.x[c] = slot[tile_slot(col, 2 * c + g)];
+    cur.sc = wr.sc[it % kRing][col];
     const float sc = tile_scores(cur, ahi, alo, cf);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
-    if (hist && g == 0 && rel + col < nrow) atomicAdd(&lh[score_key(sc) >> kTkShift0], 1u);
-    if (it + kDepth < TPW) load_tile(cur, krs, srs, rel + kDepth * kStride + col, g);
+    if (hist && g == 0 && rel + col < nrow) atomicAdd(&pu.lh[score_key(sc) >> kTkShift0], 1u);
+    // the slot is refilled only after its contents are in registers (consumed by the MFMAs above)
+    if (it + kRing < TPW) issue(it + kRing);
     rel += kStride;
   }
   if (hist) {   // this chunk's counts into the row's histogram (read by the next kernel)
     __syncthreads();
     uint32_t* gh = tk_hist(a.topk_ws, t);
     for (int i = threadIdx.x; i < kTkBins; i += kThreads)
-      if (lh[i]) atomicAdd(&gh[i], lh[i]);
+      if (pu.lh[i]) atomicAdd(&gh[i], pu.lh[i]);
   }
 }
 
@@ -423,8 +543,6 @@ constexpr int kGroup = 4;
 constexpr int kRingTiles = 8;                    // key tiles in flight per workgroup
 constexpr int kTileBytes = kTile * kD;           // 4 KiB
 
-typedef __attribute__((address_space(3))) void* lds_vp;
-
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_vp)lds);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
@@ -432,11 +550,6 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_vp)lds);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt out of range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 // Barrier for LDS hand-offs that does not wait for global loads in flight.
 __device__ __forceinline__ void lds_sync() {
@@ -446,9 +559,6 @@ __device__ __forceinline__ void lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-// 16-byte slot of (row r, chunk k) of a tile in LDS: chunks are XOR-swizzled by row pair so that the
-// 16 lanes of a ds_read_b128 quarter (rows col..col+15, one chunk) hit 16 different bank groups.
-__device__ __forceinline__ int tile_slot(int r, int k) { return 8 * r + (k ^ ((r >> 1) & 7)); }
 
 struct SharedTiles {
   u32x4 key[kRingTiles][kTile * kD / 16];

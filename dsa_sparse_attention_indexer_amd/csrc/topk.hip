@@ -428,6 +428,14 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
 
 size_t topk_ws_bytes(int T) { return tk_total_words(T) * sizeof(uint32_t); }
 
+hipError_t launch_topk_hist(const TopkLaunch& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const int64_t cols = a.ld < a.ncap ? a.ld : a.ncap;
+  const dim3 seg_grid((unsigned)((cols + kTkSeg - 1) / kTkSeg), (unsigned)a.T);
+  hipLaunchKernelGGL(k_topk_hist, seg_grid, dim3(kCT), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkLaunch& a, bool hist_given, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int64_t cols = a.ld < a.ncap ? a.ld : a.ncap;

@@ -13,9 +13,9 @@ from typing import Optional
 
 import torch
 
-from . import (dsa_block_select, dsa_block_select_workspace_size, dsa_indexer_scores, dsa_indexer_topk,
-               dsa_indexer_workspace_size, dsa_sparse_mla_decode, dsa_sparse_mla_prefill,
-               dsa_sparse_mla_workspace_size, dsa_topk, indexer_desc, mla_desc, topk_workspace)
+from . import (dsa_block_select, dsa_block_select_workspace_size, dsa_indexer_scores, dsa_indexer_scores_hist,
+               dsa_indexer_topk, dsa_indexer_workspace_size, dsa_sparse_mla_decode, dsa_sparse_mla_prefill,
+               dsa_sparse_mla_workspace_size, dsa_topk, dsa_topk_hist, indexer_desc, mla_desc, topk_workspace)
 
 
 @dataclasses.dataclass
@@ -90,16 +90,30 @@ def index_and_select(wl, buf: StepBuffers, stream=None):
                             inv_freq=wl.inv_freq, ws=buf.ws_index, topk_ws=buf.ws_topk, stream=stream)
 
 
+def index_scores_hist(wl, buf: StepBuffers, stream=None):
+    """The scores plus the first-digit histogram (first half of index_and_select)."""
+    return dsa_indexer_scores_hist(wl.index_q, wl.index_w, wl.q_seq, wl.q_pos, wl.index_k, buf.scores, wl.topk,
+                                   buf.ws_topk, k_scale=wl.index_k_scale, ssmax_s=wl.ssmax_s, ssmax_b=wl.ssmax_b,
+                                   inv_freq=wl.inv_freq, ws=buf.ws_index, stream=stream)
+
+
+def select_hist(wl, buf: StepBuffers, stream=None):
+    """The top-k from the scores and histogram index_scores_hist left (second half)."""
+    return dsa_topk_hist(buf.scores, wl.q_pos, wl.topk, buf.idx, buf.length, wl.max_ctx, buf.ws_topk, stream=stream)
+
+
 def layer_step(wl, buf: StepBuffers, *, prefill: bool = False, block_sparse: bool = False,
-               shared_from: Optional[StepBuffers] = None, num_splits: int = 0, fused: bool = False, stream=None):
+               shared_from: Optional[StepBuffers] = None, num_splits: int = 0, fused: bool = True, stream=None):
     """Scores -> selection -> sparse MLA; with shared_from, only the MLA over that selection.
 
-    fused: scores and top-k through dsa_indexer_topk (else the two separate calls)."""
+    fused (default): the score kernel also builds the first radix digit's histogram and the top-k
+    continues from it (index_scores_hist + select_hist); else dsa_indexer_scores and dsa_topk."""
     if shared_from is not None:
         return attend(wl, buf, prefill=prefill, num_splits=num_splits, idx=shared_from.idx,
                       length=shared_from.length, stream=stream)
     if fused and not block_sparse:
-        index_and_select(wl, buf, stream)
+        index_scores_hist(wl, buf, stream)
+        select_hist(wl, buf, stream)
     else:
         index_scores(wl, buf, stream)
         select(wl, buf, block_sparse=block_sparse, stream=stream)

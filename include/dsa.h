@@ -153,6 +153,25 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* desc, const void* q, con
                               float* scores, int64_t ld_scores, int32_t k, int32_t* idx, int32_t* len,
                               void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream);
 
+/* The two halves of dsa_indexer_topk as separate calls, for callers that schedule or time the
+ * score stream and the selection apart.  dsa_indexer_scores_hist writes the scores (as
+ * dsa_indexer_scores) and leaves each row's first-radix-digit histogram in `topk_ws` (built inside
+ * the fp8 score kernel, else by a histogram pass after it); dsa_topk_hist then selects k columns of
+ * each row from those scores and that histogram and leaves the workspace zeroed.  Issued back to
+ * back with the same arguments they give exactly dsa_indexer_topk's results (rows hold
+ * min(q_pos + 1, max_ctx) scores).  dsa_topk_hist must follow a dsa_indexer_scores_hist call on the
+ * same scores and workspace with no other top-k call on that workspace in between; otherwise its
+ * selection is undefined (it still reads and writes only its own buffers). */
+dsa_status_t dsa_indexer_scores_hist(const dsa_indexer_desc_t* desc, const void* q, const float* w,
+                                     const int32_t* q_seq, const int32_t* q_pos,
+                                     const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                                     const void* k_cache, const float* k_scale,
+                                     float* scores, int64_t ld_scores, int32_t k,
+                                     void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream);
+dsa_status_t dsa_topk_hist(const dsa_indexer_desc_t* desc, const float* scores, int64_t ld_scores,
+                           const int32_t* q_pos, int32_t k, int32_t* idx, int32_t* len,
+                           void* topk_ws, size_t topk_ws_bytes, void* stream);
+
 /* ============================================================================================
  * 2b. Block-sparse selection
  * --------------------------------------------------------------------------------------------

@@ -392,6 +392,10 @@ FUSED_CASES = [
     ("ragged", dict(seq_lens=[9000, 2048, 2049, 1, 4097], max_ctx=9000), False),
     ("prefill_positions", dict(seq_lens=[7000], max_ctx=7000, q_positions=[0, 2047, 2048, 5000, 6999]), False),
     ("constant_keys", dict(seq_lens=[6000, 3000], max_ctx=6000), True),   # every score ties
+    # paths where the histogram comes from a pass after the scores: fp32 keys, and 300 queries
+    # (the grouped score kernel)
+    ("f32_keys", dict(seq_lens=[5000, 2500], max_ctx=5000, fp8=False, q_dtype=torch.float32), False),
+    ("grouped_300_queries", dict(seq_lens=[6000], max_ctx=6000, q_positions=list(range(2000, 6000, 13))[:300]), False),
 ]
 
 
@@ -403,15 +407,19 @@ def test_fused_index_topk_equals_separate_calls(dsa, name, kw, constant):
         g.index_k[:] = g.index_k[0, 0]
         g.index_k_scale[:] = g.index_k_scale[0, 0]
     P = _pipe()
-    sep, fus = P.alloc_buffers(g), P.alloc_buffers(g)
+    sep, fus, spl = P.alloc_buffers(g), P.alloc_buffers(g), P.alloc_buffers(g)
     P.index_scores(g, sep)
     P.select(g, sep)
     P.index_and_select(g, fus)
+    P.index_scores_hist(g, spl)   # the same in two calls (dsa_indexer_scores_hist + dsa_topk_hist)
+    P.select_hist(g, spl)
     torch.cuda.synchronize()
     for t in range(wl.num_q):
         n = int(wl.q_pos[t]) + 1
         assert torch.equal(sep.scores[t, :n], fus.scores[t, :n]), f"{name} q{t}: scores differ"
+        assert torch.equal(sep.scores[t, :n], spl.scores[t, :n]), f"{name} q{t}: split-call scores differ"
     assert torch.equal(sep.idx, fus.idx) and torch.equal(sep.length, fus.length), f"{name}: selections differ"
+    assert torch.equal(sep.idx, spl.idx) and torch.equal(sep.length, spl.length), f"{name}: split-call selections differ"
     if constant:   # all scores equal: the lowest k columns win
         idx = fus.idx.cpu().numpy()
         for t in range(wl.num_q):
