@@ -400,6 +400,58 @@ struct WaveRing {
   float sc[kRing][kTile];
 };
 
+// Query-prep inputs loaded with assembly loads, so that the compiler does not wait for the key
+// gathers issued after them (it cannot see those and would drain the whole load counter before
+// the first use).  prep_landed<N> waits until at most N later operations are outstanding; the
+// values are tied to that wait so that nothing reads them earlier.
+__device__ __forceinline__ u32x4 aload16(const void* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ float aload4(const float* p) {
+  float v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
+template <bool BF16Q>
+__device__ __forceinline__ PrepIn prep_issue(const IndexerLaunch& a, int t) {
+  const int tid = threadIdx.x;
+  const int h = tid >> 3, part = tid & 7;
+  const int hc = min(h, a.H - 1);
+  PrepIn in;
+  const size_t base = ((size_t)t * a.H + hc) * kD + 16 * part;
+  if (BF16Q) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + base);
+    in.raw[0] = aload16(src);
+    in.raw[1] = aload16(src + 1);
+  } else {
+    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.q) + base);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) in.raw[i] = aload16(src + i);
+  }
+  const int th = min(tid, a.H - 1);
+  const float* pf = a.rope_dim > 0 ? a.inv_freq : a.w;
+  const float* ps = a.ssmax_s ? a.ssmax_s : a.w;
+  const float* pb = a.ssmax_s ? a.ssmax_b : a.w;
+  in.invf = aload4(pf + (a.rope_dim > 0 ? min(tid, a.rope_dim / 2 - 1) : 0));
+  in.ss = aload4(ps + th);
+  in.sb = aload4(pb + th);
+  in.wv = aload4(a.w + (size_t)t * a.H + th);
+  return in;
+}
+
+template <int N, bool BF16Q>
+__device__ __forceinline__ void prep_landed(PrepIn& in) {
+  wait_vm<N>();
+  if (BF16Q)
+    asm volatile("" : "+v"(in.raw[0]), "+v"(in.raw[1]), "+v"(in.invf), "+v"(in.ss), "+v"(in.sb), "+v"(in.wv));
+  else
+    asm volatile("" : "+v"(in.raw[0]), "+v"(in.raw[1]), "+v"(in.raw[2]), "+v"(in.raw[3]), "+v"(in.invf),
+                 "+v"(in.ss), "+v"(in.sb), "+v"(in.wv));
+}
+
 // TPW: 32-key tiles per wave (a workgroup covers 4 * 32 * TPW keys).  HIST: also histogram the
 // first top-k digit of this chunk's scores into the top-k workspace (the fused selection path).
 //
@@ -454,14 +506,13 @@ k_index_scores_fp8(IndexerLaunch a) {
     if (lane < kTile) bdma4(srs, (row0 + lane) * 4u, &wr.sc[j % kRing][0]);   // 32 scales: lanes 0..31
   };
 
-  // The first key tiles go out first; the query prep (RoPE and SSMax, power-of-two scaling, hi/lo
-  // fp16 split) runs while they are in flight.
-  const PrepIn pin = prep_load<BF16Q>(a, t);
-  __builtin_amdgcn_sched_barrier(0);
+  // The query-prep inputs go out, then the first key tiles; the prep (RoPE and SSMax, power-of-two
+  // scaling, hi/lo fp16 split) runs as soon as its inputs have landed, while the tiles are in flight.
+  PrepIn pin = prep_issue<BF16Q>(a, t);
 #pragma unroll
   for (int i = 0; i < kRing; ++i)
     if (i < TPW) issue(i);
-  __builtin_amdgcn_sched_barrier(0);
+  prep_landed<5 * (kRing < TPW ? kRing : TPW), BF16Q>(pin);
   prep_compute<BF16Q>(sm, pin, a, p);
   prep_scales(sm, a);
   // this lane's MFMA A operands (row m = lane & 31, half g) for the 8 K-steps, and its 16
