@@ -33,16 +33,25 @@ __device__ inline uint32_t* tk_hist(void* ws, int t) { return tk_row(ws, t); }
 
 // Block-wide exclusive prefix sum over NT threads (a multiple of 64, at most 1024); *total, if
 // given, gets the sum.  sbuf: at least NT/64 words.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS round trips): shifts by
+// 1, 2, 4 and 8 lanes within each 16-lane row (lanes shifted in from outside the row read 0), then
+// the total of row 0 is added to row 1 and of row 2 to row 3 (row_bcast:15), and the total of rows
+// 0-1 to rows 2 and 3 (row_bcast:31).
+__device__ inline uint32_t tk_wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);    // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);    // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);    // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);    // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 template <int NT>
 __device__ inline uint32_t tk_excl_scan(uint32_t v, uint32_t* total, uint32_t* sbuf) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = tk_wave_incl_scan(v);
   if (lane == 63) sbuf[wave] = x;
   __syncthreads();
   uint32_t off = 0, tot = 0;
