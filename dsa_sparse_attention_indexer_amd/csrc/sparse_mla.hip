@@ -242,12 +242,11 @@ k_mla_fp8(MlaLaunch a) {
   const int slot_end = min(slot0 + a.per_split, a.topk);   // this split's slots before the length cut
   constexpr int RPT = kRowsChunk / kMlaThreads;
   int rv[RPT];
-  auto load_rows = [&](int cb) {
+  auto load_rows = [&](int cb) {   // unconditional loads (slot clamped into the row): all in flight together
 #pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-      const int i = tid + kMlaThreads * u;
-      rv[u] = cb + i < slot_end ? irow[cb + i] : -1;
-    }
+    for (int u = 0; u < RPT; ++u) rv[u] = irow[min(cb + tid + kMlaThreads * u, a.topk - 1)];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) rv[u] = cb + tid + kMlaThreads * u < slot_end ? rv[u] : -1;
   };
   load_rows(slot0);
   constexpr int KH = KSTEPS / 2;                        // K-steps per half
@@ -584,9 +583,41 @@ k_mla_f32(MlaLaunch a) {
 constexpr int kCombineHeads = 4;                      // waves (heads) per workgroup
 constexpr int kCombineThreads = 64 * kCombineHeads;
 
+// Maximum and sum over the 64 lanes of a wave with DPP moves (no LDS round trips): row shifts by
+// 1, 2, 4 and 8 lanes, then row broadcasts of lanes 15 and 31, leave the result in lane 63, which
+// is read into a scalar.
+__device__ __forceinline__ float wave_max(float x) {
+  int v = __builtin_bit_cast(int, x);
+  auto step = [&](auto CTRL, auto RMASK) {
+    const int o = __builtin_amdgcn_update_dpp(v, v, decltype(CTRL)::value, decltype(RMASK)::value, 0xf, false);
+    v = __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, v), __builtin_bit_cast(float, o)));
+  };
+  step(IntC<0x111>(), IntC<0xf>());   // row_shr:1 (lanes without a source keep their own value)
+  step(IntC<0x112>(), IntC<0xf>());   // row_shr:2
+  step(IntC<0x114>(), IntC<0xf>());   // row_shr:4
+  step(IntC<0x118>(), IntC<0xf>());   // row_shr:8
+  step(IntC<0x142>(), IntC<0xa>());   // row_bcast:15 into rows 1 and 3
+  step(IntC<0x143>(), IntC<0xc>());   // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 63));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  auto step = [&](auto CTRL, auto RMASK) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(CTRL)::value,
+                                                               decltype(RMASK)::value, 0xf, true));
+  };
+  step(IntC<0x111>(), IntC<0xf>());   // row_shr:1 (lanes without a source add 0)
+  step(IntC<0x112>(), IntC<0xf>());
+  step(IntC<0x114>(), IntC<0xf>());
+  step(IntC<0x118>(), IntC<0xf>());
+  step(IntC<0x142>(), IntC<0xa>());
+  step(IntC<0x143>(), IntC<0xc>());
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 template <bool BF16>
 __global__ void __launch_bounds__(kCombineThreads) k_mla_combine(MlaLaunch a) {
   constexpr int SB = BF16 ? 16 : 8;                   // splits per batch of loads
+  constexpr int NV = BF16 ? 1 : 2;                    // 16-byte loads per split and lane
   int t, hq;
   if (!xcd_query_map((a.H + kCombineHeads - 1) / kCombineHeads, a.T, &t, &hq)) return;
   const int lane = threadIdx.x & 63;
@@ -602,40 +633,33 @@ __global__ void __launch_bounds__(kCombineThreads) k_mla_combine(MlaLaunch a) {
     m = stats[2 * i];
     l = stats[2 * i + 1];
   }
-  float v[SB][8];
+  // A batch of SB splits: every load is unconditional (split indices past the end are clamped to
+  // the last split, whose weight below is then 0 for them), so the whole batch is in flight at
+  // once; the values are decoded where they are used.
+  u32x4 raw[SB][NV];
   auto load = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      if (s0 + j < a.splits) {
-        const size_t off = base + (size_t)(s0 + j) * sstride;
-        if (BF16) {
-          const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.ws) + off);
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[j][2 * e] = __uint_as_float(w4[e] << 16);
-            v[j][2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
-          }
-        } else {
-          const float4 x = *reinterpret_cast<const float4*>(a.ws + off);
-          const float4 y = *reinterpret_cast<const float4*>(a.ws + off + 4);
-          v[j][0] = x.x; v[j][1] = x.y; v[j][2] = x.z; v[j][3] = x.w;
-          v[j][4] = y.x; v[j][5] = y.y; v[j][6] = y.z; v[j][7] = y.w;
-        }
+      const size_t off = base + (size_t)min(s0 + j, a.splits - 1) * sstride;
+      if (BF16) {
+        raw[j][0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.ws) + off);
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+        raw[j][0] = *reinterpret_cast<const u32x4*>(a.ws + off);
+        raw[j][NV - 1] = *reinterpret_cast<const u32x4*>(a.ws + off + 4);
       }
     }
   };
+  auto value = [&](int j, int e) -> float {
+    if (BF16) {
+      const uint32_t w2 = raw[j][0][e >> 1];
+      return __uint_as_float((e & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
+    }
+    return __uint_as_float(raw[j][e >> 2][e & 3]);
+  };
   load(0);
-  float M = m;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float M = wave_max(m);
   const float w = (M == -INFINITY || lane >= a.splits) ? 0.f : exp2f(m - M);
-  float Ls = w * l;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
+  const float Ls = wave_sum(w * l);
   // normalised (bf16) partials carry their own sum l
   const float wt = Ls > 0.f ? (BF16 ? w * l : w) / Ls : 0.f;
   if (lane == 0 && a.lse) a.lse[(size_t)t * a.H + h] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
@@ -644,9 +668,9 @@ __global__ void __launch_bounds__(kCombineThreads) k_mla_combine(MlaLaunch a) {
     if (s0 > 0) load(s0);
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      const float wj = __shfl(wt, min(s0 + j, 63));
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), min(s0 + j, 63)));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj, v[j][e], acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj, value(j, e), acc[e]);
     }
   }
   float* outp = a.out + ((size_t)t * a.H + h) * a.kv_lora + 8 * lane;

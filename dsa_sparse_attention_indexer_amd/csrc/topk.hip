@@ -44,21 +44,17 @@ __device__ inline uint32_t lanes_below(uint64_t m) {
 
 // Element (q, e) of thread tid stands for column c0 + 4*NT*q + 4*tid + e: each float4 load of a
 // wave covers 1 KiB of contiguous scores.  Loads keys; bit 4q+e of the mask is set when the
-// column is < n.  All loads are issued before any is used.
+// column is < n (n >= 1).  Every load is an unconditional float4 (a slice at or past n reads the
+// row's last aligned float4 instead, which is in range because rows are a multiple of 4 long, and
+// is masked out), so all of them are in flight together.
 template <int Q, int NT>
 __device__ __forceinline__ uint32_t load_slices(const float* row, int n, int c0, uint32_t key[Q][4]) {
   float4 v[Q];
+  const int clast = (n - 1) & ~3;
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int c = c0 + 4 * NT * q + 4 * (int)threadIdx.x;
-    if (c + 4 <= n) {
-      v[q] = *reinterpret_cast<const float4*>(row + c);
-    } else {
-      v[q].x = c < n ? row[c] : 0.f;
-      v[q].y = c + 1 < n ? row[c + 1] : 0.f;
-      v[q].z = c + 2 < n ? row[c + 2] : 0.f;
-      v[q].w = c + 3 < n ? row[c + 3] : 0.f;
-    }
+    v[q] = *reinterpret_cast<const float4*>(row + min(c, clast));
   }
   uint32_t mask = 0;
 #pragma unroll
