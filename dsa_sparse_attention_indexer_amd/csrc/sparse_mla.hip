@@ -467,10 +467,48 @@ k_mla_fp8(MlaLaunch a) {
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   // oacc[md][i] = O^T[dim ODIM*half + 16md + 4g + i][head c]
+  if (a.splits > 1 && bf16_partials(a)) {
+    // bf16 split partials leave through LDS so that every store covers whole lines: this wave's
+    // 16 heads x 256 dims in two rounds of 8 heads, each head row then stored as 32 lanes x 16
+    // contiguous bytes, non-temporally (the partials stream out during the kernel instead of being
+    // written back from L2 when it ends).  The raw slots are free: every wave has passed the last
+    // tile's second barrier, after which no gather or dequantisation touches them.  No branch
+    // depends on the lane: in each round the lanes of the other round's heads write a discard row
+    // (row 8), and a wave barrier keeps the round's writes before its reads.
+    constexpr int kStageRow = 2 * C::ODIM + 16;            // bytes per staged head row (padded)
+    constexpr int kStageWords = kStageRow / 4;
+    static_assert(8 * 9 * kStageRow <= (int)sizeof(sl), "staging space");
+    uint32_t* stage = static_cast<uint32_t*>(__builtin_assume_aligned(
+        reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(&sl[0]) + wave * 9 * kStageRow), 16));
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const size_t hstride = (size_t)a.splits * a.kv_lora;   // bf16 between consecutive heads' partials
+    uint16_t* dst0 = reinterpret_cast<uint16_t*>(a.ws) + (((size_t)t * a.H + 16 * hg) * a.splits + split) * a.kv_lora +
+                     C::ODIM * half;
 #pragma unroll
-  for (int md = 0; md < MD; ++md) {
-    float o[4] = {oacc[md][0], oacc[md][1], oacc[md][2], oacc[md][3]};
-    write_partial_or_final(a, t, split, head, m_run, l_tot, o, C::ODIM * half + 16 * md + 4 * g, 4);
+    for (int ph = 0; ph < 2; ++ph) {
+      const int wrow = (c >> 3) == ph ? (c & 7) : 8;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        uint32_t* w = stage + wrow * kStageWords + (16 * md + 4 * g) / 2;
+        w[0] = cvt2_bf16(float2v{oacc[md][0] * inv, oacc[md][1] * inv});
+        w[1] = cvt2_bf16(float2v{oacc[md][2] * inv, oacc[md][3] * inv});
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int row = 2 * k + (lane >> 5), ch = lane & 31;
+        const uint32_t* r = stage + row * kStageWords + 4 * ch;
+        const u32x4 v = {r[0], r[1], r[2], r[3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst0 + (size_t)(8 * ph + row) * hstride + 8 * ch));
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      float o[4] = {oacc[md][0], oacc[md][1], oacc[md][2], oacc[md][3]};
+      write_partial_or_final(a, t, split, head, m_run, l_tot, o, C::ODIM * half + 16 * md + 4 * g, 4);
+    }
   }
   if (g == 0 && half == 0) write_stats(a, t, split, head, m_run, l_tot);
 }
