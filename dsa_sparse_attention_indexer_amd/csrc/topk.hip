@@ -26,8 +26,8 @@
 namespace dsa {
 namespace {
 
-constexpr int kCT = 256;                   // hist / collect threads
-constexpr int kCQ = kTkSeg / (4 * kCT);    // float4 slices per collect thread (8)
+constexpr int kCT = 512;                   // hist / collect threads
+constexpr int kCQ = kTkSeg / (4 * kCT);    // float4 slices per collect thread (4)
 constexpr int kRT = 1024;                  // resolve threads
 constexpr int kSQ = 4;                     // float4 slices per resolve thread and streaming round
 
