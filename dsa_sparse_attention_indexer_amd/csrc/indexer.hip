@@ -452,6 +452,26 @@ __device__ __forceinline__ void prep_landed(PrepIn& in) {
                  "+v"(in.ss), "+v"(in.sb), "+v"(in.wv));
 }
 
+// Vector-memory operations issued after tile it's gathers and before its wait, per wave of the
+// decode kernel: iteration m issues the gathers of tile m + kRing (five loads, when that tile
+// exists) right after reading its slot, then stores its 32 scores (one store); tiles 0..kRing-1
+// are gathered before the loop.
+constexpr int kLoadsPerTile = 5;   // four 16-byte row loads and one scale load
+constexpr int ring_wait(int it, int tpw) {
+  int n = 0;
+  if (it < kRing) {
+    for (int j = it + 1; j < kRing && j < tpw; ++j) n += kLoadsPerTile;
+    for (int m = 0; m < it; ++m) n += (m + kRing < tpw ? kLoadsPerTile : 0) + 1;
+  } else {
+    n += 1;   // the store of iteration it - kRing, issued after that iteration's gathers
+    for (int m = it - kRing + 1; m < it; ++m) n += (m + kRing < tpw ? kLoadsPerTile : 0) + 1;
+  }
+  return n;
+}
+static_assert(ring_wait(0, 32) == 10 && ring_wait(1, 32) == 11 && ring_wait(2, 32) == 12 && ring_wait(3, 32) == 13 &&
+                      ring_wait(29, 32) == 13 && ring_wait(30, 32) == 8 && ring_wait(31, 32) == 3,
+              "ring wait counts");
+
 // TPW: 32-key tiles per wave (a workgroup covers 4 * 32 * TPW keys).  HIST: also histogram the
 // first top-k digit of this chunk's scores into the top-k workspace (the fused selection path).
 //
@@ -464,7 +484,6 @@ template <int TPW, bool HIST, bool BF16Q>
 __global__ void __launch_bounds__(kThreads)
 k_index_scores_fp8(IndexerLaunch a) {
   constexpr int chunk = 4 * kTile * TPW;
-  constexpr int kLoadsPerTile = 5;          // four 16-byte row loads and one scale load
   __shared__ __attribute__((aligned(16))) WaveRing ring[4];
   // query prep, then (fused path) the chunk's histogram: the histogram reuses the prep's space
   __shared__ __attribute__((aligned(16))) union PrepOrHist {
@@ -547,21 +566,19 @@ k_index_scores_fp8(IndexerLaunch a) {
     __syncthreads();
   }
 
-  // Fully unrolled: the vmcnt of every wait is a compile-time count.  Before tile it is read, the
-  // loads issued after its own are those of the later tiles already in the ring and the score
-  // stores of the earlier iterations issued after it.
+  // Fully unrolled: the vmcnt of every wait is a compile-time count (ring_wait).  A slot is
+  // refilled as soon as its contents are in registers, before the tile's matrix work, so the next
+  // gather is in flight while this tile is scored.
   uint32_t rel = wave * kTile;
 #pragma unroll
   for (int it = 0; it < TPW; ++it) {
-    const int later_tiles = (it + kRing - 1 < TPW ? kRing - 1 : TPW - 1 - it);
-    const int later_stores = it < kRing - 1 ? it : kRing - 1;
-    switch (later_tiles * kLoadsPerTile + later_stores) {
+    switch (ring_wait(it, TPW)) {
 #define DSA_WAIT_CASE(N) case N: wait_vm<N>(); break;
       DSA_WAIT_CASE(0) DSA_WAIT_CASE(1) DSA_WAIT_CASE(2) DSA_WAIT_CASE(3) DSA_WAIT_CASE(4) DSA_WAIT_CASE(5)
       DSA_WAIT_CASE(6) DSA_WAIT_CASE(7) DSA_WAIT_CASE(8) DSA_WAIT_CASE(9) DSA_WAIT_CASE(10) DSA_WAIT_CASE(11)
-      DSA_WAIT_CASE(12)
+      DSA_WAIT_CASE(12) DSA_WAIT_CASE(13)
 #undef DSA_WAIT_CASE
-      default: wait_vm<0>(); break;
+      default: wait_vm<0>(); break;   // (not reached for kRing <= 3)
     }
     asm volatile("" ::: "memory");           // the ring reads below stay after the wait
     KeyTile cur;
@@ -569,11 +586,13 @@ k_index_scores_fp8(IndexerLaunch a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) cur.x[c] = slot[tile_slot(col, 2 * c + g)];
     cur.sc = wr.sc[it % kRing][col];
+    if (it + kRing < TPW) {
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): the slot's contents are in registers
+      issue(it + kRing);
+    }
     const float sc = tile_scores(cur, ahi, alo, cf);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
     if (hist && g == 0 && rel + col < nrow) atomicAdd(&pu.lh[score_key(sc) >> kTkShift0], 1u);
-    // the slot is refilled only after its contents are in registers (consumed by the MFMAs above)
-    if (it + kRing < TPW) issue(it + kRing);
     rel += kStride;
   }
   if (hist) {   // this chunk's counts into the row's histogram (read by the next kernel)
