@@ -259,6 +259,11 @@ MLA_CASES = [
     # selections wider than the 2048 slots staged in LDS at a time (and top-k above 4096)
     ("fp8_topk4100_prefill", dict(seq_lens=[6000], max_ctx=6000, q_positions=[5999, 4500, 3000], topk=4100), True, 0),
     ("fp8_topk4100_decode", dict(seq_lens=[6000, 5000], max_ctx=6000, topk=4100), False, 0),
+    # the other head counts of the fp8 path, 32 splits (two batches of partials in the combine) and
+    # one split (the decode writes its output directly)
+    ("fp8_rope_h48_split32", dict(seq_lens=[3000, 2200], max_ctx=3000, mla_heads=48), False, 32),
+    ("fp8_nope_h32", dict(seq_lens=[2600, 1500], max_ctx=2600, rope=False, mla_heads=32), False, 0),
+    ("fp8_rope_h16_split1", dict(seq_lens=[2500], max_ctx=2500, mla_heads=16), False, 1),
 ]
 
 
