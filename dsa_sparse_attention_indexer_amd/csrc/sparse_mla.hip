@@ -50,10 +50,6 @@ __device__ __forceinline__ int ks_row_of_key(int kappa) {
   return 16 * ((kappa >> 2) & 1) + 4 * (kappa >> 3) + (kappa & 3);
 }
 
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
-}
-
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
