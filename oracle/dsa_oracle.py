@@ -29,6 +29,15 @@ What it computes, and where the pages say so:
   P = softmax(z), O_g = sum_t P_t c_t[:512] (V is the latent), LSE_g = log sum exp z.
   NoPE layers are MLA with zero rope dims on the same cache layout ("NoPE, SSMax and
   LeRoPE" on the vLLM page; "NoPE layers" bullet on the colibri page).
+* Cache writers -- the indexer key of a token is k = LayerNorm(wk(x)), rotated on its
+  first 64 dims on RoPE layers ("mistral-large4.md", "What differs from GLM-5.2", bullet
+  "The indexer"), quantised to FP8 with one scale per token and written into the index
+  cache ("Day 0 support for Mistral Large 4 on vLLM", "ROCm implementation details",
+  "DSA indexer on AITER": 132 bytes per token, one layout shared by writer and readers).
+  A latent row (512 latent + 64 rotary dims, "Model architecture") has its rotary slice
+  rotated at the token's position and is stored as FP8 with one scale per 64 elements.
+  The quantiser is scale = amax / 448 (1 for an all-zero group) and code = the nearest
+  E4M3FN value of x / scale, ties to the even code, saturated at +-448.
 * Block-sparse selection -- "vLLM adds NVFP4 serving for MiniMax M3.1 Flash at 76
   concurrent sequences", the three MiniMax Sparse Attention steps: 128-token blocks,
   16 blocks selected with the most recent block always kept, exact attention over the
@@ -65,6 +74,43 @@ def decode_e4m3fn(codes) -> np.ndarray:
     v = np.where(e == 0, sub, normal)
     v = np.where((e == 15) & (m == 7), np.nan, v)
     return sign * v
+
+
+def encode_e4m3fn(v) -> np.ndarray:
+    """Nearest E4M3FN code of each value: ties go to the even code (even mantissa), magnitudes
+    above 448 saturate to 448, the sign is kept (also for zero), NaN gives 0x7F.
+
+    The candidates are the 127 finite non-negative magnitudes of decode_e4m3fn, in code order
+    (which is increasing magnitude).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    mags = decode_e4m3fn(np.arange(127, dtype=np.uint8))      # codes 0x00..0x7E
+    a = np.minimum(np.abs(v), 448.0)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 126)  # mags[hi] >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+    return np.where(np.isnan(v), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def quantize_e4m3_rows(x, block: int, precision=np.float64):
+    """Codes and scales of the rows of x, one scale per `block` elements along the last dim.
+
+    scale = amax / 448 (1 where amax is 0); code = encode_e4m3fn(x / scale).  `precision` is the
+    float type in which x, the scale and the quotient are rounded before the code is chosen
+    (float32 to take the decision as a float32 kernel does).  Returns (uint8 codes, scales).
+    """
+    x = np.asarray(x, dtype=np.float64).astype(precision)
+    d = x.shape[-1]
+    assert d % block == 0
+    xb = x.reshape(*x.shape[:-1], d // block, block)
+    amax = np.abs(xb).max(axis=-1)
+    scale = np.where(amax > 0, amax / precision(448.0), precision(1.0)).astype(precision)
+    q = (xb / scale[..., None]).astype(precision)
+    return encode_e4m3fn(q.astype(np.float64)).reshape(x.shape), scale.astype(np.float64)
 
 
 def decode_bf16(bits) -> np.ndarray:
@@ -288,6 +334,43 @@ def dense_mla_row(wl, query: int):
     p = int(wl.q_pos[query])
     rows = cache_rows(wl, int(wl.q_seq[query]), np.arange(p + 1))
     return mla_attend(wl.mla_q[query], rows, wl.rope_dim, wl.softmax_scale)
+
+
+# ----------------------------------------------------------------------------------------------
+# Cache writers: the indexer key path and latent rows
+# ----------------------------------------------------------------------------------------------
+
+
+def layer_norm(y, weight, bias, eps: float) -> np.ndarray:
+    """LayerNorm over the last dim: (y - mean) / sqrt(var + eps) * weight + bias, with the
+    population variance (mean of squared deviations)."""
+    y = np.asarray(y, dtype=np.float64)
+    mu = y.mean(axis=-1, keepdims=True)
+    var = ((y - mu) ** 2).mean(axis=-1, keepdims=True)
+    out = (y - mu) / np.sqrt(var + eps) * to_f64(weight)
+    return out + (0.0 if bias is None else to_f64(bias))
+
+
+def index_key(x, wk, ln_w, ln_b, eps: float, pos: int, inv_freq=None) -> np.ndarray:
+    """Indexer key of one token before quantisation: LayerNorm(wk(x)), then RoPE on the first
+    2*len(inv_freq) dims at the token's position (no rotation when inv_freq is None).
+
+    x [D] (the token's hidden state), wk [128][D] (the projection's weight: output dim first).
+    """
+    y = to_f64(wk) @ to_f64(x)
+    k = layer_norm(y, ln_w, ln_b, eps)
+    if inv_freq is not None:
+        k = rope_interleaved(k, rope_angles(pos, inv_freq))
+    return k
+
+
+def latent_row(kv, pos: int, inv_freq=None, kv_lora: int = 512) -> np.ndarray:
+    """A latent cache row before quantisation: the 512 latent dims as given, the rotary slice
+    (dims 512..575) rotated at the token's position (unrotated when inv_freq is None)."""
+    r = np.array(to_f64(kv), copy=True)
+    if inv_freq is not None:
+        r[kv_lora:] = rope_interleaved(r[kv_lora:], rope_angles(pos, inv_freq))
+    return r
 
 
 # ----------------------------------------------------------------------------------------------

@@ -353,3 +353,127 @@ def test_cache_byte_arithmetic_matches_pages():
     assert g["kv_owner_layers"] * workloads.KV_ROW + g["total_indexer"] == g["total_rocm_e4m3"]
     assert g["kv_owner_layers"] * 2 * workloads.KV_ROW + g["total_indexer"] == g["total_bf16"]
     assert round(g["total_bf16"] / g["total_rocm_e4m3"], 2) == g["capacity_ratio_bf16_over_e4m3"]
+
+
+# ---------------------------------------------------------------------------------------------
+# Cache writers: the E4M3FN encoder, the quantiser, the indexer key path and latent rows
+# ---------------------------------------------------------------------------------------------
+
+def _e4m3_magnitudes():
+    return torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3fn_encoder_matches_torch_cast_on_ties_and_random_values():
+    m = _e4m3_magnitudes()
+    mids = (m[:-1] + m[1:]) / 2                          # every tie between neighbours
+    rng = np.random.default_rng(7)
+    rand = np.concatenate([rng.normal(0, s, 20000) for s in (1e-3, 0.05, 1.0, 30.0, 150.0)])
+    v = np.concatenate([m, mids, -mids, rand, [0.0, -0.0, 448.0, -448.0]])
+    v = v[np.abs(v) <= 448.0]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = O.encode_e4m3fn(v)
+    # torch rounds from float64 directly (no double rounding), so codes agree bit for bit
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3fn_encoder_ties_go_to_even_code_and_saturates():
+    m = _e4m3_magnitudes()
+    for c in range(126):
+        mid = (m[c] + m[c + 1]) / 2
+        assert O.encode_e4m3fn(mid) == (c if c % 2 == 0 else c + 1)
+        assert O.encode_e4m3fn(-mid) == 0x80 | (c if c % 2 == 0 else c + 1)
+        assert O.decode_e4m3fn(O.encode_e4m3fn(m[c])) == m[c]          # exact values round-trip
+    assert O.encode_e4m3fn(449.0) == 0x7E and O.encode_e4m3fn(-1e9) == 0xFE
+    assert O.encode_e4m3fn(np.nan) == 0x7F
+
+
+def test_quantiser_maps_the_group_maximum_to_448_and_bounds_the_error():
+    rng = np.random.default_rng(8)
+    x = rng.normal(0, 3.0, (50, 128))
+    x[3] = 0.0
+    codes, scale = O.quantize_e4m3_rows(x, 128)
+    assert scale.shape == (50, 1) and scale[3, 0] == 1.0 and np.all(codes[3] & 0x7F == 0)
+    for r in (0, 1, 2, 10, 49):
+        j = int(np.argmax(np.abs(x[r])))
+        assert codes[r, j] & 0x7F == 0x7E                # |x| = amax -> 448
+        assert np.isclose(scale[r, 0], np.abs(x[r]).max() / 448.0, rtol=0, atol=0)
+    back = O.decode_e4m3fn(codes) * scale
+    # relative half-spacing of E4M3 normals is 2^-4; subnormals are at most 2^-10 x scale off
+    err = np.abs(back - x)
+    assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale) + 1e-12)
+    # the same quantiser also produces the synthetic caches' format: 64-element groups
+    c64, s64 = O.quantize_e4m3_rows(x[:, :128], 64)
+    assert s64.shape == (50, 2)
+    assert np.array_equal(c64[:, :64], O.quantize_e4m3_rows(x[:, :64], 64)[0])
+
+
+def test_quantiser_in_float32_agrees_with_torch_float32_pipeline():
+    rng = np.random.default_rng(9)
+    x = rng.normal(0, 1.0, (200, 576)).astype(np.float32)
+    codes, scale = O.quantize_e4m3_rows(x, 64, precision=np.float32)
+    xt = torch.from_numpy(x).reshape(200, 9, 64)
+    amax = xt.abs().amax(-1)
+    st = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    ref = (xt / st.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8).reshape(200, 576).numpy()
+    assert np.array_equal(codes, ref)
+    assert np.array_equal(scale, st.double().numpy())
+
+
+def test_layer_norm_matches_torch_layer_norm():
+    rng = np.random.default_rng(10)
+    y = rng.normal(0.3, 2.0, (7, 128))
+    w, b = rng.uniform(0.5, 1.5, 128), rng.normal(0, 0.2, 128)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(y), (128,), torch.from_numpy(w), torch.from_numpy(b),
+                                         eps=1e-5).numpy()
+    assert np.allclose(O.layer_norm(y, w, b, 1e-5), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_index_key_with_identity_projection_is_layer_norm_then_rope():
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 1, 128)
+    eye = np.eye(128)
+    one, zero = np.ones(128), np.zeros(128)
+    k0 = O.index_key(x, eye, one, zero, 1e-6, pos=0, inv_freq=workloads.inv_freq_table().numpy())
+    k_norope = O.index_key(x, eye, one, zero, 1e-6, pos=0)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (128,), eps=1e-6).numpy()
+    assert np.allclose(k0, ref, atol=1e-12) and np.allclose(k_norope, ref, atol=1e-12)   # pos 0: no turn
+    # closed forms of a unit LayerNorm: zero mean, mean square var / (var + eps)
+    var = x.var()
+    assert abs(k_norope.mean()) < 1e-12 and np.isclose((k_norope ** 2).mean(), var / (var + 1e-6), rtol=1e-12)
+
+
+def test_index_key_projection_orientation_and_rope_pairs():
+    rng = np.random.default_rng(12)
+    D = 96
+    x = rng.normal(0, 1, D)
+    wk = rng.normal(0, 1, (128, D))
+    w, b = rng.uniform(0.5, 1.5, 128), rng.normal(0, 0.1, 128)
+    invf = workloads.inv_freq_table().numpy().astype(np.float64)
+    pos = 777
+    k = O.index_key(x, wk, w, b, 1e-6, pos, invf)
+    # brute force: output o is the dot of wk's row o with x (wk is [out][in])
+    y = np.array([sum(wk[o, i] * x[i] for i in range(D)) for o in range(128)])
+    base = O.layer_norm(y, w, b, 1e-6)
+    assert np.allclose(k[64:], base[64:], rtol=1e-12, atol=1e-12)          # dims past 64 unrotated
+    for j in (0, 5, 31):
+        a = pos * invf[j]
+        c, s = math.cos(a), math.sin(a)
+        assert np.isclose(k[2 * j], base[2 * j] * c - base[2 * j + 1] * s, atol=1e-12)
+        assert np.isclose(k[2 * j + 1], base[2 * j] * s + base[2 * j + 1] * c, atol=1e-12)
+    # a transposed projection gives a different key
+    wk_sq = rng.normal(0, 1, (128, 128))
+    xs = rng.normal(0, 1, 128)
+    assert not np.allclose(O.index_key(xs, wk_sq, w, b, 1e-6, 0), O.index_key(xs, wk_sq.T, w, b, 1e-6, 0))
+
+
+def test_latent_row_rotates_only_the_rotary_slice():
+    rng = np.random.default_rng(13)
+    kv = rng.normal(0, 1, 576)
+    invf = workloads.inv_freq_table().numpy().astype(np.float64)
+    r = O.latent_row(kv, 1234, invf)
+    assert np.array_equal(r[:512], kv[:512])
+    pe, rpe = kv[512:].reshape(32, 2), r[512:].reshape(32, 2)
+    assert np.allclose(np.linalg.norm(pe, axis=1), np.linalg.norm(rpe, axis=1), rtol=1e-12)
+    a = 1234 * invf[3]
+    assert np.isclose(r[512 + 6], kv[512 + 6] * math.cos(a) - kv[512 + 7] * math.sin(a), atol=1e-12)
+    assert np.array_equal(O.latent_row(kv, 1234, None), kv)                  # NoPE layer: as given

@@ -232,6 +232,82 @@ def config4(device="cpu", seed=4, batch=4, ctx=524288):
                          max_ctx=ctx, num_heads=4, device=device)
 
 
+HIDDEN = 6144   # Mistral Large 4 hidden size (the indexer key projection's input width)
+
+
+@dataclasses.dataclass
+class InsertBatch:
+    """Inputs of the cache writers for T new tokens.
+
+    Layouts (row-major, contiguous):
+      x          [T][hidden] bf16      hidden states entering the indexer key projection
+      wk         [128][hidden] bf16    that projection's weight (output dim first)
+      ln_w, ln_b [128] f32             the key LayerNorm's weight and bias
+      eps        float                 LayerNorm epsilon
+      kv         [T][576] bf16         latent rows (512 latent + 64 rotary dims) to be cached
+      pos        [T] int32             0-based position of each token in its sequence
+      seq        [T] int32             its sequence
+      slot       [T] int64             destination cache row: seq * max_ctx + pos, -1 = skip
+      inv_freq   [32] f32 or None      rotary frequencies (None on NoPE layers)
+    """
+    name: str
+    x: torch.Tensor
+    wk: torch.Tensor
+    ln_w: torch.Tensor
+    ln_b: torch.Tensor
+    eps: float
+    kv: torch.Tensor
+    pos: torch.Tensor
+    seq: torch.Tensor
+    slot: torch.Tensor
+    inv_freq: Optional[torch.Tensor]
+    num_seqs: int
+    max_ctx: int
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.pos.shape[0])
+
+
+def make_insert_batch(*, name: str, seed: int, positions, seqs, num_seqs: int, max_ctx: int,
+                      hidden: int = HIDDEN, rope: bool = True, skip=(), device="cpu") -> InsertBatch:
+    """Draw the cache writers' inputs: x ~ N(0, 1), wk ~ N(0, 1/hidden) (so each projected
+    output is about unit-variance), LayerNorm weight U(0.9, 1.1) and bias N(0, 0.1^2),
+    eps 1e-6, latent rows N(0, 1/576).  Tokens listed in `skip` get slot -1 (padding)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed))
+    pos = torch.as_tensor(positions, dtype=torch.int32).flatten()
+    seq = torch.as_tensor(seqs, dtype=torch.int32).flatten()
+    assert pos.shape == seq.shape and int(pos.max()) < max_ctx and int(seq.max()) < num_seqs
+    T = int(pos.shape[0])
+    x = _normal(gen, (T, hidden), dev).to(torch.bfloat16)
+    wk = _normal(gen, (INDEX_HEAD_DIM, hidden), dev, 1.0 / math.sqrt(hidden)).to(torch.bfloat16)
+    ln_w = _uniform(gen, (INDEX_HEAD_DIM,), dev, 0.9, 1.1)
+    ln_b = _normal(gen, (INDEX_HEAD_DIM,), dev, 0.1)
+    kv = _normal(gen, (T, KV_ROW), dev, 1.0 / math.sqrt(KV_ROW)).to(torch.bfloat16)
+    slot = seq.to(torch.int64) * max_ctx + pos.to(torch.int64)
+    for t in skip:
+        slot[t] = -1
+    return InsertBatch(name=name, x=x, wk=wk, ln_w=ln_w, ln_b=ln_b, eps=1e-6, kv=kv, pos=pos.to(dev),
+                       seq=seq.to(dev), slot=slot.to(dev), inv_freq=inv_freq_table().to(dev) if rope else None,
+                       num_seqs=num_seqs, max_ctx=max_ctx)
+
+
+def insert_decode(device="cpu", seed=20, batch=16, ctx=131072, rope=True):
+    """One decode step's new tokens: the last position of each of `batch` sequences."""
+    return make_insert_batch(name=f"insert_decode_b{batch}_ctx{ctx}", seed=seed, positions=[ctx - 1] * batch,
+                             seqs=list(range(batch)), num_seqs=batch, max_ctx=ctx, rope=rope, device=device)
+
+
+def insert_prefill(device="cpu", seed=21, prefix=61440, chunk=4096, rope=True):
+    """A prefill chunk's new tokens: positions prefix .. prefix + chunk - 1 of one sequence."""
+    total = prefix + chunk
+    return make_insert_batch(name=f"insert_prefill_{chunk}_on_{prefix}", seed=seed,
+                             positions=list(range(prefix, total)), seqs=[0] * chunk, num_seqs=1,
+                             max_ctx=total, rope=rope, device=device)
+
+
 def slice_query(wl: Workload, t: int) -> Workload:
     """Query t and its own sequence only (B = 1), copied to the CPU: what the oracle needs to
     recompute one query of a large workload."""
