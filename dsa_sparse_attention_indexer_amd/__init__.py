@@ -43,6 +43,11 @@ class MlaDesc(ctypes.Structure):
                 ("num_splits", ctypes.c_int32)]
 
 
+class IndexKDesc(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("ld_x", ctypes.c_int64),
+                ("rope_dim", ctypes.c_int32), ("eps", ctypes.c_float), ("num_slots", ctypes.c_int64)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python dsa_sparse_attention_indexer_amd/build.py` "
@@ -66,6 +71,9 @@ def _load():
         "dsa_sparse_mla_workspace_size": (SZ, [ctypes.POINTER(MlaDesc)]),
         "dsa_sparse_mla_decode": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P]),
         "dsa_sparse_mla_prefill": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dsa_index_k_insert_workspace_size": (SZ, [ctypes.POINTER(IndexKDesc)]),
+        "dsa_index_k_insert": (I32, [ctypes.POINTER(IndexKDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dsa_latent_insert": (I32, [I32, I32, P, I64, P, P, P, I64, P, P, P]),
     }
     for name, (res, args) in sig.items():
         if not hasattr(lib, name):
@@ -82,7 +90,8 @@ _lib = _load()
 EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_indexer_topk",
             "dsa_indexer_scores_hist", "dsa_topk_hist",
             "dsa_topk_workspace_size", "dsa_topk", "dsa_block_select_workspace_size", "dsa_block_select", "dsa_sparse_mla_workspace_size",
-            "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill"]
+            "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_index_k_insert_workspace_size",
+            "dsa_index_k_insert", "dsa_latent_insert"]
 
 
 def lib():
@@ -352,3 +361,65 @@ def dsa_sparse_mla_prefill(q, kv, kv_scale, q_seq, idx, length, out, lse=None, s
     """Sparse MLA for chunked prefill (one workgroup per query)."""
     return _mla(_lib.dsa_sparse_mla_prefill, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale, 0,
                 ws, stream)
+
+
+# ------------------------------------------------------------------------------------------------
+# 0. cache writers
+# ------------------------------------------------------------------------------------------------
+
+def index_k_desc(x, hidden, rope_dim, eps, num_slots) -> IndexKDesc:
+    return IndexKDesc(x.shape[0], int(hidden), x.stride(0), int(rope_dim), float(eps), int(num_slots))
+
+
+def dsa_index_k_insert_workspace_size(desc: IndexKDesc) -> int:
+    return int(_lib.dsa_index_k_insert_workspace_size(ctypes.byref(desc)))
+
+
+def dsa_index_k_insert(x, wk, ln_w, ln_b, pos, slot, k_cache, k_scale, inv_freq=None, eps=1e-6, ws=None,
+                       stream=None):
+    """Indexer keys of x's tokens (LayerNorm of the key projection, RoPE when inv_freq is given,
+    FP8 with one scale per token) written into k_cache / k_scale at rows `slot` (-1 = skip).
+
+    x [T][hidden] bf16 (rows may be strided), wk [128][hidden] bf16, ln_w / ln_b [128] f32,
+    pos [T] i32, slot [T] i64, k_cache [..., 128] uint8 / float8_e4m3fn, k_scale [...] f32."""
+    T, hidden = x.shape
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 GPU tensor with unit column stride")
+    _dev("wk", wk, torch.bfloat16, (128, hidden))
+    _dev("ln_w", ln_w, torch.float32, (128,))
+    _dev("ln_b", ln_b, torch.float32, (128,))
+    _dev("pos", pos, torch.int32, (T,))
+    _dev("slot", slot, torch.int64, (T,))
+    _dev("inv_freq", inv_freq, torch.float32, (32,))
+    _dev("k_cache", k_cache, (torch.uint8, torch.float8_e4m3fn))
+    _dev("k_scale", k_scale, torch.float32)
+    if k_cache.shape[-1] != 128 or k_cache.numel() // 128 != k_scale.numel():
+        raise ValueError("k_cache must hold 128-byte rows, one k_scale per row")
+    d = index_k_desc(x, hidden, 64 if inv_freq is not None else 0, eps, k_scale.numel())
+    need = dsa_index_k_insert_workspace_size(d)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _dev("ws", ws, torch.uint8)
+    _check(_lib.dsa_index_k_insert(ctypes.byref(d), _ptr(x), _ptr(wk), _ptr(ln_w), _ptr(ln_b), _ptr(pos),
+                                   _ptr(inv_freq), _ptr(slot), _ptr(k_cache), _ptr(k_scale), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream)))
+    return k_cache, k_scale
+
+
+def dsa_latent_insert(kv, pos, slot, kv_cache, kv_scale, inv_freq=None, stream=None):
+    """Latent rows kv [T][576] bf16 (rotary slice rotated when inv_freq is given) written as FP8
+    with one scale per 64 elements into kv_cache [..., 576] / kv_scale [..., 9] at rows `slot`."""
+    T = kv.shape[0]
+    if kv.dtype != torch.bfloat16 or not kv.is_cuda or kv.stride(1) != 1 or kv.shape[1] != 576:
+        raise ValueError("kv must be a [T][576] bf16 GPU tensor with unit column stride")
+    _dev("pos", pos, torch.int32, (T,))
+    _dev("slot", slot, torch.int64, (T,))
+    _dev("inv_freq", inv_freq, torch.float32, (32,))
+    _dev("kv_cache", kv_cache, (torch.uint8, torch.float8_e4m3fn))
+    _dev("kv_scale", kv_scale, torch.float32)
+    if kv_cache.shape[-1] != 576 or kv_cache.numel() // 576 * 9 != kv_scale.numel():
+        raise ValueError("kv_cache must hold 576-byte rows, nine kv_scale entries per row")
+    _check(_lib.dsa_latent_insert(T, 64 if inv_freq is not None else 0, _ptr(kv), kv.stride(0), _ptr(pos),
+                                  _ptr(inv_freq), _ptr(slot), kv_cache.numel() // 576, _ptr(kv_cache),
+                                  _ptr(kv_scale), _stream(stream)))
+    return kv_cache, kv_scale

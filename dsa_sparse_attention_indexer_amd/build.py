@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "block_select.hip", "sparse_mla.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "block_select.hip", "sparse_mla.hip", "cache_insert.hip"]
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 # Packed fp32 instructions are kept out of generated code (plain scalar fp32 only).
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -339,3 +339,78 @@ dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* d, const void* q, cons
 }
 
 }  // extern "C"
+
+// ---- cache writers --------------------------------------------------------------------------
+
+namespace {
+
+size_t kinsert_ws_bytes(const dsa_index_k_desc_t* d) {
+  if (!d || d->num_tokens <= 0 || d->hidden < 32 || d->hidden % 32 != 0) return 0;
+  int s, per;
+  dsa::kinsert_geometry(d->num_tokens, d->hidden, &s, &per);
+  return (size_t)s * d->num_tokens * 128 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_index_k_insert_workspace_size(const dsa_index_k_desc_t* d) { return kinsert_ws_bytes(d); }
+
+dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* d, const void* x, const void* wk, const float* ln_w,
+                                const float* ln_b, const int32_t* pos, const float* inv_freq, const int64_t* slot,
+                                uint8_t* k_cache, float* k_scale, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsa_index_k_insert";
+  Checker ck;
+  if (!d) { ck.need(false, "desc is NULL"); return ck.finish(fn); }
+  ck.need(d->num_tokens >= 0 && d->num_tokens <= (1 << 24), "num_tokens must be in [0, 2^24]");
+  ck.support(d->hidden >= 32 && d->hidden <= (1 << 20) && d->hidden % 32 == 0,
+             "hidden must be a multiple of 32 in [32, 2^20]");
+  ck.need(d->ld_x >= d->hidden && d->ld_x % 8 == 0, "ld_x must be >= hidden and a multiple of 8");
+  ck.support(d->rope_dim == 0 || d->rope_dim == 64, "rope_dim must be 0 or 64");
+  ck.need(d->eps >= 0.f, "eps must be >= 0");
+  ck.need(d->num_slots >= 0, "num_slots must be >= 0");
+  if (d->num_tokens > 0) {
+    ck.need(x && wk && ln_w && pos && slot && k_cache && k_scale, "x, wk, ln_w, pos, slot, k_cache and k_scale must be non-NULL");
+    ck.need(d->rope_dim == 0 || inv_freq != nullptr, "inv_freq is required when rope_dim is 64");
+    ck.need(aligned(x, 16) && aligned(wk, 16), "x and wk must be 16-byte aligned");
+    ck.need(aligned(k_cache, 2), "k_cache must be 2-byte aligned");
+    const size_t need = kinsert_ws_bytes(d);
+    ck.need(ws != nullptr && ws_bytes >= need && aligned(ws, 16),
+            "workspace missing, misaligned or smaller than dsa_index_k_insert_workspace_size()");
+  }
+  dsa_status_t st = ck.finish(fn);
+  if (st != DSA_OK || d->num_tokens == 0) return st;
+  dsa::KInsertLaunch a{};
+  a.T = d->num_tokens; a.D = d->hidden; a.rope_dim = d->rope_dim;
+  dsa::kinsert_geometry(a.T, a.D, &a.splits, &a.steps_per_split);
+  a.ld_x = d->ld_x; a.nslots = d->num_slots; a.eps = d->eps;
+  a.x = static_cast<const uint16_t*>(x); a.wk = static_cast<const uint16_t*>(wk);
+  a.ln_w = ln_w; a.ln_b = ln_b; a.pos = pos; a.inv_freq = inv_freq; a.slot = slot;
+  a.k_cache = k_cache; a.k_scale = k_scale; a.ws = static_cast<float*>(ws);
+  return hip_status(fn, dsa::launch_index_k_insert(a, (hipStream_t)stream));
+}
+
+dsa_status_t dsa_latent_insert(int32_t num_tokens, int32_t rope_dim, const void* kv, int64_t ld_kv,
+                               const int32_t* pos, const float* inv_freq, const int64_t* slot, int64_t num_slots,
+                               uint8_t* kv_cache, float* kv_scale, void* stream) {
+  const char* fn = "dsa_latent_insert";
+  Checker ck;
+  ck.need(num_tokens >= 0 && num_tokens <= (1 << 24), "num_tokens must be in [0, 2^24]");
+  ck.support(rope_dim == 0 || rope_dim == 64, "rope_dim must be 0 or 64");
+  ck.need(ld_kv >= 576, "ld_kv must be >= 576");
+  ck.need(num_slots >= 0, "num_slots must be >= 0");
+  if (num_tokens > 0) {
+    ck.need(kv && pos && slot && kv_cache && kv_scale, "kv, pos, slot, kv_cache and kv_scale must be non-NULL");
+    ck.need(rope_dim == 0 || inv_freq != nullptr, "inv_freq is required when rope_dim is 64");
+  }
+  dsa_status_t st = ck.finish(fn);
+  if (st != DSA_OK || num_tokens == 0) return st;
+  dsa::LatentInsertLaunch a{};
+  a.T = num_tokens; a.rope_dim = rope_dim; a.ld_kv = ld_kv; a.nslots = num_slots;
+  a.kv = static_cast<const uint16_t*>(kv); a.pos = pos; a.inv_freq = inv_freq; a.slot = slot;
+  a.kv_cache = kv_cache; a.kv_scale = kv_scale;
+  return hip_status(fn, dsa::launch_latent_insert(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

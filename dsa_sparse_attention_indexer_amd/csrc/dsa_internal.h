@@ -67,6 +67,33 @@ struct MlaLaunch {
   float* ws;  // split partials: [T][H][splits][kv_lora] O, then [T][H][splits] m and l
 };
 
+struct KInsertLaunch {
+  int T, D, rope_dim, splits, steps_per_split;   // splits of the hidden dim, 32-wide steps each
+  int64_t ld_x, nslots;
+  float eps;
+  const uint16_t* x;      // [T][ld_x] bf16
+  const uint16_t* wk;     // [128][D] bf16
+  const float* ln_w;
+  const float* ln_b;      // NULL = no bias
+  const int32_t* pos;
+  const float* inv_freq;
+  const int64_t* slot;
+  uint8_t* k_cache;       // [nslots][128] E4M3FN
+  float* k_scale;         // [nslots]
+  float* ws;              // [splits][T][128] partial projections
+};
+
+struct LatentInsertLaunch {
+  int T, rope_dim;
+  int64_t ld_kv, nslots;
+  const uint16_t* kv;     // [T][ld_kv] bf16, 576 used
+  const int32_t* pos;
+  const float* inv_freq;
+  const int64_t* slot;
+  uint8_t* kv_cache;      // [nslots][576] E4M3FN
+  float* kv_scale;        // [nslots][9]
+};
+
 // ---- sizes shared between validation and the kernels ----------------------------------------
 
 constexpr int64_t kTopkMaxCols = int64_t(1) << 22;   // columns a top-k row may have
@@ -75,6 +102,7 @@ size_t topk_ws_bytes(int T);
 size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype);
 bool indexer_grouped(int T, dsa_dtype_t k_dtype);   // many-query path: no fused first top-k digit
 size_t block_select_ws_bytes(int T, int64_t ld, int block);
+void kinsert_geometry(int T, int D, int* splits, int* steps_per_split);   // hidden-dim split
 
 // ---- launchers (return the HIP status of the last launch) -----------------------------------
 
@@ -83,6 +111,8 @@ hipError_t launch_topk(const TopkLaunch& a, bool hist_given, hipStream_t s);
 hipError_t launch_topk_hist(const TopkLaunch& a, hipStream_t s);   // the first-digit histogram only
 hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s);
+hipError_t launch_index_k_insert(const KInsertLaunch& a, hipStream_t s);
+hipError_t launch_latent_insert(const LatentInsertLaunch& a, hipStream_t s);
 
 }  // namespace dsa
 
@@ -99,6 +129,20 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Sine and cosine of the RoPE angle p * inv_freq.  The product is exact in float64 (24-bit times
+// 26-bit); it is reduced to [-pi, pi] in float64 with a two-term 2*pi (error far below float32
+// resolution up to p = 2^26), and the sine and cosine of the reduced angle are taken in float32
+// (about one ulp).
+__device__ __forceinline__ void rope_sincos(int p, float inv_freq, float* sn, float* cs) {
+  constexpr double kInv2Pi = 0.15915494309189535;
+  constexpr double k2PiHi = 6.283185307179586;
+  constexpr double k2PiLo = 2.4492935982947064e-16;
+  const double ang = (double)p * (double)inv_freq;
+  const double k = rint(ang * kInv2Pi);
+  const double r = fma(-k, k2PiLo, fma(-k, k2PiHi, ang));
+  sincosf((float)r, sn, cs);
+}
 
 }  // namespace dsa
 #endif

@@ -95,17 +95,8 @@ __device__ void prep_compute(PrepSmem& sm, const PrepIn& in, const IndexerLaunch
   const int h = tid >> 3, part = tid & 7;
   const int npairs = a.rope_dim / 2;
   if (tid < npairs) {
-    // p * inv_freq[j] is exact in float64 (24-bit times 26-bit); it is reduced to [-pi, pi] in
-    // float64 with a two-term 2*pi (error far below float32 resolution up to p = 2^26), and the
-    // sine and cosine of the reduced angle are taken in float32 (about one ulp).
-    constexpr double kInv2Pi = 0.15915494309189535;
-    constexpr double k2PiHi = 6.283185307179586;
-    constexpr double k2PiLo = 2.4492935982947064e-16;
-    const double ang = (double)p * (double)in.invf;
-    const double k = rint(ang * kInv2Pi);
-    const double r = fma(-k, k2PiLo, fma(-k, k2PiHi, ang));
     float sn, cs;
-    sincosf((float)r, &sn, &cs);
+    rope_sincos(p, in.invf, &sn, &cs);
     sm.cs[tid] = cs;
     sm.sn[tid] = sn;
   }

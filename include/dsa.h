@@ -11,6 +11,9 @@
  *      dsa_block_select     block-sparse alternative: top-16 128-token blocks, recent block kept
  *   3. dsa_sparse_mla_decode / dsa_sparse_mla_prefill
  *                           exact absorbed-MLA attention over the selected keys only
+ *   0. dsa_index_k_insert / dsa_latent_insert
+ *                           the writers that put each new token's indexer key and latent row
+ *                           into the FP8 caches that stages 1 and 3 read
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -240,6 +243,69 @@ dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* desc, const void* q, c
                                     const float* kv_scale, const int32_t* q_seq, const int32_t* idx,
                                     const int32_t* len, float* out, float* lse,
                                     void* ws, size_t ws_bytes, void* stream);
+
+/* ============================================================================================
+ * 0. Cache writers
+ * --------------------------------------------------------------------------------------------
+ * Indexer key ("mistral-large4.md", "What differs from GLM-5.2", bullet "The indexer";
+ * "Day 0 support for Mistral Large 4 on vLLM", "ROCm implementation details", "DSA indexer on
+ * AITER": the key is quantised to FP8 with one scale per token and written straight into the
+ * index cache, in the layout its readers use).  For token t with hidden state x[t]:
+ *
+ *   y     = wk . x[t]                                  (128 outputs; wk is [128][hidden])
+ *   k     = (y - mean(y)) / sqrt(var(y) + eps) * ln_w + ln_b     (var: mean squared deviation)
+ *   k     = RoPE_p(k) on RoPE layers: pairs (2j, 2j+1), j < 32, rotated by p * inv_freq[j],
+ *           p = pos[t]
+ *   scale = max|k| / 448 (1 if k = 0);  code_i = E4M3FN(k_i / scale), round to nearest even,
+ *           saturated to +-448
+ *   k_cache[slot[t]][0..128) = codes, k_scale[slot[t]] = scale
+ *
+ * Arguments (device pointers unless noted)
+ *   desc     host descriptor below
+ *   x        [num_tokens][ld_x] BF16, 16-byte aligned     hidden states
+ *   wk       [128][hidden] BF16, 16-byte aligned          key projection weight (output dim first)
+ *   ln_w     [128] f32;  ln_b [128] f32 or NULL (no bias)
+ *   pos      [num_tokens] i32;  inv_freq [32] f32 (RoPE layers; ignored when rope_dim = 0)
+ *   slot     [num_tokens] i64  destination row; in the readers' layout seq * max_ctx + position.
+ *            A negative slot (padding token) or one >= num_slots is skipped.
+ *   k_cache  [num_slots][128] E4M3FN bytes;  k_scale [num_slots] f32 (the index cache and its
+ *            per-token scales as dsa_indexer_scores reads them)
+ *   ws       workspace of dsa_index_k_insert_workspace_size(desc) bytes, 16-byte aligned
+ *            (partial projections; its contents need not be initialised)
+ * Supported: hidden a multiple of 32; rope_dim 0 or 64.  Rows whose slot is not written keep
+ * their contents.  Two tokens with the same slot race (either row may remain).
+ * ==========================================================================================*/
+typedef struct {
+  int32_t num_tokens;       /* T                                                             */
+  int32_t hidden;           /* width of x and wk rows (6144 on Mistral Large 4)              */
+  int64_t ld_x;             /* row stride of x in elements, >= hidden, a multiple of 8       */
+  int32_t rope_dim;         /* 64 (RoPE layer) or 0 (NoPE layer)                             */
+  float eps;                /* LayerNorm epsilon                                             */
+  int64_t num_slots;        /* rows of k_cache                                               */
+} dsa_index_k_desc_t;
+
+size_t dsa_index_k_insert_workspace_size(const dsa_index_k_desc_t* desc);
+dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* desc, const void* x, const void* wk,
+                                const float* ln_w, const float* ln_b, const int32_t* pos,
+                                const float* inv_freq, const int64_t* slot, uint8_t* k_cache,
+                                float* k_scale, void* ws, size_t ws_bytes, void* stream);
+
+/* Latent row ("Day 0 support for Mistral Large 4 on vLLM", "Model architecture": 512 latent
+ * dims and 64 rotary dims per token; "ROCm implementation details", "FP8 latent cache": the row
+ * is stored as E4M3 codes).  For token t, row r = kv[t][0..576):
+ *   r[512..576) rotated at p = pos[t] on RoPE layers (pairs (512+2j, 512+2j+1) by p * inv_freq[j]);
+ *   on NoPE layers (rope_dim = 0) the row is stored as given (the readers ignore that slice);
+ *   per 64-element group g: scale_g = max|r_g| / 448 (1 if 0), codes as for the key;
+ *   kv_cache[slot[t]][0..576) = codes, kv_scale[slot[t]][g] = scale_g.
+ * The latent part arrives final (any normalisation of it is applied upstream).
+ *   kv       [num_tokens][ld_kv] BF16 (ld_kv >= 576);  pos, inv_freq, slot as above
+ *   kv_cache [num_slots][576] E4M3FN bytes;  kv_scale [num_slots][9] f32 (the latent cache as
+ *            dsa_sparse_mla_decode / _prefill read it, with kv_scale_block = 64)
+ * No workspace.  Skipped slots and races as above.
+ * ==========================================================================================*/
+dsa_status_t dsa_latent_insert(int32_t num_tokens, int32_t rope_dim, const void* kv, int64_t ld_kv,
+                               const int32_t* pos, const float* inv_freq, const int64_t* slot,
+                               int64_t num_slots, uint8_t* kv_cache, float* kv_scale, void* stream);
 
 #ifdef __cplusplus
 }

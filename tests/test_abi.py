@@ -99,3 +99,24 @@ def test_zero_queries_is_a_no_op(dsa):
     L = dsa.lib()
     assert L.dsa_topk(None, 8, None, 0, 2048, None, None, None, 0, None) == dsa.DSA_OK
     assert L.dsa_last_error().decode() == ""
+
+
+def test_cache_writers_validate_arguments(dsa):
+    d = dsa.IndexKDesc(16, 6144, 6144, 64, 1e-6, 1000)
+    assert dsa.dsa_index_k_insert_workspace_size(d) > 0
+    # geometry: T = 16 is one token tile, so the hidden dim is split into 96 slices of 64
+    assert dsa.dsa_index_k_insert_workspace_size(d) == 96 * 16 * 128 * 4
+    assert dsa.dsa_index_k_insert_workspace_size(dsa.IndexKDesc(4096, 6144, 6144, 64, 1e-6, 1)) == 4 * 4096 * 128 * 4
+    bad = dsa.IndexKDesc(16, 100, 96, 32, -1.0, 1000)
+    st = dsa.lib().dsa_index_k_insert(ctypes.byref(bad), *([None] * 10), 0, None)
+    msg = dsa.lib().dsa_last_error().decode()
+    assert st in (dsa.DSA_ERR_ARG, dsa.DSA_ERR_UNSUPPORTED)
+    for frag in ("hidden must be a multiple of 32", "ld_x must be", "rope_dim must be 0 or 64", "eps must be",
+                 "must be non-NULL", "workspace"):
+        assert frag in msg, (frag, msg)
+    st = dsa.lib().dsa_latent_insert(4, 16, None, 100, None, None, None, 10, None, None, None)
+    msg = dsa.lib().dsa_last_error().decode()
+    assert st == dsa.DSA_ERR_ARG and "ld_kv must be >= 576" in msg and "rope_dim must be 0 or 64" in msg
+    zero = dsa.IndexKDesc(0, 6144, 6144, 64, 1e-6, 0)
+    assert dsa.lib().dsa_index_k_insert(ctypes.byref(zero), *([None] * 10), 0, None) == dsa.DSA_OK
+    assert dsa.lib().dsa_latent_insert(0, 64, None, 576, None, None, None, 0, None, None, None) == dsa.DSA_OK
