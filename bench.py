@@ -89,6 +89,37 @@ def counter_traffic():
         return None
 
 
+def cache_writer_rates(dsa, timed, dev):
+    import torch
+    import workloads
+    """Per-call time and algorithmic bandwidth of the cache writers for one decode step's 16 new
+    tokens and one 4096-token prefill chunk.  Keys read: x (2 B x hidden per token) and the
+    key projection's weight (2 B x 128 x hidden, once per call); written: 132 B per token.  Latent
+    rows: 1152 B read, 612 B written per token.  The destination rows are numbered densely (the
+    writers' cost does not depend on where the rows lie)."""
+    out = {}
+    for name, b in (("decode_b16", workloads.insert_decode(device=dev)),
+                    ("prefill_4096", workloads.insert_prefill(device=dev))):
+        T, D = b.x.shape
+        slot = torch.arange(T, dtype=torch.int64, device=dev)
+        kc = torch.empty((T, 128), dtype=torch.uint8, device=dev)
+        ks = torch.empty((T,), dtype=torch.float32, device=dev)
+        lc = torch.empty((T, 576), dtype=torch.uint8, device=dev)
+        ls = torch.empty((T, 9), dtype=torch.float32, device=dev)
+        d = dsa.index_k_desc(b.x, D, 64, b.eps, T)
+        ws = torch.empty(dsa.dsa_index_k_insert_workspace_size(d), dtype=torch.uint8, device=dev)
+        tk = timed(lambda: dsa.dsa_index_k_insert(b.x, b.wk, b.ln_w, b.ln_b, b.pos, slot, kc, ks,
+                                                  inv_freq=b.inv_freq, eps=b.eps, ws=ws))
+        tl = timed(lambda: dsa.dsa_latent_insert(b.kv, b.pos, slot, lc, ls, inv_freq=b.inv_freq))
+        kbytes = T * 2 * D + 2 * 128 * D + T * 132
+        lbytes = T * (2 * 576 + 576 + 36)
+        out[f"index_k_insert_{name}"] = {"us_per_call": tk * 1e6, "gb_per_s": kbytes / tk / 1e9,
+                                          "bytes_per_call": kbytes}
+        out[f"latent_insert_{name}"] = {"us_per_call": tl * 1e6, "gb_per_s": lbytes / tl / 1e9,
+                                         "bytes_per_call": lbytes}
+    return out
+
+
 def cpu_baseline(wl, seconds):
     """The float64 oracle on whole queries of the same workload, on this host's cores."""
     import workloads
@@ -131,6 +162,7 @@ def main():
 
     import torch
     import workloads
+    import dsa_sparse_attention_indexer_amd as dsa
     from dsa_sparse_attention_indexer_amd import pipeline
 
     dev = torch.device("cuda:0")
@@ -247,6 +279,8 @@ def main():
         variants["decode_b64_ctx16k_32k"] = {"us_per_step": t1 * 1e6, "tok_per_s": w1[0].num_q / t1}
         del w1, b1
         log("variants: " + ", ".join(f"{k} {v['us_per_step']:.1f} us" for k, v in variants.items()))
+        variants["cache_writers"] = cache_writer_rates(dsa, timed, dev)
+        log("cache writers: " + ", ".join(f"{k} {v['us_per_call']:.1f} us" for k, v in variants["cache_writers"].items()))
 
     cpu = None
     if not args.no_cpu_baseline:
