@@ -346,9 +346,7 @@ namespace {
 
 size_t kinsert_ws_bytes(const dsa_index_k_desc_t* d) {
   if (!d || d->num_tokens <= 0 || d->hidden < 32 || d->hidden % 32 != 0) return 0;
-  int s, per;
-  dsa::kinsert_geometry(d->num_tokens, d->hidden, &s, &per);
-  return (size_t)s * d->num_tokens * 128 * sizeof(float);
+  return (size_t)dsa::kinsert_splits(d->num_tokens, d->hidden) * d->num_tokens * 128 * sizeof(float);
 }
 
 }  // namespace
@@ -383,7 +381,7 @@ dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* d, const void* x, cons
   if (st != DSA_OK || d->num_tokens == 0) return st;
   dsa::KInsertLaunch a{};
   a.T = d->num_tokens; a.D = d->hidden; a.rope_dim = d->rope_dim;
-  dsa::kinsert_geometry(a.T, a.D, &a.splits, &a.steps_per_split);
+  a.splits = dsa::kinsert_splits(a.T, a.D);
   a.ld_x = d->ld_x; a.nslots = d->num_slots; a.eps = d->eps;
   a.x = static_cast<const uint16_t*>(x); a.wk = static_cast<const uint16_t*>(wk);
   a.ln_w = ln_w; a.ln_b = ln_b; a.pos = pos; a.inv_freq = inv_freq; a.slot = slot;

@@ -9,10 +9,13 @@
 //   k_kproj    partial projections y = x . wk^T over a slice of the hidden dim for a tile of 64
 //              tokens.  Wave w owns outputs 32w..32w+31 (two 16-row M blocks of
 //              v_mfma_f32_16x16x32_bf16, weight rows as M) against the tile's four 16-token N
-//              blocks; every operand is 8 consecutive bf16 of one row, loaded straight from global
-//              memory (16 bytes per lane).  The hidden dim is cut into slices so that a decode
-//              step's handful of tokens still spreads the weight's read over many CUs; the fp32
-//              partials go to the workspace, [slice][token][128].
+//              blocks.  Both operands pass through LDS in 256-dim blocks loaded one block ahead
+//              with whole 512-byte row segments per 32 threads (operands read straight from global
+//              memory as 16-byte pieces of 64 rows, one MFMA step per load, reached only ≈1.2 TB/s
+//              on the token rows).  The hidden dim is cut into slices that interleave its 256-dim
+//              blocks, so that a decode step's handful of tokens still spreads the weight's read
+//              over many CUs and the slices of one tile read neighbouring pieces of the same rows;
+//              the fp32 partials go to the workspace, [slice][token][128].
 //   k_kfinish  one workgroup per token: its four waves sum interleaved slices, then one wave, lane
 //              j holding dims 2j and 2j+1 (exactly one RoPE pair), applies LayerNorm with the
 //              population variance, the rotation of pairs j < rope_dim/2 by p * inv_freq[j],
@@ -34,9 +37,11 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKeyDim = 128;
 constexpr int kTileTok = 64;       // tokens per projection tile
+constexpr int kNB = kTileTok / 16;  // 16-token MFMA blocks per tile
 constexpr int kStep = 32;          // hidden dims per MFMA step
 constexpr int kProjThreads = 256;  // 4 waves x 32 outputs
 constexpr int kFinThreads = 256;   // key finish: one token per workgroup; latent: 4 tokens
@@ -62,58 +67,108 @@ __device__ __forceinline__ uint32_t fp8_pair(float v0, float v1, float scale) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
-__device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+// LDS tiles of one macro step: kMacro hidden dims of the tile's 64 token rows and of the 128
+// weight rows, rows padded by 16 bytes (consecutive rows start 4 banks apart).
+constexpr int kMacro = 256;
+constexpr int kRowPad = kMacro + 8;
+struct ProjSmem {
+  uint16_t x[kTileTok][kRowPad];
+  uint16_t w[kKeyDim][kRowPad];
+};
+constexpr int kXPieces = kTileTok * kMacro / 8 / kProjThreads;   // 16-byte pieces per thread
+constexpr int kWPieces = kKeyDim * kMacro / 8 / kProjThreads;
+
+// Global -> registers -> LDS, one macro step ahead: 32 consecutive threads read one row's
+// kMacro dims (512 contiguous bytes), so every load instruction covers whole row segments.
+// Token rows past the end read the last token's row; pieces past the slice read its last piece
+// again (in bounds; their steps are not computed), so no load is predicated.
+__device__ __forceinline__ void proj_load(const KInsertLaunch& a, int t0, int kc, int kend, u32x4 (&xr)[kXPieces],
+                                          u32x4 (&wr)[kWPieces]) {
+#pragma unroll
+  for (int i = 0; i < kXPieces; ++i) {
+    const int pc = i * kProjThreads + (int)threadIdx.x;
+    const int row = pc >> 5, col = min(kc + (pc & 31) * 8, kend - 8);
+    xr[i] = *reinterpret_cast<const u32x4*>(a.x + (size_t)min(t0 + row, a.T - 1) * a.ld_x + col);
+  }
+#pragma unroll
+  for (int i = 0; i < kWPieces; ++i) {
+    const int pc = i * kProjThreads + (int)threadIdx.x;
+    const int row = pc >> 5, col = min(kc + (pc & 31) * 8, kend - 8);
+    wr[i] = *reinterpret_cast<const u32x4*>(a.wk + (size_t)row * a.D + col);
+  }
+}
+
+__device__ __forceinline__ void proj_store(ProjSmem& sm, const u32x4 (&xr)[kXPieces], const u32x4 (&wr)[kWPieces]) {
+#pragma unroll
+  for (int i = 0; i < kXPieces; ++i) {
+    const int pc = i * kProjThreads + (int)threadIdx.x;
+    *reinterpret_cast<u32x4*>(&sm.x[pc >> 5][(pc & 31) * 8]) = xr[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kWPieces; ++i) {
+    const int pc = i * kProjThreads + (int)threadIdx.x;
+    *reinterpret_cast<u32x4*>(&sm.w[pc >> 5][(pc & 31) * 8]) = wr[i];
+  }
 }
 
 __global__ void __launch_bounds__(kProjThreads) k_kproj(KInsertLaunch a) {
+  __shared__ __attribute__((aligned(16))) ProjSmem sm;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * kTileTok;
   const int split = blockIdx.y;
-  const int kbeg = split * a.steps_per_split * kStep;
-  const int kend = min(a.D, kbeg + a.steps_per_split * kStep);
   const int r = lane & 15, kg = (lane >> 4) * 8;   // operand row within a block, its 8 dims
-  // A operands: weight rows 32*wave + 16*mb + r; B operands: token rows t0 + 16*nb + r (tokens
-  // past the end read the last token's row and are not stored)
-  const uint16_t* wrow[2];
-  const uint16_t* xrow[4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) wrow[mb] = a.wk + (size_t)(32 * wave + 16 * mb + r) * a.D + kg;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) xrow[nb] = a.x + (size_t)min(t0 + 16 * nb + r, a.T - 1) * a.ld_x + kg;
-  float4v acc[2][4];
+  float4v acc[2][kNB];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = float4v{0.f, 0.f, 0.f, 0.f};
-  bf16x8 wa[2], xb[4];
-  if (kbeg < kend) {
+    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // this slice: the 256-dim blocks split, split + splits, ... (the slices of one tile read
+  // neighbouring blocks of the same rows at about the same time), walked from a starting block
+  // that depends on the tile, so that the tiles, which share the weight, do not all read the same
+  // weight block at the same time
+  const int nblk = (a.D + kMacro - 1) / kMacro;
+  const int n = (nblk - split + a.splits - 1) / a.splits;
+  const int rot = (int)(blockIdx.x % (unsigned)n);
+  auto kat = [&](int j) {
+    const int jj = j + rot;
+    return (split + (jj >= n ? jj - n : jj) * a.splits) * kMacro;
+  };
+  u32x4 xr[kXPieces], wr[kWPieces];
+  proj_load(a, t0, kat(0), min(a.D, kat(0) + kMacro), xr, wr);
+  proj_store(sm, xr, wr);
+  __syncthreads();
+  for (int j = 0; j < n; ++j) {
+    const int kc = kat(j);
+    const bool more = j + 1 < n;
+    if (more) {   // in flight during this block's products
+      const int kn = kat(j + 1);
+      proj_load(a, t0, kn, min(a.D, kn + kMacro), xr, wr);
+    }
+    const int nsteps = min(kMacro, a.D - kc) / kStep;
+    for (int u = 0; u < nsteps; ++u) {
+      bf16x8 wa[2], xb[kNB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) wa[mb] = load8(wrow[mb] + kbeg);
+      for (int mb = 0; mb < 2; ++mb)
+        wa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.w[32 * wave + 16 * mb + r][u * kStep + kg]));
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) xb[nb] = load8(xrow[nb] + kbeg);
-  }
-  for (int k = kbeg; k < kend; k += kStep) {
-    // the next step's operands are in flight while this step's products run
-    const int kn = k + kStep < kend ? k + kStep : k;
-    bf16x8 wn[2], xn[4];
+      for (int nb = 0; nb < kNB; ++nb)
+        xb[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.x[16 * nb + r][u * kStep + kg]));
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) wn[mb] = load8(wrow[mb] + kn);
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) xn[nb] = load8(xrow[nb] + kn);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[mb], xb[nb], acc[mb][nb], 0, 0, 0);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) wa[mb] = wn[mb];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) xb[nb] = xn[nb];
+        for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[mb], xb[nb], acc[mb][nb], 0, 0, 0);
+    }
+    if (more) {
+      __syncthreads();   // every wave is done reading this macro step's tiles
+      proj_store(sm, xr, wr);
+      __syncthreads();
+    }
   }
   // C block (mb, nb): lane holds outputs 32*wave + 16*mb + 4*(lane/16) + 0..3 of token
   // t0 + 16*nb + lane%16: one 16-byte store into [split][token][128]
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < kNB; ++nb) {
     const int t = t0 + 16 * nb + r;
     if (t < a.T) {
       float* dst = a.ws + ((size_t)split * a.T + t) * kKeyDim + 32 * wave + 4 * (lane >> 4);
@@ -207,15 +262,11 @@ __global__ void __launch_bounds__(kFinThreads) k_latent(LatentInsertLaunch a) {
 
 }  // namespace
 
-void kinsert_geometry(int T, int D, int* splits, int* steps_per_split) {
-  const int steps = D / kStep;
+int kinsert_splits(int T, int D) {
+  const int blocks = (D + kMacro - 1) / kMacro;
   const int tiles = (T + kTileTok - 1) / kTileTok;
-  int s = (256 + tiles - 1) / tiles;             // about one workgroup per CU
-  s = std::min(s, std::max(1, steps / 2));       // at least two steps per slice
-  s = std::max(s, 1);
-  const int per = (steps + s - 1) / s;
-  *steps_per_split = per;
-  *splits = (steps + per - 1) / per;             // no empty slice
+  const int s = (256 + tiles - 1) / tiles;       // about one workgroup per CU
+  return std::max(1, std::min(s, blocks));
 }
 
 hipError_t launch_index_k_insert(const KInsertLaunch& a, hipStream_t s) {

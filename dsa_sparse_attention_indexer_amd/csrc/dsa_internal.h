@@ -68,7 +68,7 @@ struct MlaLaunch {
 };
 
 struct KInsertLaunch {
-  int T, D, rope_dim, splits, steps_per_split;   // splits of the hidden dim, 32-wide steps each
+  int T, D, rope_dim, splits;   // split s sums the 256-dim blocks s, s + splits, ... of the hidden dim
   int64_t ld_x, nslots;
   float eps;
   const uint16_t* x;      // [T][ld_x] bf16
@@ -102,7 +102,7 @@ size_t topk_ws_bytes(int T);
 size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype);
 bool indexer_grouped(int T, dsa_dtype_t k_dtype);   // many-query path: no fused first top-k digit
 size_t block_select_ws_bytes(int T, int64_t ld, int block);
-void kinsert_geometry(int T, int D, int* splits, int* steps_per_split);   // hidden-dim split
+int kinsert_splits(int T, int D);   // hidden-dim splits of the key projection
 
 // ---- launchers (return the HIP status of the last launch) -----------------------------------
 

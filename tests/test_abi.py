@@ -104,8 +104,8 @@ def test_zero_queries_is_a_no_op(dsa):
 def test_cache_writers_validate_arguments(dsa):
     d = dsa.IndexKDesc(16, 6144, 6144, 64, 1e-6, 1000)
     assert dsa.dsa_index_k_insert_workspace_size(d) > 0
-    # geometry: T = 16 is one token tile, so the hidden dim is split into 96 slices of 64
-    assert dsa.dsa_index_k_insert_workspace_size(d) == 96 * 16 * 128 * 4
+    # geometry: T = 16 is one token tile, so the hidden dim's 24 blocks of 256 are 24 slices
+    assert dsa.dsa_index_k_insert_workspace_size(d) == 24 * 16 * 128 * 4
     assert dsa.dsa_index_k_insert_workspace_size(dsa.IndexKDesc(4096, 6144, 6144, 64, 1e-6, 1)) == 4 * 4096 * 128 * 4
     bad = dsa.IndexKDesc(16, 100, 96, 32, -1.0, 1000)
     st = dsa.lib().dsa_index_k_insert(ctypes.byref(bad), *([None] * 10), 0, None)
