@@ -372,7 +372,7 @@ dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* d, const void* x, cons
     ck.need(x && wk && ln_w && pos && slot && k_cache && k_scale, "x, wk, ln_w, pos, slot, k_cache and k_scale must be non-NULL");
     ck.need(d->rope_dim == 0 || inv_freq != nullptr, "inv_freq is required when rope_dim is 64");
     ck.need(aligned(x, 16) && aligned(wk, 16), "x and wk must be 16-byte aligned");
-    ck.need(aligned(k_cache, 2), "k_cache must be 2-byte aligned");
+    ck.need(aligned(k_cache, 2) && aligned(k_scale, 4), "k_cache must be 2-byte and k_scale 4-byte aligned");
     const size_t need = kinsert_ws_bytes(d);
     ck.need(ws != nullptr && ws_bytes >= need && aligned(ws, 16),
             "workspace missing, misaligned or smaller than dsa_index_k_insert_workspace_size()");
@@ -400,6 +400,7 @@ dsa_status_t dsa_latent_insert(int32_t num_tokens, int32_t rope_dim, const void*
   ck.need(num_slots >= 0, "num_slots must be >= 0");
   if (num_tokens > 0) {
     ck.need(kv && pos && slot && kv_cache && kv_scale, "kv, pos, slot, kv_cache and kv_scale must be non-NULL");
+    ck.need(aligned(kv, 2) && aligned(kv_scale, 4), "kv must be 2-byte and kv_scale 4-byte aligned");
     ck.need(rope_dim == 0 || inv_freq != nullptr, "inv_freq is required when rope_dim is 64");
   }
   dsa_status_t st = ck.finish(fn);

@@ -268,7 +268,7 @@ dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* desc, const void* q, c
  *   pos      [num_tokens] i32;  inv_freq [32] f32 (RoPE layers; ignored when rope_dim = 0)
  *   slot     [num_tokens] i64  destination row; in the readers' layout seq * max_ctx + position.
  *            A negative slot (padding token) or one >= num_slots is skipped.
- *   k_cache  [num_slots][128] E4M3FN bytes;  k_scale [num_slots] f32 (the index cache and its
+ *   k_cache  [num_slots][128] E4M3FN bytes, 2-byte aligned;  k_scale [num_slots] f32 (the index cache and its
  *            per-token scales as dsa_indexer_scores reads them)
  *   ws       workspace of dsa_index_k_insert_workspace_size(desc) bytes, 16-byte aligned
  *            (partial projections; its contents need not be initialised)
@@ -298,7 +298,7 @@ dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* desc, const void* x, c
  *   per 64-element group g: scale_g = max|r_g| / 448 (1 if 0), codes as for the key;
  *   kv_cache[slot[t]][0..576) = codes, kv_scale[slot[t]][g] = scale_g.
  * The latent part arrives final (any normalisation of it is applied upstream).
- *   kv       [num_tokens][ld_kv] BF16 (ld_kv >= 576);  pos, inv_freq, slot as above
+ *   kv       [num_tokens][ld_kv] BF16 (ld_kv >= 576), 2-byte aligned;  pos, inv_freq, slot as above
  *   kv_cache [num_slots][576] E4M3FN bytes;  kv_scale [num_slots][9] f32 (the latent cache as
  *            dsa_sparse_mla_decode / _prefill read it, with kv_scale_block = 64)
  * No workspace.  Skipped slots and races as above.
