@@ -400,7 +400,8 @@ dsa_status_t dsa_latent_insert(int32_t num_tokens, int32_t rope_dim, const void*
   ck.need(num_slots >= 0, "num_slots must be >= 0");
   if (num_tokens > 0) {
     ck.need(kv && pos && slot && kv_cache && kv_scale, "kv, pos, slot, kv_cache and kv_scale must be non-NULL");
-    ck.need(aligned(kv, 2) && aligned(kv_scale, 4), "kv must be 2-byte and kv_scale 4-byte aligned");
+    ck.need(aligned(kv, 16) && ld_kv % 8 == 0 && aligned(kv_cache, 8) && aligned(kv_scale, 4),
+            "kv must be 16-byte aligned with ld_kv a multiple of 8, kv_cache 8-byte and kv_scale 4-byte aligned");
     ck.need(rope_dim == 0 || inv_freq != nullptr, "inv_freq is required when rope_dim is 64");
   }
   dsa_status_t st = ck.finish(fn);

@@ -24,8 +24,9 @@
 //              scale stored at the token's slot.
 // Latent row ("Day 0 support for Mistral Large 4 on vLLM", "Model architecture": 512 latent and 64
 // rotary dims per token; FP8 with one scale per 64 elements, the layout the attention kernels read):
-//   k_latent   one wave per token: per 64-element group the bf16 values, the rotary group rotated
-//              at the token's position on RoPE layers, the group's scale and codes as above.
+//   k_latent   one wave per token, 8 lanes per 64-element group (16-byte loads, 8-byte code
+//              stores): the rotary group rotated at the token's position on RoPE layers (each lane's
+//              four pairs are its own), each group's scale and codes as above.
 // Tokens whose slot is negative (padding) or not below the cache's row count are skipped.
 
 #include "dsa_internal.h"
@@ -232,7 +233,37 @@ __global__ void __launch_bounds__(kFinThreads) k_kfinish(KInsertLaunch a) {
   if (lane == 0) a.k_scale[slot] = scale;
 }
 
+// Max over the 8 lanes 8i..8i+7 of a wave (xor shuffles within the group).
+__device__ __forceinline__ float group8_max(float x) {
+#pragma unroll
+  for (int o = 4; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Eight codes of v[0..8) / scale, byte i = code of v[i].
+__device__ __forceinline__ uint2 fp8_eight(const float (&v)[8], float scale) {
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(v[i] / scale, -448.f), 448.f);
+  uint32_t w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)w0, true);
+  uint32_t w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+  w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)w1, true);
+  return make_uint2(w0, w1);
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4& raw, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(raw[i] << 16);
+    v[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+  }
+}
+
 __global__ void __launch_bounds__(kFinThreads) k_latent(LatentInsertLaunch a) {
+  // one wave per token: lane l holds latent elements 8l..8l+7 (64-element group l/8, its eight
+  // lanes reduce the group's maximum), and lanes 0..7 also hold the rotary group's elements
+  // 512+8l..512+8l+7, whose four RoPE pairs are all the lane's own
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kFinThreads / 64) + wave;
   if (t >= a.T) return;
@@ -240,24 +271,33 @@ __global__ void __launch_bounds__(kFinThreads) k_latent(LatentInsertLaunch a) {
   if (slot < 0 || slot >= a.nslots) return;
   const uint16_t* src = a.kv + (size_t)t * a.ld_kv;
   constexpr int G = kLatRow / kLatGroup;
-  float v[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) v[g] = __uint_as_float((uint32_t)src[g * kLatGroup + lane] << 16);
+  const u32x4 raw = *reinterpret_cast<const u32x4*>(src + 8 * lane);
+  const u32x4 rraw = *reinterpret_cast<const u32x4*>(src + 512 + 8 * (lane & 7));
+  float v[8], r[8];
+  bf16x8_to_f32(raw, v);
+  bf16x8_to_f32(rraw, r);
   if (a.rope_dim) {
-    // the rotary group: lanes 2j and 2j+1 hold pair j
-    float sn, cs;
-    rope_sincos(a.pos[t], a.inv_freq[lane >> 1], &sn, &cs);
-    const float other = __shfl_xor(v[G - 1], 1);
-    v[G - 1] = (lane & 1) ? other * sn + v[G - 1] * cs : v[G - 1] * cs - other * sn;
-  }
-  uint8_t* dst = a.kv_cache + slot * kLatRow;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float amax = wave_max(fabsf(v[g]));
-    const float scale = amax > 0.f ? amax / 448.f : 1.f;
-    dst[g * kLatGroup + lane] = (uint8_t)fp8_pair(v[g], 0.f, scale);
-    if (lane == 0) a.kv_scale[slot * G + g] = scale;
+    for (int i = 0; i < 4; ++i) {
+      float sn, cs;
+      rope_sincos(a.pos[t], a.inv_freq[4 * (lane & 7) + i], &sn, &cs);
+      const float e = r[2 * i], o = r[2 * i + 1];
+      r[2 * i] = e * cs - o * sn;
+      r[2 * i + 1] = e * sn + o * cs;
+    }
   }
+  float m = 0.f, mr = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { m = fmaxf(m, fabsf(v[i])); mr = fmaxf(mr, fabsf(r[i])); }
+  m = group8_max(m);
+  mr = group8_max(mr);
+  const float scale = m > 0.f ? m / 448.f : 1.f;
+  const float rscale = mr > 0.f ? mr / 448.f : 1.f;
+  uint8_t* dst = a.kv_cache + slot * kLatRow;
+  *reinterpret_cast<uint2*>(dst + 8 * lane) = fp8_eight(v, scale);
+  if (lane < 8) *reinterpret_cast<uint2*>(dst + 512 + 8 * lane) = fp8_eight(r, rscale);
+  if ((lane & 7) == 0) a.kv_scale[slot * G + (lane >> 3)] = scale;
+  if (lane == 0) a.kv_scale[slot * G + G - 1] = rscale;
 }
 
 }  // namespace

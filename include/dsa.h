@@ -298,8 +298,9 @@ dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* desc, const void* x, c
  *   per 64-element group g: scale_g = max|r_g| / 448 (1 if 0), codes as for the key;
  *   kv_cache[slot[t]][0..576) = codes, kv_scale[slot[t]][g] = scale_g.
  * The latent part arrives final (any normalisation of it is applied upstream).
- *   kv       [num_tokens][ld_kv] BF16 (ld_kv >= 576), 2-byte aligned;  pos, inv_freq, slot as above
- *   kv_cache [num_slots][576] E4M3FN bytes;  kv_scale [num_slots][9] f32 (the latent cache as
+ *   kv       [num_tokens][ld_kv] BF16 (ld_kv >= 576, a multiple of 8), 16-byte aligned;
+ *            pos, inv_freq, slot as above
+ *   kv_cache [num_slots][576] E4M3FN bytes, 8-byte aligned;  kv_scale [num_slots][9] f32 (the latent cache as
  *            dsa_sparse_mla_decode / _prefill read it, with kv_scale_block = 64)
  * No workspace.  Skipped slots and races as above.
  * ==========================================================================================*/
