@@ -16,8 +16,9 @@
 //              blocks, so that a decode step's handful of tokens still spreads the weight's read
 //              over many CUs and the slices of one tile read neighbouring pieces of the same rows;
 //              the fp32 partials go to the workspace, [slice][token][128].
-//   k_kfinish  one workgroup per token: its four waves sum interleaved slices, then one wave, lane
-//              j holding dims 2j and 2j+1 (exactly one RoPE pair), applies LayerNorm with the
+//   k_kfinish  one wave per token (one workgroup per token when there are more than four
+//              slices, its waves summing interleaved slices), lane j holding dims 2j and 2j+1
+//              (exactly one RoPE pair): the slices' sum, LayerNorm with the
 //              population variance, the rotation of pairs j < rope_dim/2 by p * inv_freq[j],
 //              scale = amax / 448 (1 for an all-zero key) and the codes of k / scale, clamped to
 //              +-448 and rounded to nearest even by v_cvt_pk_fp8_f32; one 128-byte row and its
@@ -181,35 +182,47 @@ __global__ void __launch_bounds__(kProjThreads) k_kproj(KInsertLaunch a) {
 
 __global__ void __launch_bounds__(kFinThreads) k_kfinish(KInsertLaunch a) {
   __shared__ float2 red[kFinThreads / 64][kKeyDim / 2];
+  constexpr int W = kFinThreads / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x;
+  // up to W slices: one wave per token; more: one workgroup per token, wave w summing the slices
+  // w, w + W, ... and wave 0 adding the W sums
+  const bool per_wave = a.splits <= W;
+  const int t = per_wave ? blockIdx.x * W + wave : blockIdx.x;
+  if (t >= a.T) return;
   const int64_t slot = a.slot[t];
   if (slot < 0 || slot >= a.nslots) return;
-  // wave w sums the slices s = w, w + 4, ...; wave 0 then adds the four sums
   const float2* part = reinterpret_cast<const float2*>(a.ws) + (size_t)t * (kKeyDim / 2) + lane;
   const size_t sstride = (size_t)a.T * (kKeyDim / 2);
-  constexpr int W = kFinThreads / 64;
   float y0 = 0.f, y1 = 0.f;
-  int s = wave;
-  for (; s + 3 * W < a.splits; s += 4 * W) {
-    float2 v[4];
+  if (per_wave) {
+    float2 v[W];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = part[(size_t)(s + i * W) * sstride];
+    for (int i = 0; i < W; ++i) v[i] = part[(size_t)min(i, a.splits - 1) * sstride];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { y0 += v[i].x; y1 += v[i].y; }
+    for (int i = 0; i < W; ++i)
+      if (i < a.splits) { y0 += v[i].x; y1 += v[i].y; }
+  } else {
+    int s = wave;
+    for (; s + 3 * W < a.splits; s += 4 * W) {
+      float2 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = part[(size_t)(s + i * W) * sstride];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { y0 += v[i].x; y1 += v[i].y; }
+    }
+    for (; s < a.splits; s += W) {
+      const float2 v = part[(size_t)s * sstride];
+      y0 += v.x;
+      y1 += v.y;
+    }
+    red[wave][lane] = make_float2(y0, y1);
+    __syncthreads();
+    if (wave != 0) return;
+    y0 = 0.f;
+    y1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) { y0 += red[w][lane].x; y1 += red[w][lane].y; }
   }
-  for (; s < a.splits; s += W) {
-    const float2 v = part[(size_t)s * sstride];
-    y0 += v.x;
-    y1 += v.y;
-  }
-  red[wave][lane] = make_float2(y0, y1);
-  __syncthreads();
-  if (wave != 0) return;
-  y0 = 0.f;
-  y1 = 0.f;
-#pragma unroll
-  for (int w = 0; w < W; ++w) { y0 += red[w][lane].x; y1 += red[w][lane].y; }
   // LayerNorm over the 128 dims
   const float mean = wave_sum(y0 + y1) * (1.f / kKeyDim);
   const float d0 = y0 - mean, d1 = y1 - mean;
@@ -313,7 +326,9 @@ hipError_t launch_index_k_insert(const KInsertLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const dim3 g1((unsigned)((a.T + kTileTok - 1) / kTileTok), (unsigned)a.splits);
   hipLaunchKernelGGL(k_kproj, g1, dim3(kProjThreads), 0, s, a);
-  hipLaunchKernelGGL(k_kfinish, dim3((unsigned)a.T), dim3(kFinThreads), 0, s, a);
+  const int W = kFinThreads / 64;
+  const unsigned g2 = a.splits <= W ? (unsigned)((a.T + W - 1) / W) : (unsigned)a.T;
+  hipLaunchKernelGGL(k_kfinish, dim3(g2), dim3(kFinThreads), 0, s, a);
   return hipGetLastError();
 }
 
