@@ -34,6 +34,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace dsa {
 namespace {
 

@@ -111,6 +111,8 @@ KEY_CASES = [
     ("small_hidden_one_step", list(range(70)), [0] * 70, 1, 80, 32, True, ()),
     ("hidden_96_odd_steps", list(range(0, 130, 2)), [0] * 65, 1, 200, 96, True, (0,)),
     ("hidden_4160", [1 << 20] * 3 + [7, 9], [0, 1, 2, 3, 3], 4, (1 << 20) + 1, 4160, True, ()),
+    ("single_token", [5], [0], 1, 10, 6144, True, ()),
+    ("tile_plus_one_nope", list(range(65)), [0] * 65, 1, 70, 6144, False, (64,)),
 ]
 
 
@@ -163,6 +165,7 @@ LATENT_CASES = [
     ("rope_ragged", list(range(300, 337)), [0] * 37, 1, 400, True, ()),
     ("nope_two_seqs_skip", list(range(90)) * 2, [0] * 90 + [1] * 90, 2, 100, False, (4, 95)),
     ("rope_decode_b16", [131071] * 16, list(range(16)), 16, 131072, True, ()),
+    ("single_token_far", [(1 << 26) - 1], [0], 1, 1 << 26, True, ()),
 ]
 
 
