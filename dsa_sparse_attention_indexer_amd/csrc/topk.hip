@@ -344,15 +344,28 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   if (tid < S) sm.tpre[tid] = pre;
   __syncthreads();
   const uint2* items = reinterpret_cast<const uint2*>(rw + kTkOffItems);
-  for (uint32_t i = tid; i < total; i += kRT) {
-    int lo = 0, hi = S - 1;   // the last segment starting at or before i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sm.tpre[mid] <= i) lo = mid; else hi = mid - 1;
+  // four items per thread per round, their loads issued together (past the end: the last item
+  // again, not stored), so a typical row pays the load latency once
+  for (uint32_t i0 = tid; i0 < total; i0 += 4 * kRT) {
+    uint2 it[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = min(i0 + (uint32_t)(u * kRT), total - 1);
+      int lo = 0, hi = S - 1;   // the last segment starting at or before i
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sm.tpre[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      it[u] = items[sm.tst[lo] + (i - sm.tpre[lo])];
     }
-    const uint2 it = items[sm.tst[lo] + (i - sm.tpre[lo])];
-    sm.key[i] = it.x;
-    sm.col[i] = it.y;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = i0 + (uint32_t)(u * kRT);
+      if (i < total) {
+        sm.key[i] = it[u].x;
+        sm.col[i] = it[u].y;
+      }
+    }
   }
   __syncthreads();
 
