@@ -96,21 +96,19 @@ def encode_e4m3fn(v) -> np.ndarray:
     return np.where(np.isnan(v), np.uint8(0x7F), code).astype(np.uint8)
 
 
-def quantize_e4m3_rows(x, block: int, precision=np.float64):
+def quantize_e4m3_rows(x, block: int):
     """Codes and scales of the rows of x, one scale per `block` elements along the last dim.
 
-    scale = amax / 448 (1 where amax is 0); code = encode_e4m3fn(x / scale).  `precision` is the
-    float type in which x, the scale and the quotient are rounded before the code is chosen
-    (float32 to take the decision as a float32 kernel does).  Returns (uint8 codes, scales).
+    scale = amax / 448 (1 where amax is 0); code = encode_e4m3fn(x / scale), everything in
+    float64.  Returns (uint8 codes, float64 scales).
     """
-    x = np.asarray(x, dtype=np.float64).astype(precision)
+    x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     assert d % block == 0
     xb = x.reshape(*x.shape[:-1], d // block, block)
     amax = np.abs(xb).max(axis=-1)
-    scale = np.where(amax > 0, amax / precision(448.0), precision(1.0)).astype(precision)
-    q = (xb / scale[..., None]).astype(precision)
-    return encode_e4m3fn(q.astype(np.float64)).reshape(x.shape), scale.astype(np.float64)
+    scale = np.where(amax > 0, amax / 448.0, 1.0)
+    return encode_e4m3fn(xb / scale[..., None]).reshape(x.shape), scale
 
 
 def decode_bf16(bits) -> np.ndarray:

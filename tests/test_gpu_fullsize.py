@@ -11,7 +11,7 @@ import torch
 
 import workloads
 from oracle import dsa_oracle as O
-from tests.parity_util import check_attention, check_block_selection, check_selection
+from tests.parity_util import check_attention, check_block_selection, check_selection, mla_lse_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -39,9 +39,12 @@ def _check_queries(wl, buf, samples, *, block=False, fp8=True, where=""):
         if block:
             check_block_selection(idx, ln, ref, n - 1, where=f"{where} q{t}")
         else:
-            check_selection(idx, ln, ref, wl.topk, f"{where} q{t}")
+            check_selection(idx, ln, ref, wl.topk, f"{where} q{t}", rms_admitted_ok=False)
         ro, rl = O.sparse_mla_row(sub, 0, idx, ln)
-        check_attention(buf.out[t].cpu().numpy(), buf.lse[t].cpu().numpy(), ro, rl, fp8, f"{where} q{t}")
+        bound = mla_lse_bound(O.to_f64(sub.mla_q[0]), O.cache_rows(sub, 0, idx[:ln][idx[:ln] >= 0]), sub.rope_dim,
+                              sub.softmax_scale, fp8)
+        check_attention(buf.out[t].cpu().numpy(), buf.lse[t].cpu().numpy(), ro, rl, fp8, f"{where} q{t}",
+                        lse_abs=bound)
         print(f"{where} q{t}: ok (n={n}, len={ln})", flush=True)
 
 

@@ -12,7 +12,7 @@ import torch
 
 import workloads
 from oracle import dsa_oracle as O
-from tests.parity_util import check_attention, check_selection
+from tests.parity_util import check_attention, check_selection, mla_lse_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -248,6 +248,15 @@ def test_block_select_many_blocks(dsa):
 # sparse MLA on a given selection
 # ---------------------------------------------------------------------------------------------
 
+def _mla_ref(wl, t, idx, ln):
+    """The oracle's attention for query t over idx[:ln] and the LSE bound for the kernel's rounding."""
+    idx = np.asarray(idx)
+    sel = idx[:ln][idx[:ln] >= 0]
+    rows = O.cache_rows(wl, int(wl.q_seq[t]), sel)
+    ro, rl = O.mla_attend(wl.mla_q[t], rows, wl.rope_dim, wl.softmax_scale)
+    return ro, rl, mla_lse_bound(O.to_f64(wl.mla_q[t]), rows, wl.rope_dim, wl.softmax_scale, wl.fp8)
+
+
 MLA_CASES = [
     ("fp8_rope_decode", dict(seq_lens=[3000, 2500, 900], max_ctx=3000), False, 0),
     ("fp8_nope_decode", dict(seq_lens=[2600, 2100], max_ctx=2600, rope=False), False, 0),
@@ -278,8 +287,8 @@ def test_sparse_mla_matches_oracle(dsa, name, kw, prefill, splits):
     idx, ln = buf.idx.cpu().numpy(), buf.length.cpu().numpy()
     out, lse = buf.out.cpu().numpy(), buf.lse.cpu().numpy()
     for t in range(wl.num_q):
-        ro, rl = O.sparse_mla_row(wl, t, idx[t], int(ln[t]))
-        check_attention(out[t], lse[t], ro, rl, wl.fp8, f"{name} q{t}")
+        ro, rl, bound = _mla_ref(wl, t, idx[t], int(ln[t]))
+        check_attention(out[t], lse[t], ro, rl, wl.fp8, f"{name} q{t}", lse_abs=bound)
 
 
 def test_sparse_mla_ragged_lists_and_empty(dsa):
@@ -351,9 +360,9 @@ def test_layer_step_end_to_end(dsa, name, kw, block):
             ref, rl = O.block_select_row(s, int(wl.q_pos[t]))
             assert ln[t] == rl and np.array_equal(idx[t], ref), f"{name} q{t}: block selection differs"
         else:
-            check_selection(idx[t], ln[t], s, wl.topk, f"{name} q{t}")
-        ro, rl = O.sparse_mla_row(wl, t, idx[t], int(ln[t]))
-        check_attention(out[t], lse[t], ro, rl, True, f"{name} q{t}")
+            check_selection(idx[t], ln[t], s, wl.topk, f"{name} q{t}", rms_admitted_ok=False)
+        ro, rl, bound = _mla_ref(wl, t, idx[t], int(ln[t]))
+        check_attention(out[t], lse[t], ro, rl, True, f"{name} q{t}", lse_abs=bound)
 
 
 def test_shared_indexer_layer_reuses_selection(dsa):
@@ -452,3 +461,114 @@ def test_fused_workspace_reused_across_shapes(dsa):
             n = int(wl.q_pos[t]) + 1
             ref, rl = O.topk_row(sc[t, :n].astype(np.float64), wl.topk)
             assert ln[t] == rl and np.array_equal(idx[t], ref), f"call {i} q{t}: selection differs"
+
+
+# ---------------------------------------------------------------------------------------------
+# sparse MLA with peaked softmax: logits spread over many binades, so the running maximum moves
+# after the first tile (the lazy rescale of the accumulators) and the split combine weighs
+# partials that differ by many powers of two
+# ---------------------------------------------------------------------------------------------
+
+def _log2_range(wl, t, idx, ln):
+    """Per-head spread (log2) of the logits over the selection, and how far (log2) the maximum over
+    the whole list exceeds the maximum over its first 32 keys."""
+    sel = np.asarray(idx)[:ln]
+    rows = O.cache_rows(wl, int(wl.q_seq[t]), sel[sel >= 0])
+    q = O.to_f64(wl.mla_q[t])
+    d = 512 + wl.rope_dim
+    z = wl.softmax_scale * (q[:, :d] @ rows[:, :d].T) / math.log(2.0)
+    return z.max(1) - z.min(1), z.max(1) - z[:, :32].max(1)
+
+
+PEAKED_CASES = [
+    # name, make_workload kwargs, prefill, splits
+    ("fp8_rope_decode_auto", dict(seq_lens=[3000, 2500, 2100], max_ctx=3000), False, 0),
+    ("fp8_rope_decode_split1", dict(seq_lens=[3000, 2500], max_ctx=3000), False, 1),
+    ("fp8_rope_decode_split3", dict(seq_lens=[4000, 3000], max_ctx=4000), False, 3),
+    ("fp8_rope_decode_split32", dict(seq_lens=[3000, 2200], max_ctx=3000), False, 32),
+    ("fp8_rope_prefill", dict(seq_lens=[2600], max_ctx=2600, q_positions=[2100, 2599, 100]), True, 0),
+    ("fp8_nope_decode", dict(seq_lens=[2600, 2100], max_ctx=2600, rope=False), False, 0),
+    ("fp8_nope_prefill", dict(seq_lens=[2600], max_ctx=2600, rope=False, q_positions=[2599, 2300]), True, 0),
+    ("f32_rope_decode", dict(seq_lens=[2500, 3000], max_ctx=3000, fp8=False, q_dtype=torch.float32), False, 0),
+    ("f32_nope_prefill", dict(seq_lens=[2200], max_ctx=2200, fp8=False, q_dtype=torch.float32, rope=False,
+                              q_positions=[2199, 2000]), True, 0),
+]
+
+
+@pytest.mark.parametrize("name,kw,prefill,splits", PEAKED_CASES, ids=[c[0] for c in PEAKED_CASES])
+def test_sparse_mla_peaked_softmax(dsa, name, kw, prefill, splits):
+    """Queries ~N(0, 64^2): per-head logits span tens of binades over the selection."""
+    wl = workloads.make_workload(name=name, seed=222, mla_q_std=64.0, **kw)
+    g = wl.to("cuda")
+    P = _pipe()
+    buf = P.alloc_buffers(g, prefill=prefill, num_splits=splits)
+    P.layer_step(g, buf, prefill=prefill, num_splits=splits)
+    torch.cuda.synchronize()
+    idx, ln = buf.idx.cpu().numpy(), buf.length.cpu().numpy()
+    out, lse = buf.out.cpu().numpy(), buf.lse.cpu().numpy()
+    spread = []
+    for t in range(wl.num_q):
+        rng_, late = _log2_range(wl, t, idx[t], int(ln[t]))
+        spread.append(np.median(rng_))
+        ro, rl, bound = _mla_ref(wl, t, idx[t], int(ln[t]))
+        check_attention(out[t], lse[t], ro, rl, wl.fp8, f"{name} q{t}", lse_abs=bound)
+        # zeroed logits would put the LSE at ln(len): far outside the bound
+        assert np.all(np.abs(np.log(float(ln[t])) - rl) > 10 * (bound + 1e-3)), f"{name} q{t}: LSE check is blind"
+    assert min(spread) > 20.0, f"{name}: logits not peaked enough ({spread})"
+
+
+LATE_PEAK_CASES = [
+    # name, fp8, rope, prefill, splits, list lengths
+    ("fp8_rope_decode_auto", True, True, False, 0, [2048, 1500]),
+    ("fp8_rope_decode_split1", True, True, False, 1, [2048, 700]),
+    ("fp8_rope_decode_split3", True, True, False, 3, [2048, 1999]),
+    ("fp8_rope_decode_split32", True, True, False, 32, [2048, 2047]),
+    ("fp8_rope_prefill", True, True, True, 0, [2048, 1200]),
+    ("fp8_nope_decode", True, False, False, 0, [2048, 1800]),
+    ("f32_rope_decode", False, True, False, 0, [2048, 1500]),
+    ("f32_rope_prefill", False, True, True, 0, [2048, 333]),
+]
+
+
+@pytest.mark.parametrize("name,fp8,rope,prefill,splits,lens", LATE_PEAK_CASES, ids=[c[0] for c in LATE_PEAK_CASES])
+def test_sparse_mla_peak_in_last_tile_of_last_split(dsa, name, fp8, rope, prefill, splits, lens):
+    """Every head's largest logit is the list's last key (the last tile of the last split), by a
+    margin that grows across the heads from 2 to 60 natural-log units over the others: the
+    running maximum jumps in the last tile, and the split combine weighs that split's partial
+    against the others by up to 2^-80."""
+    n = 4000
+    T = len(lens)
+    wl = workloads.make_workload(name=name, seed=333 + splits, seq_lens=[n] * T, max_ctx=n, fp8=fp8, rope=rope,
+                                 q_dtype=torch.bfloat16 if fp8 else torch.float32)
+    rng = np.random.default_rng(44 + splits)
+    idx = np.full((T, 2048), -1, np.int32)
+    d = 512 + wl.rope_dim
+    q = O.to_f64(wl.mla_q).copy()
+    for t, L in enumerate(lens):
+        sel = np.sort(rng.choice(n, L, replace=False))
+        idx[t, :L] = sel
+        c = O.cache_rows(wl, t, sel[-1:])[0, :d]           # the peak key: the last slot of the list
+        margin = np.linspace(2.0, 60.0, wl.mla_heads)       # nats above a typical logit
+        q[t, :, :d] = 0.5 * q[t, :, :d] + (margin / (wl.softmax_scale * float(c @ c)))[:, None] * c[None, :]
+    wl.mla_q = torch.from_numpy(q).to(wl.mla_q.dtype)
+    lens_t = torch.as_tensor(lens, dtype=torch.int32)
+    g = wl.to("cuda")
+    out = torch.empty(T, wl.mla_heads, 512, device="cuda")
+    lse = torch.empty(T, wl.mla_heads, device="cuda")
+    ws = None
+    if not prefill:
+        need = dsa.dsa_sparse_mla_workspace_size(dsa.mla_desc(g.mla_q, g.kv, torch.empty(T, 2048, dtype=torch.int32),
+                                                              wl.softmax_scale, splits))
+        ws = torch.empty(max(16, need), dtype=torch.uint8, device="cuda")
+        dsa.dsa_sparse_mla_decode(g.mla_q, g.kv, g.kv_scale, g.q_seq, torch.from_numpy(idx).cuda(), lens_t.cuda(),
+                                  out, lse, softmax_scale=wl.softmax_scale, num_splits=splits, ws=ws)
+    else:
+        dsa.dsa_sparse_mla_prefill(g.mla_q, g.kv, g.kv_scale, g.q_seq, torch.from_numpy(idx).cuda(), lens_t.cuda(),
+                                   out, lse, softmax_scale=wl.softmax_scale)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for t, L in enumerate(lens):
+        _, late = _log2_range(wl, t, idx[t], L)
+        assert np.median(late) > 8.0, f"{name} q{t}: the peak does not move the running maximum ({np.median(late)})"
+        ro, rl, bound = _mla_ref(wl, t, idx[t], L)
+        check_attention(o[t], l[t], ro, rl, fp8, f"{name} q{t}", lse_abs=bound)

@@ -236,6 +236,38 @@ def test_topk_exhaustive_tiny():
                     assert s[a] > s[b] or (s[a] == s[b] and a < b)
 
 
+@pytest.mark.parametrize("alphabet", [None, 2, 3, 7])
+@pytest.mark.parametrize("k", [1, 2, 5, 16, 63, 64])
+def test_kth_score_is_the_kth_entry_of_the_brute_force_order(alphabet, k):
+    """kth_score(s, k) is the score of the k-th key in the (score desc, index asc) order that
+    defines the selection, i.e. the lowest selected score: at most k-1 keys score above it and
+    at least k score at or above it.  Checked against a plain sort by a Python key function,
+    on tie-heavy rows and on rows one shorter, equal to and one longer than k."""
+    rng = np.random.default_rng(100 * k + (alphabet or 0))
+    for n in (k - 1, k, k + 1, 3 * k + 5, 200):
+        if n < 1:
+            continue
+        s = rng.standard_normal(n) if alphabet is None else rng.integers(-1, alphabet - 1, n).astype(np.float64)
+        got = O.kth_score(s, k)
+        if n <= k:
+            assert got is None
+            continue
+        order = sorted(range(n), key=lambda t: (-s[t], t))
+        assert got == s[order[k - 1]]
+        assert np.sum(s > got) <= k - 1 and np.sum(s >= got) >= k
+        # the selection's lowest score is this value, and no unselected key scores above it
+        idx, ln = O.topk_row(s, k)
+        assert min(s[idx[:ln]]) == got and np.all(np.delete(s, idx[:ln]) <= got)
+
+
+def test_kth_score_hand_values():
+    s = np.array([3.0, 1.0, 3.0, 2.0, 3.0, 0.5])
+    assert O.kth_score(s, 1) == 3.0 and O.kth_score(s, 3) == 3.0
+    assert O.kth_score(s, 4) == 2.0 and O.kth_score(s, 5) == 1.0
+    assert O.kth_score(s, 6) is None
+    assert O.kth_score(np.array([-0.0, 0.0, -1.0]), 2) == 0.0
+
+
 # ---------------------------------------------------------------------------------------------
 # Block select
 # ---------------------------------------------------------------------------------------------
@@ -407,16 +439,28 @@ def test_quantiser_maps_the_group_maximum_to_448_and_bounds_the_error():
     assert np.array_equal(c64[:, :64], O.quantize_e4m3_rows(x[:, :64], 64)[0])
 
 
-def test_quantiser_in_float32_agrees_with_torch_float32_pipeline():
+def test_quantiser_agrees_with_torch_cast_of_the_float64_quotient():
+    """The float64 quantiser against torch's E4M3FN cast of the same float64 quotient.  torch
+    rounds a float64 through float32 first, so the two may differ only where the quotient lies
+    within float32 rounding of a midpoint between two codes (double rounding); none of these
+    values does, so every code must match."""
     rng = np.random.default_rng(9)
-    x = rng.normal(0, 1.0, (200, 576)).astype(np.float32)
-    codes, scale = O.quantize_e4m3_rows(x, 64, precision=np.float32)
+    x = rng.normal(0, 1.0, (200, 576))
+    x[5, :64] = 0.0                                   # an all-zero group: scale 1, codes 0
+    codes, scale = O.quantize_e4m3_rows(x, 64)
     xt = torch.from_numpy(x).reshape(200, 9, 64)
     amax = xt.abs().amax(-1)
     st = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-    ref = (xt / st.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8).reshape(200, 576).numpy()
+    quot = xt / st.unsqueeze(-1)
+    ref = quot.to(torch.float8_e4m3fn).view(torch.uint8).reshape(200, 576).numpy()
+    mags = O.decode_e4m3fn(np.arange(127, dtype=np.uint8))
+    mids = (mags[1:] + mags[:-1]) / 2
+    q = np.abs(quot.reshape(200, 576).numpy())
+    near_mid = np.min(np.abs(q[..., None] - mids), axis=-1) <= 2.0 ** -23 * q
+    assert not near_mid.any()
     assert np.array_equal(codes, ref)
-    assert np.array_equal(scale, st.double().numpy())
+    assert np.array_equal(scale, st.numpy())
+    assert scale[5, 0] == 1.0 and np.all(codes[5, :64] == 0)
 
 
 def test_layer_norm_matches_torch_layer_norm():
