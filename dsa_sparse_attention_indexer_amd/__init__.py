@@ -270,7 +270,8 @@ def dsa_topk_workspace_size(num_q: int, ld: int, k: int) -> int:
 
 
 def topk_workspace(num_q: int, ld: int, k: int, device) -> torch.Tensor:
-    """A zero-filled top-k workspace (the library keeps it zeroed between calls)."""
+    """A zero-filled top-k workspace (every call clears what it used; stale contents only slow a
+    call down)."""
     return torch.zeros(max(16, dsa_topk_workspace_size(num_q, ld, k)), dtype=torch.uint8, device=device)
 
 

@@ -13,13 +13,16 @@
 //            the k-th largest key and appends every key whose first digit is >= b0 (all keys
 //            above b0 plus the candidates inside it; a few thousand per row) to the row's item
 //            list, in column order within the segment, with ballot/mbcnt compaction.
-//   resolve  one workgroup per row loads the items into LDS in column order, finds the exact
-//            k-th key among the candidates (bits 19..10, then 9..0), and with one ordered pass
-//            keeps the keys above it and the lowest columns among the keys equal to it.  The
-//            output is ascending by construction: no sort and no merge.
-// If a row's items do not fit in LDS (heavy ties) or k is large, the resolve workgroup instead
-// streams the row.  Every decision is made on the integer keys, so the result is exact and
-// deterministic.
+//   resolve  one workgroup per row loads the items into LDS in column order, checks from them
+//            that the histogram's bin b0 really holds the k-th largest key (fewer than k items
+//            above b0, at least k at or above it), finds the exact k-th key among the candidates
+//            (bits 19..10, then 9..0), and with one ordered pass keeps the keys above it and the
+//            lowest columns among the keys equal to it.  The output is ascending by
+//            construction: no sort and no merge.
+// If a row's items do not fit in LDS (heavy ties), k is large, or the check fails (a histogram
+// left over from an interrupted call, or built for another k), the resolve workgroup instead
+// selects by exact passes over the row, first digit included.  Every decision is made on the
+// integer keys, so the result is exact and deterministic; the histogram only decides how fast.
 
 #include "topk_common.h"
 
@@ -180,7 +183,9 @@ __global__ void __launch_bounds__(kCT) k_topk_collect(TopkLaunch a) {
   }
   __syncthreads();
   const uint32_t st = base;
-  if (st + total > (uint32_t)kTkItemCap) return;   // the row overflows: resolve streams it
+  // the row overflows (or the counter held a stale value): nothing is written, the resolve
+  // kernel sees it in the segment table and streams the row
+  if (st > (uint32_t)kTkItemCap || total > (uint32_t)kTkItemCap - st) return;
   uint2* items = reinterpret_cast<uint2*>(rw + kTkOffItems);
 #pragma unroll
   for (int q = 0; q < kCQ; ++q) {
@@ -224,15 +229,18 @@ __device__ void lds_digit(const uint32_t* keys, int cnt, uint32_t prefix, int sh
   tk_find_bin<nb, kRT>(sm.hist, need, sm.sbuf, digit, need_out);
 }
 
-// The same over the row in memory (streaming finish).
+// The same over the row in memory (streaming finish).  shift + BITS == 32 is the first digit (no
+// prefix).
 template <int BITS>
 __device__ void row_digit(const float* row, int n, uint32_t prefix, int shift, uint32_t need,
                           ResolveSmem& sm, int* digit, uint32_t* need_out) {
   constexpr int nb = 1 << BITS;
   constexpr int bits = BITS;
+  static_assert(nb <= kTkBins, "digit histogram fits");
   for (int i = threadIdx.x; i < nb; i += kRT) sm.hist[i] = 0;
   __syncthreads();
-  const int hs = shift + bits;
+  const bool top = shift + bits >= 32;
+  const int hs = top ? 0 : shift + bits;
   for (int c0 = 0; c0 < n; c0 += 4 * kRT * kSQ) {
     uint32_t key[kSQ][4];
     const uint32_t mask = load_slices<kSQ, kRT>(row, n, c0, key);
@@ -240,19 +248,22 @@ __device__ void row_digit(const float* row, int n, uint32_t prefix, int shift, u
     for (int q = 0; q < kSQ; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> hs) == prefix)
+        if (((mask >> (4 * q + e)) & 1u) && (top || (key[q][e] >> hs) == prefix))
           atomicAdd(&sm.hist[(key[q][e] >> shift) & (nb - 1)], 1u);
   }
   __syncthreads();
   tk_find_bin<nb, kRT>(sm.hist, need, sm.sbuf, digit, need_out);
 }
 
-// Streaming finish: the exact k-th key from two passes over the row, then one ordered pass that
-// emits every key above it and the lowest columns among the keys equal to it.
-__device__ void finish_streaming(const TopkLaunch& a, int t, int n, uint32_t b0, uint32_t need0, ResolveSmem& sm) {
+// Streaming finish: the exact k-th key from three passes over the row (first digit, then bits
+// 19..10 and 9..0), then one ordered pass that emits every key above it and the lowest columns
+// among the keys equal to it.  It reads nothing from the workspace.
+__device__ void finish_streaming(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
   const float* row = a.scores + (size_t)t * a.ld;
-  int d1, d2;
-  uint32_t need1, need2;
+  int b0i, d1, d2;
+  uint32_t need0, need1, need2;
+  row_digit<12>(row, n, 0u, kTkShift0, (uint32_t)a.k, sm, &b0i, &need0);
+  const uint32_t b0 = (uint32_t)b0i;
   row_digit<10>(row, n, b0, 10, need0, sm, &d1, &need1);
   row_digit<10>(row, n, (b0 << 10) | (uint32_t)d1, 0, need1, sm, &d2, &need2);
   const uint32_t thr = (b0 << 20) | ((uint32_t)d1 << 10) | (uint32_t)d2;
@@ -302,72 +313,100 @@ __device__ void finish_streaming(const TopkLaunch& a, int t, int n, uint32_t b0,
 
 __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   __shared__ __attribute__((aligned(16))) ResolveSmem sm;
+  static_assert(kTkBins == 4 * kRT, "one uint4 of histogram per thread");
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = row_n(a, t);
   int32_t* out = a.idx + (size_t)t * a.k;
-  if (n <= a.k) {   // every visible column, then padding
+  uint32_t* rw = tk_row(a.ws, t);
+  if (n <= a.k) {   // every visible column, then padding; a histogram left by an earlier call is cleared
     for (int i = tid; i < a.k; i += kRT) out[i] = i < n ? i : -1;
-    if (tid == 0 && a.len) a.len[t] = n;
+    reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) {
+      rw[kTkOffCtr] = 0u;
+      if (a.len) a.len[t] = n;
+    }
     return;
   }
-  uint32_t* rw = tk_row(a.ws, t);
 
-  // the row's histogram, item count and segment table in one round of loads; the histogram and
-  // the count are then zeroed for the next call
+  // the row's histogram and segment table in one round of loads; the histogram and the item
+  // counter are then zeroed for the next call
   const int S = (n + kTkSeg - 1) / kTkSeg;
   uint32_t cnt_s = 0;
+  bool seg_bad = false;
   {
     const uint4 h = reinterpret_cast<const uint4*>(rw)[tid];
     uint2 te = make_uint2(0u, 0u);
     if (tid < S) te = reinterpret_cast<const uint2*>(rw + kTkOffTable)[tid];
-    if (tid == 0) sm.sbuf[24] = rw[kTkOffCtr];
     sm.hist[4 * tid] = h.x; sm.hist[4 * tid + 1] = h.y; sm.hist[4 * tid + 2] = h.z; sm.hist[4 * tid + 3] = h.w;
     if (tid < S) sm.tst[tid] = te.x;
     cnt_s = te.y;
+    // a segment whose items did not fit (or whose start came from a stale counter) wrote none
+    seg_bad = tid < S && (te.x > (uint32_t)kTkItemCap || te.y > (uint32_t)kTkItemCap - te.x);
     __syncthreads();
     reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) rw[kTkOffCtr] = 0u;
   }
-  const uint32_t total = sm.sbuf[24];
+  const bool overflow = __syncthreads_or(seg_bad) != 0;
   int b0;
-  uint32_t need0;
-  tk_find_bin<kTkBins, kRT>(sm.hist, (uint32_t)a.k, sm.sbuf, &b0, &need0);
-  if (a.k > kTkFastK || total > (uint32_t)kTkItemCap) {
-    finish_streaming(a, t, n, (uint32_t)b0, need0, sm);
+  uint32_t need_hint;
+  tk_find_bin<kTkBins, kRT>(sm.hist, (uint32_t)a.k, sm.sbuf, &b0, &need_hint);
+  if (a.k > kTkFastK || overflow) {
+    finish_streaming(a, t, n, sm);
     if (tid == 0 && a.len) a.len[t] = a.k;
     return;
   }
 
   // items into LDS in column order: segment s holds items tpre[s].. of the row, stored from tst[s]
-  const uint32_t pre = tk_excl_scan<kRT>(cnt_s, nullptr, sm.sbuf);
+  uint32_t total;
+  const uint32_t pre = tk_excl_scan<kRT>(cnt_s, &total, sm.sbuf);
+  if (total > (uint32_t)kTkItemCap) {   // (not reached when every segment fit; kept as a guard)
+    finish_streaming(a, t, n, sm);
+    if (tid == 0 && a.len) a.len[t] = a.k;
+    return;
+  }
   if (tid < S) sm.tpre[tid] = pre;
   __syncthreads();
   const uint2* items = reinterpret_cast<const uint2*>(rw + kTkOffItems);
   // four items per thread per round, their loads issued together (past the end: the last item
-  // again, not stored), so a typical row pays the load latency once
-  for (uint32_t i0 = tid; i0 < total; i0 += 4 * kRT) {
-    uint2 it[4];
+  // again, not stored), so a typical row pays the load latency once; the items above b0 are
+  // counted on the way
+  uint32_t gt_b0 = 0;
+  if (total > 0) {
+    for (uint32_t i0 = tid; i0 < total; i0 += 4 * kRT) {
+      uint2 it[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t i = min(i0 + (uint32_t)(u * kRT), total - 1);
-      int lo = 0, hi = S - 1;   // the last segment starting at or before i
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sm.tpre[mid] <= i) lo = mid; else hi = mid - 1;
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = min(i0 + (uint32_t)(u * kRT), total - 1);
+        int lo = 0, hi = S - 1;   // the last segment starting at or before i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sm.tpre[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        it[u] = items[sm.tst[lo] + (i - sm.tpre[lo])];
       }
-      it[u] = items[sm.tst[lo] + (i - sm.tpre[lo])];
-    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t i = i0 + (uint32_t)(u * kRT);
-      if (i < total) {
-        sm.key[i] = it[u].x;
-        sm.col[i] = it[u].y;
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + (uint32_t)(u * kRT);
+        if (i < total) {
+          sm.key[i] = it[u].x;
+          sm.col[i] = it[u].y;
+          gt_b0 += (it[u].x >> kTkShift0) > (uint32_t)b0 ? 1u : 0u;
+        }
       }
     }
   }
-  __syncthreads();
+  // The items are every key whose first digit is >= b0 (the collect kernels all read the same
+  // histogram).  b0 holds the k-th largest key iff fewer than k of them lie above b0 and at least
+  // k at or above it; otherwise the histogram did not describe these scores.
+  uint32_t above_b0;
+  tk_excl_scan<kRT>(gt_b0, &above_b0, sm.sbuf);
+  if (!(above_b0 < (uint32_t)a.k && (uint32_t)a.k <= total)) {
+    finish_streaming(a, t, n, sm);
+    if (tid == 0 && a.len) a.len[t] = a.k;
+    return;
+  }
+  const uint32_t need0 = (uint32_t)a.k - above_b0;
 
   // the exact k-th key among the candidates (the items inside b0): bits 19..10 first
   int d1;

@@ -1,13 +1,17 @@
 // Device-side pieces of the exact top-k shared by the index-score kernel (which can build the
 // first radix digit's histogram while it scores) and the top-k kernels.
 //
-// Per-row workspace (32-bit words), zero before first use; the resolve kernel that finishes a row
-// clears its histogram and counter again, so one zeroed workspace serves any sequence of calls:
+// Per-row workspace (32-bit words):
 //   hist   [kTkBins]        counts of the first radix digit (score-key bits 31..20)
-//   ctr    [4]              ctr[0]: items appended by the collect kernel
+//   ctr    [4]              ctr[0]: item slots handed out by the collect kernel
 //   table  [kTkMaxSeg][2]   per segment: first item, item count (written by every live segment)
 //   items  [kTkItemCap][2]  (key, column) of every score whose first digit is >= the threshold
 //                           digit, in column order within each segment
+// The histogram only steers the fast path: the resolve kernel checks against the collected items
+// that the digit it names holds the k-th largest key, and otherwise selects by exact passes over
+// the row.  The resolve kernel that finishes a row clears its histogram and counter, so stale
+// contents (an interrupted call, a different k, a workspace never cleared) cost speed, never
+// correctness.
 #pragma once
 
 #include "dsa_internal.h"
@@ -67,8 +71,9 @@ __device__ inline uint32_t tk_excl_scan(uint32_t v, uint32_t* total, uint32_t* s
 }
 
 // The bin of an NB-bin histogram (16-byte aligned) that holds the need-th largest key: returns it
-// and the count still needed inside it, identically in every thread.  Thread i owns NB/NT
-// consecutive bins counted from the top.  sbuf: at least 22 words.
+// and the count still needed inside it, identically in every thread.  If the histogram holds
+// fewer than need keys, bin 0 and need are returned.  Thread i owns NB/NT consecutive bins counted
+// from the top.  sbuf: at least 22 words.
 template <int NB, int NT>
 __device__ inline void tk_find_bin(const uint32_t* h, uint32_t need, uint32_t* sbuf, int* bin_out,
                                    uint32_t* need_out) {
@@ -89,6 +94,7 @@ __device__ inline void tk_find_bin(const uint32_t* h, uint32_t need, uint32_t* s
   uint32_t local = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) local += c[i];
+  if (threadIdx.x == 0) { sbuf[20] = 0u; sbuf[21] = need; }   // ordered before the finder by the scan's barrier
   uint32_t above = tk_excl_scan<NT>(local, nullptr, sbuf);
 #pragma unroll
   for (int i = PER - 1; i >= 0; --i) {

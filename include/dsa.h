@@ -94,9 +94,11 @@ int32_t dsa_abi_version(void);
  *            ws may be NULL.
  *
  * Supported: head_dim == 128; 1 <= num_heads <= 32; rope_dim in {0, 64}; q_dtype F32 or BF16;
- * k_dtype F32 (fp32 vector path) or FP8_E4M3FN (matrix-core path).  The FP8 path computes q'
- * in float64, splits it into two fp16 terms and accumulates in fp32; its scores agree with
- * the real-number definition to about 1e-6 of the score scale.
+ * k_dtype F32 (fp32 vector path) or FP8_E4M3FN (matrix-core path).  Both paths form the rotary
+ * angles p * inv_freq[j] exactly and reduce them to [-pi, pi] in float64, then evaluate sine,
+ * cosine, the SSMax factor and the rotation in float32 (about 1e-7 relative).  The FP8 path
+ * splits q' into two fp16 terms (22 significant bits) and accumulates in fp32; its scores agree
+ * with the real-number definition to about 1e-6 of the score scale.
  * ==========================================================================================*/
 typedef struct {
   int32_t num_q;       /* T: query tokens                                                   */
@@ -134,10 +136,13 @@ dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* desc, const void* q, c
  *   idx      [num_q][k] i32;          len [num_q] i32 (may be NULL)
  *   ws       device workspace of at least dsa_topk_workspace_size(num_q, ld_scores, k) bytes,
  *            16-byte aligned (about 148 KiB per query: the row's first-digit histogram and the
- *            keys that survive it).  It must be zero-filled once before its first use (hipMemset);
- *            every completed call leaves its bookkeeping zeroed again, so no clearing is needed
- *            between calls, whatever num_q, ld_scores and k they use.  Calls that overlap in time
- *            must not share a workspace.
+ *            keys that survive it).  Its contents never decide a selection: the histogram only
+ *            steers a fast path whose premise (the k-th largest key lies in the bin it names) is
+ *            checked against the scores themselves, and rows that fail the check are selected by
+ *            exact passes over the row.  Every call clears what it used, so a workspace that is
+ *            zero-filled once (hipMemset) keeps every call on the fast path; stale or random
+ *            contents cost one slower call, never a wrong one.  Calls that overlap in time must
+ *            not share a workspace.
  * Supported: 1 <= k <= 65536; ld_scores <= 4194304 and a multiple of 4; scores 16-byte aligned.
  * ==========================================================================================*/
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t num_q,
@@ -162,9 +167,10 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* desc, const void* q, con
  * the fp8 score kernel, else by a histogram pass after it); dsa_topk_hist then selects k columns of
  * each row from those scores and that histogram and leaves the workspace zeroed.  Issued back to
  * back with the same arguments they give exactly dsa_indexer_topk's results (rows hold
- * min(q_pos + 1, max_ctx) scores).  dsa_topk_hist must follow a dsa_indexer_scores_hist call on the
- * same scores and workspace with no other top-k call on that workspace in between; otherwise its
- * selection is undefined (it still reads and writes only its own buffers). */
+ * min(q_pos + 1, max_ctx) scores).  dsa_topk_hist is meant to follow a dsa_indexer_scores_hist call
+ * on the same scores and workspace with the same k.  If it does not (the histogram is missing,
+ * doubled, left by an interrupted call or built for another k), its selection is still exact: the
+ * rows whose histogram does not match their scores are selected by exact passes over the row. */
 dsa_status_t dsa_indexer_scores_hist(const dsa_indexer_desc_t* desc, const void* q, const float* w,
                                      const int32_t* q_seq, const int32_t* q_pos,
                                      const float* ssmax_s, const float* ssmax_b, const float* inv_freq,

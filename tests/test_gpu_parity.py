@@ -463,6 +463,79 @@ def test_fused_workspace_reused_across_shapes(dsa):
             assert ln[t] == rl and np.array_equal(idx[t], ref), f"call {i} q{t}: selection differs"
 
 
+def _check_rows_exact(wl, buf, k, where):
+    """The selection equals the oracle's top-k of the GPU's own scores, bit for bit."""
+    idx, ln = buf.idx.cpu().numpy(), buf.length.cpu().numpy()
+    sc = buf.scores.cpu().numpy()
+    for t in range(wl.num_q):
+        n = min(int(wl.q_pos[t]) + 1, wl.max_ctx)
+        ref, rl = O.topk_row(sc[t, :n].astype(np.float64), k)
+        assert ln[t] == rl and np.array_equal(idx[t, :k], ref), f"{where} q{t}: selection differs"
+
+
+def test_topk_workspace_stale_state_self_heals(dsa):
+    """The top-k workspace carries a histogram between the two halves of a selection.  Whatever an
+    earlier call left in it (an interrupted scores_hist, a histogram built for another k, two
+    histograms piled up, none at all, or random bytes), every later selection is exact, and the
+    call after a recovery finds the workspace clean again."""
+    P = _pipe()
+    wl = workloads.make_workload(name="stale", seed=1212, seq_lens=[20000, 9000, 3000, 2049], max_ctx=20000).to("cuda")
+    buf = P.alloc_buffers(wl)
+    k = wl.topk
+
+    def pair():
+        P.index_scores_hist(wl, buf)
+        P.select_hist(wl, buf)
+        torch.cuda.synchronize()
+        _check_rows_exact(wl, buf, k, "pair")
+
+    pair()
+    # 1. interrupted: scores + histogram, no selection; then a normal pair on the same workspace
+    P.index_scores_hist(wl, buf)
+    torch.cuda.synchronize()
+    pair()
+    # 2. scores + histogram twice (the histogram counts every key twice), then the selection
+    P.index_scores_hist(wl, buf)
+    P.index_scores_hist(wl, buf)
+    P.select_hist(wl, buf)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, buf, k, "double histogram")
+    pair()
+    # 3. a selection with no histogram before it (the previous selection cleared it)
+    P.select_hist(wl, buf)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, buf, k, "no histogram")
+    # 4. histogram built for k = 2048, selection with k = 4000 (rows of 3000 and 2049 keys take
+    #    every key and must clear what the histogram left), then matched calls again
+    idx_big = torch.empty(wl.num_q, 4000, dtype=torch.int32, device="cuda")
+    P.index_scores_hist(wl, buf)
+    dsa.dsa_topk_hist(buf.scores, wl.q_pos, 4000, idx_big, buf.length, wl.max_ctx, buf.ws_topk)
+    torch.cuda.synchronize()
+    sc = buf.scores.cpu().numpy()
+    ib = idx_big.cpu().numpy()
+    for t in range(wl.num_q):
+        n = int(wl.q_pos[t]) + 1
+        ref, rl = O.topk_row(sc[t, :n].astype(np.float64), 4000)
+        assert np.array_equal(ib[t], ref), f"k mismatch q{t}"
+    pair()
+    pair()
+    # 5. the separate top-k call after an interrupted fused half
+    P.index_scores_hist(wl, buf)
+    P.select(wl, buf)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, buf, k, "separate call after an interrupted half")
+    pair()
+    # 6. a workspace of random bytes (never cleared)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    buf.ws_topk.copy_(torch.randint(0, 256, buf.ws_topk.shape, generator=gen, device="cuda", dtype=torch.int32)
+                      .to(torch.uint8))
+    pair()
+    pair()
+    P.select(wl, buf)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, buf, k, "separate call on a used workspace")
+
+
 # ---------------------------------------------------------------------------------------------
 # sparse MLA with peaked softmax: logits spread over many binades, so the running maximum moves
 # after the first tile (the lazy rescale of the accumulators) and the split combine weighs
