@@ -71,6 +71,8 @@ def _load():
         "dsa_sparse_mla_workspace_size": (SZ, [ctypes.POINTER(MlaDesc)]),
         "dsa_sparse_mla_decode": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P]),
         "dsa_sparse_mla_prefill": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dsa_sparse_mla_noalloc_max_bytes": (SZ, []),
+        "dsa_sparse_mla_decode_noalloc": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P]),
         "dsa_index_k_insert_workspace_size": (SZ, [ctypes.POINTER(IndexKDesc)]),
         "dsa_index_k_insert": (I32, [ctypes.POINTER(IndexKDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "dsa_latent_insert": (I32, [I32, I32, P, I64, P, P, P, I64, P, P, P]),
@@ -90,7 +92,8 @@ _lib = _load()
 EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_indexer_topk",
             "dsa_indexer_scores_hist", "dsa_topk_hist",
             "dsa_topk_workspace_size", "dsa_topk", "dsa_block_select_workspace_size", "dsa_block_select", "dsa_sparse_mla_workspace_size",
-            "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_index_k_insert_workspace_size",
+            "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_sparse_mla_noalloc_max_bytes",
+            "dsa_sparse_mla_decode_noalloc", "dsa_index_k_insert_workspace_size",
             "dsa_index_k_insert", "dsa_latent_insert"]
 
 
@@ -355,6 +358,28 @@ def dsa_sparse_mla_decode(q, kv, kv_scale, q_seq, idx, length, out, lse=None, so
     """Sparse MLA for decode (each query's selection split over several workgroups)."""
     return _mla(_lib.dsa_sparse_mla_decode, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale,
                 num_splits, ws, stream)
+
+
+def dsa_sparse_mla_decode_noalloc(q, kv, kv_scale, q_seq, idx, length, out, lse=None, softmax_scale=None,
+                                  num_splits=0, stream=None):
+    """dsa_sparse_mla_decode with the split partials in the library's per-GPU scratch buffer (no
+    workspace argument, nothing allocated)."""
+    T, H, DQ = q.shape
+    B, max_ctx, row = kv.shape
+    _dev("q", q, (torch.float32, torch.bfloat16))
+    _dev("kv", kv, (torch.float32, torch.uint8, torch.float8_e4m3fn))
+    _dev("kv_scale", kv_scale, torch.float32, (B, max_ctx, row // 64))
+    _dev("q_seq", q_seq, torch.int32, (T,))
+    _dev("idx", idx, torch.int32)
+    _dev("length", length, torch.int32, (T,))
+    _dev("out", out, torch.float32, (T, H, 512))
+    _dev("lse", lse, torch.float32, (T, H))
+    if row != 576 or DQ not in (512, 576):
+        raise ValueError("kv rows must be 576 wide and q 512 (NoPE) or 576 (RoPE) wide")
+    d = mla_desc(q, kv, idx, softmax_scale, num_splits)
+    _check(_lib.dsa_sparse_mla_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(q_seq),
+                                              _ptr(idx), _ptr(length), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
 
 
 def dsa_sparse_mla_prefill(q, kv, kv_scale, q_seq, idx, length, out, lse=None, softmax_scale=None, ws=None,

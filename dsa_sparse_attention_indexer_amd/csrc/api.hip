@@ -5,6 +5,7 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <mutex>
 #include <string>
 
 namespace {
@@ -257,6 +258,11 @@ int auto_splits(const dsa_mla_desc_t* d, bool decode) {
 }
 
 void split_geometry(const dsa_mla_desc_t* d, bool decode, int* splits, int* per_split) {
+  if (d->topk < 1 || d->num_splits < 0) {   // an invalid descriptor (rejected by the caller's checks)
+    *splits = 1;
+    *per_split = 32;
+    return;
+  }
   int s = auto_splits(d, decode);
   int per = (d->topk + s - 1) / s;
   per = (per + 31) / 32 * 32;
@@ -336,6 +342,71 @@ dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* d, const void* q, cons
                                     const int32_t* q_seq, const int32_t* idx, const int32_t* len, float* out,
                                     float* lse, void* ws, size_t ws_bytes, void* stream) {
   return mla_call("dsa_sparse_mla_prefill", false, d, q, kv, kv_scale, q_seq, idx, len, out, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- sparse MLA decode without allocation ----------------------------------------------------
+
+// Split partials and statistics of dsa_sparse_mla_decode_noalloc, one copy per GPU for the life of
+// the process.  In host code this name is a host-side stand-in, not device memory: the device
+// address is looked up once per device with hipGetSymbolAddress, and only that address is handed
+// to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on its first use there).
+hipError_t scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_sparse_mla_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+dsa_status_t dsa_sparse_mla_decode_noalloc(const dsa_mla_desc_t* d, const void* q, const void* kv,
+                                           const float* kv_scale, const int32_t* q_seq, const int32_t* idx,
+                                           const int32_t* len, float* out, float* lse, void* stream) {
+  const char* fn = "dsa_sparse_mla_decode_noalloc";
+  Checker ck;
+  if (!d) { ck.need(false, "desc is NULL"); return ck.finish(fn); }
+  const size_t need = d->num_q > 0 ? mla_ws_bytes(d, true) : 0;
+  if (need > kNoAllocScratchBytes) {
+    ck.fail(false, "needs %zu bytes of split partials, above the %zu bytes this entry point holds per GPU "
+            "(use fewer queries or splits, or dsa_sparse_mla_decode with a workspace)", need, kNoAllocScratchBytes);
+    return ck.finish(fn);
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_on_current_device(&ws);
+    if (e != hipSuccess) {
+      g_err = std::string(fn) + ": device address of the scratch buffer: " + hipGetErrorString(e);
+      return DSA_ERR_HIP;
+    }
+  }
+  return mla_call(fn, true, d, q, kv, kv_scale, q_seq, idx, len, out, lse, ws, need > 0 ? kNoAllocScratchBytes : 0,
+                  stream);
 }
 
 }  // extern "C"

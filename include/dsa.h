@@ -250,6 +250,22 @@ dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* desc, const void* q, c
                                     const int32_t* len, float* out, float* lse,
                                     void* ws, size_t ws_bytes, void* stream);
 
+/* Sparse MLA decode that allocates nothing, for callers that cannot allocate device memory or
+ * size a workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same computation, kernels and results as dsa_sparse_mla_decode, with the split
+ * partials kept in a scratch buffer the library holds on each GPU for the life of the process
+ * (dsa_sparse_mla_noalloc_max_bytes() bytes, 64 MiB; it is looked up on a device's first call).
+ * A call whose partials need more (dsa_sparse_mla_workspace_size(desc) above that; about 4 * 514 *
+ * num_heads bytes per query and split, e.g. 256 query-splits of 64 heads = 33.7 MB) returns
+ * DSA_ERR_UNSUPPORTED before launching anything.  Every call on a GPU shares that GPU's buffer:
+ * calls that overlap in time on one GPU (other streams, other threads) race and give undefined
+ * results; calls in stream order do not.  The buffer is fully rewritten before it is read, so no
+ * call depends on what an earlier one left in it.  No hipMalloc, hipFree or other allocation. */
+size_t dsa_sparse_mla_noalloc_max_bytes(void);
+dsa_status_t dsa_sparse_mla_decode_noalloc(const dsa_mla_desc_t* desc, const void* q, const void* kv,
+                                           const float* kv_scale, const int32_t* q_seq, const int32_t* idx,
+                                           const int32_t* len, float* out, float* lse, void* stream);
+
 /* ============================================================================================
  * 0. Cache writers
  * --------------------------------------------------------------------------------------------

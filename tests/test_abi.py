@@ -120,3 +120,20 @@ def test_cache_writers_validate_arguments(dsa):
     zero = dsa.IndexKDesc(0, 6144, 6144, 64, 1e-6, 0)
     assert dsa.lib().dsa_index_k_insert(ctypes.byref(zero), *([None] * 10), 0, None) == dsa.DSA_OK
     assert dsa.lib().dsa_latent_insert(0, 64, None, 576, None, None, None, 0, None, None, None) == dsa.DSA_OK
+
+
+def test_noalloc_mla_rejects_oversized_partials_before_touching_the_gpu(dsa):
+    L = dsa.lib()
+    assert L.dsa_sparse_mla_noalloc_max_bytes() == 64 << 20
+    d = dsa.MlaDesc(16, 64, 512, 64, 16, 4096, 2048, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN, 64, 0.07, 64)
+    st = L.dsa_sparse_mla_decode_noalloc(ctypes.byref(d), None, None, None, None, None, None, None, None, None)
+    msg = L.dsa_last_error().decode()
+    assert st == dsa.DSA_ERR_UNSUPPORTED and "67108864 bytes" in msg, msg
+
+
+def test_mla_rejects_a_zero_topk_without_dividing_by_zero(dsa):
+    L = dsa.lib()
+    d = dsa.MlaDesc(2, 64, 512, 64, 1, 100, 0, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN, 64, 0.07, 0)
+    st = L.dsa_sparse_mla_decode(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None)
+    assert st == dsa.DSA_ERR_ARG and "topk" in L.dsa_last_error().decode()
+    assert L.dsa_sparse_mla_workspace_size(ctypes.byref(d)) == 0
