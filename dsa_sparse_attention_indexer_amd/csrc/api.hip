@@ -248,9 +248,10 @@ namespace {
 int auto_splits(const dsa_mla_desc_t* d, bool decode) {
   if (!decode) return 1;
   if (d->num_splits > 0) return d->num_splits;
-  // Enough workgroups to cover the 256 CUs once; each split keeps >= 32 selected keys.
+  // Enough workgroups to cover the 256 CUs once; each split keeps >= 64 selected keys (one tile of
+  // the fp8 kernel).
   int s = (256 + d->num_q - 1) / (d->num_q > 0 ? d->num_q : 1);
-  const int max_by_keys = (d->topk + 31) / 32;
+  const int max_by_keys = (d->topk + 63) / 64;
   if (s > max_by_keys) s = max_by_keys;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
@@ -265,7 +266,7 @@ void split_geometry(const dsa_mla_desc_t* d, bool decode, int* splits, int* per_
   }
   int s = auto_splits(d, decode);
   int per = (d->topk + s - 1) / s;
-  per = (per + 31) / 32 * 32;
+  per = (per + 63) / 64 * 64;   // whole 64-key tiles per split
   s = (d->topk + per - 1) / per;
   if (s < 1) s = 1;
   *splits = s;
@@ -298,6 +299,8 @@ dsa_status_t mla_call(const char* fn, bool decode, const dsa_mla_desc_t* d, cons
     ck.support(d->q_dtype == DSA_BF16, "the FP8 cache path takes BF16 queries");
     ck.support(d->num_heads >= 16 && d->num_heads <= 64 && d->num_heads % 16 == 0,
                "num_heads must be 16, 32, 48 or 64 on the FP8 path");
+    // the kernel addresses a sequence's latent rows with 32-bit byte offsets
+    ck.support((uint64_t)d->max_ctx * 576 < (uint64_t(1) << 32), "max_ctx must be <= 7456540 on the FP8 path");
   } else {
     ck.support(d->kv_dtype == DSA_F32, "kv_dtype must be F32 or FP8_E4M3FN");
     ck.support(d->q_dtype == DSA_F32, "the F32 cache path takes F32 queries");

@@ -3,20 +3,10 @@
 // and RoPE dim 64, one latent KV head shared by all 64 heads, V = the latent; NoPE layers are
 // the same with zero RoPE dims on the same cache layout).
 //
-// fp8 cache, bf16 query (matrix-core path), one workgroup = 4 waves = up to 64 heads:
-//   * 32-key tiles are gathered by row index straight from HBM into registers (16 bytes per lane,
-//     issued one tile ahead of the compute), dequantised once per workgroup to bf16 (code * scale,
-//     v_cvt_pk_f32_fp8 / v_cvt_pk_bf16_f32, round to nearest even) and stored key-major in LDS.
-//   * wave w owns heads 16w..16w+15.  Its bf16 query stays in registers as the B operand of
-//     v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, keys as M).  The key rows are placed in LDS in an
-//     order that makes the S^T accumulator of each lane hold exactly the 8 consecutive keys that
-//     the P.V step needs in its B operand, so probabilities go from accumulators to MFMA operands
-//     without touching LDS.
-//   * P.V (O^T = V^T P^T) reads its V^T operand from the same key-major tile with
-//     ds_read_b64_tr_b16: a 16-lane group that points lane j at row 4*(j/4)+.., dims 4*(j%4)..+3
-//     gets back, per lane, four consecutive keys of one dim -- the MFMA operand layout.
-//   * online softmax in the log2 domain with fp32 statistics; fp32 accumulation.
-// fp32 cache, fp32 query: the same tiling with fp32 vector FMAs (8 lanes per head).
+// fp8 cache, bf16 query (matrix-core path): see the wave-specialised kernel k_mla_fp8_ws below
+// (8 waves per workgroup: 4 for the logits and softmax, 4 for P.V; fp8 codes converted exactly to
+// bf16 in registers, the fp32 block scales applied in fp32).
+// fp32 cache, fp32 query: 16-key tiles with fp32 vector FMAs (8 lanes per head).
 //
 // Decode splits a query's selection over `splits` workgroups; each writes an unnormalised partial
 // output with its running max and sum, and a combine kernel merges them exactly.
@@ -33,22 +23,14 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 
-constexpr int kThreads = 256;
-constexpr int kTileK = 32;
 constexpr int kRow = 576;                 // latent row: 512 + 64
 constexpr int kLora = 512;
 constexpr int kBlocks = kRow / 64;        // scales per row
-constexpr int kKsStride = kRow + 8;       // bf16 per key-major row (1168 B: rows shift by 4 banks)
 constexpr int kRowsChunk = 2048;          // selection slots staged in LDS at a time (fp8 path)
 constexpr float kLazyLog2 = 8.f;          // the running maximum lags the true one by at most this (log2)
 constexpr float kNoMax = -1.0e30f;        // running maximum before the first valid key (fp8 path)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-// Key kappa (0..31) of a tile lives in key-major LDS row 16*((kappa>>2)&1) + 4*(kappa>>3) + (kappa&3).
-__device__ __forceinline__ int ks_row_of_key(int kappa) {
-  return 16 * ((kappa >> 2) & 1) + 4 * (kappa >> 3) + (kappa & 3);
-}
 
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -94,19 +76,6 @@ __device__ __forceinline__ void write_stats(const MlaLaunch& a, int t, int split
   }
 }
 
-typedef short short4v __attribute__((ext_vector_type(4)));
-
-// 16 fp8 codes times one scale -> 16 bf16 (8 dwords), nearest even.
-__device__ __forceinline__ void dequant16(const u32x4 raw, float s, u32x4& lo, u32x4& hi) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float2v a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[w], false) * s;
-    const float2v b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[w], true) * s;
-    const uint32_t pa = cvt2_bf16(a), pb = cvt2_bf16(b);
-    if (w < 2) { lo[2 * w] = pa; lo[2 * w + 1] = pb; } else { hi[2 * w - 4] = pa; hi[2 * w - 3] = pb; }
-  }
-}
-
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits 3:0 and
@@ -117,25 +86,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Gathers straight into LDS: lane l's 16 (4) bytes from global address g land at LDS byte
-// lds + 16*l (4*l); lds must be the same in every lane.  Written as inline assembly so that the
-// compiler does not track these loads as LDS writes -- it would otherwise make later LDS accesses
-// wait for every gather in flight.  The callers wait for them explicitly (wait_vmcnt) before a
-// barrier, and vmcnt counts them like any other vector-memory load.
-__device__ __forceinline__ void gather16_to_lds(const void* g, void* lds) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
-}
-__device__ __forceinline__ void gather4_to_lds(const void* g, void* lds) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
-}
-
-// Maximum over lanes l and l ^ 16 (ds_swizzle swap of 16-lane halves) and over l and l ^ 32
-// (v_permlane32_swap), without the address arithmetic of a bpermute shuffle.
-__device__ __forceinline__ float max_xor16(float x) {
-  return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));
-}
+// Maximum over lanes l and l ^ 32 (v_permlane32_swap), without the address arithmetic of a bpermute
+// shuffle.
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
                                                   false, false);
@@ -164,349 +116,397 @@ __device__ __forceinline__ bool xcd_query_map(int inner, int T, int* t, int* j) 
 }
 inline unsigned xcd_grid(int inner, int T) { return (unsigned)(8 * inner * ((T + 7) / 8)); }
 
-constexpr int kMlaThreads = 512;   // fp8 path: 8 waves = 4 head groups x 2 halves
-constexpr int kSlots = 3;          // raw tiles in LDS: the next one to dequantise plus two in flight
+constexpr int kMlaThreads = 512;   // fp8 path: 8 waves
 
 template <int V>
 struct IntC {
   static constexpr int value = V;
 };
 
+// ---------------------------------------------------------------------------------------------
+// fp8 cache, bf16 query: wave-specialised kernel on v_mfma_f32_32x32x16_bf16
+//
+// One workgroup of 8 waves per (query, split); 64-key tiles.  The fp8 rows and their scales are
+// gathered into a ring of three LDS slots and never dequantised as a whole: every fp8 code is
+// converted exactly to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8 with unit scale), and the
+// per-(key, 64-element block) fp32 scales are applied in fp32:
+//   * QK waves 0..3, wave = (head group hg of 32 heads, key half kg of 32 keys): S^T[32 keys x 32
+//     heads] block by block -- for each 64-dim block an accumulator of 4 MFMAs (K codes as A, the
+//     bf16 query as B, held in registers), then S^T += scale(key, block) * block accumulator.
+//     The logits are exact up to fp32 accumulation.  Online softmax (lazy rescale) per head with the
+//     other key half's maximum exchanged through LDS; P (fp32) goes to LDS in the lane order of the
+//     PV operand.
+//   * PV waves 4..7, wave = 128 output dims of all 64 heads: O^T[128 dims x 64 heads] +=
+//     V^T . (P scale(key, block))^T, V^T read from the fp8 slot with ds_read_b64_tr_b8 (8 keys of one
+//     dim per lane) and converted exactly; the V scales are folded into the bf16 P operand.
+//     The PV waves also issue the gathers.
+// Each SIMD holds one QK and one PV wave, so one wave's matrix work overlaps the other's vector
+// work.  Tile tau: phase A -- QK(tau) || PV(tau-1) and the gathers of tile tau+2; phase B --
+// softmax(tau) || the PV waves read tile tau's V bytes into registers (its slot is then free).
+// Within a 32-key half, tile key kappa sits in LDS row lrow(kappa) (bits 2 and 3 swapped), so that
+// the rows behind a QK lane's accumulator run in key order and the P values of a lane are the 8
+// consecutive keys the PV operand needs.
+// ---------------------------------------------------------------------------------------------
+
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2* lds_i2p;
+
+constexpr int kT2 = 64;        // keys per tile
+constexpr int kS2 = 3;         // raw tiles in LDS
+
+__device__ __forceinline__ int perm23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+__device__ __forceinline__ int lrow(int k) { return (k & ~31) | perm23(k & 31); }   // an involution
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words over `bytes` bytes from `base` (loads past the end read zero).
+__device__ __forceinline__ i32x4 buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32) & 0xFFFF),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+// Gathers through a buffer descriptor straight into LDS: lane l's 16 (4) bytes at byte voff of the
+// buffer land at LDS byte lds + 16*l (4*l).  One 32-bit offset per lane; waited for with vmcnt.
+__device__ __forceinline__ void bgather16(i32x4 rs, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void bgather4(i32x4 rs, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(lds) : "memory", "m0");
+}
+
+// Slot layout.  Codes: [row group i = R/16][64-byte segment j][16 rows][4 chunks of 16 bytes], the
+// chunks of a segment rotated by row (swz) so that 16 consecutive rows reading the same chunk, and
+// the 8 rows of a transposing read, hit different banks.  PV wave pw gathers row group pw: one
+// 64-lane load per segment, four lanes per row, every load of a lane from the same cache row.
+// Scales: [row group][block][16 keys] (by tile key, not LDS row).
+__device__ __forceinline__ int swz(int m16) { return ((m16 >> 1) + (m16 >> 3)) & 3; }
+
 template <int ROPE>
-struct MlaFp8 {
-  static constexpr int DQ = kLora + ROPE;               // bytes of a latent row that are used
-  static constexpr int KSTEPS = DQ / 32;
-  static constexpr int CHUNKS = DQ / 16;                // 16-byte chunks per used row
-  static constexpr int NSC = DQ / 64;                   // scales per used row
-  static constexpr int WROWS = kTileK / 8;              // rows of a tile each wave gathers
-  static constexpr int WCH = WROWS * CHUNKS;            // chunks per wave and tile
-  static constexpr int WCHI = (WCH + 63) / 64;          // chunk loads per wave and tile
-  static constexpr int WSC = WROWS * NSC;               // scale words per wave and tile
-  static constexpr int WSCI = (WSC + 63) / 64;          // scale loads per wave and tile
-  static constexpr int LPT = WCHI + WSCI;               // LDS-direct loads per wave and tile
-  static constexpr int NCH = kTileK * CHUNKS;
-  static constexpr int FULL = NCH / kMlaThreads;        // whole chunks each thread dequantises
-  static constexpr int REM = NCH - FULL * kMlaThreads;  // the rest, split into 4-byte quarters
-  static_assert(4 * REM <= kMlaThreads, "at most one quarter chunk per thread");
-  static constexpr int ODIM = kLora / 2;                // output dims per wave
+struct M2 {
+  static constexpr int DQ = kLora + ROPE;        // used bytes of a latent row
+  static constexpr int NB = DQ / 64;             // scale blocks used
+  static constexpr int NJ = DQ / 64;             // 64-byte segments per row
+  static constexpr int CODES = kT2 * DQ;
+  static constexpr int SLOT = CODES + NB * kT2 * 4;
+  static constexpr int NP = DQ / 32;             // 32-dim pairs of K-steps
+  static constexpr int NSC = (NB + 3) / 4;       // scale loads per PV wave and tile
+  static constexpr int LPT = NJ + NSC;           // LDS-direct loads per PV wave and tile
+  // byte offset of 16-byte chunk c of LDS row R
+  static __device__ __forceinline__ int pos(int R, int c) {
+    return (((R >> 4) * NJ + (c >> 2)) * 16 + (R & 15)) * 64 + 16 * ((c & 3) ^ swz(R & 15));
+  }
 };
 
-// Wave w = 4 * half + hg owns heads 16hg..16hg+15.  For each 32-key tile it computes the partial
-// S^T over its half of the query dims (K-steps KH*half..KH*half+KH-1) for all 32 keys, adds the
-// other half's partial through LDS, and accumulates O^T for output dims 256*half..256*half+255.
-// Per lane: the query slice (KH operands) and 64 accumulator registers.
-//
-// Tiles are software-pipelined over two bf16 buffers (ks0, ks1) and kSlots raw slots, two
-// barriers per tile tau:
-//   B0  ks[tau & 1] holds tile tau, tile tau+1's gathers are in their slot, the other bf16 buffer
-//       and tile tau's slot are free;
-//   phase 1: gathers of tile tau+3 into tile tau's slot; the partial QK^T of tile tau on the
-//       matrix cores while the same waves dequantise tile tau+1 into the other buffer (independent
-//       instruction streams the compiler interleaves); partial scores to LDS;
-//   B1  both halves' partial scores are in LDS;
-//   phase 2: online softmax and PV of tile tau.
+// 8 fp8 codes (two dwords) -> 8 bf16, exact
+__device__ __forceinline__ bf16x8 codes_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int ROPE>
+struct Mla2Smem {
+  using C = M2<ROPE>;
+  uint8_t slot[kS2][C::SLOT];          // codes [64 LDS rows][RS], then scales [NB][64 keys]
+  float pbuf[2][4][64][8];             // P of the current tile: [head tile][K-step][lane][8 keys]
+  float scl[4][2][64];                 // per PV wave: V scales of its two blocks, current tile
+  int rows[kRowsChunk];                // cache row of every slot of the chunk, -1 if none
+  float xmax[2][2][32];                // QK: per (head group, key half) tile maxima
+  float alpha[64];                     // rescale factor of the tile, per head
+  float lsum[2][2][32];                // epilogue: softmax sums per (head group, key half)
+  int flags[2];                        // per head group: the tile moved the running maximum
+};
+
 template <int ROPE>
 __global__ void __launch_bounds__(kMlaThreads)
-k_mla_fp8(MlaLaunch a) {
+k_mla_fp8_ws(MlaLaunch a) {
+  using C = M2<ROPE>;
   int t, split;
   if (!xcd_query_map(a.splits, a.T, &t, &split)) return;
-  using C = MlaFp8<ROPE>;
-  constexpr int DQ = C::DQ, KSTEPS = C::KSTEPS, CHUNKS = C::CHUNKS, NSC = C::NSC, WROWS = C::WROWS;
-  constexpr int LPT = C::LPT;
-  constexpr int MD = C::ODIM / 16;                      // 16-dim output tiles per wave
-  // Raw fp8 rows and scales of a tile, gathered straight into LDS.
-  struct Slot {
-    uint8_t raw[kTileK * DQ];
-    float sc[kTileK * NSC];
-  };
-  typedef uint16_t KsTile[kTileK][kKsStride];
-  __shared__ __attribute__((aligned(16))) Slot sl[kSlots];
-  __shared__ __attribute__((aligned(16))) KsTile ks0, ks1;
-  __shared__ __attribute__((aligned(16))) float4v xz[2][4][2][64];   // partial scores swapped between halves
-  __shared__ int rows[kRowsChunk];                      // row of every slot of the current chunk, -1 if none
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hg = wave & 3, half = wave >> 2;
-  const int c = lane & 15, g = lane >> 4;
+  __shared__ __attribute__((aligned(16))) Mla2Smem<ROPE> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slot0 = split * a.per_split;
-  const bool active = 16 * hg < a.H;
-  const int head = 16 * hg + c;
-  const float zscale = a.softmax_scale * kLog2e;
   const int32_t* irow = a.idx + (size_t)t * a.topk;
-
-  // The first chunk's row indices and the query are loaded before the selection length and the
-  // sequence are known, so that all of these loads are in flight together.
-  const int slot_end = min(slot0 + a.per_split, a.topk);   // this split's slots before the length cut
-  constexpr int RPT = kRowsChunk / kMlaThreads;
+  const int slot_end = min(slot0 + a.per_split, a.topk);
+  // The row indices are loaded and staged by the PV waves alone, so that the first gathers (which
+  // need them) do not wait behind the QK waves' query loads.
+  constexpr int kPvThreads = kMlaThreads / 2;
+  constexpr int RPT = kRowsChunk / kPvThreads;
+  const int ptid = tid - kPvThreads;                     // PV thread index (PV waves only)
   int rv[RPT];
   auto load_rows = [&](int cb) {   // unconditional loads (slot clamped into the row): all in flight together
 #pragma unroll
-    for (int u = 0; u < RPT; ++u) rv[u] = irow[min(cb + tid + kMlaThreads * u, a.topk - 1)];
+    for (int u = 0; u < RPT; ++u) rv[u] = irow[min(cb + ptid + kPvThreads * u, a.topk - 1)];
 #pragma unroll
-    for (int u = 0; u < RPT; ++u) rv[u] = cb + tid + kMlaThreads * u < slot_end ? rv[u] : -1;
+    for (int u = 0; u < RPT; ++u) rv[u] = cb + ptid + kPvThreads * u < slot_end ? rv[u] : -1;
   };
-  load_rows(slot0);
-  constexpr int KH = KSTEPS / 2;                        // K-steps per half
-  static_assert(KSTEPS % 2 == 0, "query dims split in two halves");
-  bf16x8 qreg[KH];                                      // zero in waves without heads
-#pragma unroll
-  for (int s = 0; s < KH; ++s) qreg[s] = bf16x8{};
-  if (active) {
-    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + head) * DQ + 32 * KH * half;
-#pragma unroll
-    for (int s = 0; s < KH; ++s)
-      qreg[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 32 * s + 8 * g));
-  }
+  const int nht = (a.H + 31) / 32;                       // head tiles of 32
   const int b = clampi(a.q_seq[t], 0, a.B - 1);
   const int L = a.len ? clampi(a.len[t], 0, a.topk) : a.topk;
   const int slot1 = min(L, slot0 + a.per_split);
   const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(a.kv) + (size_t)b * a.max_ctx * kRow;
   const float* scseq = a.kv_scale + (size_t)b * a.max_ctx * kBlocks;
+  const float zscale = a.softmax_scale * kLog2e;
 
-  float m_run = kNoMax, l_run = 0.f;
-  float4v oacc[MD];
-#pragma unroll
-  for (int md = 0; md < MD; ++md) oacc[md] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  // Wave w gathers rows WROWS*w.. of tile tau: their chunks and scales are contiguous in the slot,
-  // and lane l of a load lands at 16*l (4*l) bytes from the load's base.
-  auto issue = [&](Slot& s, int tau) {
-    const int* tr = rows + kTileK * tau + WROWS * wave;
-    // every row index first: the gathers are opaque to the compiler, which keeps LDS reads after them
-    int rc[C::WCHI], rs[C::WSCI];
-#pragma unroll
-    for (int j = 0; j < C::WCHI; ++j) {
-      const int i = 64 * j + lane;
-      rc[j] = max(tr[i < C::WCH ? i / CHUNKS : 0], 0);
-    }
-#pragma unroll
-    for (int j = 0; j < C::WSCI; ++j) {
-      const int i = 64 * j + lane;
-      rs[j] = max(tr[i < C::WSC ? i / NSC : 0], 0);
-    }
-#pragma unroll
-    for (int j = 0; j < C::WCHI; ++j) {
-      const int i = 64 * j + lane;
-      if (i < C::WCH)
-        gather16_to_lds(kvseq + (size_t)rc[j] * kRow + 16 * (i % CHUNKS), s.raw + WROWS * wave * DQ + 1024 * j);
-    }
-#pragma unroll
-    for (int j = 0; j < C::WSCI; ++j) {
-      const int i = 64 * j + lane;
-      if (i < C::WSC)
-        gather4_to_lds(scseq + (size_t)rs[j] * kBlocks + i % NSC, s.sc + WROWS * wave * NSC + 64 * j);
-    }
-  };
-
-  // fp8 tile -> bf16 key-major tile (code * scale, nearest even); the same share for every thread:
-  // FULL 16-byte chunks, then one 4-byte quarter of the rest.
-  auto dequant = [&](const Slot& s, KsTile& ks) {
-#pragma unroll
-    for (int m = 0; m < C::FULL; ++m) {
-      const int ch = tid + kMlaThreads * m;
-      const int r = ch / CHUNKS, cc = ch % CHUNKS;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(s.raw + 16 * ch);
-      u32x4 lo, hi;
-      dequant16(v, s.sc[r * NSC + (cc >> 2)], lo, hi);
-      u32x4* dst = reinterpret_cast<u32x4*>(&ks[ks_row_of_key(r)][16 * cc]);
-      dst[0] = lo;
-      dst[1] = hi;
-    }
-    if (C::REM > 0 && tid < 4 * C::REM) {
-      const int ch = C::FULL * kMlaThreads + (tid >> 2), qd = tid & 3;
-      const int r = ch / CHUNKS, cc = ch % CHUNKS;
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(s.raw + 16 * ch + 4 * qd);
-      const float sc = s.sc[r * NSC + (cc >> 2)];
-      const float2v lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false) * sc;
-      const float2v hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true) * sc;
-      *reinterpret_cast<uint2*>(&ks[ks_row_of_key(r)][16 * cc + 4 * qd]) = make_uint2(cvt2_bf16(lo), cvt2_bf16(hi));
-    }
-  };
-
-  // partial S^T over this half's query dims: lane (c, g) gets keys 8g + 4mb + i of head c
-  auto qk = [&](const KsTile& ks, float4v* sacc) {
-    constexpr int KB = 3;   // K operands read a batch ahead of their MFMAs
-#pragma unroll
-    for (int s0 = 0; s0 < KH; s0 += KB) {
-      bf16x8 kop[2][KB];
-#pragma unroll
-      for (int j = 0; j < KB; ++j)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          if (s0 + j < KH)
-            kop[mb][j] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(&ks[16 * mb + c][32 * (KH * half + s0 + j) + 8 * g]));
-#pragma unroll
-      for (int j = 0; j < KB; ++j)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          if (s0 + j < KH) sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[mb][j], qreg[s0 + j], sacc[mb], 0, 0, 0);
-    }
-  };
-
-  // online softmax of tile tau's scores and O^T += V^T P^T
-  auto attend = [&](const KsTile& ks, const float4v* sacc, uint32_t vmask) {
-    float z[8];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const float4v other = xz[half ^ 1][hg][mb][lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float dot = sacc[mb][i] + other[i];   // the same sum in both halves (addition commutes)
-        z[4 * mb + i] = ((vmask >> (4 * mb + i)) & 1u) ? dot * zscale : -INFINITY;
-      }
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, z[e]);
-    tmax = max_xor16(tmax);
-    tmax = max_xor32(tmax);
-    // Lazy rescaling: the reference maximum m_run only moves when the tile's maximum exceeds it by
-    // more than 2^kLazyLog2 (or on the first keys), so probabilities stay below 2^kLazyLog2 and the
-    // accumulators are rescaled rarely instead of on every tile.  O and l share m_run, so the
-    // normalised result is the same softmax.  Before the first valid key m_run is kNoMax (finite),
-    // so every exponent below is a plain hardware exp2 of a non-NaN argument.
-    const bool bump = tmax > m_run + kLazyLog2;
-    if (__ballot(bump)) {
-      const float m_new = bump ? tmax : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run is kNoMax
-      l_run *= alpha;
-      if (__ballot(bump && m_run != kNoMax)) {   // the accumulators hold keys to rescale
-#pragma unroll
-        for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
-      }
-      m_run = m_new;
-    }
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(z[e] - m_run);
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) psum += p[e];
-    l_run += psum;
-    u32x4 pk;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pk[e] = cvt2_bf16(float2v{p[2 * e], p[2 * e + 1]});
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, pk);
-    // V^T operand rows: LDS rows 16h + 4g + j/4 hold keys 8g + 4h + j/4
-    const int trow = 4 * g + (c >> 2), tcol = 4 * (c & 3) + C::ODIM * half;
-    typedef __attribute__((address_space(3))) short4v* lds_s4p;
-    constexpr int VB = 4;   // V^T operands read a batch ahead of their MFMAs
-#pragma unroll
-    for (int md0 = 0; md0 < MD; md0 += VB) {
-      short8v vv[VB];
-#pragma unroll
-      for (int j = 0; j < VB; ++j) {
-        const short4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(&ks[trow][16 * (md0 + j) + tcol]));
-        const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(&ks[16 + trow][16 * (md0 + j) + tcol]));
-        vv[j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-      for (int j = 0; j < VB; ++j)
-        oacc[md0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv[j]), pop, oacc[md0 + j], 0, 0, 0);
-    }
-  };
-
-  // One tile; KBC selects the bf16 buffer of tile tau (the other one receives tile tau+1), st is
-  // tile tau's slot.
-  auto step = [&](auto KBC, int tau, int ntiles, int st) {
-    KsTile& kcur = decltype(KBC)::value ? ks1 : ks0;
-    KsTile& knext = decltype(KBC)::value ? ks0 : ks1;
-    if (tau + 2 < ntiles) wait_vmcnt<LPT>();   // tile tau+1's gathers are done, tile tau+2's may not be
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (tau + 3 < ntiles) issue(sl[st], tau + 3);
-    // validity of this lane's 8 keys (8g + e) of tile tau
-    uint32_t vmask = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vmask |= (rows[kTileK * tau + 8 * g + e] >= 0 ? 1u : 0u) << e;
-    float4v sacc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
-    qk(kcur, sacc);
-    // the next tile (after the last one: stale slot contents into a buffer nobody reads)
-    dequant(sl[st == kSlots - 1 ? 0 : st + 1], knext);
-    xz[half][hg][0][lane] = sacc[0];
-    xz[half][hg][1][lane] = sacc[1];
-    lds_barrier();                         // both halves' partial scores are in LDS
-    if (active) attend(kcur, sacc, vmask);
-  };
-
-  for (int cb = slot0; cb < slot1; cb += kRowsChunk) {   // chunks of the split's slots (one, normally)
-    if (cb != slot0) load_rows(cb);
-    const int nslot = min(kRowsChunk, slot1 - cb);
-    const int ntiles = (nslot + kTileK - 1) / kTileK;
-    __syncthreads();                       // the previous chunk is completely consumed
+  // the rows of chunk cb into LDS (PV waves; callers hold a barrier before and after)
+  auto store_rows = [&](int nslot, int ntiles) {
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
-      const int i = tid + kMlaThreads * u;
-      if (i < ntiles * kTileK) rows[i] = (i < nslot && rv[u] >= 0 && rv[u] < a.max_ctx) ? rv[u] : -1;
+      const int i = ptid + kPvThreads * u;
+      if (i < ntiles * kT2) sm.rows[i] = (i < nslot && rv[u] >= 0 && rv[u] < a.max_ctx) ? rv[u] : -1;
     }
-    __syncthreads();
-    wait_vmcnt<0>();   // the query loads are done (tells the compiler too: no waits for them below)
-    issue(sl[0], 0);
-    if (1 < ntiles) issue(sl[1], 1);
-    if (2 < ntiles) issue(sl[2], 2);
-    if (ntiles > 2) wait_vmcnt<2 * LPT>();
-    else if (ntiles > 1) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
-    lds_barrier();                         // tile 0 is in its slot
-    dequant(sl[0], ks0);
-    int st = 0;
-    for (int tau = 0; tau < ntiles; tau += 2) {
-      step(IntC<0>(), tau, ntiles, st);
-      st = st == kSlots - 1 ? 0 : st + 1;
-      if (tau + 1 < ntiles) {
-        step(IntC<1>(), tau + 1, ntiles, st);
-        st = st == kSlots - 1 ? 0 : st + 1;
+  };
+
+  if (wave < 4) {
+    // ======================================= QK waves =======================================
+    const int hg = wave & 1, kg = wave >> 1;
+    const int m = lane & 31, h = lane >> 5;
+    const int head = 32 * hg + m;
+    const bool active = 32 * hg < a.H;
+    bf16x8 qreg[2 * C::NP];                              // K-step (p, e): dims 32p + 16h + 8e + 0..7
+#pragma unroll
+    for (int s = 0; s < 2 * C::NP; ++s) qreg[s] = bf16x8{};
+    if (active && head < a.H) {
+      const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + head) * C::DQ + 16 * h;
+#pragma unroll
+      for (int p = 0; p < C::NP; ++p) {
+        qreg[2 * p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 32 * p));
+        qreg[2 * p + 1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 32 * p + 8));
       }
     }
-  }
-  if (!active) return;
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  // oacc[md][i] = O^T[dim ODIM*half + 16md + 4g + i][head c]
-  if (a.splits > 1 && bf16_partials(a)) {
-    // bf16 split partials leave through LDS so that every store covers whole lines: this wave's
-    // 16 heads x 256 dims in two rounds of 8 heads, each head row then stored as 32 lanes x 16
-    // contiguous bytes, non-temporally (the partials stream out during the kernel instead of being
-    // written back from L2 when it ends).  The raw slots are free: every wave has passed the last
-    // tile's second barrier, after which no gather or dequantisation touches them.  No branch
-    // depends on the lane: in each round the lanes of the other round's heads write a discard row
-    // (row 8), and a wave barrier keeps the round's writes before its reads.
-    constexpr int kStageRow = 2 * C::ODIM + 16;            // bytes per staged head row (padded)
-    constexpr int kStageWords = kStageRow / 4;
-    static_assert(8 * 9 * kStageRow <= (int)sizeof(sl), "staging space");
-    uint32_t* stage = static_cast<uint32_t*>(__builtin_assume_aligned(
-        reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(&sl[0]) + wave * 9 * kStageRow), 16));
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const size_t hstride = (size_t)a.splits * a.kv_lora;   // bf16 between consecutive heads' partials
-    uint16_t* dst0 = reinterpret_cast<uint16_t*>(a.ws) + (((size_t)t * a.H + 16 * hg) * a.splits + split) * a.kv_lora +
-                     C::ODIM * half;
+    float m_run = kNoMax, l_run = 0.f;
+    for (int cb = slot0; cb < slot1; cb += kRowsChunk) {
+      const int nslot = min(kRowsChunk, slot1 - cb);
+      const int ntiles = (nslot + kT2 - 1) / kT2;
+      lds_barrier();                                     // R: the chunk's rows are in LDS
+      for (int tau = 0; tau < ntiles; ++tau) {
+        lds_barrier();                                   // A: tile tau is in its slot
+        const uint8_t* codes = sm.slot[tau % kS2];
+        const float* scs = reinterpret_cast<const float*>(codes + C::CODES);
+        // validity of this lane's 16 keys: 32kg + 16(r/8) + 8h + r%8
+        const uint64_t vmask = __ballot(sm.rows[kT2 * tau + lane] >= 0);
+        const uint32_t vbits = (uint32_t)((vmask >> (32 * kg + 8 * h)) & 0xFFull) |
+                               ((uint32_t)((vmask >> (32 * kg + 16 + 8 * h)) & 0xFFull) << 8);
+        float16v S = {};
+        if (active) {
 #pragma unroll
-    for (int ph = 0; ph < 2; ++ph) {
-      const int wrow = (c >> 3) == ph ? (c & 7) : 8;
+          for (int bl = 0; bl < C::NB; ++bl) {
+            float16v ab = {};
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        uint32_t* w = stage + wrow * kStageWords + (16 * md + 4 * g) / 2;
-        w[0] = cvt2_bf16(float2v{oacc[md][0] * inv, oacc[md][1] * inv});
-        w[1] = cvt2_bf16(float2v{oacc[md][2] * inv, oacc[md][3] * inv});
+            for (int pp = 0; pp < 2; ++pp) {
+              const int p = 2 * bl + pp;                 // dims 32p + 16h .. + 15: chunk 2p + h
+              const u32x4 raw = *reinterpret_cast<const u32x4*>(codes + C::pos(32 * kg + m, 2 * p + h));
+              ab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(codes_bf16(raw[0], raw[1]), qreg[2 * p], ab, 0, 0, 0);
+              ab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(codes_bf16(raw[2], raw[3]), qreg[2 * p + 1], ab, 0, 0, 0);
+            }
+            const float* sb0 = scs + ((2 * kg) * C::NB + bl) * 16 + 8 * h;       // keys 32kg + 8h + 0..7
+            const float* sb1 = scs + ((2 * kg + 1) * C::NB + bl) * 16 + 8 * h;   // keys 32kg + 16 + 8h + 0..7
+            const float4 s0 = *reinterpret_cast<const float4*>(sb0);
+            const float4 s1 = *reinterpret_cast<const float4*>(sb0 + 4);
+            const float4 s2 = *reinterpret_cast<const float4*>(sb1);
+            const float4 s3 = *reinterpret_cast<const float4*>(sb1 + 4);
+            const float sv[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                                  s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] = fmaf(sv[r], ab[r], S[r]);
+          }
+        }
+        float z[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          z[r] = ((vbits >> r) & 1u) ? S[r] * zscale : -INFINITY;
+          tmax = fmaxf(tmax, z[r]);
+        }
+        tmax = max_xor32(tmax);                          // this key half's 32 keys, per head
+        if (lane < 32) sm.xmax[hg][kg][m] = tmax;
+        lds_barrier();                                   // B: both key halves' maxima are in LDS
+        if (active) {
+          const float t64 = fmaxf(tmax, sm.xmax[hg][kg ^ 1][m]);
+          // lazy rescale: the reference maximum m_run only moves when the tile's maximum exceeds it
+          // by more than 2^kLazyLog2 (or on the first keys), so probabilities stay below 2^kLazyLog2
+          // and the accumulators are rescaled rarely; O and l share m_run, so the normalised result
+          // is the same softmax.  Both key halves take the same decision from the same maxima.
+          const bool bump = t64 > m_run + kLazyLog2;
+          const uint64_t any = __ballot(bump);
+          if (any) {
+            const float m_new = bump ? t64 : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
+            if (kg == 0 && lane < 32) sm.alpha[head] = alpha;
+          }
+          if (kg == 0 && lane == 0) sm.flags[hg] = any != 0;
+          float p[16];
+          float psum = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(z[r] - m_run);
+            psum += p[r];
+          }
+          l_run += psum;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float* dst = &sm.pbuf[hg][2 * kg + j][lane][0];
+            *reinterpret_cast<float4*>(dst) = make_float4(p[8 * j], p[8 * j + 1], p[8 * j + 2], p[8 * j + 3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(p[8 * j + 4], p[8 * j + 5], p[8 * j + 6], p[8 * j + 7]);
+          }
+        }
       }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int row = 2 * k + (lane >> 5), ch = lane & 31;
-        const uint32_t* r = stage + row * kStageWords + 4 * ch;
-        const u32x4 v = {r[0], r[1], r[2], r[3]};
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst0 + (size_t)(8 * ph + row) * hstride + 8 * ch));
-      }
-      __builtin_amdgcn_wave_barrier();
+      lds_barrier();                                     // F: the chunk's last P is in LDS
+    }
+    // epilogue: softmax sums per head (both lane halves, then both key halves)
+    const float l_half = l_run + __shfl_xor(l_run, 32);
+    if (lane < 32) sm.lsum[hg][kg][m] = l_half;
+    lds_barrier();                                       // G
+    if (active && kg == 0 && lane < 32 && head < a.H) {
+      const float l_tot = sm.lsum[hg][0][m] + sm.lsum[hg][1][m];
+      write_stats(a, t, split, head, m_run, l_tot);
     }
   } else {
+    // ======================================= PV waves =======================================
+    const int pw = wave - 4;                             // output dims 128pw .. 128pw + 127
+    const int c16 = lane & 15, g16 = lane >> 4, h = lane >> 5;
+    float16v O[2][4];
 #pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      float o[4] = {oacc[md][0], oacc[md][1], oacc[md][2], oacc[md][3]};
-      write_partial_or_final(a, t, split, head, m_run, l_tot, o, C::ODIM * half + 16 * md + 4 * g, 4);
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) O[ht][dt] = float16v{};
+    i32x2 vraw[4][4];                                    // V^T bytes of the tile: [K-step J][dim tile]
+
+    // This wave's gathers of tile tau: LDS rows 16pw .. 16pw + 15, one load per 64-byte segment
+    // (lane: row 16pw + lane/4, chunk lane%4 of the segment, rotated by swz) and the scales of the
+    // same 16 keys.  The latent rows and scales of the query's sequence are addressed through
+    // buffer descriptors (32-bit offsets: the host checks that a sequence's rows span less than
+    // 4 GiB).  Both row indices are read before the first load goes out.
+    const i32x4 kv_rs = buffer_words(kvseq, (uint32_t)((uint64_t)a.max_ctx * kRow));
+    const i32x4 sc_rs = buffer_words(scseq, (uint32_t)((uint64_t)a.max_ctx * kBlocks * 4));
+    const uint32_t lds_slots = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)&sm.slot[0][0]);
+    const int g_row = lrow(16 * pw + (lane >> 2));           // tile key in LDS row 16pw + lane/4
+    const int g_chunk = (lane & 3) ^ swz(lane >> 2);          // its chunk within each segment
+    auto issue = [&](int tau) {
+      const uint32_t base = lds_slots + (uint32_t)(C::SLOT * (tau % kS2));
+      const int* tr = sm.rows + kT2 * tau;
+      const uint32_t rc = (uint32_t)max(tr[g_row], 0);
+      const uint32_t rs = (uint32_t)max(tr[16 * pw + (lane & 15)], 0);
+      const uint32_t voff = rc * kRow + 16 * g_chunk;
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) bgather16(kv_rs, voff + 64 * j, base + 1024 * (pw * C::NJ + j));
+#pragma unroll
+      for (int k = 0; k < C::NSC; ++k) {
+        const int bl = 4 * k + (lane >> 4);
+        if (bl < C::NB) bgather4(sc_rs, (rs * kBlocks + bl) * 4, base + C::CODES + 64 * (pw * C::NB + 4 * k));
+      }
+    };
+    // PV of the tile whose V bytes are in vraw (its P, scales and rescale factors in LDS)
+    auto pv = [&]() {
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        if (ht < nht && sm.flags[ht]) {
+          const float al = sm.alpha[32 * ht + (lane & 31)];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) O[ht][dt] *= al;
+        }
+      }
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const bf16x8 v0 = codes_bf16((uint32_t)vraw[J][2 * bb][0], (uint32_t)vraw[J][2 * bb][1]);
+          const bf16x8 v1 = codes_bf16((uint32_t)vraw[J][2 * bb + 1][0], (uint32_t)vraw[J][2 * bb + 1][1]);
+          const float* sp = &sm.scl[pw][bb][16 * J + 8 * h];
+          const float4 s0 = *reinterpret_cast<const float4*>(sp);
+          const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
+          // both head tiles, branch-free: with at most 32 heads the second one works on P values
+          // nobody wrote and is never stored
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) {
+            const float* pp = &sm.pbuf[ht][J][lane][0];
+            const float4 p0 = *reinterpret_cast<const float4*>(pp);
+            const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
+            u32x4 pk;
+            pk[0] = cvt2_bf16(float2v{p0.x * s0.x, p0.y * s0.y});
+            pk[1] = cvt2_bf16(float2v{p0.z * s0.z, p0.w * s0.w});
+            pk[2] = cvt2_bf16(float2v{p1.x * s1.x, p1.y * s1.y});
+            pk[3] = cvt2_bf16(float2v{p1.z * s1.z, p1.w * s1.w});
+            const bf16x8 pop = __builtin_bit_cast(bf16x8, pk);
+            O[ht][2 * bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pop, O[ht][2 * bb], 0, 0, 0);
+            O[ht][2 * bb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pop, O[ht][2 * bb + 1], 0, 0, 0);
+          }
+        }
+      }
+    };
+    // tile tau's V bytes (8 keys of one dim per lane) and this wave's V scales, out of its slot
+    auto preload = [&](int tau) {
+      const uint8_t* codes = sm.slot[tau % kS2];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const int R = lrow(16 * J + 8 * (g16 >> 1) + (c16 >> 1));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {   // dims 128pw + 32dt + 16(g16&1) + 8(c16&1): chunk 8pw + 2dt + (g16&1)
+          const uint8_t* src = codes + C::pos(R, 8 * pw + 2 * dt + (g16 & 1)) + 8 * (c16 & 1);
+          vraw[J][dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2p)(src));
+        }
+      }
+      const float* scs = reinterpret_cast<const float*>(codes + C::CODES);
+      sm.scl[pw][0][lane] = scs[((lane >> 4) * C::NB + 2 * pw) * 16 + (lane & 15)];
+      sm.scl[pw][1][lane] = scs[((lane >> 4) * C::NB + 2 * pw + 1) * 16 + (lane & 15)];
+    };
+
+    load_rows(slot0);
+    for (int cb = slot0; cb < slot1; cb += kRowsChunk) {
+      if (cb != slot0) load_rows(cb);
+      const int nslot = min(kRowsChunk, slot1 - cb);
+      const int ntiles = (nslot + kT2 - 1) / kT2;
+      store_rows(nslot, ntiles);
+      lds_barrier();                                     // R
+      issue(0);
+      if (1 < ntiles) issue(1);
+      for (int tau = 0; tau < ntiles; ++tau) {
+        // tile tau has landed; tile tau + 1 (issued later) may still be in flight
+        if (tau + 1 < ntiles) wait_vmcnt<C::LPT>();
+        else wait_vmcnt<0>();
+        lds_barrier();                                   // A
+        if (tau >= 1) pv();
+        // into the slot of tile tau - 1 (free: its V bytes were read in the last phase B); after the
+        // PV, whose V registers are then dead
+        if (tau + 2 < ntiles) issue(tau + 2);
+        lds_barrier();                                   // B
+        preload(tau);
+      }
+      lds_barrier();                                     // F: the last tile's P is in LDS
+      if (ntiles > 0) pv();
+    }
+    lds_barrier();                                       // G: the softmax sums are in LDS
+    // normalise and store: lane (head 32ht + lane%32, half h) holds, for dim tile dt, dims
+    // 128pw + 32dt + 8A + 4h + 0..3 in registers 4A..4A+3
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int head = 32 * ht + (lane & 31);
+      if (ht >= nht || head >= a.H) continue;
+      const float l_tot = sm.lsum[ht][0][lane & 31] + sm.lsum[ht][1][lane & 31];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int A = 0; A < 4; ++A) {
+          const int d0 = 128 * pw + 32 * dt + 8 * A + 4 * h;
+          const float v0 = O[ht][dt][4 * A] * inv, v1 = O[ht][dt][4 * A + 1] * inv;
+          const float v2 = O[ht][dt][4 * A + 2] * inv, v3 = O[ht][dt][4 * A + 3] * inv;
+          if (a.splits == 1) {
+            *reinterpret_cast<float4*>(a.out + ((size_t)t * a.H + head) * a.kv_lora + d0) = make_float4(v0, v1, v2, v3);
+          } else {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(a.ws) + (((size_t)t * a.H + head) * a.splits + split) * a.kv_lora + d0;
+            *reinterpret_cast<uint2*>(dst) = make_uint2(cvt2_bf16(float2v{v0, v1}), cvt2_bf16(float2v{v2, v3}));
+          }
+        }
+      }
     }
   }
-  if (g == 0 && half == 0) write_stats(a, t, split, head, m_run, l_tot);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -719,8 +719,8 @@ hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s) {
   dim3 grid(a.splits, a.T);
   if (a.kv_dtype == DSA_FP8_E4M3FN) {
     const dim3 xgrid(xcd_grid(a.splits, a.T));
-    if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_fp8<64>, xgrid, dim3(kMlaThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_mla_fp8<0>, xgrid, dim3(kMlaThreads), 0, s, a);
+    if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_fp8_ws<64>, xgrid, dim3(kMlaThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_mla_fp8_ws<0>, xgrid, dim3(kMlaThreads), 0, s, a);
   } else {
     if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_f32<64>, grid, dim3(kF32Threads), 0, s, a);
     else hipLaunchKernelGGL(k_mla_f32<0>, grid, dim3(kF32Threads), 0, s, a);
