@@ -1,7 +1,7 @@
 // C ABI of libdsa: argument validation (default-deny: every violated condition is reported and
 // nothing is launched) and dispatch to the gfx950 kernels.  See include/dsa.h for the contract.
 
-#include "dsa_internal.h"
+#include "topk_common.h"
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -113,7 +113,7 @@ dsa::IndexerLaunch indexer_launch(const dsa_indexer_desc_t* d, const void* q, co
                                   int64_t ld_scores) {
   return dsa::IndexerLaunch{d->num_q, d->num_heads, d->rope_dim, d->num_seqs, d->max_ctx, d->q_dtype, d->k_dtype,
                             q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores,
-                            nullptr, 0};
+                            nullptr, 0, 0};
 }
 
 }  // namespace
@@ -153,10 +153,13 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const 
   dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
                                         ld_scores);
   const bool fused = d->k_dtype == DSA_FP8_E4M3FN && !dsa::indexer_grouped(d->num_q, d->k_dtype);
-  if (fused) { a.topk_ws = topk_ws; a.topk_k = k; }
+  // the score chunks emit their own candidates when the row's chunks fit the item table
+  const int chunk = dsa::indexer_chunk(d->num_q, d->max_ctx);
+  const bool emit = fused && k <= dsa::kTkFastK && (d->max_ctx + chunk - 1) / chunk <= dsa::kTkMaxSeg;
+  if (fused) { a.topk_ws = topk_ws; a.topk_k = k; a.topk_emit = emit; }
   hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status("dsa_indexer_topk", e);
-  dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws};
+  dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws, emit ? chunk : 0, emit};
   return hip_status("dsa_indexer_topk", dsa::launch_topk(tk, fused, (hipStream_t)stream));
 }
 
@@ -180,7 +183,7 @@ dsa_status_t dsa_indexer_scores_hist(const dsa_indexer_desc_t* d, const void* q,
   if (fused) { a.topk_ws = topk_ws; a.topk_k = k; }
   hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
   if (e != hipSuccess || fused) return hip_status("dsa_indexer_scores_hist", e);
-  dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, nullptr, nullptr, topk_ws};
+  dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, nullptr, nullptr, topk_ws, 0, 0};
   return hip_status("dsa_indexer_scores_hist", dsa::launch_topk_hist(tk, (hipStream_t)stream));
 }
 
@@ -195,7 +198,7 @@ dsa_status_t dsa_topk_hist(const dsa_indexer_desc_t* d, const float* scores, int
   check_topk_ws(ck, d->num_q, topk_ws, topk_ws_bytes);
   dsa_status_t st = ck.finish("dsa_topk_hist");
   if (st != DSA_OK || d->num_q == 0) return st;
-  dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws};
+  dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws, 0, 0};
   return hip_status("dsa_topk_hist", dsa::launch_topk(tk, true, (hipStream_t)stream));
 }
 
@@ -211,7 +214,7 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
   check_topk_ws(ck, num_q, ws, ws_bytes);
   dsa_status_t st = ck.finish("dsa_topk");
   if (st != DSA_OK || num_q == 0) return st;
-  dsa::TopkLaunch a{scores, ld_scores, ld_scores, q_pos, num_q, k, idx, len, ws};
+  dsa::TopkLaunch a{scores, ld_scores, ld_scores, q_pos, num_q, k, idx, len, ws, 0, 0};
   return hip_status("dsa_topk", dsa::launch_topk(a, false, (hipStream_t)stream));
 }
 

@@ -29,6 +29,10 @@ struct IndexerLaunch {
   // scores' first radix digit into this per-row workspace for a k-selection; NULL = scores only
   void* topk_ws;
   int topk_k;
+  // with topk_ws: each score chunk also appends its own top-k candidates (every score at or above
+  // the bin of the chunk's kq-th largest) to the row's item list, so the selection needs no second
+  // pass over the scores (dsa_indexer_topk only: the emitted items are consumed in the same call)
+  int topk_emit;
 };
 
 struct TopkLaunch {
@@ -40,6 +44,8 @@ struct TopkLaunch {
   int32_t* idx;
   int32_t* len;
   void* ws;       // per-row first-digit histograms (fused path only)
+  int seg;        // columns per entry of the row's item table (a collect segment or a score chunk)
+  int emitted;    // the score kernel emitted the items (no collect pass)
 };
 
 struct BlockSelectLaunch {
@@ -101,6 +107,7 @@ constexpr int64_t kTopkMaxCols = int64_t(1) << 22;   // columns a top-k row may 
 size_t topk_ws_bytes(int T);
 size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype);
 bool indexer_grouped(int T, dsa_dtype_t k_dtype);   // many-query path: no fused first top-k digit
+int indexer_chunk(int T, int max_ctx);              // keys per workgroup of the fp8 decode score kernel
 size_t block_select_ws_bytes(int T, int64_t ld, int block);
 int kinsert_splits(int T, int D);   // hidden-dim splits of the key projection
 

@@ -463,6 +463,66 @@ static_assert(ring_wait(0, 32) == 10 && ring_wait(1, 32) == 11 && ring_wait(2, 3
                       ring_wait(29, 32) == 13 && ring_wait(30, 32) == 8 && ring_wait(31, 32) == 3,
               "ring wait counts");
 
+// Fused selection: this chunk's candidates for the row's top-k, appended to the row's item list in
+// column order.  kq is twice the chunk's expected share of the k (its share of the row's keys) plus
+// 32; every score whose first digit is >= lb, the digit of the chunk's kq-th largest score (from the
+// chunk's histogram in LDS), is emitted, and the chunk's table entry records (first item,
+// count | lb << 16).  The top-k of the row is contained in the union of the chunks' candidates as
+// long as each chunk's lb is at or below the row's k-th digit, which the selection kernel checks
+// (it selects from the scores directly otherwise).  The scores are read back from memory: this
+// workgroup wrote them, and the barrier before makes them visible to all its threads.
+struct EmitSmem {
+  uint32_t sbuf[32];
+  uint32_t wsum[16];
+  uint32_t base;
+};
+
+template <int TPW>
+__device__ void emit_candidates(const IndexerLaunch& a, int t, int n, int c0, uint32_t nrow, const uint32_t* lh,
+                                EmitSmem& em) {
+  constexpr int chunk = 4 * kTile * TPW;
+  constexpr int Q = chunk / (4 * kThreads);
+  static_assert(Q * (kThreads / 64) <= 16, "wsum size");
+  const uint32_t share = (uint32_t)(((uint64_t)a.topk_k * chunk + (uint64_t)n - 1) / (uint64_t)n);
+  const uint32_t kq = min(nrow, 2u * share + 32u);
+  int lb;
+  uint32_t unused;
+  tk_find_bin<kTkBins, kThreads>(lh, kq, em.sbuf, &lb, &unused);
+  const float* row = a.scores + (size_t)t * a.ld;
+  uint32_t key[Q][4];
+  const uint32_t mask = tk_load_slices<Q, kThreads>(row, n, c0, key);
+  uint32_t fl[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    fl[q] = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      fl[q] |= (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> kTkShift0) >= (uint32_t)lb ? 1u : 0u) << e;
+  }
+  uint32_t pos[Q];
+  const uint32_t total = tk_ordered_slots<Q, kThreads>(fl, pos, em.wsum);
+  uint32_t* rw = tk_row(a.topk_ws, t);
+  if (threadIdx.x == 0) {
+    const uint32_t st = atomicAdd(&rw[kTkOffCtr], total);
+    em.base = st;
+    *reinterpret_cast<uint2*>(rw + kTkOffTable + 2 * blockIdx.x) = make_uint2(st, total | ((uint32_t)lb << 16));
+  }
+  __syncthreads();
+  const uint32_t st = em.base;
+  // the item list is full (or the counter held a stale value): nothing is written, and the
+  // selection kernel sees it in the table entry
+  if (st > (uint32_t)kTkItemCap || total > (uint32_t)kTkItemCap - st) return;
+  uint2* items = reinterpret_cast<uint2*>(rw + kTkOffItems);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    uint32_t p = st + pos[q];
+    const uint32_t cq = (uint32_t)(c0 + 4 * kThreads * q + 4 * (int)threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((fl[q] >> e) & 1u) items[p++] = make_uint2(key[q][e], cq + e);
+  }
+}
+
 // TPW: 32-key tiles per wave (a workgroup covers 4 * 32 * TPW keys).  HIST: also histogram the
 // first top-k digit of this chunk's scores into the top-k workspace (the fused selection path).
 //
@@ -587,10 +647,14 @@ k_index_scores_fp8(IndexerLaunch a) {
     rel += kStride;
   }
   if (hist) {   // this chunk's counts into the row's histogram (read by the next kernel)
-    __syncthreads();
+    __syncthreads();   // also makes this workgroup's score stores visible to all its threads
     uint32_t* gh = tk_hist(a.topk_ws, t);
     for (int i = threadIdx.x; i < kTkBins; i += kThreads)
       if (pu.lh[i]) atomicAdd(&gh[i], pu.lh[i]);
+    if (a.topk_emit) {
+      __shared__ EmitSmem em;
+      emit_candidates<TPW>(a, t, n, c0, nrow, pu.lh, em);
+    }
   }
 }
 
@@ -824,6 +888,12 @@ size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype) {
 
 bool indexer_grouped(int T, dsa_dtype_t k_dtype) { return k_dtype == DSA_FP8_E4M3FN && T >= kGroupedMinQueries; }
 
+// 4096-key chunks (32 tiles per wave) when that still gives >= 512 workgroups, else 1024
+int indexer_chunk(int T, int max_ctx) {
+  const int64_t big = (int64_t)T * ((max_ctx + 4095) / 4096);
+  return big >= 512 ? 4096 : 1024;
+}
+
 hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
   if (a.T == 0 || a.max_ctx == 0) return hipSuccess;
   if (indexer_grouped(a.T, a.k_dtype)) {
@@ -831,15 +901,13 @@ hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
     dim3 grid((a.max_ctx + kTile * 32 - 1) / (kTile * 32), (a.T + kGroup - 1) / kGroup);
     hipLaunchKernelGGL(k_index_scores_fp8_grouped<32>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
   } else if (a.k_dtype == DSA_FP8_E4M3FN) {
-    // 4096-key chunks (32 tiles per wave) when that still gives >= 512 workgroups, else 1024.
-    const int64_t big = (int64_t)a.T * ((a.max_ctx + 4095) / 4096);
     const bool hist = a.topk_ws != nullptr;
     const bool bf = a.q_dtype == DSA_BF16;
     auto go = [&](auto kernel, int chunk) {
       dim3 grid((a.max_ctx + chunk - 1) / chunk, a.T);
       hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
     };
-    if (big >= 512) {
+    if (indexer_chunk(a.T, a.max_ctx) == 4096) {
       if (hist) bf ? go(k_index_scores_fp8<32, true, true>, 4096) : go(k_index_scores_fp8<32, true, false>, 4096);
       else bf ? go(k_index_scores_fp8<32, false, true>, 4096) : go(k_index_scores_fp8<32, false, false>, 4096);
     } else {

@@ -5,7 +5,7 @@
 // "The indexer": the top 2048 keys are kept; the -1 slots and top-k length bound follow the vLLM
 // page's "Top-k compaction" bullet).
 //
-// Three launches; rows are cut into 8192-column segments and only the last one works per row:
+// Up to three launches; rows are cut into 8192-column segments:
 //   hist     one workgroup per segment histograms the first digit (key bits 31..20) in LDS and
 //            adds it to the row's histogram.  The fused path skips it: the index-score kernel
 //            has already built that histogram.
@@ -19,6 +19,9 @@
 //            (bits 19..10, then 9..0), and with one ordered pass keeps the keys above it and the
 //            lowest columns among the keys equal to it.  The output is ascending by
 //            construction: no sort and no merge.
+// On the fused score + top-k path the score kernel emits each chunk's candidates itself (see
+// emit_candidates in the index kernels) and only the resolve kernel runs; a chunk that emitted
+// only digits above the row's b0 sends the row to the exact passes below.
 // If a row's items do not fit in LDS (heavy ties), k is large, or the check fails (a histogram
 // left over from an interrupted call, or built for another k), the resolve workgroup instead
 // selects by exact passes over the row, first digit included.  Every decision is made on the
@@ -41,76 +44,6 @@ __device__ inline int row_n(const TopkLaunch& a, int t) {
   return (int)n;
 }
 
-__device__ inline uint32_t lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// Element (q, e) of thread tid stands for column c0 + 4*NT*q + 4*tid + e: each float4 load of a
-// wave covers 1 KiB of contiguous scores.  Loads keys; bit 4q+e of the mask is set when the
-// column is < n (n >= 1).  Every load is an unconditional float4 (a slice at or past n reads the
-// row's last aligned float4 instead, which is in range because rows are a multiple of 4 long, and
-// is masked out), so all of them are in flight together.
-template <int Q, int NT>
-__device__ __forceinline__ uint32_t load_slices(const float* row, int n, int c0, uint32_t key[Q][4]) {
-  float4 v[Q];
-  const int clast = (n - 1) & ~3;
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int c = c0 + 4 * NT * q + 4 * (int)threadIdx.x;
-    v[q] = *reinterpret_cast<const float4*>(row + min(c, clast));
-  }
-  uint32_t mask = 0;
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int c = c0 + 4 * NT * q + 4 * (int)threadIdx.x;
-    key[q][0] = score_key(v[q].x);
-    key[q][1] = score_key(v[q].y);
-    key[q][2] = score_key(v[q].z);
-    key[q][3] = score_key(v[q].w);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mask |= (c + e < n ? 1u : 0u) << (4 * q + e);
-  }
-  return mask;
-}
-
-// Ordered compaction over the workgroup for the layout above (column order = slice, wave, lane,
-// element).  fl[q] holds this thread's 4-bit selection of slice q; returns in pos[q] the slot of
-// its first selected element of slice q, and the workgroup's total.  wsum: Q * NT/64 LDS words.
-template <int Q, int NT>
-__device__ uint32_t ordered_slots(const uint32_t fl[Q], uint32_t pos[Q], uint32_t* wsum) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t below[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    uint32_t bl = 0, wt = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint64_t b = __ballot((fl[q] >> e) & 1u);
-      bl += lanes_below(b);
-      wt += (uint32_t)__popcll(b);
-    }
-    below[q] = bl;
-    if (lane == 0) wsum[q * NW + wave] = wt;
-  }
-  __syncthreads();
-  uint32_t run = 0;
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    uint32_t tq = 0, pw = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t x = wsum[q * NW + w];
-      pw += w < wave ? x : 0u;
-      tq += x;
-    }
-    pos[q] = run + pw + below[q];
-    run += tq;
-  }
-  __syncthreads();
-  return run;
-}
-
 // ------------------------------------------------------------------------------------------
 // hist: first-digit histogram of one segment, added into the row's
 // ------------------------------------------------------------------------------------------
@@ -123,7 +56,7 @@ __global__ void __launch_bounds__(kCT) k_topk_hist(TopkLaunch a) {
   if (n <= a.k || c0 >= n) return;
   const float* row = a.scores + (size_t)t * a.ld;
   uint32_t key[kCQ][4];
-  const uint32_t mask = load_slices<kCQ, kCT>(row, n, c0, key);
+  const uint32_t mask = tk_load_slices<kCQ, kCT>(row, n, c0, key);
   for (int i = threadIdx.x; i < kTkBins; i += kCT) lh[i] = 0;
   __syncthreads();
 #pragma unroll
@@ -154,7 +87,7 @@ __global__ void __launch_bounds__(kCT) k_topk_collect(TopkLaunch a) {
   const float* row = a.scores + (size_t)t * a.ld;
   uint32_t* rw = tk_row(a.ws, t);
   uint32_t key[kCQ][4];
-  const uint32_t mask = load_slices<kCQ, kCT>(row, n, c0, key);
+  const uint32_t mask = tk_load_slices<kCQ, kCT>(row, n, c0, key);
   const uint4* gh = reinterpret_cast<const uint4*>(rw);
 #pragma unroll
   for (int j = 0; j < kTkBins / (4 * kCT); ++j) {
@@ -175,7 +108,7 @@ __global__ void __launch_bounds__(kCT) k_topk_collect(TopkLaunch a) {
       fl[q] |= (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> kTkShift0) >= (uint32_t)b0 ? 1u : 0u) << e;
   }
   uint32_t pos[kCQ];
-  const uint32_t total = ordered_slots<kCQ, kCT>(fl, pos, wsum);
+  const uint32_t total = tk_ordered_slots<kCQ, kCT>(fl, pos, wsum);
   if (threadIdx.x == 0) {
     const uint32_t st = atomicAdd(&rw[kTkOffCtr], total);
     base = st;
@@ -243,7 +176,7 @@ __device__ void row_digit(const float* row, int n, uint32_t prefix, int shift, u
   const int hs = top ? 0 : shift + bits;
   for (int c0 = 0; c0 < n; c0 += 4 * kRT * kSQ) {
     uint32_t key[kSQ][4];
-    const uint32_t mask = load_slices<kSQ, kRT>(row, n, c0, key);
+    const uint32_t mask = tk_load_slices<kSQ, kRT>(row, n, c0, key);
 #pragma unroll
     for (int q = 0; q < kSQ; ++q)
 #pragma unroll
@@ -271,7 +204,7 @@ __device__ void finish_streaming(const TopkLaunch& a, int t, int n, ResolveSmem&
   uint32_t base = 0, eq_seen = 0;
   for (int c0 = 0; c0 < n; c0 += 4 * kRT * kSQ) {
     uint32_t key[kSQ][4];
-    const uint32_t mask = load_slices<kSQ, kRT>(row, n, c0, key);
+    const uint32_t mask = tk_load_slices<kSQ, kRT>(row, n, c0, key);
     uint32_t gt[kSQ], eq[kSQ], epos[kSQ], spos[kSQ];
 #pragma unroll
     for (int q = 0; q < kSQ; ++q) {
@@ -283,7 +216,7 @@ __device__ void finish_streaming(const TopkLaunch& a, int t, int n, ResolveSmem&
         eq[q] |= (in && key[q][e] == thr ? 1u : 0u) << e;
       }
     }
-    const uint32_t eq_tot = ordered_slots<kSQ, kRT>(eq, epos, sm.wsum);
+    const uint32_t eq_tot = tk_ordered_slots<kSQ, kRT>(eq, epos, sm.wsum);
 #pragma unroll
     for (int q = 0; q < kSQ; ++q) {
       uint32_t r = eq_seen + epos[q];
@@ -294,7 +227,7 @@ __device__ void finish_streaming(const TopkLaunch& a, int t, int n, ResolveSmem&
           ++r;
         }
     }
-    const uint32_t sel_tot = ordered_slots<kSQ, kRT>(gt, spos, sm.wsum);
+    const uint32_t sel_tot = tk_ordered_slots<kSQ, kRT>(gt, spos, sm.wsum);
 #pragma unroll
     for (int q = 0; q < kSQ; ++q) {
       uint32_t p = base + spos[q];
@@ -331,8 +264,8 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
 
   // the row's histogram and segment table in one round of loads; the histogram and the item
   // counter are then zeroed for the next call
-  const int S = (n + kTkSeg - 1) / kTkSeg;
-  uint32_t cnt_s = 0;
+  const int S = (n + a.seg - 1) / a.seg;
+  uint32_t cnt_s = 0, low_s = 0;
   bool seg_bad = false;
   {
     const uint4 h = reinterpret_cast<const uint4*>(rw)[tid];
@@ -340,9 +273,10 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
     if (tid < S) te = reinterpret_cast<const uint2*>(rw + kTkOffTable)[tid];
     sm.hist[4 * tid] = h.x; sm.hist[4 * tid + 1] = h.y; sm.hist[4 * tid + 2] = h.z; sm.hist[4 * tid + 3] = h.w;
     if (tid < S) sm.tst[tid] = te.x;
-    cnt_s = te.y;
+    cnt_s = te.y & 0xFFFFu;
+    low_s = te.y >> 16;                 // lowest first digit the segment emitted (0 for collect segments)
     // a segment whose items did not fit (or whose start came from a stale counter) wrote none
-    seg_bad = tid < S && (te.x > (uint32_t)kTkItemCap || te.y > (uint32_t)kTkItemCap - te.x);
+    seg_bad = tid < S && (te.x > (uint32_t)kTkItemCap || cnt_s > (uint32_t)kTkItemCap - te.x);
     __syncthreads();
     reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) rw[kTkOffCtr] = 0u;
@@ -351,7 +285,9 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   int b0;
   uint32_t need_hint;
   tk_find_bin<kTkBins, kRT>(sm.hist, (uint32_t)a.k, sm.sbuf, &b0, &need_hint);
-  if (a.k > kTkFastK || overflow) {
+  // a segment that emitted only digits above b0 may hold keys of the top k it did not emit
+  const bool incomplete = __syncthreads_or(tid < S && low_s > (uint32_t)b0) != 0;
+  if (a.k > kTkFastK || overflow || incomplete) {
     finish_streaming(a, t, n, sm);
     if (tid == 0 && a.len) a.len[t] = a.k;
     return;
@@ -369,9 +305,9 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   __syncthreads();
   const uint2* items = reinterpret_cast<const uint2*>(rw + kTkOffItems);
   // four items per thread per round, their loads issued together (past the end: the last item
-  // again, not stored), so a typical row pays the load latency once; the items above b0 are
-  // counted on the way
-  uint32_t gt_b0 = 0;
+  // again, not stored), so a typical row pays the load latency once; the items above b0 and at or
+  // above it are counted on the way (emitted segments may also hold items below b0)
+  uint32_t gt_b0 = 0, ge_b0 = 0;
   if (total > 0) {
     for (uint32_t i0 = tid; i0 < total; i0 += 4 * kRT) {
       uint2 it[4];
@@ -392,16 +328,19 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
           sm.key[i] = it[u].x;
           sm.col[i] = it[u].y;
           gt_b0 += (it[u].x >> kTkShift0) > (uint32_t)b0 ? 1u : 0u;
+          ge_b0 += (it[u].x >> kTkShift0) >= (uint32_t)b0 ? 1u : 0u;
         }
       }
     }
   }
-  // The items are every key whose first digit is >= b0 (the collect kernels all read the same
-  // histogram).  b0 holds the k-th largest key iff fewer than k of them lie above b0 and at least
-  // k at or above it; otherwise the histogram did not describe these scores.
-  uint32_t above_b0;
+  // The items hold every key whose first digit is >= b0 (collect segments read the same histogram;
+  // emitted segments were checked above).  b0 holds the k-th largest key iff fewer than k of them
+  // lie above b0 and at least k at or above it; otherwise the histogram did not describe these
+  // scores.
+  uint32_t above_b0, atleast_b0;
   tk_excl_scan<kRT>(gt_b0, &above_b0, sm.sbuf);
-  if (!(above_b0 < (uint32_t)a.k && (uint32_t)a.k <= total)) {
+  tk_excl_scan<kRT>(ge_b0, &atleast_b0, sm.sbuf);
+  if (!(above_b0 < (uint32_t)a.k && (uint32_t)a.k <= atleast_b0)) {
     finish_streaming(a, t, n, sm);
     if (tid == 0 && a.len) a.len[t] = a.k;
     return;
@@ -489,8 +428,12 @@ hipError_t launch_topk(const TopkLaunch& a, bool hist_given, hipStream_t s) {
   const int64_t cols = a.ld < a.ncap ? a.ld : a.ncap;
   const dim3 seg_grid((unsigned)((cols + kTkSeg - 1) / kTkSeg), (unsigned)a.T);
   if (!hist_given) hipLaunchKernelGGL(k_topk_hist, seg_grid, dim3(kCT), 0, s, a);
-  if (a.k <= kTkFastK) hipLaunchKernelGGL(k_topk_collect, seg_grid, dim3(kCT), 0, s, a);
-  hipLaunchKernelGGL(k_topk_resolve, dim3(a.T), dim3(kRT), 0, s, a);
+  TopkLaunch r = a;
+  if (!a.emitted) {
+    r.seg = kTkSeg;
+    if (a.k <= kTkFastK) hipLaunchKernelGGL(k_topk_collect, seg_grid, dim3(kCT), 0, s, r);
+  }
+  hipLaunchKernelGGL(k_topk_resolve, dim3(a.T), dim3(kRT), 0, s, r);
   return hipGetLastError();
 }
 

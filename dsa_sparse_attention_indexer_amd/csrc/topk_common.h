@@ -4,9 +4,11 @@
 // Per-row workspace (32-bit words):
 //   hist   [kTkBins]        counts of the first radix digit (score-key bits 31..20)
 //   ctr    [4]              ctr[0]: item slots handed out by the collect kernel
-//   table  [kTkMaxSeg][2]   per segment: first item, item count (written by every live segment)
-//   items  [kTkItemCap][2]  (key, column) of every score whose first digit is >= the threshold
-//                           digit, in column order within each segment
+//   table  [kTkMaxSeg][2]   per segment: first item, item count | (lowest digit emitted << 16),
+//                           written by every live segment (a collect segment or, on the fused path,
+//                           a score chunk)
+//   items  [kTkItemCap][2]  (key, column) of every score whose first digit is >= the segment's
+//                           lowest emitted digit, in column order within each segment
 // The histogram only steers the fast path: the resolve kernel checks against the collected items
 // that the digit it names holds the k-th largest key, and otherwise selects by exact passes over
 // the row.  The resolve kernel that finishes a row clears its histogram and counter, so stale
@@ -105,6 +107,76 @@ __device__ inline void tk_find_bin(const uint32_t* h, uint32_t need, uint32_t* s
   *bin_out = (int)sbuf[20];
   *need_out = sbuf[21];
   __syncthreads();
+}
+
+__device__ inline uint32_t tk_lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Element (q, e) of thread tid stands for column c0 + 4*NT*q + 4*tid + e: each float4 load of a
+// wave covers 1 KiB of contiguous scores.  Loads keys; bit 4q+e of the mask is set when the
+// column is < n (n >= 1).  Every load is an unconditional float4 (a slice at or past n reads the
+// row's last aligned float4 instead, which is in range because rows are a multiple of 4 long, and
+// is masked out), so all of them are in flight together.
+template <int Q, int NT>
+__device__ __forceinline__ uint32_t tk_load_slices(const float* row, int n, int c0, uint32_t key[Q][4]) {
+  float4 v[Q];
+  const int clast = (n - 1) & ~3;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = c0 + 4 * NT * q + 4 * (int)threadIdx.x;
+    v[q] = *reinterpret_cast<const float4*>(row + min(c, clast));
+  }
+  uint32_t mask = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = c0 + 4 * NT * q + 4 * (int)threadIdx.x;
+    key[q][0] = score_key(v[q].x);
+    key[q][1] = score_key(v[q].y);
+    key[q][2] = score_key(v[q].z);
+    key[q][3] = score_key(v[q].w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mask |= (c + e < n ? 1u : 0u) << (4 * q + e);
+  }
+  return mask;
+}
+
+// Ordered compaction over the workgroup for the layout above (column order = slice, wave, lane,
+// element).  fl[q] holds this thread's 4-bit selection of slice q; returns in pos[q] the slot of
+// its first selected element of slice q, and the workgroup's total.  wsum: Q * NT/64 LDS words.
+template <int Q, int NT>
+__device__ uint32_t tk_ordered_slots(const uint32_t fl[Q], uint32_t pos[Q], uint32_t* wsum) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t below[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    uint32_t bl = 0, wt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint64_t b = __ballot((fl[q] >> e) & 1u);
+      bl += tk_lanes_below(b);
+      wt += (uint32_t)__popcll(b);
+    }
+    below[q] = bl;
+    if (lane == 0) wsum[q * NW + wave] = wt;
+  }
+  __syncthreads();
+  uint32_t run = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    uint32_t tq = 0, pw = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = wsum[q * NW + w];
+      pw += w < wave ? x : 0u;
+      tq += x;
+    }
+    pos[q] = run + pw + below[q];
+    run += tq;
+  }
+  __syncthreads();
+  return run;
 }
 
 }  // namespace dsa

@@ -106,14 +106,14 @@ def layer_step(wl, buf: StepBuffers, *, prefill: bool = False, block_sparse: boo
                shared_from: Optional[StepBuffers] = None, num_splits: int = 0, fused: bool = True, stream=None):
     """Scores -> selection -> sparse MLA; with shared_from, only the MLA over that selection.
 
-    fused (default): the score kernel also builds the first radix digit's histogram and the top-k
-    continues from it (index_scores_hist + select_hist); else dsa_indexer_scores and dsa_topk."""
+    fused (default): one dsa_indexer_topk call -- the score kernel also builds the first radix
+    digit's histogram and emits each chunk's candidates, and the selection continues from them;
+    else dsa_indexer_scores and dsa_topk."""
     if shared_from is not None:
         return attend(wl, buf, prefill=prefill, num_splits=num_splits, idx=shared_from.idx,
                       length=shared_from.length, stream=stream)
     if fused and not block_sparse:
-        index_scores_hist(wl, buf, stream)
-        select_hist(wl, buf, stream)
+        index_and_select(wl, buf, stream)
     else:
         index_scores(wl, buf, stream)
         select(wl, buf, block_sparse=block_sparse, stream=stream)

@@ -441,6 +441,57 @@ def test_fused_index_topk_equals_separate_calls(dsa, name, kw, constant):
             assert np.array_equal(idx[t], np.arange(wl.topk)) if n > wl.topk else idx[t, 0] == 0
 
 
+FUSED_ORACLE_CASES = [
+    # 4096-key chunks (many workgroups) and 1024-key chunks (few), ragged rows
+    ("chunks4096", dict(seq_lens=[40000] * 12 + [9000, 2049, 2048, 100000], max_ctx=100000)),
+    ("chunks1024", dict(seq_lens=[20000, 7000, 4097], max_ctx=20000)),
+    ("nope_h4", dict(seq_lens=[30000, 12000], max_ctx=30000, rope=False, num_heads=4)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FUSED_ORACLE_CASES, ids=[c[0] for c in FUSED_ORACLE_CASES])
+def test_fused_index_topk_matches_oracle(dsa, name, kw):
+    """dsa_indexer_topk (score chunks emit their own candidates): the selection is the oracle's
+    top-k of the GPU's scores bit for bit, and within the tie band of the oracle's own scores."""
+    wl = workloads.make_workload(name=name, seed=1313, **kw)
+    g = wl.to("cuda")
+    P = _pipe()
+    buf = P.alloc_buffers(g)
+    P.index_and_select(g, buf)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, buf, wl.topk, f"fused {name}")
+    idx, ln = buf.idx.cpu().numpy(), buf.length.cpu().numpy()
+    for t in (0, wl.num_q - 1):
+        check_selection(idx[t], ln[t], O.index_scores(wl, t), wl.topk, f"fused {name} q{t}", rms_admitted_ok=False)
+
+
+def test_fused_index_topk_clustered_top_keys(dsa):
+    """The top keys of each row are packed into the last 3000 positions with distinct, increasing
+    scores: the chunks there hold far more of the top k than their share, emit only digits above
+    the row's k-th digit, and the row must take the exact passes; the result is still the oracle's
+    selection of the GPU's scores."""
+    n = 20000
+    wl = workloads.make_workload(name="clustered", seed=1414, seq_lens=[n, n], max_ctx=n)
+    for t in range(2):
+        s = O.index_scores(wl, t)
+        best = int(np.argmax(s))
+        assert s[best] > 0
+        lo = n - 3000
+        wl.index_k[t, lo:n] = wl.index_k[t, best]
+        wl.index_k_scale[t, lo:n] = wl.index_k_scale[t, best] * torch.linspace(1.0, 2.0, 3000)
+    g = wl.to("cuda")
+    P = _pipe()
+    fus, sep = P.alloc_buffers(g), P.alloc_buffers(g)
+    P.index_and_select(g, fus)
+    P.index_scores(g, sep)
+    P.select(g, sep)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, fus, wl.topk, "clustered fused")
+    assert torch.equal(fus.idx, sep.idx)
+    idx = fus.idx.cpu().numpy()
+    assert np.all(idx[:, 0] >= n - 3000), "the top keys are the packed ones"
+
+
 def test_fused_workspace_reused_across_shapes(dsa):
     P = _pipe()
     big = workloads.make_workload(name="big", seed=909, seq_lens=[12000, 8000, 5000], max_ctx=12000).to("cuda")
