@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_HIP = 0, 1, 2, 3
 DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class DsaError(RuntimeError):
@@ -60,7 +60,7 @@ def _load():
         "dsa_indexer_workspace_size": (SZ, [ctypes.POINTER(IndexerDesc)]),
         "dsa_indexer_scores": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, P, SZ, P]),
         "dsa_indexer_topk": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, P, P, P, SZ,
-                                   P, SZ, P]),
+                                   P, SZ, P, P]),
         "dsa_indexer_scores_hist": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, P, SZ,
                                           P, SZ, P]),
         "dsa_topk_hist": (I32, [ctypes.POINTER(IndexerDesc), P, I64, P, I32, P, P, P, SZ, P]),
@@ -185,9 +185,11 @@ def dsa_indexer_scores(q, w, q_seq, q_pos, k_cache, scores, k_scale=None, ssmax_
 
 
 def dsa_indexer_topk(q, w, q_seq, q_pos, k_cache, scores, k, idx, length=None, k_scale=None, ssmax_s=None,
-                     ssmax_b=None, inv_freq=None, ws=None, topk_ws=None, stream=None):
+                     ssmax_b=None, inv_freq=None, ws=None, topk_ws=None, stream=None, mid_event=None):
     """Scores and top-k selection in one call (the fp8 score kernel also builds the first radix
-    digit's histogram).  Arguments as dsa_indexer_scores plus dsa_topk's."""
+    digit's histogram and emits each chunk's candidates).  Arguments as dsa_indexer_scores plus
+    dsa_topk's; mid_event (a torch.cuda.Event) is recorded between the score kernel and the
+    selection."""
     T, H, D = q.shape
     B, max_ctx, _ = k_cache.shape
     _dev("q", q, (torch.float32, torch.bfloat16))
@@ -212,10 +214,15 @@ def dsa_indexer_topk(q, w, q_seq, q_pos, k_cache, scores, k, idx, length=None, k
         topk_ws = topk_workspace(T, ld, k, q.device)
     _dev("ws", ws, torch.uint8)
     _dev("topk_ws", topk_ws, torch.uint8)
+    ev = None
+    if mid_event is not None:
+        if mid_event.cuda_event == 0:   # created lazily by torch: make it exist
+            mid_event.record(stream)
+        ev = ctypes.c_void_p(mid_event.cuda_event)
     _check(_lib.dsa_indexer_topk(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
                                  _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores), ld, k,
                                  _ptr(idx), _ptr(length), _ptr(ws), ws.numel(), _ptr(topk_ws), topk_ws.numel(),
-                                 _stream(stream)))
+                                 _stream(stream), ev))
     return idx, length
 
 

@@ -141,7 +141,8 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const 
                               const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                               const void* k_cache, const float* k_scale,
                               float* scores, int64_t ld_scores, int32_t k, int32_t* idx, int32_t* len,
-                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream) {
+                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream,
+                              void* mid_event) {
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_topk"); }
   check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
@@ -158,6 +159,7 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const 
   const bool emit = fused && k <= dsa::kTkFastK && (d->max_ctx + chunk - 1) / chunk <= dsa::kTkMaxSeg;
   if (fused) { a.topk_ws = topk_ws; a.topk_k = k; a.topk_emit = emit; }
   hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
+  if (e == hipSuccess && mid_event) e = hipEventRecord((hipEvent_t)mid_event, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status("dsa_indexer_topk", e);
   dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws, emit ? chunk : 0, emit};
   return hip_status("dsa_indexer_topk", dsa::launch_topk(tk, fused, (hipStream_t)stream));

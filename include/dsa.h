@@ -63,7 +63,7 @@ const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t dsa_abi_version(void);
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 /* ============================================================================================
  * 1. Lightning-indexer scores
@@ -149,17 +149,24 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
                       int32_t k, int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream);
 
 /* Scores and top-k in one call: dsa_indexer_scores followed by dsa_topk, with the first radix
- * digit's histogram built inside the fp8 score kernel (the scores are still written to `scores`).
+ * digit's histogram built inside the fp8 score kernel (the scores are still written to `scores`)
+ * and, on the fp8 decode path, each score chunk emitting its own top-k candidates (the scores at or
+ * above the bin of the chunk's few-hundredth largest), so that the selection needs no second pass
+ * over the scores ("Day 0 support for Mistral Large 4 on vLLM", "Long context: decode and prefill
+ * context parallelism": each rank's local top-k candidates feed the exact global selection).  A row
+ * whose candidates cannot be shown to contain its top k is selected from the scores directly.
  * Same arguments, conventions and results as the two calls made in sequence, except that a row
  * holds min(q_pos + 1, max_ctx) scores (the score kernel's clamp).  `topk_ws` follows dsa_topk's
- * workspace rules. */
+ * workspace rules.  mid_event: NULL, or a hipEvent_t recorded on `stream` after the score kernel
+ * and before the selection kernels (for callers that time the two halves). */
 size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k);
 dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* desc, const void* q, const float* w,
                               const int32_t* q_seq, const int32_t* q_pos,
                               const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                               const void* k_cache, const float* k_scale,
                               float* scores, int64_t ld_scores, int32_t k, int32_t* idx, int32_t* len,
-                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream);
+                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream,
+                              void* mid_event);
 
 /* The two halves of dsa_indexer_topk as separate calls, for callers that schedule or time the
  * score stream and the selection apart.  dsa_indexer_scores_hist writes the scores (as

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function(dsa):
     for f in declared_functions():
         assert hasattr(lib, f), f"{f} declared in dsa.h but not exported"
     assert set(declared_functions()) == set(dsa.EXPORTED)
-    assert dsa.lib().dsa_abi_version() == 1
+    assert dsa.lib().dsa_abi_version() == 2
 
 
 def test_topk_rejects_bad_arguments_listing_every_reason(dsa):
@@ -53,7 +53,7 @@ def test_indexer_topk_requires_its_workspace(dsa):
     L = dsa.lib()
     d = dsa.IndexerDesc(2, 64, 128, 64, 1, 100, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN)
     st = L.dsa_indexer_topk(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 100, 2048,
-                            None, None, None, 0, None, 0, None)
+                            None, None, None, 0, None, 0, None, None)
     msg = L.dsa_last_error().decode()
     assert st == dsa.DSA_ERR_ARG and "top-k workspace" in msg and "non-NULL" in msg, msg
 
