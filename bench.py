@@ -10,6 +10,10 @@ One step = lightning-indexer scores over every cached key -> exact top-2048 -> s
 tensors generated on the GPU and resident in HBM before timing starts; every timed loop cycles
 through three copies of its workload's caches, so each call reads HBM as in a multi-layer decode.
 
+Inside the timed steps the library's timing hook records every kernel's own duration (the start
+and stop events of its dispatch); the roofline figure is the score kernel's average there.  --only NAME times one
+configuration alone (for profiles of that configuration's kernels).
+
 Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 """
 import argparse
@@ -90,14 +94,14 @@ def counter_traffic():
 
 
 def cache_writer_rates(dsa, timed, dev):
-    import torch
-    import workloads
     """Per-call device time and algorithmic bandwidth of the cache writers (and the wall-clock
     time per call through the binding) for one decode step's 16 new tokens and one 4096-token
     prefill chunk.  Keys read: x (2 B x hidden per token) and the
     key projection's weight (2 B x 128 x hidden, once per call); written: 132 B per token.  Latent
     rows: 1152 B read, 612 B written per token.  The destination rows are numbered densely (the
     writers' cost does not depend on where the rows lie)."""
+    import torch
+    import workloads
     out = {}
     for name, b in (("decode_b16", workloads.insert_decode(device=dev)),
                     ("prefill_4096", workloads.insert_prefill(device=dev))):
@@ -144,28 +148,175 @@ def device_time(fn, dev, n=20):
     return e0.elapsed_time(e1) * 1e-3 / n
 
 
-def cpu_baseline(wl, seconds):
-    """The float64 oracle on whole queries of the same workload, on this host's cores."""
+def oracle_rate(wl, seconds, block_sparse=False, max_queries=None):
+    """Queries per second of the float64 oracle on whole queries of wl (scores over the full
+    context, selection, sparse MLA), timed one query at a time until `seconds` have been spent."""
     import workloads
     from oracle import dsa_oracle as O
-    threads = None
+    n = wl.num_q if max_queries is None else min(wl.num_q, max_queries)
+    done, elapsed = 0, 0.0
+    while done == 0 or (elapsed < seconds and done < n):
+        sub = workloads.slice_query(wl, done)
+        t0 = time.perf_counter()
+        O.decode_layer(sub, [0], block_sparse=block_sparse)
+        elapsed += time.perf_counter() - t0
+        done += 1
+    return done / elapsed, done, elapsed
+
+
+def oracle_threads():
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        threads = max((i.get("num_threads") or 1) for i in info) if info else None
+        return max((i.get("num_threads") or 1) for i in info) if info else None
     except Exception:
-        pass
-    done, elapsed, t = 0, 0.0, 0
-    while done == 0 or (elapsed < seconds and done < wl.num_q):
-        sub = workloads.slice_query(wl, t)
-        t0 = time.perf_counter()
-        O.decode_layer(sub, [0])
-        elapsed += time.perf_counter() - t0
-        done += 1
-        t += 1
-    return {"value": done / elapsed, "unit": "tok/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+        return None
+
+
+def cpu_baseline(wl, seconds):
+    """The float64 oracle on whole queries of the headline workload, on this host's cores."""
+    rate, done, elapsed = oracle_rate(wl, seconds)
+    return {"value": rate, "unit": "tok/s", "cores": oracle_threads() or os.cpu_count(), "kind": "oracle",
             "sample": f"{done} of {wl.num_q} decode queries at context {wl.max_ctx} (full indexer scan, "
                       f"top-{wl.topk}, sparse MLA), float64 numpy, {elapsed:.1f} s"}
+
+
+def mla_rates(wl, lengths, us):
+    """Algorithmic MFMA rate and latent-gather bandwidth of a sparse-MLA stage that took `us`."""
+    sel = int(lengths.long().sum())
+    flops = sel * wl.mla_heads * MLA_FLOP_PER_KEY_HEAD
+    tflops = flops / (us * 1e-6) / 1e12
+    gbs = sel * LATENT_BYTES_PER_KEY / (us * 1e-6) / 1e9
+    return {"us": us, "selected_keys": sel, "heads": wl.mla_heads, "tflops": tflops,
+            "frac_bf16_peak": tflops / BF16_PEAK_TFLOPS, "gather_gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
+def mean(xs):
+    return sum(xs) / len(xs)
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def _demangle_kernel(m):
+    """The kernel identifier and its integer / bool template arguments from an Itanium-mangled
+    name ('_ZN3dsa12_GLOBAL__N_112k_mla_fp8_wsILi64EEEvNS_9MlaLaunchE' -> 'k_mla_fp8_ws<64>')."""
+    import re
+    for hit in re.finditer(r"k_", m):
+        p = hit.start()
+        q = p
+        while q > 0 and m[q - 1].isdigit():
+            q -= 1
+        for L in range(1, p - q + 1):
+            n = int(m[p - L:p])
+            ident = m[p:p + n]
+            rest = m[p + n:]
+            if len(ident) == n and re.fullmatch(r"k_\w+", ident) and rest[:1] in ("E", "I"):
+                if not rest.startswith("I"):
+                    return ident
+                args = re.findall(r"L([ib])(\d+)E", rest[:rest.find("EE") + 2])
+                vals = [("true" if v == "1" else "false") if t == "b" else v for t, v in args]
+                return f"{ident}<{', '.join(vals)}>"
+    return m
+
+
+def short_name(name):
+    """'void dsa::(anonymous namespace)::k_mla_fp8_ws<64>(dsa::MlaLaunch)' (or its mangled form)
+    -> 'k_mla_fp8_ws<64>'."""
+    if name.startswith("_Z"):
+        return _demangle_kernel(name)
+    head = name.split("(dsa::")[0] if "(dsa::" in name else name
+    if "<" not in head:
+        return head.rsplit("::", 1)[-1]
+    cut = head.rfind("::", 0, head.index("<"))
+    return head if cut < 0 else head[cut + 2:]
+
+
+def stage_of(kernel):
+    if kernel.startswith("k_index"):
+        return "scores"
+    if kernel.startswith(("k_topk", "k_block")):
+        return "select"
+    if kernel.startswith("k_mla"):
+        return "sparse_mla"
+    return "other"
+
+
+def staged_steps(dsa, pipeline, wls, n, buf, *, prefill=False, block_sparse=False, shared_from=None):
+    """n layer steps over the cache copies, timed on the wall clock, with each library kernel's own
+    device duration taken by the library's timing hook (start and stop events of the kernels' own
+    dispatches, so nothing is added to the stream).
+    Returns (wall seconds per step, {kernel: [us per launch]}, {stage: us per step})."""
+    import torch
+    timer = dsa.KernelTimer(8 * n)
+    with timer:
+        t0 = time.perf_counter()
+        for i in range(n):
+            pipeline.layer_step(wls[i % len(wls)], buf, prefill=prefill, block_sparse=block_sparse,
+                                shared_from=shared_from)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / n
+    per = {}
+    stages = {"scores": 0.0, "select": 0.0, "sparse_mla": 0.0}
+    for name, us in timer.results():
+        k = short_name(name)
+        per.setdefault(k, []).append(us)
+        st = stage_of(k)
+        stages[st] = stages.get(st, 0.0) + us / n
+    return wall, per, stages
+
+
+# name -> (workload maker, step kind); the headline is the first
+CONFIGS = {
+    "decode_b16_ctx128k": (lambda w, dev: w.config2("a", device=dev), {}),
+    "decode_b16_ctx128k_nope": (lambda w, dev: w.config2("b", device=dev), {}),
+    "decode_b64_ctx16k_32k": (lambda w, dev: w.config1(device=dev), {}),
+    "prefill_4096_on_61440": (lambda w, dev: w.config3(device=dev), {"prefill": True}),
+    "blocksparse_b4_ctx512k": (lambda w, dev: w.config4(device=dev), {"block_sparse": True}),
+    "decode_b1_ctx8192_f32": (lambda w, dev: w.config0(device=dev), {}),
+    "verify_b16x4_ctx128k": (lambda w, dev: w.verify_blocks(device=dev, batch=16, tokens=4, ctx=131072), {}),
+}
+
+
+def run_config(dsa, pipeline, wls, kind, steps, warmup, shared_from=None, buf=None):
+    """Warmup, then `steps` timed layer steps: wall time per step, each kernel's mean and median
+    device time, and the per-step device time of each stage."""
+    import torch
+    if buf is None:
+        buf = pipeline.alloc_buffers(wls[0], prefill=kind.get("prefill", False),
+                                     block_sparse=kind.get("block_sparse", False))
+    for i in range(warmup):
+        pipeline.layer_step(wls[i % len(wls)], buf, shared_from=shared_from, **kind)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        pipeline.layer_step(wls[i % len(wls)], buf, shared_from=shared_from, **kind)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    _, per, stages = staged_steps(dsa, pipeline, wls, steps, buf, shared_from=shared_from, **kind)
+    out = {"us_per_step": wall * 1e6, "tok_per_s": wls[0].num_q / wall,
+           "kernels_us_mean": {k: mean(v) for k, v in per.items()},
+           "kernels_us_median": {k: median(v) for k, v in per.items()},
+           "stages_us_per_step": stages}
+    if shared_from is None and not kind.get("block_sparse", False):
+        # the same step with the selection as two calls (scores written, then the top-k over them)
+        for i in range(warmup):
+            pipeline.layer_step(wls[i % len(wls)], buf, fused=False, **kind)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            pipeline.layer_step(wls[i % len(wls)], buf, fused=False, **kind)
+        torch.cuda.synchronize()
+        out["us_per_step_separate_selection"] = (time.perf_counter() - t0) / steps * 1e6
+    src = buf if shared_from is None else shared_from
+    mla_main = [v for k, v in per.items() if k.startswith("k_mla") and "combine" not in k]
+    if mla_main:
+        out["sparse_mla_kernel"] = mla_rates(wls[0], src.length, mean(mla_main[0]))
+    out["sparse_mla_stage"] = mla_rates(wls[0], src.length, stages["sparse_mla"])
+    return out, buf, per
 
 
 def main():
@@ -173,9 +324,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time on the headline workload (the other configs get a third of it each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the back-to-back score-kernel loop (profiles of the in-step kernel only)")
+    ap.add_argument("--only", choices=sorted(CONFIGS), default=None,
+                    help="time one configuration's staged layer steps only and print its figures")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -201,66 +357,80 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "dispatches": 5}))
         return
 
+    if args.only is not None:
+        make, kind = CONFIGS[args.only]
+        log(f"generating {args.only} on the GPU ...")
+        wls = cache_copies(make(workloads, dev))
+        res, _, _ = run_config(dsa, pipeline, wls, kind, args.steps, args.warmup)
+        res["config"] = args.only
+        print(json.dumps(res), flush=True)
+        return
+
     log("generating the 128K decode workload (RoPE layer) on the GPU ...")
     wa = workloads.config2("a", device=dev)
     T = wa.num_q
     buf_a = pipeline.alloc_buffers(wa)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-
     was = cache_copies(wa)
-    step_a = cycling(lambda w: pipeline.layer_step(w, buf_a), was)
 
-    # ---- headline: K timed layer steps --------------------------------------------------------
-    for _ in range(args.warmup):
-        step_a()
+    # ---- headline: K timed layer steps ------------------------------------------------------------
+    # Every step reads a different copy of the caches, so each reads HBM as inside a multi-layer
+    # decode.  The library's timing hook gives every kernel's own duration inside these steps; the
+    # score kernel's average there is the roofline's time.
+    for i in range(args.warmup):
+        pipeline.layer_step(was[i % len(was)], buf_a)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step_a()
+    for i in range(args.steps):
+        pipeline.layer_step(was[i % len(was)], buf_a)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    log(f"layer step: {ms_per_step * 1e3:.1f} us")
+    wall = (time.perf_counter() - t0) / args.steps
+    ms_per_step = 1e3 * wall
+    # the same steps again with the timing hook on (it lengthens the step on the wall clock, not
+    # the kernels): every kernel's own duration
+    hooked_wall, per, stages = staged_steps(dsa, pipeline, was, args.steps, buf_a)
+    score_name = next((k for k in per if k.startswith("k_index_scores")), None)
+    if score_name is None:
+        raise RuntimeError(f"no score kernel among the timed kernels: {sorted(per)}")
+    t_idx = mean(per[score_name])
+    t_mla = stages["sparse_mla"]
+    log(f"layer step: {ms_per_step * 1e3:.1f} us wall; in-step kernels " +
+        ", ".join(f"{k} {mean(v):.1f}" for k, v in per.items()) + " us")
 
-    # ---- per-stage durations: K back-to-back calls between two events on the launch stream -------
-    def per_call_us(fn):
-        for _ in range(2):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / args.steps
-
-    # Every stage is timed over calls that cycle through the cache copies, so each call reads HBM
-    # (as inside a real decode step), not lines left in the last-level cache by the previous call.
-    # The score kernel (with the histogram, as in the step) back to back on scratch buffers (their
-    # histogram piles up over the calls and is discarded), then score kernel + top-k pairs: the
-    # top-k's share is the difference.
-    tmp = pipeline.alloc_buffers(wa)
-    t_idx = per_call_us(cycling(lambda w: pipeline.index_scores_hist(w, tmp), was))
-    del tmp
-
-    def pair(w):
-        pipeline.index_scores_hist(w, buf_a)
-        pipeline.select_hist(w, buf_a)
-
-    t_topk = per_call_us(cycling(pair, was)) - t_idx
-    t_mla = per_call_us(cycling(lambda w: pipeline.attend(w, buf_a), was))
     keys = int((wa.q_pos.long() + 1).sum())
     idx_bytes = keys * INDEX_BYTES_PER_KEY
     achieved = idx_bytes / (t_idx * 1e-6) / 1e9
-    sel = int(buf_a.length.long().sum())
-    mla_flops = sel * wa.mla_heads * MLA_FLOP_PER_KEY_HEAD
-    mla_tflops = mla_flops / (t_mla * 1e-6) / 1e12
-    mla_gbs = sel * LATENT_BYTES_PER_KEY / (t_mla * 1e-6) / 1e9
-    log(f"index {t_idx:.1f} us, top-k {t_topk:.1f} us, MLA {t_mla:.1f} us")
+    isolated = None
+    if not args.no_isolated:
+        # The score kernel alone, back to back over the copies, with the histogram but without the
+        # candidate emission (dsa_indexer_scores_hist); its histograms pile up in a scratch
+        # workspace and are discarded.
+        tmp = pipeline.alloc_buffers(wa)
+        f = cycling(lambda w: pipeline.index_scores_hist(w, tmp), was)
+        for _ in range(2):
+            f()
+        timer = dsa.KernelTimer(args.steps)
+        with timer:
+            for _ in range(args.steps):
+                f()
+        t_iso = mean([us for _, us in timer.results()])
+        isolated = {"us": t_iso, "achieved": idx_bytes / (t_iso * 1e-6) / 1e9,
+                    "frac": idx_bytes / (t_iso * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                    "note": "score kernel alone, back to back, histogram but no candidate emission"}
+        del tmp
+        log(f"score kernel back to back: {t_iso:.1f} us")
+    mla_name = next(k for k in per if k.startswith("k_mla") and "combine" not in k)
+    headline_mla = {"kernel": mla_rates(wa, buf_a.length, mean(per[mla_name])),
+                    "stage": mla_rates(wa, buf_a.length, t_mla)}
 
     variants = {}
+    oracle_rates = {}
+    cpu_s = args.cpu_seconds / 3
     if not args.no_variants:
+        buf_c = pipeline.alloc_buffers(wa)   # shared-indexer layer: its own outputs, a's selection
+        variants["shared_indexer_layer_b16_ctx128k"], _, _ = run_config(
+            dsa, pipeline, was, {}, args.steps, args.warmup, shared_from=buf_a, buf=buf_c)
+
         def timed(fn):
             for _ in range(args.warmup):
                 fn()
@@ -271,37 +441,18 @@ def main():
             torch.cuda.synchronize()
             return (time.perf_counter() - s0) / args.steps
 
-        buf_c = pipeline.alloc_buffers(wa)   # shared-indexer layer: its own outputs, a's selection
-        tc = timed(cycling(lambda w: pipeline.layer_step(w, buf_c, shared_from=buf_a), was))
-        variants["shared_indexer_layer_b16_ctx128k"] = {"us_per_step": tc * 1e6, "tok_per_s": T / tc}
         tf = timed(cycling(lambda w: pipeline.layer_step(w, buf_c, fused=False), was))   # two separate calls
         variants["separate_index_topk_layer_b16_ctx128k"] = {"us_per_step": tf * 1e6, "tok_per_s": T / tf}
-        del buf_c
-        del was
-        log("generating the NoPE-layer workload ...")
-        wb = cache_copies(workloads.config2("b", device=dev))
-        bb = pipeline.alloc_buffers(wb[0])
-        tb = timed(cycling(lambda w: pipeline.layer_step(w, bb), wb))
-        variants["nope_layer_b16_ctx128k"] = {"us_per_step": tb * 1e6, "tok_per_s": wb[0].num_q / tb}
-        del wb, bb
-        log("generating the 4096-on-61440 chunked prefill ...")
-        w3 = cache_copies(workloads.config3(device=dev))
-        b3 = pipeline.alloc_buffers(w3[0], prefill=True)
-        t3 = timed(cycling(lambda w: pipeline.layer_step(w, b3, prefill=True), w3))
-        variants["chunked_prefill_4096_on_61440"] = {"us_per_step": t3 * 1e6, "tok_per_s": w3[0].num_q / t3}
-        del w3, b3
-        log("generating the 512K block-sparse decode ...")
-        w4 = cache_copies(workloads.config4(device=dev))
-        b4 = pipeline.alloc_buffers(w4[0], block_sparse=True)
-        t4 = timed(cycling(lambda w: pipeline.layer_step(w, b4, block_sparse=True), w4))
-        variants["block_sparse_b4_ctx512k"] = {"us_per_step": t4 * 1e6, "tok_per_s": w4[0].num_q / t4}
-        del w4, b4
-        log("generating the batch-64 16K-32K decode ...")
-        w1 = cache_copies(workloads.config1(device=dev))
-        b1 = pipeline.alloc_buffers(w1[0])
-        t1 = timed(cycling(lambda w: pipeline.layer_step(w, b1), w1))
-        variants["decode_b64_ctx16k_32k"] = {"us_per_step": t1 * 1e6, "tok_per_s": w1[0].num_q / t1}
-        del w1, b1
+        del buf_c, was
+        for name, (make, kind) in list(CONFIGS.items())[1:]:
+            log(f"generating {name} ...")
+            wls = cache_copies(make(workloads, dev))
+            variants[name], _, _ = run_config(dsa, pipeline, wls, kind, args.steps, args.warmup)
+            if not args.no_cpu_baseline:
+                r, done, el = oracle_rate(wls[0], cpu_s, block_sparse=kind.get("block_sparse", False))
+                oracle_rates[name] = {"tok_per_s": r, "sample": f"{done} of {wls[0].num_q} queries, {el:.1f} s"}
+            del wls
+            torch.cuda.synchronize()
         log("variants: " + ", ".join(f"{k} {v['us_per_step']:.1f} us" for k, v in variants.items()))
         variants["cache_writers"] = cache_writer_rates(dsa, timed, dev)
         log("cache writers: " + ", ".join(f"{k} {v['us_per_call']:.1f} us" for k, v in variants["cache_writers"].items()))
@@ -310,10 +461,12 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on host cores ...")
         cpu = cpu_baseline(wa, args.cpu_seconds)
+        if oracle_rates:
+            cpu["other_configs"] = oracle_rates
 
     res = {
         "metric": METRIC,
-        "value": T / (elapsed / args.steps),
+        "value": T / wall,
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -327,13 +480,17 @@ def main():
         "config": {"workload": "decode layer step (RoPE layer): indexer + top-2048 + sparse MLA",
                    "batch": T, "context": wa.max_ctx, "index_heads": wa.num_heads, "mla_heads": wa.mla_heads,
                    "topk": wa.topk, "kv_cache": "fp8 e4m3fn + fp32 scales"},
-        "roofline": {"bound": "hbm", "kernel": "index scores + first-digit histogram (fp8 keys)", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counter_traffic(), "bytes_per_launch": idx_bytes},
-        "stages_us": {"index_scores_hist": t_idx, "topk_from_hist": t_topk, "sparse_mla": t_mla},
+        "roofline": {"bound": "hbm", "kernel": score_name + " (scores + first-digit histogram + candidate emission)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic(), "bytes_per_launch": idx_bytes,
+                     "launch_us_in_step_mean": t_idx, "launch_us_in_step_median": median(per[score_name]),
+                     "launches": len(per[score_name]), "isolated_back_to_back": isolated},
+        "kernels_us_mean": {k: mean(v) for k, v in per.items()},
+        "kernels_us_median": {k: median(v) for k, v in per.items()},
+        "stages_us_per_step": stages,
+        "us_per_step_with_timing_hook": hooked_wall * 1e6,
         "keys_scored_per_s": keys / (t_idx * 1e-6),
-        "sparse_mla": {"tflops": mla_tflops, "frac_bf16_peak": mla_tflops / BF16_PEAK_TFLOPS,
-                       "gather_gbs": mla_gbs, "frac_hbm_peak": mla_gbs / HBM_PEAK_GBS},
+        "sparse_mla": headline_mla,
         "variants": variants,
         "cpu_baseline": cpu,
     }

@@ -57,10 +57,13 @@ def _load():
     sig = {
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_abi_version": (I32, []),
+        "dsa_timing_begin": (I32, [P, I32]),
+        "dsa_timing_end": (I32, []),
+        "dsa_timing_kernel_name": (ctypes.c_char_p, [I32]),
         "dsa_indexer_workspace_size": (SZ, [ctypes.POINTER(IndexerDesc)]),
         "dsa_indexer_scores": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, P, SZ, P]),
         "dsa_indexer_topk": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, P, P, P, SZ,
-                                   P, SZ, P, P]),
+                                   P, SZ, P]),
         "dsa_indexer_scores_hist": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, P, SZ,
                                           P, SZ, P]),
         "dsa_topk_hist": (I32, [ctypes.POINTER(IndexerDesc), P, I64, P, I32, P, P, P, SZ, P]),
@@ -94,7 +97,8 @@ EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_workspace_size", "
             "dsa_topk_workspace_size", "dsa_topk", "dsa_block_select_workspace_size", "dsa_block_select", "dsa_sparse_mla_workspace_size",
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_sparse_mla_noalloc_max_bytes",
             "dsa_sparse_mla_decode_noalloc", "dsa_index_k_insert_workspace_size",
-            "dsa_index_k_insert", "dsa_latent_insert"]
+            "dsa_index_k_insert", "dsa_latent_insert", "dsa_timing_begin", "dsa_timing_end",
+            "dsa_timing_kernel_name"]
 
 
 def lib():
@@ -185,11 +189,9 @@ def dsa_indexer_scores(q, w, q_seq, q_pos, k_cache, scores, k_scale=None, ssmax_
 
 
 def dsa_indexer_topk(q, w, q_seq, q_pos, k_cache, scores, k, idx, length=None, k_scale=None, ssmax_s=None,
-                     ssmax_b=None, inv_freq=None, ws=None, topk_ws=None, stream=None, mid_event=None):
+                     ssmax_b=None, inv_freq=None, ws=None, topk_ws=None, stream=None):
     """Scores and top-k selection in one call (the fp8 score kernel also builds the first radix
-    digit's histogram and emits each chunk's candidates).  Arguments as dsa_indexer_scores plus
-    dsa_topk's; mid_event (a torch.cuda.Event) is recorded between the score kernel and the
-    selection."""
+    digit's histogram).  Arguments as dsa_indexer_scores plus dsa_topk's."""
     T, H, D = q.shape
     B, max_ctx, _ = k_cache.shape
     _dev("q", q, (torch.float32, torch.bfloat16))
@@ -214,15 +216,10 @@ def dsa_indexer_topk(q, w, q_seq, q_pos, k_cache, scores, k, idx, length=None, k
         topk_ws = topk_workspace(T, ld, k, q.device)
     _dev("ws", ws, torch.uint8)
     _dev("topk_ws", topk_ws, torch.uint8)
-    ev = None
-    if mid_event is not None:
-        if mid_event.cuda_event == 0:   # created lazily by torch: make it exist
-            mid_event.record(stream)
-        ev = ctypes.c_void_p(mid_event.cuda_event)
     _check(_lib.dsa_indexer_topk(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
                                  _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores), ld, k,
                                  _ptr(idx), _ptr(length), _ptr(ws), ws.numel(), _ptr(topk_ws), topk_ws.numel(),
-                                 _stream(stream), ev))
+                                 _stream(stream)))
     return idx, length
 
 
@@ -456,3 +453,35 @@ def dsa_latent_insert(kv, pos, slot, kv_cache, kv_scale, inv_freq=None, stream=N
                                   _ptr(inv_freq), _ptr(slot), kv_cache.numel() // 576, _ptr(kv_cache),
                                   _ptr(kv_scale), _stream(stream)))
     return kv_cache, kv_scale
+
+
+class KernelTimer:
+    """Each library kernel's own device duration inside a running pipeline (dsa_timing_begin /
+    dsa_timing_end): within the `with` block, up to `capacity` kernels the library enqueues record
+    their dispatch's start and stop timestamps into a pair of events; no work is added to the
+    stream.  After the block, results() synchronises and returns [(kernel name, microseconds)]
+    in launch order."""
+
+    def __init__(self, capacity: int, stream=None):
+        self.capacity = int(capacity)
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * self.capacity)]
+        for e in self.events:   # torch creates its events on first record
+            e.record(stream)
+        self._handles = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
+        self.count = 0
+        self.names = []
+
+    def __enter__(self):
+        torch.cuda.synchronize()
+        _check(_lib.dsa_timing_begin(self._handles, self.capacity))
+        return self
+
+    def __exit__(self, *exc):
+        self.count = _lib.dsa_timing_end()
+        self.names = [(_lib.dsa_timing_kernel_name(i) or b"?").decode() for i in range(self.count)]
+        return False
+
+    def results(self):
+        torch.cuda.synchronize()
+        return [(self.names[i], self.events[2 * i].elapsed_time(self.events[2 * i + 1]) * 1e3)
+                for i in range(self.count)]

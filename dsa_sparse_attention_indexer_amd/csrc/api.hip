@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <mutex>
+#include <vector>
 #include <string>
 
 namespace {
@@ -45,15 +46,62 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 }  // namespace
 
+// Kernel timing hook state (dsa_timing_begin / _end).
+struct TimingHook {
+  std::mutex mu;
+  void* const* events = nullptr;
+  int cap = 0, used = 0;
+  std::vector<const void*> fns;
+};
+static TimingHook g_timing;
+
+namespace dsa {
+bool timing_take(const void* fn, hipEvent_t* start, hipEvent_t* stop) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (!g_timing.events || g_timing.used >= g_timing.cap) return false;
+  const int i = g_timing.used++;
+  g_timing.fns[(size_t)i] = fn;
+  *start = (hipEvent_t)g_timing.events[2 * i];
+  *stop = (hipEvent_t)g_timing.events[2 * i + 1];
+  return true;
+}
+}  // namespace dsa
+
 extern "C" {
 
 const char* dsa_last_error(void) { return g_err.c_str(); }
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
 
+dsa_status_t dsa_timing_begin(void* const* events, int32_t capacity) {
+  Checker ck;
+  ck.need(events != nullptr, "events is NULL");
+  ck.need(capacity >= 1 && capacity <= 65536, "capacity must be in [1, 65536]");
+  dsa_status_t st = ck.finish("dsa_timing_begin");
+  if (st != DSA_OK) return st;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.events = events;
+  g_timing.cap = capacity;
+  g_timing.used = 0;
+  g_timing.fns.assign((size_t)capacity, nullptr);
+  return DSA_OK;
+}
+
+int32_t dsa_timing_end(void) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.events = nullptr;
+  return g_timing.used;
+}
+
+const char* dsa_timing_kernel_name(int32_t i) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (i < 0 || i >= g_timing.used || (size_t)i >= g_timing.fns.size()) return nullptr;
+  return hipKernelNameRefByPtr(g_timing.fns[(size_t)i], nullptr);
+}
+
 size_t dsa_indexer_workspace_size(const dsa_indexer_desc_t* d) {
   if (!d || d->num_q <= 0) return 0;
-  return dsa::indexer_ws_bytes(d->num_q, d->k_dtype);
+  return dsa::indexer_ws_bytes(d->num_q, d->num_seqs, d->k_dtype);
 }
 
 }  // extern "C"
@@ -141,8 +189,7 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const 
                               const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                               const void* k_cache, const float* k_scale,
                               float* scores, int64_t ld_scores, int32_t k, int32_t* idx, int32_t* len,
-                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream,
-                              void* mid_event) {
+                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream) {
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_topk"); }
   check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
@@ -153,13 +200,15 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const 
   if (st != DSA_OK || d->num_q == 0) return st;
   dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
                                         ld_scores);
-  const bool fused = d->k_dtype == DSA_FP8_E4M3FN && !dsa::indexer_grouped(d->num_q, d->k_dtype);
-  // the score chunks emit their own candidates when the row's chunks fit the item table
+  // The decode score kernel builds the first digit's histogram, and its chunks emit their own
+  // candidates when the row's chunks fit the segment table.  The grouped kernel (several queries
+  // per sequence) only writes scores: its workgroups are bound by matrix work, and a per-chunk
+  // selection tail there costs more than the separate passes over the scores.
+  const bool fused = d->k_dtype == DSA_FP8_E4M3FN && !dsa::indexer_grouped(d->num_q, d->num_seqs, d->k_dtype);
   const int chunk = dsa::indexer_chunk(d->num_q, d->max_ctx);
   const bool emit = fused && k <= dsa::kTkFastK && (d->max_ctx + chunk - 1) / chunk <= dsa::kTkMaxSeg;
   if (fused) { a.topk_ws = topk_ws; a.topk_k = k; a.topk_emit = emit; }
   hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
-  if (e == hipSuccess && mid_event) e = hipEventRecord((hipEvent_t)mid_event, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status("dsa_indexer_topk", e);
   dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws, emit ? chunk : 0, emit};
   return hip_status("dsa_indexer_topk", dsa::launch_topk(tk, fused, (hipStream_t)stream));
@@ -181,7 +230,7 @@ dsa_status_t dsa_indexer_scores_hist(const dsa_indexer_desc_t* d, const void* q,
   if (st != DSA_OK || d->num_q == 0) return st;
   dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
                                         ld_scores);
-  const bool fused = d->k_dtype == DSA_FP8_E4M3FN && !dsa::indexer_grouped(d->num_q, d->k_dtype);
+  const bool fused = d->k_dtype == DSA_FP8_E4M3FN && !dsa::indexer_grouped(d->num_q, d->num_seqs, d->k_dtype);
   if (fused) { a.topk_ws = topk_ws; a.topk_k = k; }
   hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
   if (e != hipSuccess || fused) return hip_status("dsa_indexer_scores_hist", e);

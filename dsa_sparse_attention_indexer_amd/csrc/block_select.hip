@@ -173,8 +173,8 @@ hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int64_t nb = nblk_of(a.ld, a.block);
   dim3 g1((unsigned)((nb + 3) / 4), a.T);
-  hipLaunchKernelGGL(k_block_max, g1, dim3(kT), 0, s, a);
-  hipLaunchKernelGGL(k_block_pick, dim3(a.T), dim3(kPT), 0, s, a);
+  launch(k_block_max, g1, dim3(kT), 0, s, a);
+  launch(k_block_pick, dim3(a.T), dim3(kPT), 0, s, a);
   return hipGetLastError();
 }
 

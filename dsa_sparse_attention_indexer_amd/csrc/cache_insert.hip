@@ -327,17 +327,17 @@ int kinsert_splits(int T, int D) {
 hipError_t launch_index_k_insert(const KInsertLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const dim3 g1((unsigned)((a.T + kTileTok - 1) / kTileTok), (unsigned)a.splits);
-  hipLaunchKernelGGL(k_kproj, g1, dim3(kProjThreads), 0, s, a);
+  launch(k_kproj, g1, dim3(kProjThreads), 0, s, a);
   const int W = kFinThreads / 64;
   const unsigned g2 = a.splits <= W ? (unsigned)((a.T + W - 1) / W) : (unsigned)a.T;
-  hipLaunchKernelGGL(k_kfinish, dim3(g2), dim3(kFinThreads), 0, s, a);
+  launch(k_kfinish, dim3(g2), dim3(kFinThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_latent_insert(const LatentInsertLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const dim3 g((unsigned)((a.T + kFinThreads / 64 - 1) / (kFinThreads / 64)));
-  hipLaunchKernelGGL(k_latent, g, dim3(kFinThreads), 0, s, a);
+  launch(k_latent, g, dim3(kFinThreads), 0, s, a);
   return hipGetLastError();
 }
 

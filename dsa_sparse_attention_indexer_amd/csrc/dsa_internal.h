@@ -2,12 +2,27 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <stddef.h>
 
 #include "../../include/dsa.h"
 
 namespace dsa {
+
+// Every kernel of the library is enqueued through launch(): normally a plain launch; while the
+// timing hook (dsa_timing_begin) has a free pair of events, a launch that records the kernel's own
+// start and stop timestamps into them.
+bool timing_take(const void* fn, hipEvent_t* start, hipEvent_t* stop);
+
+template <typename... Params, typename... Args>
+inline void launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+  hipEvent_t e0, e1;
+  if (timing_take(reinterpret_cast<const void*>(kernel), &e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0u, static_cast<Params>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, static_cast<Params>(args)...);
+}
 
 // ---- launch parameter blocks (host-validated, passed by value to the launchers) -------------
 
@@ -105,8 +120,10 @@ struct LatentInsertLaunch {
 constexpr int64_t kTopkMaxCols = int64_t(1) << 22;   // columns a top-k row may have
 
 size_t topk_ws_bytes(int T);
-size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype);
-bool indexer_grouped(int T, dsa_dtype_t k_dtype);   // many-query path: no fused first top-k digit
+size_t indexer_ws_bytes(int T, int B, dsa_dtype_t k_dtype);
+// the grouped score kernel (fp8 keys; many queries, or several per sequence): it writes the
+// scores only, and the selection runs as separate kernels over them
+bool indexer_grouped(int T, int B, dsa_dtype_t k_dtype);
 int indexer_chunk(int T, int max_ctx);              // keys per workgroup of the fp8 decode score kernel
 size_t block_select_ws_bytes(int T, int64_t ld, int block);
 int kinsert_splits(int T, int D);   // hidden-dim splits of the key projection

@@ -467,9 +467,11 @@ static_assert(ring_wait(0, 32) == 10 && ring_wait(1, 32) == 11 && ring_wait(2, 3
 // column order.  kq is twice the chunk's expected share of the k (its share of the row's keys) plus
 // 32; every score whose first digit is >= lb, the digit of the chunk's kq-th largest score (from the
 // chunk's histogram in LDS), is emitted, and the chunk's table entry records (first item,
-// count | lb << 16).  The top-k of the row is contained in the union of the chunks' candidates as
-// long as each chunk's lb is at or below the row's k-th digit, which the selection kernel checks
-// (it selects from the scores directly otherwise).  The scores are read back from memory: this
+// count | lb << 16); the chunk's histogram bins from lb up are added into the row's.  With L the
+// largest lb of the row's chunks, the row histogram is exact from L up and the items at or above
+// L are exactly the row's keys there; when at least k keys lie at or above L the selection kernel
+// finds the row's top k among the items, and otherwise selects from the scores directly.  The
+// scores are read back from memory: this
 // workgroup wrote them, and the barrier before makes them visible to all its threads.
 struct EmitSmem {
   uint32_t sbuf[32];
@@ -488,6 +490,9 @@ __device__ void emit_candidates(const IndexerLaunch& a, int t, int n, int c0, ui
   int lb;
   uint32_t unused;
   tk_find_bin<kTkBins, kThreads>(lh, kq, em.sbuf, &lb, &unused);
+  uint32_t* gh = tk_hist(a.topk_ws, t);   // the row's histogram, from lb up (exact above the row's largest lb)
+  for (int i = lb + (int)threadIdx.x; i < kTkBins; i += kThreads)
+    if (lh[i]) atomicAdd(&gh[i], lh[i]);
   const float* row = a.scores + (size_t)t * a.ld;
   uint32_t key[Q][4];
   const uint32_t mask = tk_load_slices<Q, kThreads>(row, n, c0, key);
@@ -646,21 +651,23 @@ k_index_scores_fp8(IndexerLaunch a) {
     if (hist && g == 0 && rel + col < nrow) atomicAdd(&pu.lh[score_key(sc) >> kTkShift0], 1u);
     rel += kStride;
   }
-  if (hist) {   // this chunk's counts into the row's histogram (read by the next kernel)
+  if (hist) {
     __syncthreads();   // also makes this workgroup's score stores visible to all its threads
-    uint32_t* gh = tk_hist(a.topk_ws, t);
-    for (int i = threadIdx.x; i < kTkBins; i += kThreads)
-      if (pu.lh[i]) atomicAdd(&gh[i], pu.lh[i]);
-    if (a.topk_emit) {
+    if (a.topk_emit) {   // this chunk's candidates and its histogram from their lowest digit up
       __shared__ EmitSmem em;
       emit_candidates<TPW>(a, t, n, c0, nrow, pu.lh, em);
+    } else {             // this chunk's counts into the row's histogram (read by the next kernel)
+      uint32_t* gh = tk_hist(a.topk_ws, t);
+      for (int i = threadIdx.x; i < kTkBins; i += kThreads)
+        if (pu.lh[i]) atomicAdd(&gh[i], pu.lh[i]);
     }
   }
 }
 
-// Grouped variant for many queries (prefill).  Workgroup (x, y) scores key chunk x for the four
-// queries 4y..4y+3, one per wave, with operands prepared once per query in the workspace.  When the
-// four queries read the same sequence (consecutive queries of a chunked prefill), each 32-key tile
+// Grouped variant for many queries, or several per sequence (chunked prefill, multi-token verify
+// blocks).  Workgroup (x, y) scores key chunk x for the four queries 4y..4y+3, one per wave, with
+// operands prepared once per query in the workspace.  When the four queries read the same sequence
+// (consecutive queries of a prefill chunk or of a verify block), each 32-key tile
 // is gathered once into an LDS ring (global_load_lds, one 16-byte chunk per lane) and all four waves
 // read their MFMA B operands from it, so the key stream is read from memory once per four queries.
 // Otherwise every wave streams its own keys from memory as the decode kernel does.
@@ -881,12 +888,16 @@ k_index_scores_f32(IndexerLaunch a, const void* ws) {
 // fp8 keys take the grouped path (queries prepared once into the workspace) from this many queries on
 constexpr int kGroupedMinQueries = 256;
 
-size_t indexer_ws_bytes(int T, dsa_dtype_t k_dtype) {
-  if (k_dtype == DSA_FP8_E4M3FN && T < kGroupedMinQueries) return 0;
-  return (size_t)T * kQPrepBytes;
+// ... or when there are at least two queries per sequence (verify blocks of several tokens per
+// sequence, chunked prefill): consecutive queries of one sequence then share one key stream.
+bool indexer_grouped(int T, int B, dsa_dtype_t k_dtype) {
+  return k_dtype == DSA_FP8_E4M3FN && (T >= kGroupedMinQueries || (B > 0 && T >= 2 * B));
 }
 
-bool indexer_grouped(int T, dsa_dtype_t k_dtype) { return k_dtype == DSA_FP8_E4M3FN && T >= kGroupedMinQueries; }
+size_t indexer_ws_bytes(int T, int B, dsa_dtype_t k_dtype) {
+  if (k_dtype == DSA_FP8_E4M3FN && !indexer_grouped(T, B, k_dtype)) return 0;
+  return (size_t)T * kQPrepBytes;
+}
 
 // 4096-key chunks (32 tiles per wave) when that still gives >= 512 workgroups, else 1024
 int indexer_chunk(int T, int max_ctx) {
@@ -896,16 +907,16 @@ int indexer_chunk(int T, int max_ctx) {
 
 hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
   if (a.T == 0 || a.max_ctx == 0) return hipSuccess;
-  if (indexer_grouped(a.T, a.k_dtype)) {
-    hipLaunchKernelGGL(k_index_qprep_fp8, dim3(a.T), dim3(kThreads), 0, s, a, ws);
+  if (indexer_grouped(a.T, a.B, a.k_dtype)) {
+    launch(k_index_qprep_fp8, dim3(a.T), dim3(kThreads), 0, s, a, ws);
     dim3 grid((a.max_ctx + kTile * 32 - 1) / (kTile * 32), (a.T + kGroup - 1) / kGroup);
-    hipLaunchKernelGGL(k_index_scores_fp8_grouped<32>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
+    launch(k_index_scores_fp8_grouped<32>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
   } else if (a.k_dtype == DSA_FP8_E4M3FN) {
     const bool hist = a.topk_ws != nullptr;
     const bool bf = a.q_dtype == DSA_BF16;
     auto go = [&](auto kernel, int chunk) {
       dim3 grid((a.max_ctx + chunk - 1) / chunk, a.T);
-      hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
+      launch(kernel, grid, dim3(kThreads), 0, s, a);
     };
     if (indexer_chunk(a.T, a.max_ctx) == 4096) {
       if (hist) bf ? go(k_index_scores_fp8<32, true, true>, 4096) : go(k_index_scores_fp8<32, true, false>, 4096);
@@ -915,9 +926,9 @@ hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
       else bf ? go(k_index_scores_fp8<8, false, true>, 1024) : go(k_index_scores_fp8<8, false, false>, 1024);
     }
   } else {
-    hipLaunchKernelGGL(k_index_qprep, dim3(a.T), dim3(kThreads), 0, s, a, ws);
+    launch(k_index_qprep, dim3(a.T), dim3(kThreads), 0, s, a, ws);
     dim3 grid((a.max_ctx + kThreads - 1) / kThreads, a.T);
-    hipLaunchKernelGGL(k_index_scores_f32, grid, dim3(kThreads), 0, s, a, (const void*)ws);
+    launch(k_index_scores_f32, grid, dim3(kThreads), 0, s, a, (const void*)ws);
   }
   return hipGetLastError();
 }

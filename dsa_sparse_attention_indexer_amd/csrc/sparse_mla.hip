@@ -104,17 +104,27 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Workgroups are dispatched to the 8 XCDs round-robin by linear id.  A 1-D grid of
-// 8 * inner * ceil(T / 8) workgroups is mapped so that every workgroup of query t runs on XCD t % 8:
-// the splits of a query share one L2 for the query and the row indices, and the combine that reads
-// their partials runs on the XCD whose L2 they were written to.  Returns false for the padding.
-__device__ __forceinline__ bool xcd_query_map(int inner, int T, int* t, int* j) {
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id.  Queries are taken in groups of
+// G consecutive ones (G = T / B when every sequence has the same 2..8 queries, as in multi-token
+// decode where consecutive queries are one sequence's verify block; else 1), and a 1-D grid of
+// 8 * inner * G * ceil(T / 8G) workgroups is mapped so that every workgroup of group q runs on XCD
+// q % 8, the G queries' workgroups for the same inner index next to each other in dispatch order.
+// The splits of a query share one L2 for the query and the row indices, the combine that reads
+// their partials runs on the XCD whose L2 they were written to, and the tokens of one verify block
+// gather their (largely common) latent rows through one L2 at about the same time.  Returns false
+// for the padding.
+__host__ __device__ inline int mla_group(int T, int B) {
+  return (B > 0 && T % B == 0 && T / B >= 2 && T / B <= 8) ? T / B : 1;
+}
+__device__ __forceinline__ bool xcd_query_map(int inner, int T, int G, int* t, int* j) {
   const int id = blockIdx.x, x = id & 7, r = id >> 3;
-  *j = r % inner;
-  *t = 8 * (r / inner) + x;
+  const int per = inner * G;
+  const int rem = r % per;
+  *j = rem / G;
+  *t = G * (8 * (r / per) + x) + rem % G;
   return *t < T;
 }
-inline unsigned xcd_grid(int inner, int T) { return (unsigned)(8 * inner * ((T + 7) / 8)); }
+inline unsigned xcd_grid(int inner, int T, int G) { return (unsigned)(8 * inner * G * ((T + 8 * G - 1) / (8 * G))); }
 
 constexpr int kMlaThreads = 512;   // fp8 path: 8 waves
 
@@ -225,7 +235,7 @@ __global__ void __launch_bounds__(kMlaThreads)
 k_mla_fp8_ws(MlaLaunch a) {
   using C = M2<ROPE>;
   int t, split;
-  if (!xcd_query_map(a.splits, a.T, &t, &split)) return;
+  if (!xcd_query_map(a.splits, a.T, mla_group(a.T, a.B), &t, &split)) return;
   __shared__ __attribute__((aligned(16))) Mla2Smem<ROPE> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -653,7 +663,7 @@ __global__ void __launch_bounds__(kCombineThreads) k_mla_combine(MlaLaunch a) {
   constexpr int SB = BF16 ? 16 : 8;                   // splits per batch of loads
   constexpr int NV = BF16 ? 1 : 2;                    // 16-byte loads per split and lane
   int t, hq;
-  if (!xcd_query_map((a.H + kCombineHeads - 1) / kCombineHeads, a.T, &t, &hq)) return;
+  if (!xcd_query_map((a.H + kCombineHeads - 1) / kCombineHeads, a.T, mla_group(a.T, a.B), &t, &hq)) return;
   const int lane = threadIdx.x & 63;
   const int h = hq * kCombineHeads + (threadIdx.x >> 6);
   if (h >= a.H) return;                               // whole waves; the kernel has no barriers
@@ -718,17 +728,17 @@ hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   dim3 grid(a.splits, a.T);
   if (a.kv_dtype == DSA_FP8_E4M3FN) {
-    const dim3 xgrid(xcd_grid(a.splits, a.T));
-    if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_fp8_ws<64>, xgrid, dim3(kMlaThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_mla_fp8_ws<0>, xgrid, dim3(kMlaThreads), 0, s, a);
+    const dim3 xgrid(xcd_grid(a.splits, a.T, mla_group(a.T, a.B)));
+    if (a.rope_dim == 64) launch(k_mla_fp8_ws<64>, xgrid, dim3(kMlaThreads), 0, s, a);
+    else launch(k_mla_fp8_ws<0>, xgrid, dim3(kMlaThreads), 0, s, a);
   } else {
-    if (a.rope_dim == 64) hipLaunchKernelGGL(k_mla_f32<64>, grid, dim3(kF32Threads), 0, s, a);
-    else hipLaunchKernelGGL(k_mla_f32<0>, grid, dim3(kF32Threads), 0, s, a);
+    if (a.rope_dim == 64) launch(k_mla_f32<64>, grid, dim3(kF32Threads), 0, s, a);
+    else launch(k_mla_f32<0>, grid, dim3(kF32Threads), 0, s, a);
   }
   if (a.splits > 1) {
-    const dim3 cgrid(xcd_grid((a.H + kCombineHeads - 1) / kCombineHeads, a.T));
-    if (a.kv_dtype == DSA_FP8_E4M3FN) hipLaunchKernelGGL(k_mla_combine<true>, cgrid, dim3(kCombineThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_mla_combine<false>, cgrid, dim3(kCombineThreads), 0, s, a);
+    const dim3 cgrid(xcd_grid((a.H + kCombineHeads - 1) / kCombineHeads, a.T, mla_group(a.T, a.B)));
+    if (a.kv_dtype == DSA_FP8_E4M3FN) launch(k_mla_combine<true>, cgrid, dim3(kCombineThreads), 0, s, a);
+    else launch(k_mla_combine<false>, cgrid, dim3(kCombineThreads), 0, s, a);
   }
   return hipGetLastError();
 }

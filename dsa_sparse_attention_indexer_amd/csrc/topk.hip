@@ -262,8 +262,8 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
     return;
   }
 
-  // the row's histogram and segment table in one round of loads; the histogram and the item
-  // counter are then zeroed for the next call
+  // The row's segment table (and, for collected rows, its histogram) in one round of loads; the
+  // histogram and the item counter are then zeroed for the next call.
   const int S = (n + a.seg - 1) / a.seg;
   uint32_t cnt_s = 0, low_s = 0;
   bool seg_bad = false;
@@ -277,15 +277,27 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
     low_s = te.y >> 16;                 // lowest first digit the segment emitted (0 for collect segments)
     // a segment whose items did not fit (or whose start came from a stale counter) wrote none
     seg_bad = tid < S && (te.x > (uint32_t)kTkItemCap || cnt_s > (uint32_t)kTkItemCap - te.x);
+    if (tid == 0) sm.sbuf[28] = 0u;
     __syncthreads();
     reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) rw[kTkOffCtr] = 0u;
+    if (a.emitted && tid < S) atomicMax(&sm.sbuf[28], low_s);
   }
   const bool overflow = __syncthreads_or(seg_bad) != 0;
+  // Emitted rows: each chunk added its bins at or above its own lowest emitted digit, so with L the
+  // largest of those digits the histogram is exact from L up (and the items at or above L are
+  // exactly the row's keys there); the bins below L are dropped.
+  const uint32_t L = sm.sbuf[28];
+  if (a.emitted)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((uint32_t)(4 * tid + j) < L) sm.hist[4 * tid + j] = 0u;
+  __syncthreads();
   int b0;
   uint32_t need_hint;
   tk_find_bin<kTkBins, kRT>(sm.hist, (uint32_t)a.k, sm.sbuf, &b0, &need_hint);
-  // a segment that emitted only digits above b0 may hold keys of the top k it did not emit
+  // a segment that emitted only digits above b0 may hold keys of the top k it did not emit (for
+  // emitted rows: fewer than k keys at or above L, so b0 fell below L)
   const bool incomplete = __syncthreads_or(tid < S && low_s > (uint32_t)b0) != 0;
   if (a.k > kTkFastK || overflow || incomplete) {
     finish_streaming(a, t, n, sm);
@@ -325,10 +337,11 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
       for (int u = 0; u < 4; ++u) {
         const uint32_t i = i0 + (uint32_t)(u * kRT);
         if (i < total) {
+          const uint32_t dg = it[u].x >> kTkShift0;
           sm.key[i] = it[u].x;
           sm.col[i] = it[u].y;
-          gt_b0 += (it[u].x >> kTkShift0) > (uint32_t)b0 ? 1u : 0u;
-          ge_b0 += (it[u].x >> kTkShift0) >= (uint32_t)b0 ? 1u : 0u;
+          gt_b0 += dg > (uint32_t)b0 ? 1u : 0u;
+          ge_b0 += dg >= (uint32_t)b0 ? 1u : 0u;
         }
       }
     }
@@ -419,7 +432,7 @@ hipError_t launch_topk_hist(const TopkLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int64_t cols = a.ld < a.ncap ? a.ld : a.ncap;
   const dim3 seg_grid((unsigned)((cols + kTkSeg - 1) / kTkSeg), (unsigned)a.T);
-  hipLaunchKernelGGL(k_topk_hist, seg_grid, dim3(kCT), 0, s, a);
+  launch(k_topk_hist, seg_grid, dim3(kCT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -427,13 +440,13 @@ hipError_t launch_topk(const TopkLaunch& a, bool hist_given, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int64_t cols = a.ld < a.ncap ? a.ld : a.ncap;
   const dim3 seg_grid((unsigned)((cols + kTkSeg - 1) / kTkSeg), (unsigned)a.T);
-  if (!hist_given) hipLaunchKernelGGL(k_topk_hist, seg_grid, dim3(kCT), 0, s, a);
+  if (!hist_given) launch(k_topk_hist, seg_grid, dim3(kCT), 0, s, a);
   TopkLaunch r = a;
   if (!a.emitted) {
     r.seg = kTkSeg;
-    if (a.k <= kTkFastK) hipLaunchKernelGGL(k_topk_collect, seg_grid, dim3(kCT), 0, s, r);
+    if (a.k <= kTkFastK) launch(k_topk_collect, seg_grid, dim3(kCT), 0, s, r);
   }
-  hipLaunchKernelGGL(k_topk_resolve, dim3(a.T), dim3(kRT), 0, s, r);
+  launch(k_topk_resolve, dim3(a.T), dim3(kRT), 0, s, r);
   return hipGetLastError();
 }
 

@@ -9,9 +9,14 @@
 //                           a score chunk)
 //   items  [kTkItemCap][2]  (key, column) of every score whose first digit is >= the segment's
 //                           lowest emitted digit, in column order within each segment
-// The histogram only steers the fast path: the resolve kernel checks against the collected items
-// that the digit it names holds the k-th largest key, and otherwise selects by exact passes over
-// the row.  The resolve kernel that finishes a row clears its histogram and counter, so stale
+// Collected rows: the histogram only steers the fast path: the resolve kernel checks against the
+// collected items that the digit it names holds the k-th largest key, and otherwise selects by
+// exact passes over the row.  Emitted rows (score chunks that emit their own candidates) add only
+// their bins at or above their lowest emitted digit: with L the largest such digit of the row's
+// segments, the histogram is exact from L up and the items at or above L are exactly the row's
+// keys there; the resolve kernel drops the bins below L and proceeds as above (b0 below L means
+// fewer than k keys at or above L: exact passes).  The
+// resolve kernel that finishes a row clears its histogram and counter, so stale
 // contents (an interrupted call, a different k, a workspace never cleared) cost speed, never
 // correctness.
 #pragma once

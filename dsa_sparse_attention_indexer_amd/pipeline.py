@@ -83,13 +83,11 @@ def attend(wl, buf: StepBuffers, *, prefill: bool = False, num_splits: int = 0, 
                                  stream=stream)
 
 
-def index_and_select(wl, buf: StepBuffers, stream=None, mid_event=None):
-    """Scores and top-k in one call (histogram of the first radix digit and each chunk's candidates
-    built by the score kernel); mid_event is recorded between the score kernel and the selection."""
+def index_and_select(wl, buf: StepBuffers, stream=None):
+    """Scores and top-k in one call (histogram of the first radix digit fused into the scores)."""
     return dsa_indexer_topk(wl.index_q, wl.index_w, wl.q_seq, wl.q_pos, wl.index_k, buf.scores, wl.topk, buf.idx,
                             buf.length, k_scale=wl.index_k_scale, ssmax_s=wl.ssmax_s, ssmax_b=wl.ssmax_b,
-                            inv_freq=wl.inv_freq, ws=buf.ws_index, topk_ws=buf.ws_topk, stream=stream,
-                            mid_event=mid_event)
+                            inv_freq=wl.inv_freq, ws=buf.ws_index, topk_ws=buf.ws_topk, stream=stream)
 
 
 def index_scores_hist(wl, buf: StepBuffers, stream=None):

@@ -149,24 +149,17 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
                       int32_t k, int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream);
 
 /* Scores and top-k in one call: dsa_indexer_scores followed by dsa_topk, with the first radix
- * digit's histogram built inside the fp8 score kernel (the scores are still written to `scores`)
- * and, on the fp8 decode path, each score chunk emitting its own top-k candidates (the scores at or
- * above the bin of the chunk's few-hundredth largest), so that the selection needs no second pass
- * over the scores ("Day 0 support for Mistral Large 4 on vLLM", "Long context: decode and prefill
- * context parallelism": each rank's local top-k candidates feed the exact global selection).  A row
- * whose candidates cannot be shown to contain its top k is selected from the scores directly.
+ * digit's histogram built inside the fp8 score kernel (the scores are still written to `scores`).
  * Same arguments, conventions and results as the two calls made in sequence, except that a row
  * holds min(q_pos + 1, max_ctx) scores (the score kernel's clamp).  `topk_ws` follows dsa_topk's
- * workspace rules.  mid_event: NULL, or a hipEvent_t recorded on `stream` after the score kernel
- * and before the selection kernels (for callers that time the two halves). */
+ * workspace rules. */
 size_t dsa_topk_workspace_size(int32_t num_q, int64_t ld_scores, int32_t k);
 dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* desc, const void* q, const float* w,
                               const int32_t* q_seq, const int32_t* q_pos,
                               const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                               const void* k_cache, const float* k_scale,
                               float* scores, int64_t ld_scores, int32_t k, int32_t* idx, int32_t* len,
-                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream,
-                              void* mid_event);
+                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream);
 
 /* The two halves of dsa_indexer_topk as separate calls, for callers that schedule or time the
  * score stream and the selection apart.  dsa_indexer_scores_hist writes the scores (as
@@ -336,6 +329,27 @@ dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* desc, const void* x, c
 dsa_status_t dsa_latent_insert(int32_t num_tokens, int32_t rope_dim, const void* kv, int64_t ld_kv,
                                const int32_t* pos, const float* inv_freq, const int64_t* slot,
                                int64_t num_slots, uint8_t* kv_cache, float* kv_scale, void* stream);
+
+/* ============================================================================================
+ * Kernel timing (measurement, not serving)
+ * --------------------------------------------------------------------------------------------
+ * For benchmarks that need each kernel's own duration inside a running pipeline without adding
+ * work to the stream.  After dsa_timing_begin(events, capacity), each kernel the library enqueues
+ * (from any entry point, on any stream) takes the next pair events[2i], events[2i+1] as its start
+ * and stop events (hipExtLaunchKernel's: the timestamps of the kernel's own dispatch, no marker
+ * packets), until `capacity` kernels have taken one; later kernels are enqueued untimed.
+ *   events   2 * capacity hipEvent_t handles, created by the caller (timing enabled), which must
+ *            stay valid until the stream has passed the last timed kernel; read them with
+ *            hipEventElapsedTime after synchronising.
+ * dsa_timing_end() disarms the hook and returns how many kernels took a pair;
+ * dsa_timing_kernel_name(i) names the kernel of pair i (owned by the runtime; NULL if i is out
+ * of range).  The hook is process-wide state: arm it from the thread that enqueues the work and
+ * do not call the library from other threads meanwhile.  Returns DSA_ERR_ARG for a NULL array
+ * or capacity < 1 or > 65536.
+ * ==========================================================================================*/
+dsa_status_t dsa_timing_begin(void* const* events, int32_t capacity);
+int32_t dsa_timing_end(void);
+const char* dsa_timing_kernel_name(int32_t i);
 
 #ifdef __cplusplus
 }

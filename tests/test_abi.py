@@ -53,7 +53,7 @@ def test_indexer_topk_requires_its_workspace(dsa):
     L = dsa.lib()
     d = dsa.IndexerDesc(2, 64, 128, 64, 1, 100, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN)
     st = L.dsa_indexer_topk(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 100, 2048,
-                            None, None, None, 0, None, 0, None, None)
+                            None, None, None, 0, None, 0, None)
     msg = L.dsa_last_error().decode()
     assert st == dsa.DSA_ERR_ARG and "top-k workspace" in msg and "non-NULL" in msg, msg
 
@@ -137,3 +137,15 @@ def test_mla_rejects_a_zero_topk_without_dividing_by_zero(dsa):
     st = L.dsa_sparse_mla_decode(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None)
     assert st == dsa.DSA_ERR_ARG and "topk" in L.dsa_last_error().decode()
     assert L.dsa_sparse_mla_workspace_size(ctypes.byref(d)) == 0
+
+
+def test_timing_hook_rejects_bad_arguments_and_disarms_cleanly(dsa):
+    L = dsa.lib()
+    assert L.dsa_timing_begin(None, 4) == dsa.DSA_ERR_ARG
+    arr = (ctypes.c_void_p * 2)()
+    assert L.dsa_timing_begin(arr, 0) == dsa.DSA_ERR_ARG
+    assert L.dsa_timing_begin(arr, 65537) == dsa.DSA_ERR_ARG
+    assert L.dsa_timing_begin(arr, 1) == dsa.DSA_OK
+    assert L.dsa_timing_end() == 0          # nothing launched while armed
+    assert L.dsa_timing_kernel_name(0) is None
+    assert L.dsa_timing_end() == 0          # ending twice is harmless

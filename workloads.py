@@ -232,6 +232,33 @@ def config4(device="cpu", seed=4, batch=4, ctx=524288):
                          max_ctx=ctx, num_heads=4, device=device)
 
 
+def verify_blocks(device="cpu", seed=5, batch=16, tokens=4, ctx=131072, seq_lens=None, max_ctx=None,
+                  drift=0.25, **kw):
+    """Multi-token decode: each of `batch` sequences verifies a block of `tokens` consecutive query
+    tokens at its last positions (a speculative-decoding verify block; the block's own keys are
+    already in the caches and each token attends causally, up to its own position).  Query t is
+    token t % tokens of sequence t // tokens.  Neighbouring tokens of a text select largely the
+    same keys; here every token's index queries and head weights are its block's first token's
+    plus drift * N(0, 1), which gives that overlap.  The attention queries are independent."""
+    lens = [ctx] * batch if seq_lens is None else list(seq_lens)
+    B = len(lens)
+    pos = [n - tokens + j for n in lens for j in range(tokens)]
+    seqs = [b for b in range(B) for _ in range(tokens)]
+    wl = make_workload(name=f"verify_b{B}x{tokens}_ctx{max(lens)}_fp8", seed=seed, seq_lens=lens,
+                       max_ctx=max(lens) if max_ctx is None else max_ctx, q_positions=pos, q_seqs=seqs,
+                       device=device, **kw)
+    gen = torch.Generator(device=torch.device(device))
+    gen.manual_seed(int(seed) + 7)
+    T, H, D = wl.index_q.shape
+    anchor_q = wl.index_q.float().reshape(B, tokens, H, D)[:, :1]
+    anchor_w = wl.index_w.float().reshape(B, tokens, H)[:, :1]
+    q = anchor_q + drift * _normal(gen, (B, tokens, H, D), wl.index_q.device)
+    w = anchor_w + drift * _normal(gen, (B, tokens, H), wl.index_q.device)
+    q[:, 0], w[:, 0] = anchor_q[:, 0], anchor_w[:, 0]
+    return dataclasses.replace(wl, index_q=q.reshape(T, H, D).to(wl.index_q.dtype).contiguous(),
+                               index_w=w.reshape(T, H).contiguous())
+
+
 HIDDEN = 6144   # Mistral Large 4 hidden size (the indexer key projection's input width)
 
 
