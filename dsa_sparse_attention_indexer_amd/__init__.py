@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_HIP = 0, 1, 2, 3
 DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class DsaError(RuntimeError):
@@ -43,6 +43,11 @@ class MlaDesc(ctypes.Structure):
                 ("num_splits", ctypes.c_int32)]
 
 
+class PagingDesc(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("num_seqs", ctypes.c_int32)]
+
+
 class IndexKDesc(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("ld_x", ctypes.c_int64),
                 ("rope_dim", ctypes.c_int32), ("eps", ctypes.c_float), ("num_slots", ctypes.c_int64)]
@@ -54,6 +59,7 @@ def _load():
                           "(there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    PG = ctypes.POINTER(PagingDesc)
     sig = {
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_abi_version": (I32, []),
@@ -61,23 +67,24 @@ def _load():
         "dsa_timing_end": (I32, []),
         "dsa_timing_kernel_name": (ctypes.c_char_p, [I32]),
         "dsa_indexer_workspace_size": (SZ, [ctypes.POINTER(IndexerDesc)]),
-        "dsa_indexer_scores": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, P, SZ, P]),
+        "dsa_indexer_scores": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, P, SZ, P, PG]),
         "dsa_indexer_topk": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, P, P, P, SZ,
-                                   P, SZ, P]),
+                                   P, SZ, P, PG]),
         "dsa_indexer_scores_hist": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, P, SZ,
-                                          P, SZ, P]),
+                                          P, SZ, P, PG]),
         "dsa_topk_hist": (I32, [ctypes.POINTER(IndexerDesc), P, I64, P, I32, P, P, P, SZ, P]),
         "dsa_topk_workspace_size": (SZ, [I32, I64, I32]),
         "dsa_topk": (I32, [P, I64, P, I32, I32, P, P, P, SZ, P]),
         "dsa_block_select_workspace_size": (SZ, [I32, I64, I32]),
         "dsa_block_select": (I32, [P, I64, P, I32, I32, I32, I32, P, P, P, SZ, P]),
         "dsa_sparse_mla_workspace_size": (SZ, [ctypes.POINTER(MlaDesc)]),
-        "dsa_sparse_mla_decode": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P]),
-        "dsa_sparse_mla_prefill": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dsa_sparse_mla_decode": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P, PG]),
+        "dsa_sparse_mla_prefill": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P, PG]),
         "dsa_sparse_mla_noalloc_max_bytes": (SZ, []),
-        "dsa_sparse_mla_decode_noalloc": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P]),
+        "dsa_sparse_mla_decode_noalloc": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, PG]),
         "dsa_index_k_insert_workspace_size": (SZ, [ctypes.POINTER(IndexKDesc)]),
-        "dsa_index_k_insert": (I32, [ctypes.POINTER(IndexKDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dsa_index_k_insert": (I32, [ctypes.POINTER(IndexKDesc), P, P, P, P, P, P, P, P, P, P, SZ, P, PG]),
+        "dsa_paged_slots": (I32, [PG, I32, P, P, P, P]),
         "dsa_latent_insert": (I32, [I32, I32, P, I64, P, P, P, I64, P, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -98,7 +105,7 @@ EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_workspace_size", "
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_sparse_mla_noalloc_max_bytes",
             "dsa_sparse_mla_decode_noalloc", "dsa_index_k_insert_workspace_size",
             "dsa_index_k_insert", "dsa_latent_insert", "dsa_timing_begin", "dsa_timing_end",
-            "dsa_timing_kernel_name"]
+            "dsa_timing_kernel_name", "dsa_paged_slots"]
 
 
 def lib():
@@ -133,6 +140,43 @@ def _dev(name, t, dtype=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+class Paging:
+    """A paged cache layout (the header's "Paged caches"): block_table [num_seqs][blocks_per_seq]
+    i32 on the GPU, page_size tokens per block, num_blocks blocks in the pool, and max_ctx, the
+    longest sequence the table describes (at most blocks_per_seq * page_size)."""
+
+    def __init__(self, block_table: torch.Tensor, page_size: int, num_blocks: int, max_ctx: int):
+        _dev("block_table", block_table, torch.int32)
+        if block_table.dim() != 2:
+            raise ValueError("block_table must be [num_seqs][blocks_per_seq]")
+        self.block_table, self.page_size, self.num_blocks = block_table, int(page_size), int(num_blocks)
+        self.num_seqs, self.blocks_per_seq = int(block_table.shape[0]), int(block_table.shape[1])
+        self.max_ctx = int(max_ctx)
+        self.desc = PagingDesc(block_table.data_ptr(), self.page_size, self.blocks_per_seq, self.num_blocks,
+                               self.num_seqs)
+
+    @property
+    def pool_rows(self) -> int:
+        return self.num_blocks * self.page_size
+
+
+def _pg(paging):
+    return None if paging is None else ctypes.byref(paging.desc)
+
+
+def _seq_dims(cache, paging):
+    """(num_seqs, max_ctx) of a contiguous cache [B][max_ctx][row], or of a paged one."""
+    if paging is None:
+        return int(cache.shape[0]), int(cache.shape[1])
+    if cache.shape[0] * (cache.shape[1] if cache.dim() == 3 else 1) != paging.pool_rows:
+        raise ValueError("a paged cache must hold num_blocks * page_size rows")
+    return paging.num_seqs, paging.max_ctx
+
+
+def _rows_of(cache, paging):
+    return cache.shape[:2] if paging is None else (paging.pool_rows,)
+
+
 def _qdtype(t):
     return {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}[t.dtype]
 
@@ -149,15 +193,15 @@ def dsa_indexer_workspace_size(desc: IndexerDesc) -> int:
     return int(_lib.dsa_indexer_workspace_size(ctypes.byref(desc)))
 
 
-def indexer_desc(q, k_cache, inv_freq=None) -> IndexerDesc:
+def indexer_desc(q, k_cache, inv_freq=None, paging=None) -> IndexerDesc:
     T, H, D = q.shape
-    B, max_ctx, _ = k_cache.shape
+    B, max_ctx = _seq_dims(k_cache, paging)
     rope = 0 if inv_freq is None else 2 * int(inv_freq.numel())
     return IndexerDesc(T, H, D, rope, B, max_ctx, _qdtype(q), _kdtype(k_cache))
 
 
 def dsa_indexer_scores(q, w, q_seq, q_pos, k_cache, scores, k_scale=None, ssmax_s=None, ssmax_b=None,
-                       inv_freq=None, ws=None, stream=None):
+                       inv_freq=None, ws=None, stream=None, paging=None):
     """Fills scores[t, 0..q_pos[t]] with the lightning-indexer score of every visible key.
 
     q [T][H][128] f32|bf16, w [T][H] f32, q_seq/q_pos [T] i32, k_cache [B][max_ctx][128] f32 or
@@ -165,41 +209,41 @@ def dsa_indexer_scores(q, w, q_seq, q_pos, k_cache, scores, k_scale=None, ssmax_
     inv_freq [32] f32 on RoPE layers (None on NoPE layers), scores [T][ld] f32 with ld >= max_ctx.
     """
     T, H, D = q.shape
-    B, max_ctx, _ = k_cache.shape
+    B, max_ctx = _seq_dims(k_cache, paging)
     _dev("q", q, (torch.float32, torch.bfloat16))
     _dev("w", w, torch.float32, (T, H))
     _dev("q_seq", q_seq, torch.int32, (T,))
     _dev("q_pos", q_pos, torch.int32, (T,))
     _dev("k_cache", k_cache, (torch.float32, torch.uint8, torch.float8_e4m3fn))
-    _dev("k_scale", k_scale, torch.float32, (B, max_ctx))
+    _dev("k_scale", k_scale, torch.float32, _rows_of(k_cache, paging))
     _dev("ssmax_s", ssmax_s, torch.float32, (H,))
     _dev("ssmax_b", ssmax_b, torch.float32, (H,))
     _dev("inv_freq", inv_freq, torch.float32)
     _dev("scores", scores, torch.float32)
     if scores.dim() != 2 or scores.shape[0] != T:
         raise ValueError("scores must be [T][ld]")
-    d = indexer_desc(q, k_cache, inv_freq)
+    d = indexer_desc(q, k_cache, inv_freq, paging)
     if ws is None:
         ws = torch.empty(max(16, dsa_indexer_workspace_size(d)), dtype=torch.uint8, device=q.device)
     _dev("ws", ws, torch.uint8)
     _check(_lib.dsa_indexer_scores(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
                                    _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores),
-                                   scores.shape[1], _ptr(ws), ws.numel(), _stream(stream)))
+                                   scores.shape[1], _ptr(ws), ws.numel(), _stream(stream), _pg(paging)))
     return scores
 
 
 def dsa_indexer_topk(q, w, q_seq, q_pos, k_cache, scores, k, idx, length=None, k_scale=None, ssmax_s=None,
-                     ssmax_b=None, inv_freq=None, ws=None, topk_ws=None, stream=None):
+                     ssmax_b=None, inv_freq=None, ws=None, topk_ws=None, stream=None, paging=None):
     """Scores and top-k selection in one call (the fp8 score kernel also builds the first radix
     digit's histogram).  Arguments as dsa_indexer_scores plus dsa_topk's."""
     T, H, D = q.shape
-    B, max_ctx, _ = k_cache.shape
+    B, max_ctx = _seq_dims(k_cache, paging)
     _dev("q", q, (torch.float32, torch.bfloat16))
     _dev("w", w, torch.float32, (T, H))
     _dev("q_seq", q_seq, torch.int32, (T,))
     _dev("q_pos", q_pos, torch.int32, (T,))
     _dev("k_cache", k_cache, (torch.float32, torch.uint8, torch.float8_e4m3fn))
-    _dev("k_scale", k_scale, torch.float32, (B, max_ctx))
+    _dev("k_scale", k_scale, torch.float32, _rows_of(k_cache, paging))
     _dev("ssmax_s", ssmax_s, torch.float32, (H,))
     _dev("ssmax_b", ssmax_b, torch.float32, (H,))
     _dev("inv_freq", inv_freq, torch.float32)
@@ -209,7 +253,7 @@ def dsa_indexer_topk(q, w, q_seq, q_pos, k_cache, scores, k, idx, length=None, k
     if scores.dim() != 2 or scores.shape[0] != T:
         raise ValueError("scores must be [T][ld]")
     ld = scores.shape[1]
-    d = indexer_desc(q, k_cache, inv_freq)
+    d = indexer_desc(q, k_cache, inv_freq, paging)
     if ws is None:
         ws = torch.empty(max(16, dsa_indexer_workspace_size(d)), dtype=torch.uint8, device=q.device)
     if topk_ws is None:
@@ -219,22 +263,22 @@ def dsa_indexer_topk(q, w, q_seq, q_pos, k_cache, scores, k, idx, length=None, k
     _check(_lib.dsa_indexer_topk(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
                                  _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores), ld, k,
                                  _ptr(idx), _ptr(length), _ptr(ws), ws.numel(), _ptr(topk_ws), topk_ws.numel(),
-                                 _stream(stream)))
+                                 _stream(stream), _pg(paging)))
     return idx, length
 
 
 def dsa_indexer_scores_hist(q, w, q_seq, q_pos, k_cache, scores, k, topk_ws, k_scale=None, ssmax_s=None,
-                            ssmax_b=None, inv_freq=None, ws=None, stream=None):
+                            ssmax_b=None, inv_freq=None, ws=None, stream=None, paging=None):
     """First half of dsa_indexer_topk: the scores, plus each row's first-digit histogram left in
     topk_ws for dsa_topk_hist.  Arguments as dsa_indexer_topk (no index outputs)."""
     T, H, D = q.shape
-    B, max_ctx, _ = k_cache.shape
+    B, max_ctx = _seq_dims(k_cache, paging)
     _dev("q", q, (torch.float32, torch.bfloat16))
     _dev("w", w, torch.float32, (T, H))
     _dev("q_seq", q_seq, torch.int32, (T,))
     _dev("q_pos", q_pos, torch.int32, (T,))
     _dev("k_cache", k_cache, (torch.float32, torch.uint8, torch.float8_e4m3fn))
-    _dev("k_scale", k_scale, torch.float32, (B, max_ctx))
+    _dev("k_scale", k_scale, torch.float32, _rows_of(k_cache, paging))
     _dev("ssmax_s", ssmax_s, torch.float32, (H,))
     _dev("ssmax_b", ssmax_b, torch.float32, (H,))
     _dev("inv_freq", inv_freq, torch.float32)
@@ -242,14 +286,14 @@ def dsa_indexer_scores_hist(q, w, q_seq, q_pos, k_cache, scores, k, topk_ws, k_s
     _dev("topk_ws", topk_ws, torch.uint8)
     if scores.dim() != 2 or scores.shape[0] != T:
         raise ValueError("scores must be [T][ld]")
-    d = indexer_desc(q, k_cache, inv_freq)
+    d = indexer_desc(q, k_cache, inv_freq, paging)
     if ws is None:
         ws = torch.empty(max(16, dsa_indexer_workspace_size(d)), dtype=torch.uint8, device=q.device)
     _dev("ws", ws, torch.uint8)
     _check(_lib.dsa_indexer_scores_hist(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
                                         _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores),
                                         scores.shape[1], k, _ptr(ws), ws.numel(), _ptr(topk_ws), topk_ws.numel(),
-                                        _stream(stream)))
+                                        _stream(stream), _pg(paging)))
     return scores
 
 
@@ -322,9 +366,9 @@ def dsa_block_select(scores, q_pos, idx, length=None, block=128, nblocks=16, ws=
 # 3. sparse MLA
 # ------------------------------------------------------------------------------------------------
 
-def mla_desc(q, kv, idx, softmax_scale, num_splits=0) -> MlaDesc:
+def mla_desc(q, kv, idx, softmax_scale, num_splits=0, paging=None) -> MlaDesc:
     T, H, DQ = q.shape
-    B, max_ctx, row = kv.shape
+    B, max_ctx = _seq_dims(kv, paging)
     rope = DQ - 512
     return MlaDesc(T, H, 512, rope, B, max_ctx, idx.shape[1], _qdtype(q), _kdtype(kv), 64, float(softmax_scale),
                    int(num_splits))
@@ -334,12 +378,12 @@ def dsa_sparse_mla_workspace_size(desc: MlaDesc) -> int:
     return int(_lib.dsa_sparse_mla_workspace_size(ctypes.byref(desc)))
 
 
-def _mla(fn, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale, num_splits, ws, stream):
+def _mla(fn, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale, num_splits, ws, stream, paging=None):
     T, H, DQ = q.shape
-    B, max_ctx, row = kv.shape
+    row = kv.shape[-1]
     _dev("q", q, (torch.float32, torch.bfloat16))
     _dev("kv", kv, (torch.float32, torch.uint8, torch.float8_e4m3fn))
-    _dev("kv_scale", kv_scale, torch.float32, (B, max_ctx, row // 64))
+    _dev("kv_scale", kv_scale, torch.float32, (*_rows_of(kv, paging), row // 64))
     _dev("q_seq", q_seq, torch.int32, (T,))
     _dev("idx", idx, torch.int32)
     _dev("length", length, torch.int32, (T,))
@@ -347,32 +391,32 @@ def _mla(fn, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale, num_s
     _dev("lse", lse, torch.float32, (T, H))
     if row != 576 or DQ not in (512, 576):
         raise ValueError("kv rows must be 576 wide and q 512 (NoPE) or 576 (RoPE) wide")
-    d = mla_desc(q, kv, idx, softmax_scale, num_splits)
+    d = mla_desc(q, kv, idx, softmax_scale, num_splits, paging)
     need = dsa_sparse_mla_workspace_size(d)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     _dev("ws", ws, torch.uint8)
     _check(fn(ctypes.byref(d), _ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(q_seq), _ptr(idx), _ptr(length), _ptr(out),
-              _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+              _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream), _pg(paging)))
     return out, lse
 
 
 def dsa_sparse_mla_decode(q, kv, kv_scale, q_seq, idx, length, out, lse=None, softmax_scale=None, num_splits=0,
-                          ws=None, stream=None):
+                          ws=None, stream=None, paging=None):
     """Sparse MLA for decode (each query's selection split over several workgroups)."""
     return _mla(_lib.dsa_sparse_mla_decode, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale,
-                num_splits, ws, stream)
+                num_splits, ws, stream, paging)
 
 
 def dsa_sparse_mla_decode_noalloc(q, kv, kv_scale, q_seq, idx, length, out, lse=None, softmax_scale=None,
-                                  num_splits=0, stream=None):
+                                  num_splits=0, stream=None, paging=None):
     """dsa_sparse_mla_decode with the split partials in the library's per-GPU scratch buffer (no
     workspace argument, nothing allocated)."""
     T, H, DQ = q.shape
-    B, max_ctx, row = kv.shape
+    row = kv.shape[-1]
     _dev("q", q, (torch.float32, torch.bfloat16))
     _dev("kv", kv, (torch.float32, torch.uint8, torch.float8_e4m3fn))
-    _dev("kv_scale", kv_scale, torch.float32, (B, max_ctx, row // 64))
+    _dev("kv_scale", kv_scale, torch.float32, (*_rows_of(kv, paging), row // 64))
     _dev("q_seq", q_seq, torch.int32, (T,))
     _dev("idx", idx, torch.int32)
     _dev("length", length, torch.int32, (T,))
@@ -380,17 +424,18 @@ def dsa_sparse_mla_decode_noalloc(q, kv, kv_scale, q_seq, idx, length, out, lse=
     _dev("lse", lse, torch.float32, (T, H))
     if row != 576 or DQ not in (512, 576):
         raise ValueError("kv rows must be 576 wide and q 512 (NoPE) or 576 (RoPE) wide")
-    d = mla_desc(q, kv, idx, softmax_scale, num_splits)
+    d = mla_desc(q, kv, idx, softmax_scale, num_splits, paging)
     _check(_lib.dsa_sparse_mla_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(q_seq),
-                                              _ptr(idx), _ptr(length), _ptr(out), _ptr(lse), _stream(stream)))
+                                              _ptr(idx), _ptr(length), _ptr(out), _ptr(lse), _stream(stream),
+                                              _pg(paging)))
     return out, lse
 
 
 def dsa_sparse_mla_prefill(q, kv, kv_scale, q_seq, idx, length, out, lse=None, softmax_scale=None, ws=None,
-                           stream=None):
+                           stream=None, paging=None):
     """Sparse MLA for chunked prefill (one workgroup per query)."""
     return _mla(_lib.dsa_sparse_mla_prefill, q, kv, kv_scale, q_seq, idx, length, out, lse, softmax_scale, 0,
-                ws, stream)
+                ws, stream, paging)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -406,12 +451,13 @@ def dsa_index_k_insert_workspace_size(desc: IndexKDesc) -> int:
 
 
 def dsa_index_k_insert(x, wk, ln_w, ln_b, pos, slot, k_cache, k_scale, inv_freq=None, eps=1e-6, ws=None,
-                       stream=None):
+                       stream=None, paging=None):
     """Indexer keys of x's tokens (LayerNorm of the key projection, RoPE when inv_freq is given,
     FP8 with one scale per token) written into k_cache / k_scale at rows `slot` (-1 = skip).
 
     x [T][hidden] bf16 (rows may be strided), wk [128][hidden] bf16, ln_w / ln_b [128] f32,
-    pos [T] i32, slot [T] i64, k_cache [..., 128] uint8 / float8_e4m3fn, k_scale [...] f32."""
+    pos [T] i32, slot [T] i64, k_cache [..., 128] uint8 / float8_e4m3fn, k_scale [...] f32; with
+    paging, k_cache is the paged pool and a slot's key bytes go to its block's 16x16 tiles."""
     T, hidden = x.shape
     if x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(1) != 1:
         raise ValueError("x must be a bf16 GPU tensor with unit column stride")
@@ -432,8 +478,20 @@ def dsa_index_k_insert(x, wk, ln_w, ln_b, pos, slot, k_cache, k_scale, inv_freq=
     _dev("ws", ws, torch.uint8)
     _check(_lib.dsa_index_k_insert(ctypes.byref(d), _ptr(x), _ptr(wk), _ptr(ln_w), _ptr(ln_b), _ptr(pos),
                                    _ptr(inv_freq), _ptr(slot), _ptr(k_cache), _ptr(k_scale), _ptr(ws),
-                                   0 if ws is None else ws.numel(), _stream(stream)))
+                                   0 if ws is None else ws.numel(), _stream(stream), _pg(paging)))
     return k_cache, k_scale
+
+
+def dsa_paged_slots(paging, seq, pos, slot=None, stream=None):
+    """Pool slot of each (seq[j], pos[j]) by the paged layout rule (-1 where pos[j] < 0)."""
+    n = int(pos.numel())
+    _dev("seq", seq, torch.int32, (n,))
+    _dev("pos", pos, torch.int32, (n,))
+    if slot is None:
+        slot = torch.empty(n, dtype=torch.int64, device=pos.device)
+    _dev("slot", slot, torch.int64, (n,))
+    _check(_lib.dsa_paged_slots(_pg(paging), n, _ptr(seq), _ptr(pos), _ptr(slot), _stream(stream)))
+    return slot
 
 
 def dsa_latent_insert(kv, pos, slot, kv_cache, kv_scale, inv_freq=None, stream=None):

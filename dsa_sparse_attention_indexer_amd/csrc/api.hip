@@ -108,6 +108,21 @@ size_t dsa_indexer_workspace_size(const dsa_indexer_desc_t* d) {
 
 namespace {
 
+// The paged layout's host conditions (the header's "Paged caches"); NULL = contiguous caches.
+dsa::Paging check_paging(Checker& ck, const dsa_paging_t* pg, int32_t num_seqs, int32_t max_ctx, bool fp8) {
+  if (!pg) return dsa::Paging{nullptr, 0, 0, 0};
+  ck.support(fp8, "paged caches are FP8 only");
+  ck.need(pg->block_table != nullptr, "paging->block_table must be non-NULL");
+  ck.support(pg->page_size >= 32 && pg->page_size <= 8192 && pg->page_size % 32 == 0,
+             "paging->page_size must be a multiple of 32 in [32, 8192]");
+  ck.need(pg->blocks_per_seq >= 1, "paging->blocks_per_seq must be >= 1");
+  ck.need(pg->num_blocks >= 1, "paging->num_blocks must be >= 1");
+  ck.need(pg->num_seqs == num_seqs, "paging->num_seqs must equal the descriptor's num_seqs");
+  ck.need((int64_t)pg->blocks_per_seq * pg->page_size >= max_ctx, "paging: blocks_per_seq * page_size must be >= max_ctx");
+  ck.need((int64_t)pg->num_blocks * pg->page_size <= ((int64_t)1 << 31) - 1, "paging: the pool must hold < 2^31 rows");
+  return dsa::Paging{pg->block_table, pg->page_size, pg->blocks_per_seq, pg->num_blocks};
+}
+
 void check_indexer(Checker& ck, const dsa_indexer_desc_t* d, const void* q, const float* w, const int32_t* q_seq,
                    const int32_t* q_pos, const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                    const void* k_cache, const float* k_scale, const float* scores, int64_t ld_scores, const void* ws,
@@ -161,7 +176,7 @@ dsa::IndexerLaunch indexer_launch(const dsa_indexer_desc_t* d, const void* q, co
                                   int64_t ld_scores) {
   return dsa::IndexerLaunch{d->num_q, d->num_heads, d->rope_dim, d->num_seqs, d->max_ctx, d->q_dtype, d->k_dtype,
                             q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores,
-                            nullptr, 0, 0};
+                            nullptr, 0, 0, dsa::Paging{nullptr, 0, 0, 0}};
 }
 
 }  // namespace
@@ -172,15 +187,18 @@ dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* d, const void* q, cons
                                 const int32_t* q_seq, const int32_t* q_pos,
                                 const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                                 const void* k_cache, const float* k_scale,
-                                float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, void* stream) {
+                                float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, void* stream,
+                                const dsa_paging_t* paging) {
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_scores"); }
   check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
                 ws_bytes);
+  const dsa::Paging pg = check_paging(ck, paging, d->num_seqs, d->max_ctx, d->k_dtype == DSA_FP8_E4M3FN);
   dsa_status_t st = ck.finish("dsa_indexer_scores");
   if (st != DSA_OK || d->num_q == 0) return st;
   dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
                                         ld_scores);
+  a.pg = pg;
   return hip_status("dsa_indexer_scores", dsa::launch_indexer(a, ws, (hipStream_t)stream));
 }
 
@@ -189,17 +207,20 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const 
                               const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                               const void* k_cache, const float* k_scale,
                               float* scores, int64_t ld_scores, int32_t k, int32_t* idx, int32_t* len,
-                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream) {
+                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream,
+                              const dsa_paging_t* paging) {
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_topk"); }
   check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
                 ws_bytes);
+  const dsa::Paging pg = check_paging(ck, paging, d->num_seqs, d->max_ctx, d->k_dtype == DSA_FP8_E4M3FN);
   check_topk(ck, d->num_q, ld_scores, k, scores, q_pos, idx);
   check_topk_ws(ck, d->num_q, topk_ws, topk_ws_bytes);
   dsa_status_t st = ck.finish("dsa_indexer_topk");
   if (st != DSA_OK || d->num_q == 0) return st;
   dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
                                         ld_scores);
+  a.pg = pg;
   // The decode score kernel builds the first digit's histogram, and its chunks emit their own
   // candidates when the row's chunks fit the segment table.  The grouped kernel (several queries
   // per sequence) only writes scores: its workgroups are bound by matrix work, and a per-chunk
@@ -219,17 +240,20 @@ dsa_status_t dsa_indexer_scores_hist(const dsa_indexer_desc_t* d, const void* q,
                                      const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                                      const void* k_cache, const float* k_scale,
                                      float* scores, int64_t ld_scores, int32_t k,
-                                     void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream) {
+                                     void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream,
+                                     const dsa_paging_t* paging) {
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish("dsa_indexer_scores_hist"); }
   check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
                 ws_bytes);
+  const dsa::Paging pg = check_paging(ck, paging, d->num_seqs, d->max_ctx, d->k_dtype == DSA_FP8_E4M3FN);
   check_topk(ck, d->num_q, ld_scores, k, scores, q_pos, nullptr, false);   // no index output in this half
   check_topk_ws(ck, d->num_q, topk_ws, topk_ws_bytes);
   dsa_status_t st = ck.finish("dsa_indexer_scores_hist");
   if (st != DSA_OK || d->num_q == 0) return st;
   dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
                                         ld_scores);
+  a.pg = pg;
   const bool fused = d->k_dtype == DSA_FP8_E4M3FN && !dsa::indexer_grouped(d->num_q, d->num_seqs, d->k_dtype);
   if (fused) { a.topk_ws = topk_ws; a.topk_k = k; }
   hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
@@ -336,7 +360,7 @@ size_t mla_ws_bytes(const dsa_mla_desc_t* d, bool decode) {
 
 dsa_status_t mla_call(const char* fn, bool decode, const dsa_mla_desc_t* d, const void* q, const void* kv,
                       const float* kv_scale, const int32_t* q_seq, const int32_t* idx, const int32_t* len,
-                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream, const dsa_paging_t* paging) {
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish(fn); }
   ck.need(d->num_q >= 0 && d->num_q <= 65535, "num_q must be in [0, 65535]");
@@ -353,8 +377,10 @@ dsa_status_t mla_call(const char* fn, bool decode, const dsa_mla_desc_t* d, cons
     ck.support(d->q_dtype == DSA_BF16, "the FP8 cache path takes BF16 queries");
     ck.support(d->num_heads >= 16 && d->num_heads <= 64 && d->num_heads % 16 == 0,
                "num_heads must be 16, 32, 48 or 64 on the FP8 path");
-    // the kernel addresses a sequence's latent rows with 32-bit byte offsets
+    // the kernel addresses a sequence's latent rows (a paged pool) with 32-bit byte offsets
     ck.support((uint64_t)d->max_ctx * 576 < (uint64_t(1) << 32), "max_ctx must be <= 7456540 on the FP8 path");
+    ck.support(!paging || (uint64_t)paging->num_blocks * (uint64_t)paging->page_size * 576 < (uint64_t(1) << 32),
+               "a paged latent pool must hold fewer than 7456540 rows");
   } else {
     ck.support(d->kv_dtype == DSA_F32, "kv_dtype must be F32 or FP8_E4M3FN");
     ck.support(d->q_dtype == DSA_F32, "the F32 cache path takes F32 queries");
@@ -368,9 +394,12 @@ dsa_status_t mla_call(const char* fn, bool decode, const dsa_mla_desc_t* d, cons
     ck.need(need == 0 || (ws != nullptr && ws_bytes >= need && aligned(ws, 16)),
             "workspace missing, misaligned or smaller than dsa_sparse_mla_workspace_size()");
   }
+  const dsa::Paging pg = check_paging(ck, paging, d->num_seqs, d->max_ctx, fp8);
   dsa_status_t st = ck.finish(fn);
   if (st != DSA_OK || d->num_q == 0) return st;
   dsa::MlaLaunch a{};
+  a.pg = pg;
+  a.pool_rows = pg.table ? (int64_t)pg.nblocks * pg.page : 0;
   a.T = d->num_q; a.H = d->num_heads; a.kv_lora = d->kv_lora; a.rope_dim = d->rope_dim;
   a.B = d->num_seqs; a.max_ctx = d->max_ctx; a.topk = d->topk;
   split_geometry(d, decode, &a.splits, &a.per_split);
@@ -391,14 +420,16 @@ size_t dsa_sparse_mla_workspace_size(const dsa_mla_desc_t* d) {
 
 dsa_status_t dsa_sparse_mla_decode(const dsa_mla_desc_t* d, const void* q, const void* kv, const float* kv_scale,
                                    const int32_t* q_seq, const int32_t* idx, const int32_t* len, float* out,
-                                   float* lse, void* ws, size_t ws_bytes, void* stream) {
-  return mla_call("dsa_sparse_mla_decode", true, d, q, kv, kv_scale, q_seq, idx, len, out, lse, ws, ws_bytes, stream);
+                                   float* lse, void* ws, size_t ws_bytes, void* stream, const dsa_paging_t* paging) {
+  return mla_call("dsa_sparse_mla_decode", true, d, q, kv, kv_scale, q_seq, idx, len, out, lse, ws, ws_bytes, stream,
+                  paging);
 }
 
 dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* d, const void* q, const void* kv, const float* kv_scale,
                                     const int32_t* q_seq, const int32_t* idx, const int32_t* len, float* out,
-                                    float* lse, void* ws, size_t ws_bytes, void* stream) {
-  return mla_call("dsa_sparse_mla_prefill", false, d, q, kv, kv_scale, q_seq, idx, len, out, lse, ws, ws_bytes, stream);
+                                    float* lse, void* ws, size_t ws_bytes, void* stream, const dsa_paging_t* paging) {
+  return mla_call("dsa_sparse_mla_prefill", false, d, q, kv, kv_scale, q_seq, idx, len, out, lse, ws, ws_bytes, stream,
+                  paging);
 }
 
 }  // extern "C"
@@ -444,7 +475,8 @@ size_t dsa_sparse_mla_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
 dsa_status_t dsa_sparse_mla_decode_noalloc(const dsa_mla_desc_t* d, const void* q, const void* kv,
                                            const float* kv_scale, const int32_t* q_seq, const int32_t* idx,
-                                           const int32_t* len, float* out, float* lse, void* stream) {
+                                           const int32_t* len, float* out, float* lse, void* stream,
+                                           const dsa_paging_t* paging) {
   const char* fn = "dsa_sparse_mla_decode_noalloc";
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish(fn); }
@@ -463,7 +495,7 @@ dsa_status_t dsa_sparse_mla_decode_noalloc(const dsa_mla_desc_t* d, const void* 
     }
   }
   return mla_call(fn, true, d, q, kv, kv_scale, q_seq, idx, len, out, lse, ws, need > 0 ? kNoAllocScratchBytes : 0,
-                  stream);
+                  stream, paging);
 }
 
 }  // extern "C"
@@ -485,7 +517,8 @@ size_t dsa_index_k_insert_workspace_size(const dsa_index_k_desc_t* d) { return k
 
 dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* d, const void* x, const void* wk, const float* ln_w,
                                 const float* ln_b, const int32_t* pos, const float* inv_freq, const int64_t* slot,
-                                uint8_t* k_cache, float* k_scale, void* ws, size_t ws_bytes, void* stream) {
+                                uint8_t* k_cache, float* k_scale, void* ws, size_t ws_bytes, void* stream,
+                                const dsa_paging_t* paging) {
   const char* fn = "dsa_index_k_insert";
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish(fn); }
@@ -505,9 +538,16 @@ dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* d, const void* x, cons
     ck.need(ws != nullptr && ws_bytes >= need && aligned(ws, 16),
             "workspace missing, misaligned or smaller than dsa_index_k_insert_workspace_size()");
   }
+  if (paging) {   // the writer needs the block size only (slots come in); the pool is the cache
+    ck.support(paging->page_size >= 32 && paging->page_size <= 8192 && paging->page_size % 32 == 0,
+               "paging->page_size must be a multiple of 32 in [32, 8192]");
+    ck.need(paging->num_blocks >= 1 && (int64_t)paging->num_blocks * paging->page_size == d->num_slots,
+            "num_slots must be paging->num_blocks * paging->page_size");
+  }
   dsa_status_t st = ck.finish(fn);
   if (st != DSA_OK || d->num_tokens == 0) return st;
   dsa::KInsertLaunch a{};
+  a.page = paging ? paging->page_size : 0;
   a.T = d->num_tokens; a.D = d->hidden; a.rope_dim = d->rope_dim;
   a.splits = dsa::kinsert_splits(a.T, a.D);
   a.ld_x = d->ld_x; a.nslots = d->num_slots; a.eps = d->eps;
@@ -539,6 +579,21 @@ dsa_status_t dsa_latent_insert(int32_t num_tokens, int32_t rope_dim, const void*
   a.kv = static_cast<const uint16_t*>(kv); a.pos = pos; a.inv_freq = inv_freq; a.slot = slot;
   a.kv_cache = kv_cache; a.kv_scale = kv_scale;
   return hip_status(fn, dsa::launch_latent_insert(a, (hipStream_t)stream));
+}
+
+dsa_status_t dsa_paged_slots(const dsa_paging_t* paging, int32_t n, const int32_t* seq, const int32_t* pos,
+                             int64_t* slot, void* stream) {
+  const char* fn = "dsa_paged_slots";
+  Checker ck;
+  ck.need(paging != nullptr, "paging is NULL");
+  ck.need(n >= 0, "n must be >= 0");
+  if (!paging) return ck.finish(fn);
+  const dsa::Paging pg = check_paging(ck, paging, paging->num_seqs, 1, true);
+  ck.need(paging->num_seqs >= 1, "paging->num_seqs must be >= 1");
+  if (n > 0) ck.need(seq && pos && slot, "seq, pos and slot must be non-NULL");
+  dsa_status_t st = ck.finish(fn);
+  if (st != DSA_OK || n == 0) return st;
+  return hip_status(fn, dsa::launch_paged_slots(pg, paging->num_seqs, n, seq, pos, slot, (hipStream_t)stream));
 }
 
 }  // extern "C"

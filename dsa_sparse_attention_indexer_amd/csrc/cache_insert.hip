@@ -21,8 +21,9 @@
 //              (exactly one RoPE pair): the slices' sum, LayerNorm with the
 //              population variance, the rotation of pairs j < rope_dim/2 by p * inv_freq[j],
 //              scale = amax / 448 (1 for an all-zero key) and the codes of k / scale, clamped to
-//              +-448 and rounded to nearest even by v_cvt_pk_fp8_f32; one 128-byte row and its
-//              scale stored at the token's slot.
+//              +-448 and rounded to nearest even by v_cvt_pk_fp8_f32; one 128-byte row (in a paged
+//              cache: its eight 16-byte pieces in the block's 16x16 tiles) and its scale stored at
+//              the token's slot.
 // Latent row ("Day 0 support for Mistral Large 4 on vLLM", "Model architecture": 512 latent and 64
 // rotary dims per token; FP8 with one scale per 64 elements, the layout the attention kernels read):
 //   k_latent   one wave per token, 8 lanes per 64-element group (16-byte loads, 8-byte code
@@ -244,7 +245,10 @@ __global__ void __launch_bounds__(kFinThreads) k_kfinish(KInsertLaunch a) {
   }
   const float amax = wave_max(fmaxf(fabsf(k0), fabsf(k1)));
   const float scale = amax > 0.f ? amax / 448.f : 1.f;
-  reinterpret_cast<uint16_t*>(a.k_cache + slot * kKeyDim)[lane] = (uint16_t)fp8_pair(k0, k1, scale);
+  // contiguous rows, or the paged layout's 16x16 tiles (bytes 2 lane and 2 lane + 1 share a tile row)
+  uint8_t* dst = a.page > 0 ? a.k_cache + (slot / a.page) * a.page * kKeyDim + key_tile_byte((int)(slot % a.page), 2 * lane)
+                            : a.k_cache + slot * kKeyDim + 2 * lane;
+  *reinterpret_cast<uint16_t*>(dst) = (uint16_t)fp8_pair(k0, k1, scale);
   if (lane == 0) a.k_scale[slot] = scale;
 }
 
@@ -338,6 +342,24 @@ hipError_t launch_latent_insert(const LatentInsertLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const dim3 g((unsigned)((a.T + kFinThreads / 64 - 1) / (kFinThreads / 64)));
   launch(k_latent, g, dim3(kFinThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+namespace {
+// Pool slot of each (sequence, position) by the paged layout rule; negative positions give -1.
+__global__ void __launch_bounds__(256) k_paged_slots(Paging pg, int nseq, int n, const int32_t* seq,
+                                                      const int32_t* pos, int64_t* slot) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= n) return;
+  const int p = pos[j];
+  slot[j] = p < 0 ? -1 : paged_slot(pg, clampi(seq[j], 0, nseq - 1), p);
+}
+}  // namespace
+
+hipError_t launch_paged_slots(const Paging& pg, int nseq, int n, const int32_t* seq, const int32_t* pos, int64_t* slot,
+                              hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  launch(k_paged_slots, dim3((n + 255) / 256), dim3(256), 0, s, pg, nseq, n, seq, pos, slot);
   return hipGetLastError();
 }
 

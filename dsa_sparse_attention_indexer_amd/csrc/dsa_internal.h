@@ -26,6 +26,14 @@ inline void launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t sh
 
 // ---- launch parameter blocks (host-validated, passed by value to the launchers) -------------
 
+// Paged cache layout (the header's "Paged caches"): table == nullptr means contiguous caches.
+struct Paging {
+  const int32_t* table;   // [num_seqs][bps]
+  int page;               // tokens per block (a multiple of 32)
+  int bps;                // table columns
+  int nblocks;            // blocks in the pool
+};
+
 struct IndexerLaunch {
   int T, H, rope_dim, B, max_ctx;
   dsa_dtype_t q_dtype, k_dtype;
@@ -48,6 +56,7 @@ struct IndexerLaunch {
   // the bin of the chunk's kq-th largest) to the row's item list, so the selection needs no second
   // pass over the scores (dsa_indexer_topk only: the emitted items are consumed in the same call)
   int topk_emit;
+  Paging pg;
 };
 
 struct TopkLaunch {
@@ -86,6 +95,8 @@ struct MlaLaunch {
   float* out;
   float* lse;
   float* ws;  // split partials: [T][H][splits][kv_lora] O, then [T][H][splits] m and l
+  Paging pg;
+  int64_t pool_rows;  // rows of kv / kv_scale when paged
 };
 
 struct KInsertLaunch {
@@ -102,6 +113,7 @@ struct KInsertLaunch {
   uint8_t* k_cache;       // [nslots][128] E4M3FN
   float* k_scale;         // [nslots]
   float* ws;              // [splits][T][128] partial projections
+  int page;               // > 0: k_cache is paged with this block size (key bytes in 16x16 tiles)
 };
 
 struct LatentInsertLaunch {
@@ -137,6 +149,8 @@ hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s);
 hipError_t launch_index_k_insert(const KInsertLaunch& a, hipStream_t s);
 hipError_t launch_latent_insert(const LatentInsertLaunch& a, hipStream_t s);
+hipError_t launch_paged_slots(const Paging& pg, int nseq, int n, const int32_t* seq, const int32_t* pos, int64_t* slot,
+                              hipStream_t s);
 
 }  // namespace dsa
 
@@ -153,6 +167,20 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// The paged layout rule, shared by the cache writers and every reader.  Block of position p of
+// sequence b (the table entry clamped into the pool), and the pool slot of (b, p):
+__device__ __forceinline__ int paged_block(const Paging& pg, int b, int p) {
+  return clampi(pg.table[(size_t)b * pg.bps + min(p / pg.page, pg.bps - 1)], 0, pg.nblocks - 1);
+}
+__device__ __forceinline__ int64_t paged_slot(const Paging& pg, int b, int p) {
+  return (int64_t)paged_block(pg, b, p) * pg.page + p % pg.page;
+}
+// Byte d of the key in row i of a block, from the block's first byte: 16-token x 16-byte tiles,
+// the 8 tiles of a 16-token group side by side (a 32-row group is one contiguous 4 KiB range).
+__device__ __forceinline__ uint32_t key_tile_byte(int i, int d) {
+  return 256u * (8u * (uint32_t)(i >> 4) + (uint32_t)(d >> 4)) + 16u * (uint32_t)(i & 15) + (uint32_t)(d & 15);
+}
 
 // Sine and cosine of the RoPE angle p * inv_freq.  The product is exact in float64 (24-bit times
 // 26-bit); it is reduced to [-pi, pi] in float64 with a two-term 2*pi (error far below float32

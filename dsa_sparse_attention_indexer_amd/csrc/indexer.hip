@@ -536,7 +536,7 @@ __device__ void emit_candidates(const IndexerLaunch& a, int t, int n, int c0, ui
 // system serves markedly faster than the per-lane operand pattern; the MFMA operands are then read
 // from LDS (swizzled, conflict-free).  The ring is private, so no barrier is involved: a wave waits
 // for its own loads with vmcnt.
-template <int TPW, bool HIST, bool BF16Q>
+template <int TPW, bool HIST, bool BF16Q, bool PAGED>
 __global__ void __launch_bounds__(kThreads)
 k_index_scores_fp8(IndexerLaunch a) {
   constexpr int chunk = 4 * kTile * TPW;
@@ -561,17 +561,34 @@ k_index_scores_fp8(IndexerLaunch a) {
   const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.k_cache) + ((size_t)b * a.max_ctx + c0) * kD;
   const float* sseq = a.k_scale + (size_t)b * a.max_ctx + c0;
   float* srow = a.scores + (size_t)t * a.ld + c0;
-  const i32x4 krs = rsrc_words(kseq, nrow * kD);
-  const i32x4 srs = rsrc_words(sseq, nrow * 4u);
+  const i32x4 krs = rsrc_words(kseq, PAGED ? 0u : nrow * kD);
+  const i32x4 srs = rsrc_words(sseq, PAGED ? 0u : nrow * 4u);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(srow, nrow * 4u);
   constexpr uint32_t kStride = 4 * kTile;   // the 4 waves interleave 32-key tiles
   WaveRing& wr = ring[wave];
+  // paged caches: lane j holds the block of this wave's tile j (a tile's 32 rows lie in one block;
+  // tiles past the row's end read its last block and are never stored)
+  int blk = 0;
+  if (PAGED && lane < TPW) blk = paged_block(a.pg, b, min(c0 + wave * kTile + lane * (int)kStride, n - 1));
 
   // tile j of this wave (rows wave*32 + j*128 .. of the chunk) into ring slot j % kRing: load c
   // brings rows 8c..8c+7, lane l the 16-byte chunk stored at slot position 64c + l
   const int lr = lane >> 3, lj = lane & 7;
   auto issue = [&](int j) {
     const uint32_t row0 = wave * kTile + (uint32_t)j * kStride;
+    if (PAGED) {   // the tile's 32 rows: one contiguous 4 KiB range of 16x16 tiles in its block
+      const int bj = __builtin_amdgcn_readlane(blk, j);
+      const size_t r0 = (size_t)bj * a.pg.page + (size_t)((c0 + (int)row0) % a.pg.page);
+      const i32x4 trs = rsrc_words(reinterpret_cast<const uint8_t*>(a.k_cache) + r0 * kD, kTile * kD);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 8 * c + lr;
+        const int k = lj ^ ((r >> 1) & 7);
+        bdma16(trs, key_tile_byte(r, 16 * k), &wr.key[j % kRing][64 * c]);
+      }
+      if (lane < kTile) bdma4(rsrc_words(a.k_scale + r0, kTile * 4u), lane * 4u, &wr.sc[j % kRing][0]);
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int r = 8 * c + lr;
@@ -697,8 +714,31 @@ struct SharedTiles {
   float sc[kRingTiles][kTile];
 };
 
-// Waves of mismatched sequences: each streams its own keys (as the decode kernel does).
+// Tile it of a paged chunk (this lane's row col, half g): the tile's 4 KiB of 16x16 tiles in its
+// block, whose id lane `it` of blk holds.
+__device__ __forceinline__ void load_tile_paged(KeyTile& kt, const IndexerLaunch& a, int blk, int it, int c0, int col,
+                                                int g) {
+  const int bj = __builtin_amdgcn_readlane(blk, it);
+  const size_t r0 = (size_t)bj * a.pg.page + (size_t)((c0 + kTile * it) % a.pg.page);
+  const __amdgpu_buffer_rsrc_t trs = make_rsrc(reinterpret_cast<const uint8_t*>(a.k_cache) + r0 * kD, kTile * kD);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    kt.x[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(trs, key_tile_byte(col, 32 * c + 16 * g), 0, 0));
+  kt.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.k_scale + r0, kTile * 4u),
+                                                                         4u * col, 0, 0));
+}
+
+// The block of each of the chunk's tiles for sequence b, tile j in lane j (the last block of the
+// row for tiles past it; their scores are never stored).
 template <int TPW>
+__device__ __forceinline__ int chunk_blocks(const IndexerLaunch& a, int b, int c0, int n) {
+  static_assert(TPW <= 64, "one tile per lane");
+  const int lane = threadIdx.x & 63;
+  return lane < TPW ? paged_block(a.pg, b, min(c0 + kTile * lane, n - 1)) : 0;
+}
+
+// Waves of mismatched sequences: each streams its own keys (as the decode kernel does).
+template <int TPW, bool PAGED>
 __device__ void grouped_private_stream(const IndexerLaunch& a, int t, int c0, const half8* ahi, const half8* alo,
                                        const float* cf) {
   const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
@@ -707,25 +747,30 @@ __device__ void grouped_private_stream(const IndexerLaunch& a, int t, int c0, co
   if (c0 >= n) return;
   const uint32_t nrow = (uint32_t)(min(n, c0 + kTile * TPW) - c0);
   const __amdgpu_buffer_rsrc_t krs =
-      make_rsrc(reinterpret_cast<const uint8_t*>(a.k_cache) + ((size_t)b * a.max_ctx + c0) * kD, nrow * kD);
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.k_scale + (size_t)b * a.max_ctx + c0, nrow * 4u);
+      make_rsrc(reinterpret_cast<const uint8_t*>(a.k_cache) + ((size_t)b * a.max_ctx + c0) * kD, PAGED ? 0u : nrow * kD);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.k_scale + (size_t)b * a.max_ctx + c0, PAGED ? 0u : nrow * 4u);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.scores + (size_t)t * a.ld + c0, nrow * 4u);
   const uint32_t out_off = g == 0 ? 4u * col : 0x80000000u;
+  const int blk = PAGED ? chunk_blocks<TPW>(a, b, c0, n) : 0;
+  auto load = [&](KeyTile& kt, int it) {
+    if (PAGED) load_tile_paged(kt, a, blk, it, c0, col, g);
+    else load_tile(kt, krs, srs, it * kTile + col, g);
+  };
   KeyTile tb[kDepth];
 #pragma unroll
-  for (int i = 0; i < kDepth; ++i) load_tile(tb[i], krs, srs, i * kTile + col, g);
+  for (int i = 0; i < kDepth; ++i) load(tb[i], i);
   uint32_t rel = 0;
 #pragma unroll
   for (int it = 0; it < TPW; ++it) {
     KeyTile& cur = tb[it % kDepth];
     const float sc = tile_scores(cur, ahi, alo, cf);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
-    if (it + kDepth < TPW) load_tile(cur, krs, srs, rel + kDepth * kTile + col, g);
+    if (it + kDepth < TPW) load(cur, it + kDepth);
     rel += kTile;
   }
 }
 
-template <int TPW>
+template <int TPW, bool PAGED>
 __global__ void __launch_bounds__(kThreads)
 k_index_scores_fp8_grouped(IndexerLaunch a, const void* ws) {
   static_assert(TPW >= kRingTiles, "ring shorter than the chunk");
@@ -770,7 +815,7 @@ k_index_scores_fp8_grouped(IndexerLaunch a, const void* ws) {
   };
   if (!uniform) {
     load_operands();
-    if (live) grouped_private_stream<TPW>(a, t, c0, ahi, alo, cf);
+    if (live) grouped_private_stream<TPW, PAGED>(a, t, c0, ahi, alo, cf);
     return;
   }
 
@@ -786,8 +831,15 @@ k_index_scores_fp8_grouped(IndexerLaunch a, const void* ws) {
   // this lane's slot q = 64 * wave + lane of each tile holds row q/8's chunk (q%8) ^ swizzle
   const int q = 64 * wave + lane;
   const int qr = q >> 3, qk = (q & 7) ^ ((qr >> 1) & 7);
+  const int blk = PAGED ? chunk_blocks<TPW>(a, b, c0, nmax) : 0;
   auto issue = [&](int tau) {
     const int slot = tau % kRingTiles;
+    if (PAGED) {   // the tile's rows are one 4 KiB range of 16x16 tiles in its block
+      const size_t r0 = (size_t)__builtin_amdgcn_readlane(blk, tau) * a.pg.page + (size_t)((c0 + kTile * tau) % a.pg.page);
+      dma16(reinterpret_cast<const uint8_t*>(a.k_cache) + r0 * kD + key_tile_byte(qr, 16 * qk), &st.key[slot][64 * wave]);
+      if (lane < kTile / kGroup) dma4(a.k_scale + r0 + (kTile / kGroup) * wave + lane, &st.sc[slot][(kTile / kGroup) * wave]);
+      return;
+    }
     const int r = min(kTile * tau + qr, rows - 1);   // rows past the group's range read a valid row
     dma16(kseq + (size_t)r * kD + 16 * qk, &st.key[slot][64 * wave]);
     if (lane < kTile / kGroup) dma4(sseqp + min(kTile * tau + (kTile / kGroup) * wave + lane, rows - 1),
@@ -910,20 +962,32 @@ hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
   if (indexer_grouped(a.T, a.B, a.k_dtype)) {
     launch(k_index_qprep_fp8, dim3(a.T), dim3(kThreads), 0, s, a, ws);
     dim3 grid((a.max_ctx + kTile * 32 - 1) / (kTile * 32), (a.T + kGroup - 1) / kGroup);
-    launch(k_index_scores_fp8_grouped<32>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
+    if (a.pg.table) launch(k_index_scores_fp8_grouped<32, true>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
+    else launch(k_index_scores_fp8_grouped<32, false>, grid, dim3(kThreads), 0, s, a, (const void*)ws);
   } else if (a.k_dtype == DSA_FP8_E4M3FN) {
     const bool hist = a.topk_ws != nullptr;
     const bool bf = a.q_dtype == DSA_BF16;
+    const bool pg = a.pg.table != nullptr;
     auto go = [&](auto kernel, int chunk) {
       dim3 grid((a.max_ctx + chunk - 1) / chunk, a.T);
       launch(kernel, grid, dim3(kThreads), 0, s, a);
     };
     if (indexer_chunk(a.T, a.max_ctx) == 4096) {
-      if (hist) bf ? go(k_index_scores_fp8<32, true, true>, 4096) : go(k_index_scores_fp8<32, true, false>, 4096);
-      else bf ? go(k_index_scores_fp8<32, false, true>, 4096) : go(k_index_scores_fp8<32, false, false>, 4096);
+      if (pg) {
+        if (hist) bf ? go(k_index_scores_fp8<32, true, true, true>, 4096) : go(k_index_scores_fp8<32, true, false, true>, 4096);
+        else bf ? go(k_index_scores_fp8<32, false, true, true>, 4096) : go(k_index_scores_fp8<32, false, false, true>, 4096);
+      } else {
+        if (hist) bf ? go(k_index_scores_fp8<32, true, true, false>, 4096) : go(k_index_scores_fp8<32, true, false, false>, 4096);
+        else bf ? go(k_index_scores_fp8<32, false, true, false>, 4096) : go(k_index_scores_fp8<32, false, false, false>, 4096);
+      }
     } else {
-      if (hist) bf ? go(k_index_scores_fp8<8, true, true>, 1024) : go(k_index_scores_fp8<8, true, false>, 1024);
-      else bf ? go(k_index_scores_fp8<8, false, true>, 1024) : go(k_index_scores_fp8<8, false, false>, 1024);
+      if (pg) {
+        if (hist) bf ? go(k_index_scores_fp8<8, true, true, true>, 1024) : go(k_index_scores_fp8<8, true, false, true>, 1024);
+        else bf ? go(k_index_scores_fp8<8, false, true, true>, 1024) : go(k_index_scores_fp8<8, false, false, true>, 1024);
+      } else {
+        if (hist) bf ? go(k_index_scores_fp8<8, true, true, false>, 1024) : go(k_index_scores_fp8<8, true, false, false>, 1024);
+        else bf ? go(k_index_scores_fp8<8, false, true, false>, 1024) : go(k_index_scores_fp8<8, false, false, false>, 1024);
+      }
     }
   } else {
     launch(k_index_qprep, dim3(a.T), dim3(kThreads), 0, s, a, ws);

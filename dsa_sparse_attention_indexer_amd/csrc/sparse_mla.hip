@@ -258,16 +258,21 @@ k_mla_fp8_ws(MlaLaunch a) {
   const int b = clampi(a.q_seq[t], 0, a.B - 1);
   const int L = a.len ? clampi(a.len[t], 0, a.topk) : a.topk;
   const int slot1 = min(L, slot0 + a.per_split);
-  const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(a.kv) + (size_t)b * a.max_ctx * kRow;
-  const float* scseq = a.kv_scale + (size_t)b * a.max_ctx * kBlocks;
+  // contiguous caches: the query's sequence; paged: the whole pool (rows are pool slots)
+  const bool paged = a.pg.table != nullptr;
+  const uint8_t* kvseq = reinterpret_cast<const uint8_t*>(a.kv) + (paged ? 0 : (size_t)b * a.max_ctx * kRow);
+  const float* scseq = a.kv_scale + (paged ? 0 : (size_t)b * a.max_ctx * kBlocks);
+  const int64_t seq_rows = paged ? a.pool_rows : a.max_ctx;
   const float zscale = a.softmax_scale * kLog2e;
 
-  // the rows of chunk cb into LDS (PV waves; callers hold a barrier before and after)
+  // the rows of chunk cb into LDS (PV waves; callers hold a barrier before and after): the cache
+  // row of each selected position (its pool slot on a paged cache), -1 for none
   auto store_rows = [&](int nslot, int ntiles) {
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
       const int i = ptid + kPvThreads * u;
-      if (i < ntiles * kT2) sm.rows[i] = (i < nslot && rv[u] >= 0 && rv[u] < a.max_ctx) ? rv[u] : -1;
+      const bool ok = i < nslot && rv[u] >= 0 && rv[u] < a.max_ctx;
+      if (i < ntiles * kT2) sm.rows[i] = ok ? (paged ? (int)paged_slot(a.pg, b, rv[u]) : rv[u]) : -1;
     }
   };
 
@@ -391,10 +396,10 @@ k_mla_fp8_ws(MlaLaunch a) {
     // This wave's gathers of tile tau: LDS rows 16pw .. 16pw + 15, one load per 64-byte segment
     // (lane: row 16pw + lane/4, chunk lane%4 of the segment, rotated by swz) and the scales of the
     // same 16 keys.  The latent rows and scales of the query's sequence are addressed through
-    // buffer descriptors (32-bit offsets: the host checks that a sequence's rows span less than
+    // buffer descriptors (32-bit offsets: the host checks that a sequence's rows, or a paged pool, span less than
     // 4 GiB).  Both row indices are read before the first load goes out.
-    const i32x4 kv_rs = buffer_words(kvseq, (uint32_t)((uint64_t)a.max_ctx * kRow));
-    const i32x4 sc_rs = buffer_words(scseq, (uint32_t)((uint64_t)a.max_ctx * kBlocks * 4));
+    const i32x4 kv_rs = buffer_words(kvseq, (uint32_t)((uint64_t)seq_rows * kRow));
+    const i32x4 sc_rs = buffer_words(scseq, (uint32_t)((uint64_t)seq_rows * kBlocks * 4));
     const uint32_t lds_slots = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)&sm.slot[0][0]);
     const int g_row = lrow(16 * pw + (lane >> 2));           // tile key in LDS row 16pw + lane/4
     const int g_chunk = (lane & 3) ^ swz(lane >> 2);          // its chunk within each segment

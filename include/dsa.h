@@ -63,7 +63,44 @@ const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t dsa_abi_version(void);
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
+
+/* ============================================================================================
+ * Paged caches
+ * --------------------------------------------------------------------------------------------
+ * "Day 0 support for Mistral Large 4 on vLLM", "ROCm implementation details", "DSA indexer on
+ * AITER": the index-key cache is kept in cache blocks, the keys of a block stored in 16x16 tiles,
+ * and one layout rule is shared by the writer and every reader.  Here that rule is:
+ *
+ *   A paged cache is a pool of num_blocks blocks of page_size tokens.  Token p of sequence b lives
+ *   in block k = block_table[b * blocks_per_seq + p / page_size], row i = p % page_size, and its
+ *   pool slot is k * page_size + i.
+ *   Index keys: byte d (0..127) of the FP8 key of slot s (block k, row i) is at byte
+ *       k * page_size * 128 + 256 * (8 * (i / 16) + d / 16) + 16 * (i % 16) + d % 16
+ *     of k_cache: tiles of 16 tokens x 16 bytes, the 8 tiles of a 16-token group side by side (so
+ *     each 32-token group of a block is one contiguous 4 KiB range); its scale is k_scale[s].
+ *   Latent rows: kv_cache[s][0..576) and kv_scale[s][0..9) (whole rows: the sparse attention
+ *     gathers one row per selected token).
+ *
+ * Entry points that take `const dsa_paging_t* paging` read (or write) contiguous caches
+ * [num_seqs][max_ctx] when it is NULL, and the pool through the rule above otherwise; the caches
+ * then hold num_blocks * page_size rows, and num_seqs / max_ctx keep describing the sequences.
+ * page_size is a multiple of 32 in [32, 8192]; blocks_per_seq * page_size >= max_ctx; FP8 caches
+ * only.  The table is device data the host does not read: kernels clamp each entry into
+ * [0, num_blocks), so a bad entry reads or writes another block of the pool, never outside it.
+ * dsa_paged_slots writes slot[j] for (seq[j], pos[j]) by the same rule (for the cache writers,
+ * which take slots); pos[j] < 0 gives -1 (the writers skip it).
+ * ==========================================================================================*/
+typedef struct {
+  const int32_t* block_table;   /* [num_seqs][blocks_per_seq] i32, device                          */
+  int32_t page_size;            /* tokens per block                                                */
+  int32_t blocks_per_seq;       /* table columns                                                   */
+  int32_t num_blocks;           /* blocks in the pool                                              */
+  int32_t num_seqs;             /* table rows                                                      */
+} dsa_paging_t;
+
+dsa_status_t dsa_paged_slots(const dsa_paging_t* paging, int32_t n, const int32_t* seq, const int32_t* pos,
+                             int64_t* slot, void* stream);
 
 /* ============================================================================================
  * 1. Lightning-indexer scores
@@ -89,9 +126,11 @@ int32_t dsa_abi_version(void);
  *   ld_scores >= max_ctx
  *   ws       device workspace of at least dsa_indexer_workspace_size(desc) bytes, 16-byte
  *            aligned: the queries prepared once each (about 20 KiB per query) on the fp32-key
- *            path and, from 256 queries on (prefill), on the fp8 path; 0 bytes otherwise (the fp8
- *            decode kernel prepares its query while its first key tiles are in flight), and then
- *            ws may be NULL.
+ *            path and, on the fp8 path, from 256 queries or two queries per sequence on (chunked
+ *            prefill, multi-token verify blocks: four consecutive queries of one sequence then
+ *            share one key stream); 0 bytes otherwise (the fp8 decode kernel prepares its query
+ *            while its first key tiles are in flight), and then ws may be NULL.
+ *   paging   NULL, or the paged layout of k_cache / k_scale (see "Paged caches").
  *
  * Supported: head_dim == 128; 1 <= num_heads <= 32; rope_dim in {0, 64}; q_dtype F32 or BF16;
  * k_dtype F32 (fp32 vector path) or FP8_E4M3FN (matrix-core path).  Both paths form the rotary
@@ -117,7 +156,8 @@ dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* desc, const void* q, c
                                 const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                                 const void* k_cache, const float* k_scale,
                                 float* scores, int64_t ld_scores,
-                                void* ws, size_t ws_bytes, void* stream);
+                                void* ws, size_t ws_bytes, void* stream,
+                                const dsa_paging_t* paging);
 
 /* ============================================================================================
  * 2a. Top-k selection
@@ -159,7 +199,8 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* desc, const void* q, con
                               const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                               const void* k_cache, const float* k_scale,
                               float* scores, int64_t ld_scores, int32_t k, int32_t* idx, int32_t* len,
-                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream);
+                              void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream,
+                              const dsa_paging_t* paging);
 
 /* The two halves of dsa_indexer_topk as separate calls, for callers that schedule or time the
  * score stream and the selection apart.  dsa_indexer_scores_hist writes the scores (as
@@ -176,7 +217,8 @@ dsa_status_t dsa_indexer_scores_hist(const dsa_indexer_desc_t* desc, const void*
                                      const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                                      const void* k_cache, const float* k_scale,
                                      float* scores, int64_t ld_scores, int32_t k,
-                                     void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream);
+                                     void* ws, size_t ws_bytes, void* topk_ws, size_t topk_ws_bytes, void* stream,
+                                     const dsa_paging_t* paging);
 dsa_status_t dsa_topk_hist(const dsa_indexer_desc_t* desc, const float* scores, int64_t ld_scores,
                            const int32_t* q_pos, int32_t k, int32_t* idx, int32_t* len,
                            void* topk_ws, size_t topk_ws_bytes, void* stream);
@@ -217,6 +259,11 @@ dsa_status_t dsa_block_select(const float* scores, int64_t ld_scores, const int3
  *   out      [num_q][num_heads][kv_lora] f32;        lse [num_q][num_heads] f32 or NULL
  *   ws       workspace of dsa_sparse_mla_workspace_size(desc) bytes (0 is allowed when the
  *            query count alone fills the GPU and no split is needed)
+ *   paging   NULL, or the paged layout of kv / kv_scale (see "Paged caches"; FP8 path only, the
+ *            pool below 2^32 bytes of latent rows)
+ * Decode queries of one sequence that are consecutive and equally many per sequence (2..8, the
+ * tokens of a multi-token verify block) run on one XCD, next to each other, so that the latent
+ * rows their selections share are gathered through one L2.
  * Supported: num_heads a multiple of 16 up to 128; kv_lora == 512; rope_dim in {0, 64};
  * kv_scale_block == 64; (q F32, kv F32) on the fp32 path, (q BF16, kv FP8) on the matrix-core
  * path (fp8 x scale rounded to bf16, bf16 probabilities, fp32 accumulation).
@@ -244,11 +291,13 @@ size_t dsa_sparse_mla_workspace_size(const dsa_mla_desc_t* desc);
 dsa_status_t dsa_sparse_mla_decode(const dsa_mla_desc_t* desc, const void* q, const void* kv,
                                    const float* kv_scale, const int32_t* q_seq, const int32_t* idx,
                                    const int32_t* len, float* out, float* lse,
-                                   void* ws, size_t ws_bytes, void* stream);
+                                   void* ws, size_t ws_bytes, void* stream,
+                                   const dsa_paging_t* paging);
 dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* desc, const void* q, const void* kv,
                                     const float* kv_scale, const int32_t* q_seq, const int32_t* idx,
                                     const int32_t* len, float* out, float* lse,
-                                    void* ws, size_t ws_bytes, void* stream);
+                                    void* ws, size_t ws_bytes, void* stream,
+                                    const dsa_paging_t* paging);
 
 /* Sparse MLA decode that allocates nothing, for callers that cannot allocate device memory or
  * size a workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
@@ -264,7 +313,8 @@ dsa_status_t dsa_sparse_mla_prefill(const dsa_mla_desc_t* desc, const void* q, c
 size_t dsa_sparse_mla_noalloc_max_bytes(void);
 dsa_status_t dsa_sparse_mla_decode_noalloc(const dsa_mla_desc_t* desc, const void* q, const void* kv,
                                            const float* kv_scale, const int32_t* q_seq, const int32_t* idx,
-                                           const int32_t* len, float* out, float* lse, void* stream);
+                                           const int32_t* len, float* out, float* lse, void* stream,
+                                           const dsa_paging_t* paging);
 
 /* ============================================================================================
  * 0. Cache writers
@@ -288,8 +338,12 @@ dsa_status_t dsa_sparse_mla_decode_noalloc(const dsa_mla_desc_t* desc, const voi
  *   wk       [128][hidden] BF16, 16-byte aligned          key projection weight (output dim first)
  *   ln_w     [128] f32;  ln_b [128] f32 or NULL (no bias)
  *   pos      [num_tokens] i32;  inv_freq [32] f32 (RoPE layers; ignored when rope_dim = 0)
- *   slot     [num_tokens] i64  destination row; in the readers' layout seq * max_ctx + position.
+ *   slot     [num_tokens] i64  destination row; in the readers' contiguous layout
+ *            seq * max_ctx + position, in a paged cache the token's pool slot (dsa_paged_slots).
  *            A negative slot (padding token) or one >= num_slots is skipped.
+ *   paging   NULL (k_cache rows are 128 contiguous bytes per slot) or the paged layout: the key
+ *            bytes of a slot go to their 16x16 tiles (see "Paged caches"; num_slots is then
+ *            num_blocks * page_size).
  *   k_cache  [num_slots][128] E4M3FN bytes, 2-byte aligned;  k_scale [num_slots] f32 (the index cache and its
  *            per-token scales as dsa_indexer_scores reads them)
  *   ws       workspace of dsa_index_k_insert_workspace_size(desc) bytes, 16-byte aligned
@@ -310,7 +364,8 @@ size_t dsa_index_k_insert_workspace_size(const dsa_index_k_desc_t* desc);
 dsa_status_t dsa_index_k_insert(const dsa_index_k_desc_t* desc, const void* x, const void* wk,
                                 const float* ln_w, const float* ln_b, const int32_t* pos,
                                 const float* inv_freq, const int64_t* slot, uint8_t* k_cache,
-                                float* k_scale, void* ws, size_t ws_bytes, void* stream);
+                                float* k_scale, void* ws, size_t ws_bytes, void* stream,
+                                const dsa_paging_t* paging);
 
 /* Latent row ("Day 0 support for Mistral Large 4 on vLLM", "Model architecture": 512 latent
  * dims and 64 rotary dims per token; "ROCm implementation details", "FP8 latent cache": the row

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function(dsa):
     for f in declared_functions():
         assert hasattr(lib, f), f"{f} declared in dsa.h but not exported"
     assert set(declared_functions()) == set(dsa.EXPORTED)
-    assert dsa.lib().dsa_abi_version() == 2
+    assert dsa.lib().dsa_abi_version() == 3
 
 
 def test_topk_rejects_bad_arguments_listing_every_reason(dsa):
@@ -53,7 +53,7 @@ def test_indexer_topk_requires_its_workspace(dsa):
     L = dsa.lib()
     d = dsa.IndexerDesc(2, 64, 128, 64, 1, 100, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN)
     st = L.dsa_indexer_topk(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 100, 2048,
-                            None, None, None, 0, None, 0, None)
+                            None, None, None, 0, None, 0, None, None)
     msg = L.dsa_last_error().decode()
     assert st == dsa.DSA_ERR_ARG and "top-k workspace" in msg and "non-NULL" in msg, msg
 
@@ -62,25 +62,25 @@ def test_indexer_rejects_unsupported_shapes(dsa):
     L = dsa.lib()
     d = dsa.IndexerDesc(1, 64, 96, 32, 1, 100, dsa.DSA_BF16, dsa.DSA_BF16)
     st = L.dsa_indexer_scores(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 50, None, 0,
-                              None)
+                              None, None)
     assert st == dsa.DSA_ERR_ARG            # the NULLs and ld < max_ctx are argument errors
     msg = L.dsa_last_error().decode()
     for frag in ("head_dim", "num_heads", "rope_dim", "k_dtype", "ld_scores", "non-NULL", "workspace"):
         assert frag in msg, msg
     d = dsa.IndexerDesc(0, 64, 128, 64, 1, 100, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN)
     st = L.dsa_indexer_scores(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 100, None, 0,
-                              None)
+                              None, None)
     assert st == dsa.DSA_ERR_UNSUPPORTED and "num_heads" in L.dsa_last_error().decode()
 
 
 def test_mla_rejects_bad_dtype_combinations(dsa):
     L = dsa.lib()
     d = dsa.MlaDesc(4, 64, 512, 64, 1, 1000, 2048, dsa.DSA_F32, dsa.DSA_FP8_E4M3FN, 64, 0.07, 0)
-    st = L.dsa_sparse_mla_decode(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None)
+    st = L.dsa_sparse_mla_decode(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None, None)
     msg = L.dsa_last_error().decode()
     assert st == dsa.DSA_ERR_ARG and "BF16 queries" in msg and "non-NULL" in msg
     d = dsa.MlaDesc(0, 64, 256, 32, 1, 1000, 2048, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN, 32, 0.07, 0)
-    st = L.dsa_sparse_mla_prefill(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None)
+    st = L.dsa_sparse_mla_prefill(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None, None)
     msg = L.dsa_last_error().decode()
     assert st == dsa.DSA_ERR_UNSUPPORTED and "kv_lora" in msg and "rope_dim" in msg and "kv_scale_block" in msg
 
@@ -108,7 +108,7 @@ def test_cache_writers_validate_arguments(dsa):
     assert dsa.dsa_index_k_insert_workspace_size(d) == 24 * 16 * 128 * 4
     assert dsa.dsa_index_k_insert_workspace_size(dsa.IndexKDesc(4096, 6144, 6144, 64, 1e-6, 1)) == 4 * 4096 * 128 * 4
     bad = dsa.IndexKDesc(16, 100, 96, 32, -1.0, 1000)
-    st = dsa.lib().dsa_index_k_insert(ctypes.byref(bad), *([None] * 10), 0, None)
+    st = dsa.lib().dsa_index_k_insert(ctypes.byref(bad), *([None] * 10), 0, None, None)
     msg = dsa.lib().dsa_last_error().decode()
     assert st in (dsa.DSA_ERR_ARG, dsa.DSA_ERR_UNSUPPORTED)
     for frag in ("hidden must be a multiple of 32", "ld_x must be", "rope_dim must be 0 or 64", "eps must be",
@@ -118,7 +118,7 @@ def test_cache_writers_validate_arguments(dsa):
     msg = dsa.lib().dsa_last_error().decode()
     assert st == dsa.DSA_ERR_ARG and "ld_kv must be >= 576" in msg and "rope_dim must be 0 or 64" in msg
     zero = dsa.IndexKDesc(0, 6144, 6144, 64, 1e-6, 0)
-    assert dsa.lib().dsa_index_k_insert(ctypes.byref(zero), *([None] * 10), 0, None) == dsa.DSA_OK
+    assert dsa.lib().dsa_index_k_insert(ctypes.byref(zero), *([None] * 10), 0, None, None) == dsa.DSA_OK
     assert dsa.lib().dsa_latent_insert(0, 64, None, 576, None, None, None, 0, None, None, None) == dsa.DSA_OK
 
 
@@ -126,7 +126,7 @@ def test_noalloc_mla_rejects_oversized_partials_before_touching_the_gpu(dsa):
     L = dsa.lib()
     assert L.dsa_sparse_mla_noalloc_max_bytes() == 64 << 20
     d = dsa.MlaDesc(16, 64, 512, 64, 16, 4096, 2048, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN, 64, 0.07, 64)
-    st = L.dsa_sparse_mla_decode_noalloc(ctypes.byref(d), None, None, None, None, None, None, None, None, None)
+    st = L.dsa_sparse_mla_decode_noalloc(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None)
     msg = L.dsa_last_error().decode()
     assert st == dsa.DSA_ERR_UNSUPPORTED and "67108864 bytes" in msg, msg
 
@@ -134,7 +134,7 @@ def test_noalloc_mla_rejects_oversized_partials_before_touching_the_gpu(dsa):
 def test_mla_rejects_a_zero_topk_without_dividing_by_zero(dsa):
     L = dsa.lib()
     d = dsa.MlaDesc(2, 64, 512, 64, 1, 100, 0, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN, 64, 0.07, 0)
-    st = L.dsa_sparse_mla_decode(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None)
+    st = L.dsa_sparse_mla_decode(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None, None)
     assert st == dsa.DSA_ERR_ARG and "topk" in L.dsa_last_error().decode()
     assert L.dsa_sparse_mla_workspace_size(ctypes.byref(d)) == 0
 
