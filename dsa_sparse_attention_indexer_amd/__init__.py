@@ -77,6 +77,8 @@ def _load():
         "dsa_topk": (I32, [P, I64, P, I32, I32, P, P, P, SZ, P]),
         "dsa_block_select_workspace_size": (SZ, [I32, I64, I32]),
         "dsa_block_select": (I32, [P, I64, P, I32, I32, I32, I32, P, P, P, SZ, P]),
+        "dsa_indexer_block_select": (I32, [ctypes.POINTER(IndexerDesc), P, P, P, P, P, P, P, P, P, P, I64, I32, I32,
+                                           I32, P, P, P, SZ, P, SZ, P, PG]),
         "dsa_sparse_mla_workspace_size": (SZ, [ctypes.POINTER(MlaDesc)]),
         "dsa_sparse_mla_decode": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P, PG]),
         "dsa_sparse_mla_prefill": (I32, [ctypes.POINTER(MlaDesc), P, P, P, P, P, P, P, P, P, SZ, P, PG]),
@@ -105,7 +107,7 @@ EXPORTED = ["dsa_last_error", "dsa_abi_version", "dsa_indexer_workspace_size", "
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_sparse_mla_noalloc_max_bytes",
             "dsa_sparse_mla_decode_noalloc", "dsa_index_k_insert_workspace_size",
             "dsa_index_k_insert", "dsa_latent_insert", "dsa_timing_begin", "dsa_timing_end",
-            "dsa_timing_kernel_name", "dsa_paged_slots"]
+            "dsa_timing_kernel_name", "dsa_paged_slots", "dsa_indexer_block_select"]
 
 
 def lib():
@@ -359,6 +361,43 @@ def dsa_block_select(scores, q_pos, idx, length=None, block=128, nblocks=16, ws=
     _dev("ws", ws, torch.uint8)
     _check(_lib.dsa_block_select(_ptr(scores), ld, _ptr(q_pos), T, block, nblocks, topk, _ptr(idx),
                                  _ptr(length), _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, length
+
+
+def dsa_indexer_block_select(q, w, q_seq, q_pos, k_cache, scores, idx, length=None, block=128, nblocks=16,
+                             k_scale=None, ssmax_s=None, ssmax_b=None, inv_freq=None, ws=None, bs_ws=None,
+                             stream=None, paging=None):
+    """Scores and block-sparse selection in one call (dsa_indexer_scores then dsa_block_select; the
+    fp8 decode score kernel writes the block maxima itself)."""
+    T, H, D = q.shape
+    B, max_ctx = _seq_dims(k_cache, paging)
+    _dev("q", q, (torch.float32, torch.bfloat16))
+    _dev("w", w, torch.float32, (T, H))
+    _dev("q_seq", q_seq, torch.int32, (T,))
+    _dev("q_pos", q_pos, torch.int32, (T,))
+    _dev("k_cache", k_cache, (torch.float32, torch.uint8, torch.float8_e4m3fn))
+    _dev("k_scale", k_scale, torch.float32, _rows_of(k_cache, paging))
+    _dev("ssmax_s", ssmax_s, torch.float32, (H,))
+    _dev("ssmax_b", ssmax_b, torch.float32, (H,))
+    _dev("inv_freq", inv_freq, torch.float32)
+    _dev("scores", scores, torch.float32)
+    _dev("idx", idx, torch.int32)
+    _dev("length", length, torch.int32, (T,))
+    if scores.dim() != 2 or scores.shape[0] != T or idx.dim() != 2 or idx.shape[0] != T:
+        raise ValueError("scores must be [T][ld] and idx [T][topk]")
+    ld = scores.shape[1]
+    d = indexer_desc(q, k_cache, inv_freq, paging)
+    if ws is None:
+        ws = torch.empty(max(16, dsa_indexer_workspace_size(d)), dtype=torch.uint8, device=q.device)
+    if bs_ws is None:
+        bs_ws = torch.empty(max(16, dsa_block_select_workspace_size(T, ld, block)), dtype=torch.uint8,
+                            device=q.device)
+    _dev("ws", ws, torch.uint8)
+    _dev("bs_ws", bs_ws, torch.uint8)
+    _check(_lib.dsa_indexer_block_select(ctypes.byref(d), _ptr(q), _ptr(w), _ptr(q_seq), _ptr(q_pos), _ptr(ssmax_s),
+                                         _ptr(ssmax_b), _ptr(inv_freq), _ptr(k_cache), _ptr(k_scale), _ptr(scores),
+                                         ld, block, nblocks, idx.shape[1], _ptr(idx), _ptr(length), _ptr(ws),
+                                         ws.numel(), _ptr(bs_ws), bs_ws.numel(), _stream(stream), _pg(paging)))
     return idx, length
 
 

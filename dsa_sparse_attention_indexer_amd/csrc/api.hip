@@ -176,7 +176,7 @@ dsa::IndexerLaunch indexer_launch(const dsa_indexer_desc_t* d, const void* q, co
                                   int64_t ld_scores) {
   return dsa::IndexerLaunch{d->num_q, d->num_heads, d->rope_dim, d->num_seqs, d->max_ctx, d->q_dtype, d->k_dtype,
                             q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores,
-                            nullptr, 0, 0, dsa::Paging{nullptr, 0, 0, 0}};
+                            nullptr, 0, 0, dsa::Paging{nullptr, 0, 0, 0}, nullptr, 0, 0};
 }
 
 }  // namespace
@@ -317,6 +317,48 @@ dsa_status_t dsa_block_select(const float* scores, int64_t ld_scores, const int3
   if (st != DSA_OK || num_q == 0) return st;
   dsa::BlockSelectLaunch a{scores, ld_scores, q_pos, num_q, block, nblocks, topk, idx, len, ws};
   return hip_status("dsa_block_select", dsa::launch_block_select(a, (hipStream_t)stream));
+}
+
+dsa_status_t dsa_indexer_block_select(const dsa_indexer_desc_t* d, const void* q, const float* w,
+                                      const int32_t* q_seq, const int32_t* q_pos,
+                                      const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                                      const void* k_cache, const float* k_scale, float* scores, int64_t ld_scores,
+                                      int32_t block, int32_t nblocks, int32_t topk, int32_t* idx, int32_t* len,
+                                      void* ws, size_t ws_bytes, void* bs_ws, size_t bs_ws_bytes, void* stream,
+                                      const dsa_paging_t* paging) {
+  const char* fn = "dsa_indexer_block_select";
+  Checker ck;
+  if (!d) { ck.need(false, "desc is NULL"); return ck.finish(fn); }
+  check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
+                ws_bytes);
+  const dsa::Paging pg = check_paging(ck, paging, d->num_seqs, d->max_ctx, d->k_dtype == DSA_FP8_E4M3FN);
+  ck.need(ld_scores <= (int64_t(1) << 30), "ld_scores must be <= 2^30");
+  ck.support(block >= 1 && block <= 4096, "block must be in [1, 4096]");
+  ck.support(nblocks >= 1 && nblocks <= 64, "nblocks must be in [1, 64]");
+  ck.need(topk >= 1, "topk must be >= 1");
+  ck.need((int64_t)nblocks * block <= topk, "nblocks * block must be <= topk");
+  if (d->num_q > 0) {
+    ck.need(idx != nullptr, "idx must be non-NULL");
+    ck.need(block <= 0 || (bs_ws != nullptr && bs_ws_bytes >= dsa_block_select_workspace_size(d->num_q, ld_scores, block)),
+            "block workspace missing or smaller than dsa_block_select_workspace_size()");
+  }
+  dsa_status_t st = ck.finish(fn);
+  if (st != DSA_OK || d->num_q == 0) return st;
+  dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
+                                        ld_scores);
+  a.pg = pg;
+  // the decode score kernel emits the block maxima itself where its chunks hold whole blocks
+  const bool fused = dsa::indexer_block_max_fused(d->num_q, d->num_seqs, d->max_ctx, d->k_dtype, block);
+  if (fused) {
+    a.bmax = static_cast<uint32_t*>(bs_ws);
+    a.bblock = block;
+    a.bld = (ld_scores + block - 1) / block;
+  }
+  hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(fn, e);
+  dsa::BlockSelectLaunch b{scores, ld_scores, q_pos, d->num_q, block, nblocks, topk, idx, len, bs_ws};
+  return hip_status(fn, fused ? dsa::launch_block_pick(b, (hipStream_t)stream)
+                              : dsa::launch_block_select(b, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -4,14 +4,18 @@
 // kept blocks' keys).
 //
 // A block's score is the largest index score among its visible keys.  Two launches:
-//   1. block_max  one wave per block reduces its visible scores (block maxima -> workspace)
+//   1. block_max  one wave per block reduces its visible scores (block maxima -> workspace); the
+//                 fp8 decode score kernel can write these maxima itself (dsa_indexer_block_select)
 //   2. select     one workgroup per query: the block holding the query position is forced in, the
-//                 other nblocks-1 are taken by repeated block-wide argmax over (score, -block)
-//                 packed into one u64 (so equal scores go to the lower block), with the maxima
-//                 held in registers; the kept blocks are then ranked and expanded into ascending
-//                 key indices with -1 padding.
+//                 other nblocks-1 are the largest maxima by (score desc, block asc): the
+//                 (nblocks-1)-th largest score key by three radix passes over LDS histograms with
+//                 the maxima in registers, every key above it, and the lowest blocks among the
+//                 keys equal to it (ranked in one wave; when more than 64 keys tie, nblocks-1
+//                 rounds of block-wide argmax over (score, -block) packed into one u64 instead).
+//                 The kept blocks are then ranked and expanded into ascending key indices with -1
+//                 padding.
 
-#include "dsa_internal.h"
+#include "topk_common.h"
 
 namespace dsa {
 namespace {
@@ -70,8 +74,16 @@ __device__ inline uint64_t pack_block(uint32_t key, int64_t j) {
   return (uint64_t)key << 32 | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
 
+struct PickSmem {
+  uint32_t hist[4096];
+  uint32_t sbuf[32];
+  int eq[kMaxBlocksKept];
+  int cnt, neq;
+};
+
 __global__ void __launch_bounds__(kPT) k_block_pick(BlockSelectLaunch a) {
   __shared__ uint64_t sbuf[kPT / 64];
+  __shared__ __attribute__((aligned(16))) PickSmem ps;
   __shared__ int chosen[kMaxBlocksKept];
   __shared__ int sorted[kMaxBlocksKept];
   __shared__ int offs[kMaxBlocksKept + 1];
@@ -89,8 +101,65 @@ __global__ void __launch_bounds__(kPT) k_block_pick(BlockSelectLaunch a) {
     m = a.nblocks;
     const int recent = (int)((n - 1) / a.block);
     if (tid == 0) chosen[0] = recent;
+    bool done = false;
     if (nb <= (int64_t)kPT * kPickPer) {
-      // all candidates in registers; nblocks-1 rounds of block-wide argmax
+      // Exact select of the m-1 largest candidates (score desc, block asc) with the maxima in
+      // registers: the (m-1)-th largest key by three radix passes (12, 10 and 10 bits) over LDS
+      // histograms, every key above it, and the lowest blocks among the keys equal to it.
+      uint32_t v[kPickPer];
+#pragma unroll
+      for (int i = 0; i < kPickPer; ++i) {
+        const int64_t j = tid + (int64_t)kPT * i;
+        v[i] = (j < nb && j != recent) ? bmax[j] : 0u;   // every candidate key is >= 1
+      }
+      uint32_t need = (uint32_t)(m - 1), prefix = 0;
+      int bin;
+#pragma unroll 1
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+        const int nbins = pass == 0 ? 4096 : 1024;
+        for (int i = tid; i < 4096; i += kPT) ps.hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPickPer; ++i) {
+          const uint32_t k = v[i];
+          const bool in = k != 0u && (pass == 0 || (k >> (shift + 10)) == prefix);
+          if (in) atomicAdd(&ps.hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+        }
+        __syncthreads();
+        uint32_t left;
+        if (pass == 0) tk_find_bin<4096, kPT>(ps.hist, need, ps.sbuf, &bin, &left);
+        else tk_find_bin<1024, kPT>(ps.hist, need, ps.sbuf, &bin, &left);
+        need = left;
+        prefix = (prefix << (pass == 0 ? 12 : 10)) | (uint32_t)bin;
+      }
+      const uint32_t thr = prefix;   // the (m-1)-th largest key; `need` of the keys equal to it are kept
+      if (tid == 0) { ps.cnt = 1; ps.neq = 0; }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kPickPer; ++i) {
+        const int j = tid + kPT * i;
+        if (v[i] > thr) chosen[atomicAdd(&ps.cnt, 1)] = j;
+        else if (v[i] == thr && v[i] != 0u) {
+          const int e = atomicAdd(&ps.neq, 1);
+          if (e < kMaxBlocksKept) ps.eq[e] = j;
+        }
+      }
+      __syncthreads();
+      const int neq = ps.neq;
+      if (neq <= kMaxBlocksKept) {   // typically a handful of ties: rank them by block in one wave
+        if (tid < neq) {
+          const int j = ps.eq[tid];
+          int rank = 0;
+          for (int i = 0; i < neq; ++i) rank += ps.eq[i] < j ? 1 : 0;
+          if (rank < (int)need) chosen[ps.cnt + rank] = j;
+        }
+        done = true;
+      }
+      __syncthreads();
+    }
+    if (!done && nb <= (int64_t)kPT * kPickPer) {
+      // many equal maxima: nblocks-1 rounds of block-wide argmax over (score, -block)
       uint64_t v[kPickPer];
 #pragma unroll
       for (int i = 0; i < kPickPer; ++i) {
@@ -110,7 +179,7 @@ __global__ void __launch_bounds__(kPT) k_block_pick(BlockSelectLaunch a) {
             if (i == j / kPT) v[i] = 0ull;
         }
       }
-    } else {
+    } else if (!done) {
       // very many blocks: rescan the maxima from memory each round
       for (int r = 1; r < m; ++r) {
         __syncthreads();
@@ -174,6 +243,12 @@ hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s) {
   const int64_t nb = nblk_of(a.ld, a.block);
   dim3 g1((unsigned)((nb + 3) / 4), a.T);
   launch(k_block_max, g1, dim3(kT), 0, s, a);
+  launch(k_block_pick, dim3(a.T), dim3(kPT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_pick(const BlockSelectLaunch& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
   launch(k_block_pick, dim3(a.T), dim3(kPT), 0, s, a);
   return hipGetLastError();
 }

@@ -57,6 +57,11 @@ struct IndexerLaunch {
   // pass over the scores (dsa_indexer_topk only: the emitted items are consumed in the same call)
   int topk_emit;
   Paging pg;
+  // optional block maxima (block-sparse selection; the decode kernel without the top-k digit): the
+  // largest score key of each visible `bblock`-key block, bmax[t * bld + block]; NULL = none
+  uint32_t* bmax;
+  int bblock;
+  int64_t bld;
 };
 
 struct TopkLaunch {
@@ -138,6 +143,9 @@ size_t indexer_ws_bytes(int T, int B, dsa_dtype_t k_dtype);
 bool indexer_grouped(int T, int B, dsa_dtype_t k_dtype);
 int indexer_chunk(int T, int max_ctx);              // keys per workgroup of the fp8 decode score kernel
 size_t block_select_ws_bytes(int T, int64_t ld, int block);
+// the decode score kernel can emit the block maxima itself (blocks of whole 32-key tiles that
+// divide its chunk)
+bool indexer_block_max_fused(int T, int B, int max_ctx, dsa_dtype_t k_dtype, int block);
 int kinsert_splits(int T, int D);   // hidden-dim splits of the key projection
 
 // ---- launchers (return the HIP status of the last launch) -----------------------------------
@@ -146,6 +154,7 @@ hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s);
 hipError_t launch_topk(const TopkLaunch& a, bool hist_given, hipStream_t s);
 hipError_t launch_topk_hist(const TopkLaunch& a, hipStream_t s);   // the first-digit histogram only
 hipError_t launch_block_select(const BlockSelectLaunch& a, hipStream_t s);
+hipError_t launch_block_pick(const BlockSelectLaunch& a, hipStream_t s);   // maxima already in a.ws
 hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s);
 hipError_t launch_index_k_insert(const KInsertLaunch& a, hipStream_t s);
 hipError_t launch_latent_insert(const LatentInsertLaunch& a, hipStream_t s);

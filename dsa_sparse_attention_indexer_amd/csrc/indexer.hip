@@ -638,6 +638,13 @@ k_index_scores_fp8(IndexerLaunch a) {
       for (int i = threadIdx.x; i < kTkBins; i += kThreads) pu.lh[i] = 0;
     __syncthreads();
   }
+  // block maxima (block-sparse selection): the largest score key of each block of the chunk
+  __shared__ uint32_t sbm[HIST ? 1 : chunk / kTile];
+  const bool bm = !HIST && a.bmax != nullptr;
+  if (!HIST && bm) {
+    for (int i = threadIdx.x; i < chunk / kTile; i += kThreads) sbm[i] = 0u;
+    __syncthreads();
+  }
 
   // Fully unrolled: the vmcnt of every wait is a compile-time count (ring_wait).  A slot is
   // refilled as soon as its contents are in registers, before the tile's matrix work, so the next
@@ -666,7 +673,16 @@ k_index_scores_fp8(IndexerLaunch a) {
     const float sc = tile_scores(cur, ahi, alo, cf);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
     if (hist && g == 0 && rel + col < nrow) atomicAdd(&pu.lh[score_key(sc) >> kTkShift0], 1u);
+    if (!HIST && bm) {   // a 32-key tile lies in one block: its maximum, then the block's
+      const uint32_t kk = tk_wave_max((g == 0 && rel + col < nrow) ? score_key(sc) : 0u);
+      if (lane == 0) atomicMax(&sbm[rel / (uint32_t)a.bblock], kk);
+    }
     rel += kStride;
+  }
+  if (!HIST && bm) {   // the chunk's blocks that hold visible keys
+    __syncthreads();
+    const int nbc = ((int)nrow + a.bblock - 1) / a.bblock;
+    for (int i = threadIdx.x; i < nbc; i += kThreads) a.bmax[(size_t)t * a.bld + c0 / a.bblock + i] = sbm[i];
   }
   if (hist) {
     __syncthreads();   // also makes this workgroup's score stores visible to all its threads
@@ -942,6 +958,11 @@ constexpr int kGroupedMinQueries = 256;
 
 // ... or when there are at least two queries per sequence (verify blocks of several tokens per
 // sequence, chunked prefill): consecutive queries of one sequence then share one key stream.
+bool indexer_block_max_fused(int T, int B, int max_ctx, dsa_dtype_t k_dtype, int block) {
+  return k_dtype == DSA_FP8_E4M3FN && !indexer_grouped(T, B, k_dtype) && block % kTile == 0 &&
+         indexer_chunk(T, max_ctx) % block == 0;
+}
+
 bool indexer_grouped(int T, int B, dsa_dtype_t k_dtype) {
   return k_dtype == DSA_FP8_E4M3FN && (T >= kGroupedMinQueries || (B > 0 && T >= 2 * B));
 }

@@ -58,6 +58,18 @@ __device__ inline uint32_t tk_wave_incl_scan(uint32_t x) {
   return x;
 }
 
+// Maximum over the 64 lanes of a wave with DPP moves (the same row shifts and broadcasts as the
+// scan above); every lane gets it.
+__device__ inline uint32_t tk_wave_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true));    // row_shr:1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true));    // row_shr:2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true));    // row_shr:4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true));    // row_shr:8
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false));   // row_bcast:15
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false));   // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 template <int NT>
 __device__ inline uint32_t tk_excl_scan(uint32_t v, uint32_t* total, uint32_t* sbuf) {
   constexpr int NW = NT / 64;

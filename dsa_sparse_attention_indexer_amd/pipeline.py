@@ -13,7 +13,8 @@ from typing import Optional
 
 import torch
 
-from . import (dsa_block_select, dsa_block_select_workspace_size, dsa_indexer_scores, dsa_indexer_scores_hist,
+from . import (dsa_block_select, dsa_block_select_workspace_size, dsa_indexer_block_select, dsa_indexer_scores,
+               dsa_indexer_scores_hist,
                dsa_indexer_topk, dsa_indexer_workspace_size, dsa_sparse_mla_decode, dsa_sparse_mla_prefill,
                dsa_sparse_mla_workspace_size, dsa_topk, dsa_topk_hist, indexer_desc, mla_desc, topk_workspace)
 
@@ -90,6 +91,14 @@ def index_and_select(wl, buf: StepBuffers, stream=None):
                             inv_freq=wl.inv_freq, ws=buf.ws_index, topk_ws=buf.ws_topk, stream=stream)
 
 
+def index_and_select_blocks(wl, buf: StepBuffers, stream=None):
+    """Scores and block-sparse selection in one call (the block maxima from the score kernel)."""
+    return dsa_indexer_block_select(wl.index_q, wl.index_w, wl.q_seq, wl.q_pos, wl.index_k, buf.scores, buf.idx,
+                                    buf.length, block=128, nblocks=16, k_scale=wl.index_k_scale, ssmax_s=wl.ssmax_s,
+                                    ssmax_b=wl.ssmax_b, inv_freq=wl.inv_freq, ws=buf.ws_index, bs_ws=buf.ws_block,
+                                    stream=stream)
+
+
 def index_scores_hist(wl, buf: StepBuffers, stream=None):
     """The scores plus the first-digit histogram (first half of index_and_select)."""
     return dsa_indexer_scores_hist(wl.index_q, wl.index_w, wl.q_seq, wl.q_pos, wl.index_k, buf.scores, wl.topk,
@@ -106,13 +115,15 @@ def layer_step(wl, buf: StepBuffers, *, prefill: bool = False, block_sparse: boo
                shared_from: Optional[StepBuffers] = None, num_splits: int = 0, fused: bool = True, stream=None):
     """Scores -> selection -> sparse MLA; with shared_from, only the MLA over that selection.
 
-    fused (default): one dsa_indexer_topk call -- the score kernel also builds the first radix
-    digit's histogram and emits each chunk's candidates, and the selection continues from them;
-    else dsa_indexer_scores and dsa_topk."""
+    fused (default): one dsa_indexer_topk (dsa_indexer_block_select) call -- the score kernel also
+    builds the first radix digit's histogram and emits each chunk's candidates (the block maxima),
+    and the selection continues from them; else dsa_indexer_scores and dsa_topk (dsa_block_select)."""
     if shared_from is not None:
         return attend(wl, buf, prefill=prefill, num_splits=num_splits, idx=shared_from.idx,
                       length=shared_from.length, stream=stream)
-    if fused and not block_sparse:
+    if fused and block_sparse:
+        index_and_select_blocks(wl, buf, stream)
+    elif fused:
         index_and_select(wl, buf, stream)
     else:
         index_scores(wl, buf, stream)

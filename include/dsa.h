@@ -239,6 +239,21 @@ dsa_status_t dsa_block_select(const float* scores, int64_t ld_scores, const int3
                               int32_t num_q, int32_t block, int32_t nblocks, int32_t topk,
                               int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream);
 
+/* Scores and block selection in one call: dsa_indexer_scores, then dsa_block_select over the
+ * scores, with the same arguments and results (scores written as dsa_indexer_scores writes them).
+ * bs_ws is dsa_block_select's workspace (dsa_block_select_workspace_size(num_q, ld_scores, block)
+ * bytes); it receives each block's maximum.  On the fp8 decode path (fewer than two queries per
+ * sequence) with block a multiple of 32 that divides the score kernel's chunk (4096 keys, or
+ * 1024 when the query count is small; 128 always does), the score kernel writes the maxima itself
+ * and the selection never reads the scores back; otherwise a separate pass takes them. */
+dsa_status_t dsa_indexer_block_select(const dsa_indexer_desc_t* desc, const void* q, const float* w,
+                                      const int32_t* q_seq, const int32_t* q_pos,
+                                      const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
+                                      const void* k_cache, const float* k_scale, float* scores, int64_t ld_scores,
+                                      int32_t block, int32_t nblocks, int32_t topk, int32_t* idx, int32_t* len,
+                                      void* ws, size_t ws_bytes, void* bs_ws, size_t bs_ws_bytes, void* stream,
+                                      const dsa_paging_t* paging);
+
 /* ============================================================================================
  * 3. Sparse MLA (absorbed form, V = latent)
  * --------------------------------------------------------------------------------------------
