@@ -268,11 +268,16 @@ k_mla_fp8_ws(MlaLaunch a) {
   // the rows of chunk cb into LDS (PV waves; callers hold a barrier before and after): the cache
   // row of each selected position (its pool slot on a paged cache), -1 for none
   auto store_rows = [&](int nslot, int ntiles) {
+    // The slot addresses come from a copy of the thread index made here: formed once and kept live
+    // across the kernel they are spilled, and each reload then costs a scratch round trip.
+    int pt;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(pt) : "v"(ptid));
+    int* rp = sm.rows + pt;
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
       const int i = ptid + kPvThreads * u;
       const bool ok = i < nslot && rv[u] >= 0 && rv[u] < a.max_ctx;
-      if (i < ntiles * kT2) sm.rows[i] = ok ? (paged ? (int)paged_slot(a.pg, b, rv[u]) : rv[u]) : -1;
+      if (i < ntiles * kT2) rp[kPvThreads * u] = ok ? (paged ? (int)paged_slot(a.pg, b, rv[u]) : rv[u]) : -1;
     }
   };
 
