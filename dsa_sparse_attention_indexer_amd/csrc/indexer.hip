@@ -299,6 +299,14 @@ __device__ __forceinline__ void load_tile(KeyTile& kt, __amdgpu_buffer_rsrc_t kr
   kt.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, rel_row * 4u, 0, 0));
 }
 
+// max(x, 0) as one instruction: fmaxf on an MFMA result is preceded by a NaN-quieting max, which
+// the ReLU does not need (a NaN score only arises from NaN key codes, which no writer produces).
+__device__ __forceinline__ float relu1(float x) {
+  float r;
+  asm("v_max_f32_e32 %0, 0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // One 32-key tile: 16 MFMAs (8 K-steps x hi/lo), ReLU + head weights, halves summed across the wave.
 __device__ __forceinline__ float tile_scores(const KeyTile& kt, const half8* ahi, const half8* alo, const float* cf) {
   float16v acc = {};
@@ -313,7 +321,7 @@ __device__ __forceinline__ float tile_scores(const KeyTile& kt, const half8* ahi
   }
   float part = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) part = fmaf(cf[r], fmaxf(acc[r], 0.f), part);
+  for (int r = 0; r < 16; ++r) part = fmaf(cf[r], relu1(acc[r]), part);
   // lanes l and l^32 hold the two halves of key column l&31's head sum
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
   return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * kt.sc;
@@ -339,8 +347,8 @@ __device__ __forceinline__ void tile_scores2(const KeyTile& k0, const KeyTile& k
   float p0 = 0.f, p1 = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    p0 = fmaf(cf[r], fmaxf(a0[r], 0.f), p0);
-    p1 = fmaf(cf[r], fmaxf(a1[r], 0.f), p1);
+    p0 = fmaf(cf[r], relu1(a0[r]), p0);
+    p1 = fmaf(cf[r], relu1(a1[r]), p1);
   }
   const auto w0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p0), false, false);
   const auto w1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p1), false, false);
@@ -463,20 +471,21 @@ static_assert(ring_wait(0, 32) == 10 && ring_wait(1, 32) == 11 && ring_wait(2, 3
                       ring_wait(29, 32) == 13 && ring_wait(30, 32) == 8 && ring_wait(31, 32) == 3,
               "ring wait counts");
 
-// Fused selection: this chunk's candidates for the row's top-k, appended to the row's item list in
-// column order.  kq is twice the chunk's expected share of the k (its share of the row's keys) plus
-// 32; every score whose first digit is >= lb, the digit of the chunk's kq-th largest score (from the
-// chunk's histogram in LDS), is emitted, and the chunk's table entry records (first item,
-// count | lb << 16); the chunk's histogram bins from lb up are added into the row's.  With L the
-// largest lb of the row's chunks, the row histogram is exact from L up and the items at or above
-// L are exactly the row's keys there; when at least k keys lie at or above L the selection kernel
-// finds the row's top k among the items, and otherwise selects from the scores directly.  The
-// scores are read back from memory: this
-// workgroup wrote them, and the barrier before makes them visible to all its threads.
+// Fused selection: this chunk's candidates for the row's top-k, in column order, in the chunk's own
+// region of the row's item list (chunk c of a row of S chunks owns items c * cap .. c * cap + cap - 1,
+// cap = kTkItemCap / S, so no counter is involved).  kq is twice the chunk's expected share of the k
+// (its share of the row's keys) plus 32; every score whose first digit is >= lb, the digit of the
+// chunk's kq-th largest score (from the chunk's histogram in LDS), is emitted, and the chunk's table
+// entry records (first item, count | lb << 16); the chunk's histogram bins from lb up are added into
+// the row's.  A chunk with more candidates than its region holds writes none and an entry that
+// claims more items than the list has.  With L the largest lb of the row's chunks, the row histogram
+// is exact from L up and the items at or above L are exactly the row's keys there; when at least k
+// keys lie at or above L the selection kernel finds the row's top k among the items, and otherwise
+// selects from the scores directly.  The scores are read back from memory: this workgroup wrote
+// them, and the barrier before makes them visible to all its threads.
 struct EmitSmem {
   uint32_t sbuf[32];
   uint32_t wsum[16];
-  uint32_t base;
 };
 
 template <int TPW>
@@ -507,16 +516,13 @@ __device__ void emit_candidates(const IndexerLaunch& a, int t, int n, int c0, ui
   uint32_t pos[Q];
   const uint32_t total = tk_ordered_slots<Q, kThreads>(fl, pos, em.wsum);
   uint32_t* rw = tk_row(a.topk_ws, t);
-  if (threadIdx.x == 0) {
-    const uint32_t st = atomicAdd(&rw[kTkOffCtr], total);
-    em.base = st;
-    *reinterpret_cast<uint2*>(rw + kTkOffTable + 2 * blockIdx.x) = make_uint2(st, total | ((uint32_t)lb << 16));
-  }
-  __syncthreads();
-  const uint32_t st = em.base;
-  // the item list is full (or the counter held a stale value): nothing is written, and the
-  // selection kernel sees it in the table entry
-  if (st > (uint32_t)kTkItemCap || total > (uint32_t)kTkItemCap - st) return;
+  const uint32_t cap = (uint32_t)kTkItemCap / (uint32_t)((n + chunk - 1) / chunk);
+  const uint32_t st = (uint32_t)blockIdx.x * cap;
+  const bool fits = total <= cap;
+  if (threadIdx.x == 0)
+    *reinterpret_cast<uint2*>(rw + kTkOffTable + 2 * blockIdx.x) =
+        make_uint2(fits ? st : (uint32_t)kTkItemCap, (fits ? total : 0xFFFFu) | ((uint32_t)lb << 16));
+  if (!fits) return;
   uint2* items = reinterpret_cast<uint2*>(rw + kTkOffItems);
 #pragma unroll
   for (int q = 0; q < Q; ++q) {

@@ -20,8 +20,10 @@
 //            lowest columns among the keys equal to it.  The output is ascending by
 //            construction: no sort and no merge.
 // On the fused score + top-k path the score kernel emits each chunk's candidates itself (see
-// emit_candidates in the index kernels) and only the resolve kernel runs; a chunk that emitted
-// only digits above the row's b0 sends the row to the exact passes below.
+// emit_candidates in the index kernels) into fixed regions of the row's item list, and only the
+// resolve kernel runs (resolve_emitted: histogram, table and item regions in one round of loads,
+// the histogram searches in one wave); a chunk that emitted only digits above the row's b0 sends
+// the row to the exact passes below.
 // If a row's items do not fit in LDS (heavy ties), k is large, or the check fails (a histogram
 // left over from an interrupted call, or built for another k), the resolve workgroup instead
 // selects by exact passes over the row, first digit included.  Every decision is made on the
@@ -138,11 +140,55 @@ struct ResolveSmem {
   uint32_t key[kTkItemCap];
   uint32_t col[kTkItemCap];
   uint32_t hist[kTkBins];
-  uint32_t tst[kTkMaxSeg];    // per segment: first item in the workspace
+  uint32_t tst[kTkMaxSeg];    // per segment: first item in the workspace (emitted rows: its count)
   uint32_t tpre[kTkMaxSeg];   // per segment: first item in column order
   uint32_t sbuf[32];
   uint32_t wsum[kSQ * (kRT / 64)];
+  uint32_t hist1[1024];       // emitted rows: the second digit of the candidates inside b0
+  uint32_t wtot[kRT / 64];    // per wave: a sum
+  uint32_t wmax[kRT / 64];    // per wave: a maximum
+  uint32_t res[8];            // results handed from one wave to the workgroup
 };
+
+// The bin of an NB-bin histogram (16-byte aligned, in LDS) that holds the need-th largest key, found
+// by one wave with no barrier: lane l sums the NB/64 bins counted l-th from the top, a prefix sum
+// over the lanes names the lane whose bins hold it, and a second prefix sum over that lane's bins
+// (one per lane) names the bin.  Returns the bin and the count still needed inside it in every lane;
+// fewer than need keys in the histogram: bin 0 and need.
+template <int NB>
+__device__ inline void wave_find_bin(const uint32_t* h, uint32_t need, int* bin_out, uint32_t* need_out) {
+  constexpr int PER = NB / 64;
+  static_assert(PER % 4 == 0 && PER <= 64, "bins per lane");
+  const int lane = threadIdx.x & 63;
+  const int lo = NB - PER * (lane + 1);
+  uint32_t sum = 0;
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) {
+    const uint4 x = *reinterpret_cast<const uint4*>(h + lo + 4 * q);
+    sum += x.x + x.y + x.z + x.w;
+  }
+  const uint32_t incl = tk_wave_incl_scan(sum);
+  const uint64_t m = __ballot(incl - sum < need && need <= incl);
+  if (m == 0) {
+    *bin_out = 0;
+    *need_out = need;
+    return;
+  }
+  const int l0 = __builtin_ctzll(m);
+  const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), l0);
+  const int lo0 = NB - PER * (l0 + 1);
+  const uint32_t c = lane < PER ? h[lo0 + PER - 1 - lane] : 0u;   // lane i: the i-th of those bins from the top
+  const uint32_t inc2 = ab + tk_wave_incl_scan(c);
+  const uint64_t m2 = __ballot(lane < PER && inc2 - c < need && need <= inc2);
+  const int i = __builtin_ctzll(m2);
+  *bin_out = lo0 + PER - 1 - i;
+  *need_out = need - ((uint32_t)__builtin_amdgcn_readlane((int)inc2, i) - (uint32_t)__builtin_amdgcn_readlane((int)c, i));
+}
+
+// Sum over the 64 lanes of a wave (every lane gets it).
+__device__ inline uint32_t wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)tk_wave_incl_scan(x), 63);
+}
 
 // Among keys[0..cnt) whose bits above shift + bits equal prefix: the bits-wide digit at shift
 // that holds the need-th largest key, and the count still needed inside it.
@@ -191,7 +237,7 @@ __device__ void row_digit(const float* row, int n, uint32_t prefix, int shift, u
 // Streaming finish: the exact k-th key from three passes over the row (first digit, then bits
 // 19..10 and 9..0), then one ordered pass that emits every key above it and the lowest columns
 // among the keys equal to it.  It reads nothing from the workspace.
-__device__ void finish_streaming(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
+__device__ __forceinline__ void finish_streaming(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
   const float* row = a.scores + (size_t)t * a.ld;
   int b0i, d1, d2;
   uint32_t need0, need1, need2;
@@ -244,24 +290,215 @@ __device__ void finish_streaming(const TopkLaunch& a, int t, int n, ResolveSmem&
   }
 }
 
-__global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
-  __shared__ __attribute__((aligned(16))) ResolveSmem sm;
-  static_assert(kTkBins == 4 * kRT, "one uint4 of histogram per thread");
-  const int t = blockIdx.x;
+// Emitted rows (score chunks wrote their candidates into fixed regions: chunk s of S owns items
+// s * cap .. s * cap + cap - 1, cap = kTkItemCap / S).  The histogram, the table and every item
+// region are loaded in one round of loads; the searches over a histogram run in one wave while the
+// other waves place the items in column order, so the row takes nine workgroup barriers.  Returns
+// false (the row is then selected by the exact passes) on the same conditions as the general path.
+__device__ __forceinline__ bool resolve_emitted(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
+  constexpr int IPT = kTkItemCap / kRT;   // item slots per thread
+  static_assert(IPT % 2 == 0 && kTkMaxSeg <= kRT, "item slots and table entries per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* rw = tk_row(a.ws, t);
+  int32_t* out = a.idx + (size_t)t * a.k;
+  const int S = (n + a.seg - 1) / a.seg;
+  const uint32_t cap = (uint32_t)kTkItemCap / (uint32_t)S;
+
+  // one round of loads: this thread's four histogram bins, its table entry and item slots
+  // 2 * tid + 2 * kRT * u + {0, 1}
+  const uint4 h = reinterpret_cast<const uint4*>(rw)[tid];
+  uint2 te = make_uint2(0u, 0u);
+  if (tid < S) te = reinterpret_cast<const uint2*>(rw + kTkOffTable)[tid];
+  uint4 raw[IPT / 2];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(rw + kTkOffItems);
+#pragma unroll
+    for (int u = 0; u < IPT / 2; ++u) raw[u] = src[tid + kRT * u];
+  }
+  const uint32_t cnt_s = tid < S ? te.y & 0xFFFFu : 0u;
+  const uint32_t low_s = tid < S ? te.y >> 16 : 0u;
+  const bool bad = tid < S && (te.x != (uint32_t)tid * cap || cnt_s > cap);
+  {   // per-wave sums of the counts (segment prefix sums) and maxima of the lowest emitted digits
+    const uint32_t incl = tk_wave_incl_scan(cnt_s);
+    const uint32_t mx = tk_wave_max(low_s);
+    if (lane == 63) sm.wtot[wave] = incl;
+    if (lane == 0) sm.wmax[wave] = mx;
+    if (tid < S) sm.tpre[tid] = incl - cnt_s;   // within the wave; the waves before are added below
+  }
+  const bool overflow = __syncthreads_or(bad) != 0;                          // barrier 1
+  // the workspace histogram and counter are cleared for the next call (their values are in registers)
+  reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) rw[kTkOffCtr] = 0u;
+  if (overflow) {
+    return false;
+  }
+  uint32_t L = 0, woff = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kRT / 64; ++w) {
+    const uint32_t x = sm.wtot[w];
+    woff += w < wave ? x : 0u;
+    total += x;
+    L = max(L, sm.wmax[w]);
+  }
+  if (tid < S) {
+    sm.tpre[tid] += woff;
+    sm.tst[tid] = cnt_s;
+  }
+  // the histogram from L up (each chunk added its bins from its own lowest digit up)
+  {
+    const uint32_t b = 4u * (uint32_t)tid;
+    sm.hist[b] = b < L ? 0u : h.x;
+    sm.hist[b + 1] = b + 1 < L ? 0u : h.y;
+    sm.hist[b + 2] = b + 2 < L ? 0u : h.z;
+    sm.hist[b + 3] = b + 3 < L ? 0u : h.w;
+  }
+  sm.hist1[tid] = 0u;
+  if (tid == 0) sm.res[5] = 0u;
+  __syncthreads();                                                            // barrier 2
+  // wave 0: the first digit b0 of the k-th largest key; every wave: the items into column order
+  if (wave == 0) {
+    int b0;
+    uint32_t need0;
+    wave_find_bin<kTkBins>(sm.hist, (uint32_t)a.k, &b0, &need0);
+    if (lane == 0) sm.res[0] = (uint32_t)b0;
+  }
+  {
+    const float rcap = 1.0f / (float)cap;
+#pragma unroll
+    for (int u = 0; u < IPT / 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t slot = 2u * (uint32_t)(tid + kRT * u) + (uint32_t)e;
+        uint32_t sg = (uint32_t)((float)slot * rcap);
+        if (sg * cap > slot) --sg;
+        else if ((sg + 1) * cap <= slot) ++sg;
+        const uint32_t j = slot - sg * cap;
+        if (sg < (uint32_t)S && j < sm.tst[sg]) {
+          const uint32_t p = sm.tpre[sg] + j;
+          sm.key[p] = e ? raw[u].z : raw[u].x;
+          sm.col[p] = e ? raw[u].w : raw[u].y;
+        }
+      }
+    }
+  }
+  __syncthreads();                                                            // barrier 3
+  const uint32_t b0 = sm.res[0];
+  if (L > b0) {   // fewer than k keys at or above L: some chunk may hold keys of the top k it did not emit
+    return false;
+  }
+  // this thread's contiguous range of the items: counts above b0 and at or above it (a check of the
+  // histogram against the items), and the second-digit histogram of the items inside b0
+  const uint32_t per = (total + kRT - 1) / kRT;
+  const uint32_t i0 = min(total, per * (uint32_t)tid), i1 = min(total, i0 + per);
+  {
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t k = sm.key[i];
+      const uint32_t d = k >> kTkShift0;
+      gt += d > b0 ? 1u : 0u;
+      ge += d >= b0 ? 1u : 0u;
+      if (d == b0) atomicAdd(&sm.hist1[(k >> 10) & 1023u], 1u);
+    }
+    sm.hist[tid] = 0u;   // the first 1024 bins become the third digit's histogram
+    const uint32_t ws = wave_sum((ge << 16) | gt);   // each count is at most 16384
+    if (lane == 0) sm.wtot[wave] = ws;
+  }
+  __syncthreads();                                                            // barrier 4
+  uint32_t above_b0 = 0, atleast_b0 = 0;
+#pragma unroll
+  for (int w = 0; w < kRT / 64; ++w) {
+    const uint32_t x = sm.wtot[w];
+    above_b0 += x & 0xFFFFu;
+    atleast_b0 += x >> 16;
+  }
+  if (!(above_b0 < (uint32_t)a.k && (uint32_t)a.k <= atleast_b0)) {
+    return false;
+  }
+  const uint32_t need0 = (uint32_t)a.k - above_b0;
+  if (wave == 0) {   // the second digit (bits 19..10) of the k-th key among the candidates inside b0
+    int d1;
+    uint32_t need1;
+    wave_find_bin<1024>(sm.hist1, need0, &d1, &need1);
+    if (lane == 0) {
+      sm.res[1] = (uint32_t)d1;
+      sm.res[2] = need1;
+      sm.res[3] = sm.hist1[d1];
+    }
+  }
+  __syncthreads();                                                            // barrier 5
+  const uint32_t pre22 = (b0 << 10) | sm.res[1];
+  const uint32_t need1 = sm.res[2];
+  const uint32_t c1 = sm.res[3];   // keys sharing the top 22 bits of the k-th key
+  if (c1 <= 64u) {   // typically a handful: collected and ranked in one wave
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t k = sm.key[i];
+      if ((k >> 10) == pre22) sm.wsum[atomicAdd(&sm.res[5], 1u)] = k;
+    }
+    __syncthreads();                                                          // barrier 6
+    if (wave == 0) {
+      const uint32_t c = sm.res[5];
+      const uint32_t mine = lane < (int)c ? sm.wsum[lane] : 0u;
+      uint32_t above = 0, same = 0;
+      for (uint32_t j = 0; j < c; ++j) {
+        const uint32_t o = sm.wsum[j];
+        above += o > mine ? 1u : 0u;
+        same += o == mine ? 1u : 0u;
+      }
+      if (lane < (int)c && above < need1 && need1 <= above + same) {
+        sm.res[6] = mine;
+        sm.res[7] = need1 - above;
+      }
+    }
+  } else {           // the third digit (bits 9..0) among the keys sharing the top 22 bits
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t k = sm.key[i];
+      if ((k >> 10) == pre22) atomicAdd(&sm.hist[k & 1023u], 1u);
+    }
+    __syncthreads();                                                          // barrier 6
+    if (wave == 0) {
+      int d2;
+      uint32_t need2;
+      wave_find_bin<1024>(sm.hist, need1, &d2, &need2);
+      if (lane == 0) {
+        sm.res[6] = (pre22 << 10) | (uint32_t)d2;
+        sm.res[7] = need2;
+      }
+    }
+  }
+  __syncthreads();                                                            // barrier 7
+  const uint32_t thr = sm.res[6], need2 = sm.res[7];
+  // One ordered pass: keys above thr, and the need2 lowest columns among the keys equal to it.
+  // Item i goes to slot (#keys above thr before i) + min(#keys equal to thr before i, need2); both
+  // counts come from one scan of a packed pair (each at most 16384, so no carry crosses).
+  uint32_t ngt = 0, neq = 0;
+  for (uint32_t i = i0; i < i1; ++i) {
+    const uint32_t k = sm.key[i];
+    ngt += k > thr ? 1u : 0u;
+    neq += k == thr ? 1u : 0u;
+  }
+  const uint32_t pk = tk_excl_scan<kRT>((neq << 16) | ngt, nullptr, sm.sbuf);   // barriers 8, 9
+  uint32_t gt = pk & 0xFFFFu, eq = pk >> 16;
+  for (uint32_t i = i0; i < i1; ++i) {
+    const uint32_t k = sm.key[i];
+    if (k > thr) {
+      const uint32_t p = gt + min(eq, need2);
+      if (p < (uint32_t)a.k) out[p] = (int32_t)sm.col[i];
+      ++gt;
+    } else if (k == thr) {
+      if (eq < need2 && gt + eq < (uint32_t)a.k) out[gt + eq] = (int32_t)sm.col[i];
+      ++eq;
+    }
+  }
+  if (tid == 0 && a.len) a.len[t] = a.k;
+  return true;
+}
+
+// Collected rows (and emitted rows without the fixed item regions): the general path.  Returns false
+// when the row must be selected by the exact passes.
+__device__ __forceinline__ bool resolve_collected(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
   const int tid = threadIdx.x;
-  const int n = row_n(a, t);
   int32_t* out = a.idx + (size_t)t * a.k;
   uint32_t* rw = tk_row(a.ws, t);
-  if (n <= a.k) {   // every visible column, then padding; a histogram left by an earlier call is cleared
-    for (int i = tid; i < a.k; i += kRT) out[i] = i < n ? i : -1;
-    reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
-    if (tid == 0) {
-      rw[kTkOffCtr] = 0u;
-      if (a.len) a.len[t] = n;
-    }
-    return;
-  }
-
   // The row's segment table (and, for collected rows, its histogram) in one round of loads; the
   // histogram and the item counter are then zeroed for the next call.
   const int S = (n + a.seg - 1) / a.seg;
@@ -300,18 +537,14 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   // emitted rows: fewer than k keys at or above L, so b0 fell below L)
   const bool incomplete = __syncthreads_or(tid < S && low_s > (uint32_t)b0) != 0;
   if (a.k > kTkFastK || overflow || incomplete) {
-    finish_streaming(a, t, n, sm);
-    if (tid == 0 && a.len) a.len[t] = a.k;
-    return;
+    return false;
   }
 
   // items into LDS in column order: segment s holds items tpre[s].. of the row, stored from tst[s]
   uint32_t total;
   const uint32_t pre = tk_excl_scan<kRT>(cnt_s, &total, sm.sbuf);
   if (total > (uint32_t)kTkItemCap) {   // (not reached when every segment fit; kept as a guard)
-    finish_streaming(a, t, n, sm);
-    if (tid == 0 && a.len) a.len[t] = a.k;
-    return;
+    return false;
   }
   if (tid < S) sm.tpre[tid] = pre;
   __syncthreads();
@@ -354,9 +587,7 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   tk_excl_scan<kRT>(gt_b0, &above_b0, sm.sbuf);
   tk_excl_scan<kRT>(ge_b0, &atleast_b0, sm.sbuf);
   if (!(above_b0 < (uint32_t)a.k && (uint32_t)a.k <= atleast_b0)) {
-    finish_streaming(a, t, n, sm);
-    if (tid == 0 && a.len) a.len[t] = a.k;
-    return;
+    return false;
   }
   const uint32_t need0 = (uint32_t)a.k - above_b0;
 
@@ -422,6 +653,32 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
     }
   }
   if (tid == 0 && a.len) a.len[t] = a.k;
+  return true;
+}
+
+__global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
+  __shared__ __attribute__((aligned(16))) ResolveSmem sm;
+  static_assert(kTkBins == 4 * kRT, "one uint4 of histogram per thread");
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = row_n(a, t);
+  int32_t* out = a.idx + (size_t)t * a.k;
+  uint32_t* rw = tk_row(a.ws, t);
+  if (n <= a.k) {   // every visible column, then padding; a histogram left by an earlier call is cleared
+    for (int i = tid; i < a.k; i += kRT) out[i] = i < n ? i : -1;
+    reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) {
+      rw[kTkOffCtr] = 0u;
+      if (a.len) a.len[t] = n;
+    }
+    return;
+  }
+
+  const bool done = (a.emitted && a.k <= kTkFastK) ? resolve_emitted(a, t, n, sm) : resolve_collected(a, t, n, sm);
+  if (!done) {
+    finish_streaming(a, t, n, sm);
+    if (tid == 0 && a.len) a.len[t] = a.k;
+  }
 }
 
 }  // namespace

@@ -8,7 +8,9 @@
 //                           written by every live segment (a collect segment or, on the fused path,
 //                           a score chunk)
 //   items  [kTkItemCap][2]  (key, column) of every score whose first digit is >= the segment's
-//                           lowest emitted digit, in column order within each segment
+//                           lowest emitted digit, in column order within each segment; collect
+//                           segments take their slots from ctr[0], score chunk s of a row of S
+//                           chunks owns slots s * (kTkItemCap / S) onwards
 // Collected rows: the histogram only steers the fast path: the resolve kernel checks against the
 // collected items that the digit it names holds the k-th largest key, and otherwise selects by
 // exact passes over the row.  Emitted rows (score chunks that emit their own candidates) add only

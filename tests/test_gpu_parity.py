@@ -492,6 +492,41 @@ def test_fused_index_topk_clustered_top_keys(dsa):
     assert np.all(idx[:, 0] >= n - 3000), "the top keys are the packed ones"
 
 
+def test_fused_index_topk_overflow_ties_and_stale_workspace(dsa):
+    """Fused selection on 1024-key chunks (98 per row, so each chunk's item region holds 167):
+    row 0 has 2000 keys that tie for the top score, so the chunks holding them emit more candidates
+    than their regions hold and the row takes the exact passes; row 1 takes the emitted path.  Then
+    the same call on a workspace holding a stale histogram (an interrupted split call) and on one
+    of random bytes.  Every selection is the oracle's top-k of the GPU's scores."""
+    n0, n1 = 100000, 60000
+    wl = workloads.make_workload(name="overflow", seed=1515, seq_lens=[n0, n1], max_ctx=n0)
+    s = O.index_scores(wl, 0)
+    best = int(np.argmax(s))
+    wl.index_k[0, 50000:52000] = wl.index_k[0, best]
+    wl.index_k_scale[0, 50000:52000] = wl.index_k_scale[0, best]
+    g = wl.to("cuda")
+    P = _pipe()
+    buf = P.alloc_buffers(g)
+    P.index_and_select(g, buf)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, buf, wl.topk, "tied block")
+    idx = buf.idx.cpu().numpy()
+    assert np.isin(np.arange(50000, 52000), idx[0]).all(), "the tied top keys are all kept"
+    P.index_scores_hist(g, buf)   # a histogram left behind by an interrupted split call
+    P.index_and_select(g, buf)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, buf, wl.topk, "stale histogram")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    buf.ws_topk.copy_(torch.randint(0, 256, buf.ws_topk.shape, generator=gen, device="cuda", dtype=torch.int32)
+                      .to(torch.uint8))
+    P.index_and_select(g, buf)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, buf, wl.topk, "random workspace")
+    P.index_and_select(g, buf)
+    torch.cuda.synchronize()
+    _check_rows_exact(wl, buf, wl.topk, "after recovery")
+
+
 def test_fused_workspace_reused_across_shapes(dsa):
     P = _pipe()
     big = workloads.make_workload(name="big", seed=909, seq_lens=[12000, 8000, 5000], max_ctx=12000).to("cuda")
