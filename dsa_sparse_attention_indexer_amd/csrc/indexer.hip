@@ -283,6 +283,12 @@ struct KeyTile {
   float sc;     // the row's fp8 scale
 };
 
+// Cache policy of the score stores: non-temporal.  The scores are written once and read by the
+// selection (or the caller) after the kernel; kept out of the L2 as dirty lines, they neither compete
+// with the key stream there nor have to be written back at the end of the kernel (measured: the
+// kernel and the hand-over to the next one are both shorter).
+constexpr int kStreamStore = 2;   // the nt bit of the buffer store's cache-policy operand
+
 // Buffer resource (gfx9 raw buffer, no swizzle) over `bytes` bytes from `base`.  Accesses at or past
 // `bytes` are dropped by the hardware (loads return 0, stores do nothing), which keeps tail
 // handling free of branches -- and the compiler's wait counts static.
@@ -677,7 +683,7 @@ k_index_scores_fp8(IndexerLaunch a) {
       issue(it + kRing);
     }
     const float sc = tile_scores(cur, ahi, alo, cf);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, kStreamStore);
     if (hist && g == 0 && rel + col < nrow) atomicAdd(&pu.lh[score_key(sc) >> kTkShift0], 1u);
     if (!HIST && bm) {   // a 32-key tile lies in one block: its maximum, then the block's
       const uint32_t kk = tk_wave_max((g == 0 && rel + col < nrow) ? score_key(sc) : 0u);
@@ -786,7 +792,7 @@ __device__ void grouped_private_stream(const IndexerLaunch& a, int t, int c0, co
   for (int it = 0; it < TPW; ++it) {
     KeyTile& cur = tb[it % kDepth];
     const float sc = tile_scores(cur, ahi, alo, cf);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, kStreamStore);
     if (it + kDepth < TPW) load(cur, it + kDepth);
     rel += kTile;
   }
