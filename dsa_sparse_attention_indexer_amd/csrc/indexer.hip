@@ -914,9 +914,10 @@ k_index_scores_fp8_grouped(IndexerLaunch a, const void* ws) {
       k1.sc = st.sc[s1][col];
       float r0, r1;
       tile_scores2(k0, k1, ahi, alo, cf, r0, r1);   // past the last tile, k1 holds stale data: not stored
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r0), ors, out_off + 4u * rel, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r0), ors, out_off + 4u * rel, 0, kStreamStore);
       if (tau + 1 < ntiles)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r1), ors, out_off + 4u * (rel + kTile), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r1), ors, out_off + 4u * (rel + kTile), 0,
+                                              kStreamStore);
     }
   }
 }
