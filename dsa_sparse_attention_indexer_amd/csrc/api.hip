@@ -232,7 +232,10 @@ dsa_status_t dsa_indexer_topk(const dsa_indexer_desc_t* d, const void* q, const 
   hipError_t e = dsa::launch_indexer(a, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status("dsa_indexer_topk", e);
   dsa::TopkLaunch tk{scores, ld_scores, d->max_ctx, q_pos, d->num_q, k, idx, len, topk_ws, emit ? chunk : 0, emit};
-  return hip_status("dsa_indexer_topk", dsa::launch_topk(tk, fused, (hipStream_t)stream));
+  // scores nobody histogrammed (grouped or fp32 score kernels): as dsa_topk
+  if (fused) return hip_status("dsa_indexer_topk", dsa::launch_topk(tk, true, (hipStream_t)stream));
+  return hip_status("dsa_indexer_topk", dsa::topk_direct_pays(d->num_q) ? dsa::launch_topk_direct(tk, (hipStream_t)stream)
+                                                                         : dsa::launch_topk(tk, false, (hipStream_t)stream));
 }
 
 dsa_status_t dsa_indexer_scores_hist(const dsa_indexer_desc_t* d, const void* q, const float* w,
@@ -290,7 +293,8 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
   dsa_status_t st = ck.finish("dsa_topk");
   if (st != DSA_OK || num_q == 0) return st;
   dsa::TopkLaunch a{scores, ld_scores, ld_scores, q_pos, num_q, k, idx, len, ws, 0, 0};
-  return hip_status("dsa_topk", dsa::launch_topk(a, false, (hipStream_t)stream));
+  return hip_status("dsa_topk", dsa::topk_direct_pays(num_q) ? dsa::launch_topk_direct(a, (hipStream_t)stream)
+                                                              : dsa::launch_topk(a, false, (hipStream_t)stream));
 }
 
 size_t dsa_block_select_workspace_size(int32_t num_q, int64_t ld_scores, int32_t block) {

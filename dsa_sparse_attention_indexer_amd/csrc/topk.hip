@@ -290,6 +290,80 @@ __device__ __forceinline__ void finish_streaming(const TopkLaunch& a, int t, int
   }
 }
 
+// The selection from the row's candidates in LDS (sm.key / sm.col[0, total), in column order: every
+// key whose first digit is >= b0, where b0 holds the k-th largest key and need0 of its keys are
+// still needed): the exact k-th key from two more 10-bit digits, then one ordered pass that keeps
+// the keys above it and the lowest columns among the keys equal to it.  Writes the row's output
+// and length.
+__device__ __forceinline__ void select_from_items(const TopkLaunch& a, int t, uint32_t total, uint32_t b0,
+                                                  uint32_t need0, ResolveSmem& sm) {
+  const int tid = threadIdx.x;
+  int32_t* out = a.idx + (size_t)t * a.k;
+
+  // the exact k-th key among the candidates (the items inside b0): bits 19..10 first
+  int d1;
+  uint32_t need1;
+  lds_digit<10>(sm.key, (int)total, b0, 10, need0, sm, &d1, &need1);
+  const uint32_t pre22 = (b0 << 10) | (uint32_t)d1;
+  uint32_t thr, need2;
+  const uint32_t c1 = sm.hist[d1];   // keys sharing the top 22 bits of the k-th key
+  __syncthreads();                   // read before the histogram is reused below
+  if (c1 <= 64u) {
+    // typically a handful of keys share the top 22 bits: collect them and rank them in one wave
+    if (tid == 0) sm.sbuf[25] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < total; i += kRT) {
+      const uint32_t k = sm.key[i];
+      if ((k >> 10) == pre22) sm.wsum[atomicAdd(&sm.sbuf[25], 1u)] = k;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t c = sm.sbuf[25];
+      const uint32_t mine = tid < (int)c ? sm.wsum[tid] : 0u;
+      uint32_t above = 0, same = 0;
+      for (uint32_t j = 0; j < c; ++j) {
+        const uint32_t o = sm.wsum[j];
+        above += o > mine ? 1u : 0u;
+        same += o == mine ? 1u : 0u;
+      }
+      if (tid < (int)c && above < need1 && need1 <= above + same) { sm.sbuf[26] = mine; sm.sbuf[27] = need1 - above; }
+    }
+    __syncthreads();
+    thr = sm.sbuf[26];
+    need2 = sm.sbuf[27];
+  } else {
+    int d2;
+    lds_digit<10>(sm.key, (int)total, pre22, 0, need1, sm, &d2, &need2);
+    thr = (pre22 << 10) | (uint32_t)d2;
+  }
+
+  // One ordered pass: keys above thr, and the need2 lowest columns among the keys equal to it.
+  // Item i goes to slot (#keys above thr before i) + min(#keys equal to thr before i, need2); both
+  // counts come from one scan of a packed pair (each at most 16384, so no carry crosses).
+  const uint32_t per = (total + kRT - 1) / kRT;
+  const uint32_t i0 = min(total, per * tid), i1 = min(total, i0 + per);
+  uint32_t ngt = 0, neq = 0;
+  for (uint32_t i = i0; i < i1; ++i) {
+    const uint32_t k = sm.key[i];
+    ngt += k > thr ? 1u : 0u;
+    neq += k == thr ? 1u : 0u;
+  }
+  const uint32_t pk = tk_excl_scan<kRT>((neq << 16) | ngt, nullptr, sm.sbuf);
+  uint32_t gt = pk & 0xFFFFu, eq = pk >> 16;
+  for (uint32_t i = i0; i < i1; ++i) {
+    const uint32_t k = sm.key[i];
+    if (k > thr) {
+      const uint32_t p = gt + min(eq, need2);
+      if (p < (uint32_t)a.k) out[p] = (int32_t)sm.col[i];
+      ++gt;
+    } else if (k == thr) {
+      if (eq < need2 && gt + eq < (uint32_t)a.k) out[gt + eq] = (int32_t)sm.col[i];
+      ++eq;
+    }
+  }
+  if (tid == 0 && a.len) a.len[t] = a.k;
+}
+
 // Emitted rows (score chunks wrote their candidates into fixed regions: chunk s of S owns items
 // s * cap .. s * cap + cap - 1, cap = kTkItemCap / S).  The histogram, the table and every item
 // region are loaded in one round of loads; the searches over a histogram run in one wave while the
@@ -590,69 +664,7 @@ __device__ __forceinline__ bool resolve_collected(const TopkLaunch& a, int t, in
     return false;
   }
   const uint32_t need0 = (uint32_t)a.k - above_b0;
-
-  // the exact k-th key among the candidates (the items inside b0): bits 19..10 first
-  int d1;
-  uint32_t need1;
-  lds_digit<10>(sm.key, (int)total, (uint32_t)b0, 10, need0, sm, &d1, &need1);
-  const uint32_t pre22 = ((uint32_t)b0 << 10) | (uint32_t)d1;
-  uint32_t thr, need2;
-  const uint32_t c1 = sm.hist[d1];   // keys sharing the top 22 bits of the k-th key
-  __syncthreads();                   // read before the histogram is reused below
-  if (c1 <= 64u) {
-    // typically a handful of keys share the top 22 bits: collect them and rank them in one wave
-    if (tid == 0) sm.sbuf[25] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < total; i += kRT) {
-      const uint32_t k = sm.key[i];
-      if ((k >> 10) == pre22) sm.wsum[atomicAdd(&sm.sbuf[25], 1u)] = k;
-    }
-    __syncthreads();
-    if (tid < 64) {
-      const uint32_t c = sm.sbuf[25];
-      const uint32_t mine = tid < (int)c ? sm.wsum[tid] : 0u;
-      uint32_t above = 0, same = 0;
-      for (uint32_t j = 0; j < c; ++j) {
-        const uint32_t o = sm.wsum[j];
-        above += o > mine ? 1u : 0u;
-        same += o == mine ? 1u : 0u;
-      }
-      if (tid < (int)c && above < need1 && need1 <= above + same) { sm.sbuf[26] = mine; sm.sbuf[27] = need1 - above; }
-    }
-    __syncthreads();
-    thr = sm.sbuf[26];
-    need2 = sm.sbuf[27];
-  } else {
-    int d2;
-    lds_digit<10>(sm.key, (int)total, pre22, 0, need1, sm, &d2, &need2);
-    thr = (pre22 << 10) | (uint32_t)d2;
-  }
-
-  // One ordered pass: keys above thr, and the need2 lowest columns among the keys equal to it.
-  // Item i goes to slot (#keys above thr before i) + min(#keys equal to thr before i, need2); both
-  // counts come from one scan of a packed pair (each at most 16384, so no carry crosses).
-  const uint32_t per = (total + kRT - 1) / kRT;
-  const uint32_t i0 = min(total, per * tid), i1 = min(total, i0 + per);
-  uint32_t ngt = 0, neq = 0;
-  for (uint32_t i = i0; i < i1; ++i) {
-    const uint32_t k = sm.key[i];
-    ngt += k > thr ? 1u : 0u;
-    neq += k == thr ? 1u : 0u;
-  }
-  const uint32_t pk = tk_excl_scan<kRT>((neq << 16) | ngt, nullptr, sm.sbuf);
-  uint32_t gt = pk & 0xFFFFu, eq = pk >> 16;
-  for (uint32_t i = i0; i < i1; ++i) {
-    const uint32_t k = sm.key[i];
-    if (k > thr) {
-      const uint32_t p = gt + min(eq, need2);
-      if (p < (uint32_t)a.k) out[p] = (int32_t)sm.col[i];
-      ++gt;
-    } else if (k == thr) {
-      if (eq < need2 && gt + eq < (uint32_t)a.k) out[gt + eq] = (int32_t)sm.col[i];
-      ++eq;
-    }
-  }
-  if (tid == 0 && a.len) a.len[t] = a.k;
+  select_from_items(a, t, total, (uint32_t)b0, need0, sm);
   return true;
 }
 
@@ -681,9 +693,87 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// direct: one workgroup per row, no workspace, for rows whose scores no kernel has histogrammed
+// (the scores of the grouped and fp32 score kernels, and the separate top-k call)
+// ------------------------------------------------------------------------------------------
+
+// Two passes over the row: the first digit's histogram in LDS gives b0 (the digit holding the k-th
+// largest key), then every key whose first digit is >= b0 goes straight into LDS in column order
+// (the ordered compaction of the collect kernel, without the global item list), and the selection
+// finishes there.  Returns false when the candidates do not fit in LDS (heavy ties: exact passes).
+__device__ __forceinline__ bool direct_fast(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
+  const float* row = a.scores + (size_t)t * a.ld;
+  int b0i;
+  uint32_t need0;
+  row_digit<12>(row, n, 0u, kTkShift0, (uint32_t)a.k, sm, &b0i, &need0);
+  const uint32_t b0 = (uint32_t)b0i;
+  constexpr int Q2 = 2;   // slices per thread in the collecting pass (register budget at 1024 threads)
+  uint32_t base = 0;
+  for (int c0 = 0; c0 < n; c0 += 4 * kRT * Q2) {
+    uint32_t key[Q2][4];
+    const uint32_t mask = tk_load_slices<Q2, kRT>(row, n, c0, key);
+    uint32_t fl[Q2], pos[Q2];
+#pragma unroll
+    for (int q = 0; q < Q2; ++q) {
+      fl[q] = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        fl[q] |= (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> kTkShift0) >= b0 ? 1u : 0u) << e;
+    }
+    const uint32_t tot = tk_ordered_slots<Q2, kRT>(fl, pos, sm.wsum);
+    if (base + tot > (uint32_t)kTkItemCap) return false;   // (block-uniform)
+#pragma unroll
+    for (int q = 0; q < Q2; ++q) {
+      uint32_t p = base + pos[q];
+      const uint32_t cq = (uint32_t)(c0 + 4 * kRT * q + 4 * (int)threadIdx.x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((fl[q] >> e) & 1u) {
+          sm.key[p] = key[q][e];
+          sm.col[p] = cq + e;
+          ++p;
+        }
+    }
+    base += tot;
+  }
+  __syncthreads();   // the items are in LDS for every thread
+  select_from_items(a, t, base, b0, need0, sm);
+  return true;
+}
+
+__global__ void __launch_bounds__(kRT) k_topk_direct(TopkLaunch a) {
+  __shared__ __attribute__((aligned(16))) ResolveSmem sm;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = row_n(a, t);
+  int32_t* out = a.idx + (size_t)t * a.k;
+  if (a.ws) {   // a workspace given with the call: leave its row clean, as the resolve kernel does
+    uint32_t* rw = tk_row(a.ws, t);
+    reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) rw[kTkOffCtr] = 0u;
+  }
+  if (n <= a.k) {   // every visible column, then padding
+    for (int i = tid; i < a.k; i += kRT) out[i] = i < n ? i : -1;
+    if (tid == 0 && a.len) a.len[t] = n;
+    return;
+  }
+  const bool done = a.k <= kTkFastK && direct_fast(a, t, n, sm);
+  if (!done) {
+    finish_streaming(a, t, n, sm);
+    if (tid == 0 && a.len) a.len[t] = a.k;
+  }
+}
+
 }  // namespace
 
 size_t topk_ws_bytes(int T) { return tk_total_words(T) * sizeof(uint32_t); }
+
+hipError_t launch_topk_direct(const TopkLaunch& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  launch(k_topk_direct, dim3(a.T), dim3(kRT), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk_hist(const TopkLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;

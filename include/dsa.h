@@ -176,20 +176,25 @@ dsa_status_t dsa_indexer_scores(const dsa_indexer_desc_t* desc, const void* q, c
  *   idx      [num_q][k] i32;          len [num_q] i32 (may be NULL)
  *   ws       device workspace of at least dsa_topk_workspace_size(num_q, ld_scores, k) bytes,
  *            16-byte aligned (about 148 KiB per query: the row's first-digit histogram and the
- *            keys that survive it).  Its contents never decide a selection: the histogram only
- *            steers a fast path whose premise (the k-th largest key lies in the bin it names) is
- *            checked against the scores themselves, and rows that fail the check are selected by
- *            exact passes over the row.  Every call clears what it used, so a workspace that is
- *            zero-filled once (hipMemset) keeps every call on the fast path; stale or random
- *            contents cost one slower call, never a wrong one.  Calls that overlap in time must
- *            not share a workspace.
+ *            keys that survive it).  With many rows (128 or more) dsa_topk selects each row in one
+ *            kernel (two passes over the row, the candidates kept on chip) and only clears the
+ *            workspace rows; with fewer, and on the fused and split calls below, the workspace
+ *            carries the rows' histograms and candidates between kernels.  Its contents never decide a
+ *            selection: the histogram only steers a fast path whose premise (the k-th largest key
+ *            lies in the bin it names) is checked against the scores themselves, and rows that
+ *            fail the check are selected by exact passes over the row.  Every call clears what it
+ *            used, so a workspace that is zero-filled once (hipMemset) keeps every call on the
+ *            fast path; stale or random contents cost one slower call, never a wrong one.  Calls
+ *            that overlap in time must not share a workspace.
  * Supported: 1 <= k <= 65536; ld_scores <= 4194304 and a multiple of 4; scores 16-byte aligned.
  * ==========================================================================================*/
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t num_q,
                       int32_t k, int32_t* idx, int32_t* len, void* ws, size_t ws_bytes, void* stream);
 
 /* Scores and top-k in one call: dsa_indexer_scores followed by dsa_topk, with the first radix
- * digit's histogram built inside the fp8 score kernel (the scores are still written to `scores`).
+ * digit's histogram built inside the fp8 decode score kernel and each score chunk's candidates
+ * emitted by it (the scores are still written to `scores`); scores from the grouped or fp32 score
+ * kernels are selected as dsa_topk does.
  * Same arguments, conventions and results as the two calls made in sequence, except that a row
  * holds min(q_pos + 1, max_ctx) scores (the score kernel's clamp).  `topk_ws` follows dsa_topk's
  * workspace rules. */
