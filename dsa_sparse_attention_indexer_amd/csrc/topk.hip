@@ -698,44 +698,99 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
 // (the scores of the grouped and fp32 score kernels, and the separate top-k call)
 // ------------------------------------------------------------------------------------------
 
+// Raw float4 slices of a row (layout of tk_load_slices: element (q, e) of thread tid is column
+// c0 + 4*kRT*q + 4*tid + e; slices past the row read its last aligned float4 and are masked later).
+template <int Q>
+__device__ __forceinline__ void row_slices(const float* row, int n, int c0, float4 (&v)[Q]) {
+  const int clast = (n - 1) & ~3;
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+    v[q] = *reinterpret_cast<const float4*>(row + min(c0 + 4 * kRT * q + 4 * (int)threadIdx.x, clast));
+}
+
 // Two passes over the row: the first digit's histogram in LDS gives b0 (the digit holding the k-th
 // largest key), then every key whose first digit is >= b0 goes straight into LDS in column order
 // (the ordered compaction of the collect kernel, without the global item list), and the selection
-// finishes there.  Returns false when the candidates do not fit in LDS (heavy ties: exact passes).
+// finishes there.  Each pass issues the next round's loads before it works on the current round.
+// Returns false when the candidates do not fit in LDS (heavy ties: exact passes).
 __device__ __forceinline__ bool direct_fast(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
+  constexpr int Q = 2;                 // float4 slices per thread and round
+  constexpr int STEP = 4 * kRT * Q;    // columns per round
   const float* row = a.scores + (size_t)t * a.ld;
+  const int tid = threadIdx.x;
+  auto keys_of = [&](const float4 (&v)[Q], int c0, uint32_t (&key)[Q][4]) {
+    uint32_t mask = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int c = c0 + 4 * kRT * q + 4 * tid;
+      key[q][0] = score_key(v[q].x);
+      key[q][1] = score_key(v[q].y);
+      key[q][2] = score_key(v[q].z);
+      key[q][3] = score_key(v[q].w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mask |= (c + e < n ? 1u : 0u) << (4 * q + e);
+    }
+    return mask;
+  };
+  // pass 1: the first digit's histogram
+  for (int i = tid; i < kTkBins; i += kRT) sm.hist[i] = 0;
+  __syncthreads();
+  {
+    float4 cur[Q], nxt[Q];
+    row_slices<Q>(row, n, 0, cur);
+    for (int c0 = 0; c0 < n; c0 += STEP) {
+      row_slices<Q>(row, n, c0 + STEP, nxt);   // unconditional (clamped past the row): stays in flight
+      uint32_t key[Q][4];
+      const uint32_t mask = keys_of(cur, c0, key);
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((mask >> (4 * q + e)) & 1u) atomicAdd(&sm.hist[key[q][e] >> kTkShift0], 1u);
+#pragma unroll
+      for (int q = 0; q < Q; ++q) cur[q] = nxt[q];
+    }
+  }
+  __syncthreads();
   int b0i;
   uint32_t need0;
-  row_digit<12>(row, n, 0u, kTkShift0, (uint32_t)a.k, sm, &b0i, &need0);
+  tk_find_bin<kTkBins, kRT>(sm.hist, (uint32_t)a.k, sm.sbuf, &b0i, &need0);
   const uint32_t b0 = (uint32_t)b0i;
-  constexpr int Q2 = 2;   // slices per thread in the collecting pass (register budget at 1024 threads)
+  // pass 2: the candidates into LDS in column order
   uint32_t base = 0;
-  for (int c0 = 0; c0 < n; c0 += 4 * kRT * Q2) {
-    uint32_t key[Q2][4];
-    const uint32_t mask = tk_load_slices<Q2, kRT>(row, n, c0, key);
-    uint32_t fl[Q2], pos[Q2];
+  {
+    float4 cur[Q], nxt[Q];
+    row_slices<Q>(row, n, 0, cur);
+    for (int c0 = 0; c0 < n; c0 += STEP) {
+      row_slices<Q>(row, n, c0 + STEP, nxt);   // unconditional (clamped past the row): stays in flight
+      uint32_t key[Q][4];
+      const uint32_t mask = keys_of(cur, c0, key);
+      uint32_t fl[Q], pos[Q];
 #pragma unroll
-    for (int q = 0; q < Q2; ++q) {
-      fl[q] = 0;
+      for (int q = 0; q < Q; ++q) {
+        fl[q] = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        fl[q] |= (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> kTkShift0) >= b0 ? 1u : 0u) << e;
+        for (int e = 0; e < 4; ++e)
+          fl[q] |= (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> kTkShift0) >= b0 ? 1u : 0u) << e;
+      }
+      const uint32_t tot = tk_ordered_slots<Q, kRT>(fl, pos, sm.wsum);
+      if (base + tot > (uint32_t)kTkItemCap) return false;   // (block-uniform)
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        uint32_t p = base + pos[q];
+        const uint32_t cq = (uint32_t)(c0 + 4 * kRT * q + 4 * tid);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((fl[q] >> e) & 1u) {
+            sm.key[p] = key[q][e];
+            sm.col[p] = cq + e;
+            ++p;
+          }
+      }
+      base += tot;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) cur[q] = nxt[q];
     }
-    const uint32_t tot = tk_ordered_slots<Q2, kRT>(fl, pos, sm.wsum);
-    if (base + tot > (uint32_t)kTkItemCap) return false;   // (block-uniform)
-#pragma unroll
-    for (int q = 0; q < Q2; ++q) {
-      uint32_t p = base + pos[q];
-      const uint32_t cq = (uint32_t)(c0 + 4 * kRT * q + 4 * (int)threadIdx.x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((fl[q] >> e) & 1u) {
-          sm.key[p] = key[q][e];
-          sm.col[p] = cq + e;
-          ++p;
-        }
-    }
-    base += tot;
   }
   __syncthreads();   // the items are in LDS for every thread
   select_from_items(a, t, base, b0, need0, sm);
