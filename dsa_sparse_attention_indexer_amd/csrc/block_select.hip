@@ -75,7 +75,10 @@ __device__ inline uint64_t pack_block(uint32_t key, int64_t j) {
 }
 
 struct PickSmem {
-  uint32_t hist[4096];
+  uint32_t hist[4096];   // first digit
+  uint32_t h1[1024];     // second and third digits
+  uint32_t h2[1024];
+  uint32_t res[2];       // a digit search's result: bin, count still needed
   uint32_t sbuf[32];
   int eq[kMaxBlocksKept];
   int cnt, neq;
@@ -113,25 +116,32 @@ __global__ void __launch_bounds__(kPT) k_block_pick(BlockSelectLaunch a) {
         v[i] = (j < nb && j != recent) ? bmax[j] : 0u;   // every candidate key is >= 1
       }
       uint32_t need = (uint32_t)(m - 1), prefix = 0;
-      int bin;
+      // the three histograms are cleared together; each digit's bin is then found by one wave
+      for (int i = tid; i < 4096; i += kPT) ps.hist[i] = 0u;
+      for (int i = tid; i < 1024; i += kPT) { ps.h1[i] = 0u; ps.h2[i] = 0u; }
+      __syncthreads();
 #pragma unroll 1
       for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
         const int nbins = pass == 0 ? 4096 : 1024;
-        for (int i = tid; i < 4096; i += kPT) ps.hist[i] = 0u;
-        __syncthreads();
+        uint32_t* h = pass == 0 ? ps.hist : (pass == 1 ? ps.h1 : ps.h2);
 #pragma unroll
         for (int i = 0; i < kPickPer; ++i) {
           const uint32_t k = v[i];
           const bool in = k != 0u && (pass == 0 || (k >> (shift + 10)) == prefix);
-          if (in) atomicAdd(&ps.hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+          if (in) atomicAdd(&h[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
         }
         __syncthreads();
-        uint32_t left;
-        if (pass == 0) tk_find_bin<4096, kPT>(ps.hist, need, ps.sbuf, &bin, &left);
-        else tk_find_bin<1024, kPT>(ps.hist, need, ps.sbuf, &bin, &left);
-        need = left;
-        prefix = (prefix << (pass == 0 ? 12 : 10)) | (uint32_t)bin;
+        if (tid < 64) {
+          int bin;
+          uint32_t left;
+          if (pass == 0) tk_wave_find_bin<4096>(h, need, &bin, &left);
+          else tk_wave_find_bin<1024>(h, need, &bin, &left);
+          if (tid == 0) { ps.res[0] = (uint32_t)bin; ps.res[1] = left; }
+        }
+        __syncthreads();
+        need = ps.res[1];
+        prefix = (prefix << (pass == 0 ? 12 : 10)) | ps.res[0];
       }
       const uint32_t thr = prefix;   // the (m-1)-th largest key; `need` of the keys equal to it are kept
       if (tid == 0) { ps.cnt = 1; ps.neq = 0; }

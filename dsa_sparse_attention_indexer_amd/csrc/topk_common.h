@@ -128,6 +128,46 @@ __device__ inline void tk_find_bin(const uint32_t* h, uint32_t need, uint32_t* s
   __syncthreads();
 }
 
+// The bin of an NB-bin histogram (16-byte aligned, in LDS) that holds the need-th largest key, found
+// by one wave with no barrier: lane l sums the NB/64 bins counted l-th from the top, a prefix sum
+// over the lanes names the lane whose bins hold it, and a second prefix sum over that lane's bins
+// (one per lane) names the bin.  Returns the bin and the count still needed inside it in every lane;
+// fewer than need keys in the histogram: bin 0 and need.
+template <int NB>
+__device__ inline void tk_wave_find_bin(const uint32_t* h, uint32_t need, int* bin_out, uint32_t* need_out) {
+  constexpr int PER = NB / 64;
+  static_assert(PER % 4 == 0 && PER <= 64, "bins per lane");
+  const int lane = threadIdx.x & 63;
+  const int lo = NB - PER * (lane + 1);
+  uint32_t sum = 0;
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) {
+    const uint4 x = *reinterpret_cast<const uint4*>(h + lo + 4 * q);
+    sum += x.x + x.y + x.z + x.w;
+  }
+  const uint32_t incl = tk_wave_incl_scan(sum);
+  const uint64_t m = __ballot(incl - sum < need && need <= incl);
+  if (m == 0) {
+    *bin_out = 0;
+    *need_out = need;
+    return;
+  }
+  const int l0 = __builtin_ctzll(m);
+  const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), l0);
+  const int lo0 = NB - PER * (l0 + 1);
+  const uint32_t c = lane < PER ? h[lo0 + PER - 1 - lane] : 0u;   // lane i: the i-th of those bins from the top
+  const uint32_t inc2 = ab + tk_wave_incl_scan(c);
+  const uint64_t m2 = __ballot(lane < PER && inc2 - c < need && need <= inc2);
+  const int i = __builtin_ctzll(m2);
+  *bin_out = lo0 + PER - 1 - i;
+  *need_out = need - ((uint32_t)__builtin_amdgcn_readlane((int)inc2, i) - (uint32_t)__builtin_amdgcn_readlane((int)c, i));
+}
+
+// Sum over the 64 lanes of a wave (every lane gets it).
+__device__ inline uint32_t tk_wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)tk_wave_incl_scan(x), 63);
+}
+
 __device__ inline uint32_t tk_lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
