@@ -10,20 +10,21 @@
 //            adds it to the row's histogram.  The fused path skips it: the index-score kernel
 //            has already built that histogram.
 //   collect  one workgroup per segment finds, from the row's histogram, the bin b0 that holds
-//            the k-th largest key and appends every key whose first digit is >= b0 (all keys
-//            above b0 plus the candidates inside it; a few thousand per row) to the row's item
-//            list, in column order within the segment, with ballot/mbcnt compaction.
-//   resolve  one workgroup per row loads the items into LDS in column order, checks from them
+//            the k-th largest key and writes every key whose first digit is >= b0 (all keys
+//            above b0 plus the candidates inside it; a few thousand per row) to the segment's own
+//            region of the row's item list, in column order, with ballot/mbcnt compaction.
+//   resolve  one workgroup per row loads the histogram, the segment table and every item region
+//            in one round of loads and places the items in LDS in column order, checks from them
 //            that the histogram's bin b0 really holds the k-th largest key (fewer than k items
 //            above b0, at least k at or above it), finds the exact k-th key among the candidates
-//            (bits 19..10, then 9..0), and with one ordered pass keeps the keys above it and the
-//            lowest columns among the keys equal to it.  The output is ascending by
-//            construction: no sort and no merge.
+//            (bits 19..10, then 9..0; each histogram searched by one wave), and with one ordered
+//            pass keeps the keys above it and the lowest columns among the keys equal to it.  The
+//            output is ascending by construction: no sort and no merge.
 // On the fused score + top-k path the score kernel emits each chunk's candidates itself (see
-// emit_candidates in the index kernels) into fixed regions of the row's item list, and only the
-// resolve kernel runs (resolve_emitted: histogram, table and item regions in one round of loads,
-// the histogram searches in one wave); a chunk that emitted only digits above the row's b0 sends
-// the row to the exact passes below.
+// emit_candidates in the index kernels) into the same kind of regions, and only the resolve kernel
+// runs; a chunk that emitted only digits above the row's b0 sends the row to the exact passes.
+// With many rows and no histogram (the grouped and fp32 score kernels, the separate call), one
+// kernel per row (direct) streams the row twice and keeps the candidates on chip.
 // If a row's items do not fit in LDS (heavy ties), k is large, or the check fails (a histogram
 // left over from an interrupted call, or built for another k), the resolve workgroup instead
 // selects by exact passes over the row, first digit included.  Every decision is made on the
@@ -80,7 +81,6 @@ __global__ void __launch_bounds__(kCT) k_topk_collect(TopkLaunch a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[kTkBins];
   __shared__ uint32_t sbuf[32];
   __shared__ uint32_t wsum[kCQ * (kCT / 64)];
-  __shared__ uint32_t base;
   const int t = blockIdx.y;
   const int n = row_n(a, t);
   const int seg = blockIdx.x;
@@ -111,16 +111,16 @@ __global__ void __launch_bounds__(kCT) k_topk_collect(TopkLaunch a) {
   }
   uint32_t pos[kCQ];
   const uint32_t total = tk_ordered_slots<kCQ, kCT>(fl, pos, wsum);
-  if (threadIdx.x == 0) {
-    const uint32_t st = atomicAdd(&rw[kTkOffCtr], total);
-    base = st;
-    *reinterpret_cast<uint2*>(rw + kTkOffTable + 2 * seg) = make_uint2(st, total);
-  }
-  __syncthreads();
-  const uint32_t st = base;
-  // the row overflows (or the counter held a stale value): nothing is written, the resolve
-  // kernel sees it in the segment table and streams the row
-  if (st > (uint32_t)kTkItemCap || total > (uint32_t)kTkItemCap - st) return;
+  // segment s of the row's S owns items s * cap .. s * cap + cap - 1 (cap = kTkItemCap / S); a
+  // segment with more candidates writes none and an entry that claims more items than the list
+  // has, and the resolve kernel then streams the row
+  const uint32_t cap = (uint32_t)kTkItemCap / (uint32_t)((n + kTkSeg - 1) / kTkSeg);
+  const uint32_t st = (uint32_t)seg * cap;
+  const bool fits = total <= cap;
+  if (threadIdx.x == 0)
+    *reinterpret_cast<uint2*>(rw + kTkOffTable + 2 * seg) =
+        make_uint2(fits ? st : (uint32_t)kTkItemCap, fits ? total : 0xFFFFu);
+  if (!fits) return;
   uint2* items = reinterpret_cast<uint2*>(rw + kTkOffItems);
 #pragma unroll
   for (int q = 0; q < kCQ; ++q) {
@@ -324,12 +324,14 @@ __device__ __forceinline__ void select_from_items(const TopkLaunch& a, int t, ui
   if (tid == 0 && a.len) a.len[t] = a.k;
 }
 
-// Emitted rows (score chunks wrote their candidates into fixed regions: chunk s of S owns items
-// s * cap .. s * cap + cap - 1, cap = kTkItemCap / S).  The histogram, the table and every item
+// A row's candidates are in fixed regions of its item list (segment s of S -- a collect segment or
+// a score chunk -- owns items s * cap .. s * cap + cap - 1, cap = kTkItemCap / S), and its table
+// entry gives (first item, count | lowest digit emitted << 16; 0 for collect segments, which emit
+// every key from the row's b0 up).  The histogram, the table and every item
 // region are loaded in one round of loads; the searches over a histogram run in one wave while the
 // other waves place the items in column order, so the row takes nine workgroup barriers.  Returns
 // false (the row is then selected by the exact passes) on the same conditions as the general path.
-__device__ __forceinline__ bool resolve_emitted(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
+__device__ __forceinline__ bool resolve_items(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
   constexpr int IPT = kTkItemCap / kRT;   // item slots per thread
   static_assert(IPT % 2 == 0 && kTkMaxSeg <= kRT, "item slots and table entries per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -527,107 +529,6 @@ __device__ __forceinline__ bool resolve_emitted(const TopkLaunch& a, int t, int 
   return true;
 }
 
-// Collected rows (and emitted rows without the fixed item regions): the general path.  Returns false
-// when the row must be selected by the exact passes.
-__device__ __forceinline__ bool resolve_collected(const TopkLaunch& a, int t, int n, ResolveSmem& sm) {
-  const int tid = threadIdx.x;
-  int32_t* out = a.idx + (size_t)t * a.k;
-  uint32_t* rw = tk_row(a.ws, t);
-  // The row's segment table (and, for collected rows, its histogram) in one round of loads; the
-  // histogram and the item counter are then zeroed for the next call.
-  const int S = (n + a.seg - 1) / a.seg;
-  uint32_t cnt_s = 0, low_s = 0;
-  bool seg_bad = false;
-  {
-    const uint4 h = reinterpret_cast<const uint4*>(rw)[tid];
-    uint2 te = make_uint2(0u, 0u);
-    if (tid < S) te = reinterpret_cast<const uint2*>(rw + kTkOffTable)[tid];
-    sm.hist[4 * tid] = h.x; sm.hist[4 * tid + 1] = h.y; sm.hist[4 * tid + 2] = h.z; sm.hist[4 * tid + 3] = h.w;
-    if (tid < S) sm.tst[tid] = te.x;
-    cnt_s = te.y & 0xFFFFu;
-    low_s = te.y >> 16;                 // lowest first digit the segment emitted (0 for collect segments)
-    // a segment whose items did not fit (or whose start came from a stale counter) wrote none
-    seg_bad = tid < S && (te.x > (uint32_t)kTkItemCap || cnt_s > (uint32_t)kTkItemCap - te.x);
-    if (tid == 0) sm.sbuf[28] = 0u;
-    __syncthreads();
-    reinterpret_cast<uint4*>(rw)[tid] = make_uint4(0u, 0u, 0u, 0u);
-    if (tid == 0) rw[kTkOffCtr] = 0u;
-    if (a.emitted && tid < S) atomicMax(&sm.sbuf[28], low_s);
-  }
-  const bool overflow = __syncthreads_or(seg_bad) != 0;
-  // Emitted rows: each chunk added its bins at or above its own lowest emitted digit, so with L the
-  // largest of those digits the histogram is exact from L up (and the items at or above L are
-  // exactly the row's keys there); the bins below L are dropped.
-  const uint32_t L = sm.sbuf[28];
-  if (a.emitted)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if ((uint32_t)(4 * tid + j) < L) sm.hist[4 * tid + j] = 0u;
-  __syncthreads();
-  int b0;
-  uint32_t need_hint;
-  tk_find_bin<kTkBins, kRT>(sm.hist, (uint32_t)a.k, sm.sbuf, &b0, &need_hint);
-  // a segment that emitted only digits above b0 may hold keys of the top k it did not emit (for
-  // emitted rows: fewer than k keys at or above L, so b0 fell below L)
-  const bool incomplete = __syncthreads_or(tid < S && low_s > (uint32_t)b0) != 0;
-  if (a.k > kTkFastK || overflow || incomplete) {
-    return false;
-  }
-
-  // items into LDS in column order: segment s holds items tpre[s].. of the row, stored from tst[s]
-  uint32_t total;
-  const uint32_t pre = tk_excl_scan<kRT>(cnt_s, &total, sm.sbuf);
-  if (total > (uint32_t)kTkItemCap) {   // (not reached when every segment fit; kept as a guard)
-    return false;
-  }
-  if (tid < S) sm.tpre[tid] = pre;
-  __syncthreads();
-  const uint2* items = reinterpret_cast<const uint2*>(rw + kTkOffItems);
-  // four items per thread per round, their loads issued together (past the end: the last item
-  // again, not stored), so a typical row pays the load latency once; the items above b0 and at or
-  // above it are counted on the way (emitted segments may also hold items below b0)
-  uint32_t gt_b0 = 0, ge_b0 = 0;
-  if (total > 0) {
-    for (uint32_t i0 = tid; i0 < total; i0 += 4 * kRT) {
-      uint2 it[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = min(i0 + (uint32_t)(u * kRT), total - 1);
-        int lo = 0, hi = S - 1;   // the last segment starting at or before i
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sm.tpre[mid] <= i) lo = mid; else hi = mid - 1;
-        }
-        it[u] = items[sm.tst[lo] + (i - sm.tpre[lo])];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = i0 + (uint32_t)(u * kRT);
-        if (i < total) {
-          const uint32_t dg = it[u].x >> kTkShift0;
-          sm.key[i] = it[u].x;
-          sm.col[i] = it[u].y;
-          gt_b0 += dg > (uint32_t)b0 ? 1u : 0u;
-          ge_b0 += dg >= (uint32_t)b0 ? 1u : 0u;
-        }
-      }
-    }
-  }
-  // The items hold every key whose first digit is >= b0 (collect segments read the same histogram;
-  // emitted segments were checked above).  b0 holds the k-th largest key iff fewer than k of them
-  // lie above b0 and at least k at or above it; otherwise the histogram did not describe these
-  // scores.
-  uint32_t above_b0, atleast_b0;
-  tk_excl_scan<kRT>(gt_b0, &above_b0, sm.sbuf);
-  tk_excl_scan<kRT>(ge_b0, &atleast_b0, sm.sbuf);
-  if (!(above_b0 < (uint32_t)a.k && (uint32_t)a.k <= atleast_b0)) {
-    return false;
-  }
-  const uint32_t need0 = (uint32_t)a.k - above_b0;
-  select_from_items(a, t, total, (uint32_t)b0, need0, sm);
-  return true;
-}
-
 __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
   __shared__ __attribute__((aligned(16))) ResolveSmem sm;
   static_assert(kTkBins == 4 * kRT, "one uint4 of histogram per thread");
@@ -646,7 +547,7 @@ __global__ void __launch_bounds__(kRT) k_topk_resolve(TopkLaunch a) {
     return;
   }
 
-  const bool done = (a.emitted && a.k <= kTkFastK) ? resolve_emitted(a, t, n, sm) : resolve_collected(a, t, n, sm);
+  const bool done = a.k <= kTkFastK && resolve_items(a, t, n, sm);
   if (!done) {
     finish_streaming(a, t, n, sm);
     if (tid == 0 && a.len) a.len[t] = a.k;

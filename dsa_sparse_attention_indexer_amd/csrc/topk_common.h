@@ -3,14 +3,14 @@
 //
 // Per-row workspace (32-bit words):
 //   hist   [kTkBins]        counts of the first radix digit (score-key bits 31..20)
-//   ctr    [4]              ctr[0]: item slots handed out by the collect kernel
+//   ctr    [4]              reserved (cleared by every selection)
 //   table  [kTkMaxSeg][2]   per segment: first item, item count | (lowest digit emitted << 16),
 //                           written by every live segment (a collect segment or, on the fused path,
 //                           a score chunk)
 //   items  [kTkItemCap][2]  (key, column) of every score whose first digit is >= the segment's
-//                           lowest emitted digit, in column order within each segment; collect
-//                           segments take their slots from ctr[0], score chunk s of a row of S
-//                           chunks owns slots s * (kTkItemCap / S) onwards
+//                           lowest emitted digit, in column order within each segment; segment
+//                           s of a row of S (collect segments or score chunks) owns slots
+//                           s * (kTkItemCap / S) onwards
 // Collected rows: the histogram only steers the fast path: the resolve kernel checks against the
 // collected items that the digit it names holds the k-th largest key, and otherwise selects by
 // exact passes over the row.  Emitted rows (score chunks that emit their own candidates) add only
