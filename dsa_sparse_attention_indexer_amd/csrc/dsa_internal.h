@@ -102,6 +102,10 @@ struct MlaLaunch {
   float* ws;  // split partials: [T][H][splits][kv_lora] O, then [T][H][splits] m and l
   Paging pg;
   int64_t pool_rows;  // rows of kv / kv_scale when paged
+  // head split (fp8 path): T and H above count virtual queries of H heads each, hs of them per real
+  // query (the [T][64][...] query, output and LSE arrays read as [hs T][64 / hs][...]); the row
+  // indices, lengths and sequence of virtual query t are those of real query t / hs
+  int hs;
 };
 
 struct KInsertLaunch {

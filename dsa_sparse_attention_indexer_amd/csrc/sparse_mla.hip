@@ -230,7 +230,8 @@ struct Mla2Smem {
   int flags[2];                        // per head group: the tile moved the running maximum
 };
 
-template <int ROPE>
+// NHT: head tiles of 32 (2 for up to 64 heads, 1 for up to 32: the P.V waves then do half the work)
+template <int ROPE, int NHT>
 __global__ void __launch_bounds__(kMlaThreads)
 k_mla_fp8_ws(MlaLaunch a) {
   using C = M2<ROPE>;
@@ -240,7 +241,8 @@ k_mla_fp8_ws(MlaLaunch a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slot0 = split * a.per_split;
-  const int32_t* irow = a.idx + (size_t)t * a.topk;
+  const int tr = t / a.hs;                               // the real query (head split)
+  const int32_t* irow = a.idx + (size_t)tr * a.topk;
   const int slot_end = min(slot0 + a.per_split, a.topk);
   // The row indices are loaded and staged by the PV waves alone, so that the first gathers (which
   // need them) do not wait behind the QK waves' query loads.
@@ -254,9 +256,9 @@ k_mla_fp8_ws(MlaLaunch a) {
 #pragma unroll
     for (int u = 0; u < RPT; ++u) rv[u] = cb + ptid + kPvThreads * u < slot_end ? rv[u] : -1;
   };
-  const int nht = (a.H + 31) / 32;                       // head tiles of 32
-  const int b = clampi(a.q_seq[t], 0, a.B - 1);
-  const int L = a.len ? clampi(a.len[t], 0, a.topk) : a.topk;
+  constexpr int nht = NHT;                               // head tiles of 32
+  const int b = clampi(a.q_seq[tr], 0, a.B - 1);
+  const int L = a.len ? clampi(a.len[tr], 0, a.topk) : a.topk;
   const int slot1 = min(L, slot0 + a.per_split);
   // contiguous caches: the query's sequence; paged: the whole pool (rows are pool slots)
   const bool paged = a.pg.table != nullptr;
@@ -391,9 +393,9 @@ k_mla_fp8_ws(MlaLaunch a) {
     // ======================================= PV waves =======================================
     const int pw = wave - 4;                             // output dims 128pw .. 128pw + 127
     const int c16 = lane & 15, g16 = lane >> 4, h = lane >> 5;
-    float16v O[2][4];
+    float16v O[NHT][4];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+    for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) O[ht][dt] = float16v{};
     i32x2 vraw[4][4];                                    // V^T bytes of the tile: [K-step J][dim tile]
@@ -425,7 +427,7 @@ k_mla_fp8_ws(MlaLaunch a) {
     // PV of the tile whose V bytes are in vraw (its P, scales and rescale factors in LDS)
     auto pv = [&]() {
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
+      for (int ht = 0; ht < NHT; ++ht) {
         if (ht < nht && sm.flags[ht]) {
           const float al = sm.alpha[32 * ht + (lane & 31)];
 #pragma unroll
@@ -441,10 +443,9 @@ k_mla_fp8_ws(MlaLaunch a) {
           const float* sp = &sm.scl[pw][bb][16 * J + 8 * h];
           const float4 s0 = *reinterpret_cast<const float4*>(sp);
           const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
-          // both head tiles, branch-free: with at most 32 heads the second one works on P values
-          // nobody wrote and is never stored
+          // every head tile of the workgroup (NHT), branch-free
 #pragma unroll
-          for (int ht = 0; ht < 2; ++ht) {
+          for (int ht = 0; ht < NHT; ++ht) {
             const float* pp = &sm.pbuf[ht][J][lane][0];
             const float4 p0 = *reinterpret_cast<const float4*>(pp);
             const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
@@ -505,7 +506,7 @@ k_mla_fp8_ws(MlaLaunch a) {
     // normalise and store: lane (head 32ht + lane%32, half h) holds, for dim tile dt, dims
     // 128pw + 32dt + 8A + 4h + 0..3 in registers 4A..4A+3
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
+    for (int ht = 0; ht < NHT; ++ht) {
       const int head = 32 * ht + (lane & 31);
       if (ht >= nht || head >= a.H) continue;
       const float l_tot = sm.lsum[ht][0][lane & 31] + sm.lsum[ht][1][lane & 31];
@@ -739,8 +740,13 @@ hipError_t launch_sparse_mla(const MlaLaunch& a, hipStream_t s) {
   dim3 grid(a.splits, a.T);
   if (a.kv_dtype == DSA_FP8_E4M3FN) {
     const dim3 xgrid(xcd_grid(a.splits, a.T, mla_group(a.T, a.B)));
-    if (a.rope_dim == 64) launch(k_mla_fp8_ws<64>, xgrid, dim3(kMlaThreads), 0, s, a);
-    else launch(k_mla_fp8_ws<0>, xgrid, dim3(kMlaThreads), 0, s, a);
+    if (a.H > 32) {
+      if (a.rope_dim == 64) launch(k_mla_fp8_ws<64, 2>, xgrid, dim3(kMlaThreads), 0, s, a);
+      else launch(k_mla_fp8_ws<0, 2>, xgrid, dim3(kMlaThreads), 0, s, a);
+    } else {
+      if (a.rope_dim == 64) launch(k_mla_fp8_ws<64, 1>, xgrid, dim3(kMlaThreads), 0, s, a);
+      else launch(k_mla_fp8_ws<0, 1>, xgrid, dim3(kMlaThreads), 0, s, a);
+    }
   } else {
     if (a.rope_dim == 64) launch(k_mla_f32<64>, grid, dim3(kF32Threads), 0, s, a);
     else launch(k_mla_f32<0>, grid, dim3(kF32Threads), 0, s, a);

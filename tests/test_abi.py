@@ -90,7 +90,15 @@ def test_workspace_queries(dsa):
     assert dsa.dsa_topk_workspace_size(0, 131072, 2048) == 0
     assert dsa.dsa_block_select_workspace_size(4, 524288, 128) == 4 * 4096 * 4
     d = dsa.MlaDesc(16, 64, 512, 64, 16, 131072, 2048, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN, 64, 0.07, 0)
+    # automatic splits at batch 16 run each query as two 32-head halves: 32 x 8 splits of 256 keys,
+    # partials for 16 queries x 8 splits x 64 heads
+    assert dsa.dsa_sparse_mla_workspace_size(d) == 16 * 8 * 64 * 514 * 4
+    d.num_splits = 16   # explicit splits: no head split
     assert dsa.dsa_sparse_mla_workspace_size(d) == 16 * 16 * 64 * 514 * 4
+    d.num_q = 64
+    d.num_splits = 0    # batch 64: 4 splits of 512 keys, no head split
+    assert dsa.dsa_sparse_mla_workspace_size(d) == 64 * 4 * 64 * 514 * 4
+    d.num_q = 16
     d.num_splits = 1
     assert dsa.dsa_sparse_mla_workspace_size(d) == 0
 

@@ -316,6 +316,42 @@ def test_sparse_mla_ragged_lists_and_empty(dsa):
         assert np.all(o[2] == 0) and np.all(np.isneginf(l[2]))
 
 
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "nope"])
+def test_sparse_mla_head_split_matches_oracle(dsa, rope):
+    """Automatic splits at 8..32 queries run each query as two 32-head halves (the halves share the
+    row lists; their partials and statistics are separate): 12 queries, peaked softmax, ragged and
+    empty lists, -1 holes; every query against the oracle, and the same call with explicit splits
+    (no head split) agrees to the same tolerance."""
+    T, n = 12, 6000
+    wl = workloads.make_workload(name="hsplit", seed=1717, seq_lens=[n] * T, max_ctx=n, rope=rope, mla_q_std=16.0)
+    rng = np.random.default_rng(17)
+    lens = np.array([2048, 2048, 1999, 1024, 777, 300, 256, 255, 64, 63, 1, 0], np.int32)
+    idx = np.full((T, 2048), -1, np.int32)
+    for t in range(T):
+        idx[t, :lens[t]] = np.sort(rng.choice(n, lens[t], replace=False))
+    idx[0, 500:530] = -1
+    g = wl.to("cuda")
+    it, lt = torch.from_numpy(idx).cuda(), torch.from_numpy(lens).cuda()
+    res = []
+    for splits in (0, 8):
+        out = torch.empty(T, 64, 512, device="cuda")
+        lse = torch.empty(T, 64, device="cuda")
+        dsa.dsa_sparse_mla_decode(g.mla_q, g.kv, g.kv_scale, g.q_seq, it, lt, out, lse,
+                                  softmax_scale=wl.softmax_scale, num_splits=splits)
+        torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), lse.cpu().numpy()))
+    for (o, l), tag in zip(res, ("auto (head split)", "explicit 8 splits")):
+        for t in range(T):
+            if lens[t] == 0:
+                assert np.all(o[t] == 0) and np.all(np.isneginf(l[t])), f"{tag} q{t}"
+                continue
+            sel = idx[t, :lens[t]]
+            rows = O.cache_rows(wl, t, sel[sel >= 0])
+            ro, rl = O.mla_attend(wl.mla_q[t], rows, wl.rope_dim, wl.softmax_scale)
+            bound = mla_lse_bound(O.to_f64(wl.mla_q[t]), rows, wl.rope_dim, wl.softmax_scale, True)
+            check_attention(o[t], l[t], ro, rl, True, f"{tag} q{t}", lse_abs=bound)
+
+
 def test_sparse_equals_dense_when_selection_covers_context(dsa):
     wl = workloads.make_workload(name="dense", seed=404, seq_lens=[1800, 2048], max_ctx=2048)
     g = wl.to("cuda")

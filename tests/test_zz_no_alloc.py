@@ -57,7 +57,8 @@ def _both(dsa, wl, idx, lens, splits):
 
 def test_noalloc_decode_matches_the_workspace_entry_point(dsa):
     assert dsa.lib().dsa_sparse_mla_noalloc_max_bytes() == 64 << 20
-    # call 1: four 4000-row sequences, automatic splits (64 per query: 33.7 MB of partials)
+    # call 1: four 4000-row sequences, automatic splits (each query as two 32-head halves, 32 splits
+    # each: 16.8 MB of partials)
     big = workloads.make_workload(name="na1", seed=71, seq_lens=[4000] * 4, max_ctx=4000, mla_q_std=8.0)
     lens1 = [2048, 1999, 2048, 77]
     _both(dsa, big, _lists(4000, lens1, 1), lens1, 0)
