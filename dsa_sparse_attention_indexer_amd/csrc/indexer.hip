@@ -663,26 +663,22 @@ k_index_scores_fp8(IndexerLaunch a) {
     __syncthreads();
   }
 
-  // Fully unrolled: the vmcnt of every wait is a compile-time count (ring_wait).  A slot is
-  // refilled as soon as its contents are in registers, before the tile's matrix work, so the next
-  // gather is in flight while this tile is scored.
+  // Every wait's vmcnt is a compile-time count (ring_wait): the first kRing tiles and the last two
+  // are unrolled, and the tiles between run as a rolled loop of kRing-tile groups whose waits are all
+  // ring_wait's steady value (each copy in a group also knows its ring slot).  A slot is refilled as
+  // soon as its contents are in registers, before the tile's matrix work, so the next gather is in
+  // flight while this tile is scored.  The rolled middle keeps the kernel's code small: it is
+  // fetched again after the other kernels of a step have run.
   uint32_t rel = wave * kTile;
-#pragma unroll
-  for (int it = 0; it < TPW; ++it) {
-    switch (ring_wait(it, TPW)) {
-#define DSA_WAIT_CASE(N) case N: wait_vm<N>(); break;
-      DSA_WAIT_CASE(0) DSA_WAIT_CASE(1) DSA_WAIT_CASE(2) DSA_WAIT_CASE(3) DSA_WAIT_CASE(4) DSA_WAIT_CASE(5)
-      DSA_WAIT_CASE(6) DSA_WAIT_CASE(7) DSA_WAIT_CASE(8) DSA_WAIT_CASE(9) DSA_WAIT_CASE(10) DSA_WAIT_CASE(11)
-      DSA_WAIT_CASE(12) DSA_WAIT_CASE(13)
-#undef DSA_WAIT_CASE
-      default: wait_vm<0>(); break;   // (not reached for kRing <= 3)
-    }
+  auto step = [&](auto slot_c, auto wait_c, int it) {
+    constexpr int S = decltype(slot_c)::value;
+    wait_vm<decltype(wait_c)::value>();
     asm volatile("" ::: "memory");           // the ring reads below stay after the wait
     KeyTile cur;
-    const u32x4* slot = wr.key[it % kRing];
+    const u32x4* slot = wr.key[S];
 #pragma unroll
     for (int c = 0; c < 4; ++c) cur.x[c] = slot[tile_slot(col, 2 * c + g)];
-    cur.sc = wr.sc[it % kRing][col];
+    cur.sc = wr.sc[S][col];
     if (it + kRing < TPW) {
       __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): the slot's contents are in registers
       issue(it + kRing);
@@ -695,7 +691,21 @@ k_index_scores_fp8(IndexerLaunch a) {
       if (lane == 0) atomicMax(&sbm[rel / (uint32_t)a.bblock], kk);
     }
     rel += kStride;
+  };
+  static_assert(kRing == 3 && TPW >= kRing + 2 && (TPW - 2 - kRing) % kRing == 0, "loop split");
+  static_assert(ring_wait(kRing, TPW) == ring_wait(TPW - 3, TPW), "steady wait count");
+  step(std::integral_constant<int, 0>(), std::integral_constant<int, ring_wait(0, TPW)>(), 0);
+  step(std::integral_constant<int, 1>(), std::integral_constant<int, ring_wait(1, TPW)>(), 1);
+  step(std::integral_constant<int, 2>(), std::integral_constant<int, ring_wait(2, TPW)>(), 2);
+  constexpr int kSteady = ring_wait(kRing, TPW);
+#pragma unroll 1
+  for (int it = kRing; it < TPW - 2; it += kRing) {
+    step(std::integral_constant<int, 0>(), std::integral_constant<int, kSteady>(), it);
+    step(std::integral_constant<int, 1>(), std::integral_constant<int, kSteady>(), it + 1);
+    step(std::integral_constant<int, 2>(), std::integral_constant<int, kSteady>(), it + 2);
   }
+  step(std::integral_constant<int, (TPW - 2) % kRing>(), std::integral_constant<int, ring_wait(TPW - 2, TPW)>(), TPW - 2);
+  step(std::integral_constant<int, (TPW - 1) % kRing>(), std::integral_constant<int, ring_wait(TPW - 1, TPW)>(), TPW - 1);
   if (!HIST && bm) {   // the chunk's blocks that hold visible keys
     __syncthreads();
     const int nbc = ((int)nrow + a.bblock - 1) / a.bblock;
