@@ -305,12 +305,13 @@ __device__ __forceinline__ void load_tile(KeyTile& kt, __amdgpu_buffer_rsrc_t kr
   kt.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, rel_row * 4u, 0, 0));
 }
 
-// max(x, 0) as one instruction: fmaxf on an MFMA result is preceded by a NaN-quieting max, which
-// the ReLU does not need (a NaN score only arises from NaN key codes, which no writer produces).
+// max(x, 0) as one instruction: a signed integer max of the bit pattern with 0 (negative floats,
+// -0 included, have the sign bit set, so they become +0; non-negative floats keep their bits).
+// fmaxf would add a NaN-quieting max first, which the ReLU does not need (a NaN score only arises
+// from NaN key codes, which no writer produces).  Written in C, not assembly, so that the compiler
+// sees the read of the MFMA result and keeps the wait states it needs.
 __device__ __forceinline__ float relu1(float x) {
-  float r;
-  asm("v_max_f32_e32 %0, 0, %1" : "=v"(r) : "v"(x));
-  return r;
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
 // One 32-key tile: 16 MFMAs (8 K-steps x hi/lo), ReLU + head weights, halves summed across the wave.
@@ -938,6 +939,183 @@ k_index_scores_fp8_grouped(IndexerLaunch a, const void* ws) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Many queries per sequence (chunked prefill): query tiles over long key ranges
+// ------------------------------------------------------------------------------------------
+
+constexpr int kQtPerWave = 2;                      // queries per wave (their operands stay in registers)
+constexpr int kQtQueries = kQtPerWave * kGroup;    // 8 consecutive queries per workgroup
+constexpr int kQtRange = 8192;                     // keys per workgroup (256 tiles)
+
+// One 32-key tile for two queries: the tile's fp16 B operands are converted once and feed both
+// queries' MFMA chains (independent accumulators, interleaved).  Raised wave priority for the matrix
+// chains, as in tile_scores2.
+__device__ __forceinline__ void tile_scores_q2(const KeyTile& k, const half8* ah0, const half8* al0, const half8* ah1,
+                                               const half8* al1, const float* cf0, const float* cf1, float& s0,
+                                               float& s1) {
+  float16v a0 = {}, a1 = {};
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const half8 x = fp8x8_to_half8(k.x[c][2 * h], k.x[c][2 * h + 1]);
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah0[2 * c + h], x, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah1[2 * c + h], x, a1, 0, 0, 0);
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(al0[2 * c + h], x, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(al1[2 * c + h], x, a1, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    p0 = fmaf(cf0[r], relu1(a0[r]), p0);
+    p1 = fmaf(cf1[r], relu1(a1[r]), p1);
+  }
+  const auto w0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p0), false, false);
+  const auto w1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p1), false, false);
+  s0 = (__uint_as_float(w0[0]) + __uint_as_float(w0[1])) * k.sc;
+  s1 = (__uint_as_float(w1[0]) + __uint_as_float(w1[1])) * k.sc;
+}
+
+// A workgroup scores 8 consecutive queries (two per wave) over one 8192-key range of their
+// sequence: each 32-key tile is gathered once into the eight-tile LDS ring and feeds 8 queries, so
+// the key stream per flop is half that of the four-query grouped kernel and the query operands are
+// loaded once per 256 tiles instead of once per 32.  Work items (range, group) are listed
+// range-major and cut into 8 contiguous parts, one per XCD (workgroups go to the XCDs round-robin
+// by linear id): the workgroups of one XCD share a few key ranges, which its L2 holds.  A group
+// whose queries read several sequences makes one pass per sequence.
+__global__ void __launch_bounds__(kThreads)
+k_index_scores_fp8_qtile(IndexerLaunch a, const void* ws, int n_ranges, int n_groups) {
+  static_assert(kQtRange % (2 * kTile) == 0, "ranges are whole tile pairs");
+  __shared__ __attribute__((aligned(16))) SharedTiles st;
+  __shared__ int sseq[kQtQueries], sn[kQtQueries];
+  const int total = n_ranges * n_groups;
+  const int per_xcd = (total + 7) / 8;
+  const int item = (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u);
+  if (item >= total) return;
+  const int range = item / n_groups, grp = item % n_groups;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, col = lane & 31;
+  const int c0 = range * kQtRange;
+  if (threadIdx.x < kQtQueries) {
+    const int t = kQtQueries * grp + threadIdx.x;
+    sseq[threadIdx.x] = t < a.T ? clampi(a.q_seq[t], 0, a.B - 1) : -1;
+    sn[threadIdx.x] = t < a.T ? clampi(a.q_pos[t], -1, a.max_ctx - 1) + 1 : 0;
+  }
+  __syncthreads();
+
+  half8 ahi[kQtPerWave][8], alo[kQtPerWave][8];
+  float cf[kQtPerWave][16];
+  int tq[kQtPerWave];
+#pragma unroll
+  for (int j = 0; j < kQtPerWave; ++j) {   // (a query past T loads the last one's operands; never stored)
+    tq[j] = kQtQueries * grp + kQtPerWave * wave + j;
+    const QPrepFp8* qp = reinterpret_cast<const QPrepFp8*>(reinterpret_cast<const uint8_t*>(ws) +
+                                                           (size_t)min(tq[j], a.T - 1) * kQPrepBytes);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ahi[j][e] = __builtin_bit_cast(half8, qp->a[2 * e][lane]);
+      alo[j][e] = __builtin_bit_cast(half8, qp->a[2 * e + 1][lane]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cf[j][r] = qp->cf[r][lane];
+  }
+  const uint32_t out_off = g == 0 ? 4u * col : 0x80000000u;
+  const int q = 64 * wave + lane;
+  const int qr = q >> 3, qk = (q & 7) ^ ((qr >> 1) & 7);
+  constexpr int LPT = 2;   // LDS-direct loads per wave and tile
+
+  // One pass of the shared stream per sequence among the group's queries (one pass when the
+  // group's queries share a sequence, as in a prefill chunk); each pass stores only its queries.
+  uint32_t done = 0;
+#pragma unroll
+  for (int i = 0; i < kQtQueries; ++i) done |= sseq[i] < 0 ? 1u << i : 0u;
+  for (int pass = 0; done != (1u << kQtQueries) - 1; ++pass) {
+    const int first = __builtin_ctz(~done);
+    const int b = sseq[first];
+    uint32_t mask = 0;
+    int nmax = 0;
+#pragma unroll
+    for (int i = 0; i < kQtQueries; ++i)
+      if (!((done >> i) & 1u) && sseq[i] == b) {
+        mask |= 1u << i;
+        nmax = max(nmax, sn[i]);
+      }
+    done |= mask;
+    if (c0 >= nmax) continue;   // no query of this sequence sees the range
+    if (pass > 0) __syncthreads();   // every wave is done with the ring of the last pass
+
+    const int rows = min(nmax - c0, kQtRange);
+    const int ntiles = (rows + kTile - 1) / kTile;
+    const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.k_cache) + ((size_t)b * a.max_ctx + c0) * kD;
+    const float* sseqp = a.k_scale + (size_t)b * a.max_ctx + c0;
+    __amdgpu_buffer_rsrc_t ors[kQtPerWave];
+    uint32_t nrow = 0;
+#pragma unroll
+    for (int j = 0; j < kQtPerWave; ++j) {
+      const int i = kQtPerWave * wave + j;
+      const uint32_t nr = (mask >> i) & 1u ? (uint32_t)max(0, min(sn[i] - c0, kQtRange)) : 0u;
+      ors[j] = make_rsrc(a.scores + (size_t)min(tq[j], a.T - 1) * a.ld + c0, nr * 4u);
+      nrow = max(nrow, nr);
+    }
+    auto issue = [&](int tau) {
+      const int slot = tau % kRingTiles;
+      const int r = min(kTile * tau + qr, rows - 1);   // rows past the group's range read a valid row
+      dma16(kseq + (size_t)r * kD + 16 * qk, &st.key[slot][64 * wave]);
+      if (lane < kTile / kGroup)
+        dma4(sseqp + min(kTile * tau + (kTile / kGroup) * wave + lane, rows - 1), &st.sc[slot][(kTile / kGroup) * wave]);
+    };
+#pragma unroll
+    for (int i = 0; i < kRingTiles; ++i)
+      if (i < ntiles) issue(i);
+    wait_vm<0>();   // (the first pass: the operands too)
+#pragma unroll 1
+    for (int tau = 0; tau < ntiles; tau += 2) {
+      // gathers issued so far: the first ring's worth, then two per step from step 1 on (after the
+      // wait); tiles tau and tau + 1 have landed once at most the later ones are outstanding (the
+      // score stores issued since count as later too, which only makes the wait stricter)
+      const int step = tau >> 1;
+      const int issued = min(ntiles, kRingTiles + 2 * max(step - 1, 0));
+      const int later = issued - min(tau + 1, ntiles - 1) - 1;
+      switch (later) {
+        case 7: wait_vm<7 * LPT>(); break;
+        case 6: wait_vm<6 * LPT>(); break;
+        case 5: wait_vm<5 * LPT>(); break;
+        case 4: wait_vm<4 * LPT>(); break;
+        case 3: wait_vm<3 * LPT>(); break;
+        case 2: wait_vm<2 * LPT>(); break;
+        case 1: wait_vm<LPT>(); break;
+        default: wait_vm<0>(); break;
+      }
+      lds_sync();   // tiles tau, tau + 1 are in LDS for every wave; every wave is done with the last pair
+      if (step >= 1) {
+        if (tau - 2 + kRingTiles < ntiles) issue(tau - 2 + kRingTiles);
+        if (tau - 1 + kRingTiles < ntiles) issue(tau - 1 + kRingTiles);
+      }
+#pragma unroll 1
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t rel = (uint32_t)(kTile * (tau + e));
+        if (tau + e < ntiles && rel < nrow) {
+          const int sl = (tau + e) % kRingTiles;
+          KeyTile k;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) k.x[c] = st.key[sl][tile_slot(col, 2 * c + g)];
+          k.sc = st.sc[sl][col];
+          float r0, r1;
+          tile_scores_q2(k, ahi[0], alo[0], ahi[1], alo[1], cf[0], cf[1], r0, r1);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r0), ors[0], out_off + 4u * rel, 0,
+                                                kStreamStore);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r1), ors[1], out_off + 4u * rel, 0,
+                                                kStreamStore);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // fp32 keys: vector FMAs
 // ------------------------------------------------------------------------------------------
 
@@ -1006,9 +1184,21 @@ int indexer_chunk(int T, int max_ctx) {
   return big >= 512 ? 4096 : 1024;
 }
 
+// Query tiles (8 queries of a sequence over 8192-key ranges) where sequences average 16 or more
+// queries and the work items fill two workgroups per CU; contiguous caches only.
+static bool indexer_qtile(const IndexerLaunch& a) {
+  const int64_t items = (int64_t)((a.T + kQtQueries - 1) / kQtQueries) * ((a.max_ctx + kQtRange - 1) / kQtRange);
+  return a.pg.table == nullptr && a.B > 0 && a.T >= 16 * a.B && items >= 512;
+}
+
 hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
   if (a.T == 0 || a.max_ctx == 0) return hipSuccess;
-  if (indexer_grouped(a.T, a.B, a.k_dtype)) {
+  if (indexer_grouped(a.T, a.B, a.k_dtype) && indexer_qtile(a)) {
+    launch(k_index_qprep_fp8, dim3(a.T), dim3(kThreads), 0, s, a, ws);
+    const int n_ranges = (a.max_ctx + kQtRange - 1) / kQtRange, n_groups = (a.T + kQtQueries - 1) / kQtQueries;
+    const int per_xcd = (n_ranges * n_groups + 7) / 8;
+    launch(k_index_scores_fp8_qtile, dim3(8 * per_xcd), dim3(kThreads), 0, s, a, (const void*)ws, n_ranges, n_groups);
+  } else if (indexer_grouped(a.T, a.B, a.k_dtype)) {
     launch(k_index_qprep_fp8, dim3(a.T), dim3(kThreads), 0, s, a, ws);
     dim3 grid((a.max_ctx + kTile * 32 - 1) / (kTile * 32), (a.T + kGroup - 1) / kGroup);
     if (a.pg.table) launch(k_index_scores_fp8_grouped<32, true>, grid, dim3(kThreads), 0, s, a, (const void*)ws);

@@ -69,6 +69,51 @@ def test_index_scores_match_oracle(dsa, name, kw):
         assert np.all(err <= _score_tol(ref)), f"{name} q{t}: max err {err.max():.3g} rms {np.sqrt(np.mean(ref**2)):.3g}"
 
 
+def _qtile_case(name):
+    """Workloads of the query-tile score kernel (sequences averaging 16 or more queries, 8-query
+    groups x 8192-key ranges filling 512 or more workgroups): a ragged prefill-like chunk and three
+    sequences whose queries interleave, so that groups span sequences."""
+    rng = np.random.default_rng(17)
+    if name == "qtile_one_seq":
+        pos = np.sort(rng.choice(70001, size=461, replace=False))
+        pos[0], pos[-1] = 0, 70000
+        return workloads.make_workload(name=name, seed=31, seq_lens=[70001], max_ctx=70001,
+                                       q_positions=pos.tolist())
+    lens = [40000, 17000, 9000]
+    seqs = np.repeat(np.arange(3), [420, 260, 141])          # runs of one sequence ...
+    cut = rng.choice(seqs.size, size=60, replace=False)        # ... with 60 queries moved around
+    seqs[np.sort(cut)] = rng.permutation(seqs[cut])
+    pos = np.array([rng.integers(0, lens[b]) for b in seqs])
+    pos[:3] = [lens[seqs[0]] - 1, 0, 8191]
+    return workloads.make_workload(name=name, seed=32, seq_lens=lens, max_ctx=40000,
+                                   q_positions=pos.tolist(), q_seqs=seqs.tolist())
+
+
+@pytest.mark.parametrize("name", ["qtile_one_seq", "qtile_mixed_seqs"])
+def test_index_scores_query_tiles_match_oracle(dsa, name):
+    wl = _qtile_case(name)
+    T, B = wl.num_q, wl.num_seqs
+    assert T >= 16 * B and -(-T // 8) * -(-wl.max_ctx // 8192) >= 512   # the query-tile kernel's range
+    g = wl.to("cuda")
+    buf = _pipe().alloc_buffers(g)
+    buf.scores.fill_(float("nan"))
+    _pipe().index_scores(g, buf)
+    torch.cuda.synchronize()
+    sc = buf.scores.cpu().numpy()
+    keys = [O.cache_keys(wl, b, int(wl.seq_len[b])) for b in range(B)]   # decoded once per sequence
+    s_s = None if wl.ssmax_s is None else O.to_f64(wl.ssmax_s)
+    s_b = None if wl.ssmax_b is None else O.to_f64(wl.ssmax_b)
+    inv = None if wl.inv_freq is None else O.to_f64(wl.inv_freq)
+    for t in range(T):
+        p, b = int(wl.q_pos[t]), int(wl.q_seq[t])
+        qp = O.index_query(wl.index_q[t], p, s_s, s_b, inv)
+        ref = O.index_scores_row(qp, O.to_f64(wl.index_w[t]), keys[b][:p + 1])
+        got = sc[t, :p + 1].astype(np.float64)
+        err = np.abs(got - ref)
+        assert np.all(err <= _score_tol(ref)), f"{name} q{t} (seq {b}, p {p}): max err {err.max():.3g}"
+        assert np.all(np.isnan(sc[t, p + 1:])), f"{name} q{t}: columns past p written"
+
+
 def test_index_scores_exact_on_integers(dsa):
     """Integer q, fp8 keys and weights, unit scales, no RoPE / SSMax: S * 64 is an exact integer."""
     T, H, L = 2, 32, 700
