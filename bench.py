@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tok/s at 128K ctx (indexer+top-2048+sparse MLA); % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+F16_PEAK_TFLOPS = 2500.0
 INDEX_BYTES_PER_KEY = 128 + 4 + 4      # fp8 key row + fp32 scale read, fp32 score written
 LATENT_BYTES_PER_KEY = 576 + 9 * 4     # fp8 latent row + 9 fp32 scales
 MLA_FLOP_PER_KEY_HEAD = 2 * (576 + 512)   # QK^T over 576 dims and PV over 512, per selected key and head
@@ -191,6 +192,18 @@ def mla_rates(wl, lengths, us):
             "frac_bf16_peak": tflops / BF16_PEAK_TFLOPS, "gather_gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
+def index_rates(wl, us):
+    """MFMA rate of a many-query score kernel (prefill, verify blocks) that took `us`: every visible
+    (query, key) pair is a 32-head x 128-dim product per fp16 term of q', and the kernel issues two
+    terms (the hi and lo parts); the algorithmic rate counts the real heads and one term."""
+    keys = int((wl.q_pos.long().clamp(min=-1, max=wl.max_ctx - 1) + 1).sum())
+    issued = keys * 2 * 2 * 32 * 128
+    alg = keys * 2 * wl.num_heads * 128
+    return {"us": us, "visible_keys": keys, "issued_tflops": issued / (us * 1e-6) / 1e12,
+            "frac_f16_peak": issued / (us * 1e-6) / 1e12 / F16_PEAK_TFLOPS,
+            "algorithmic_tflops": alg / (us * 1e-6) / 1e12}
+
+
 def mean(xs):
     return sum(xs) / len(xs)
 
@@ -312,6 +325,9 @@ def run_config(dsa, pipeline, wls, kind, steps, warmup, shared_from=None, buf=No
         torch.cuda.synchronize()
         out["us_per_step_separate_selection"] = (time.perf_counter() - t0) / steps * 1e6
     src = buf if shared_from is None else shared_from
+    idx_main = [v for k, v in per.items() if k.startswith(("k_index_scores_fp8_grouped", "k_index_scores_fp8_qtile"))]
+    if idx_main and shared_from is None:
+        out["index_scores_kernel"] = index_rates(wls[0], mean(idx_main[0]))
     mla_main = [v for k, v in per.items() if k.startswith("k_mla") and "combine" not in k]
     if mla_main:
         out["sparse_mla_kernel"] = mla_rates(wls[0], src.length, mean(mla_main[0]))
