@@ -984,7 +984,11 @@ __device__ __forceinline__ void tile_scores_q2(const KeyTile& k, const half8* ah
 // loaded once per 256 tiles instead of once per 32.  Work items (range, group) are listed
 // range-major and cut into 8 contiguous parts, one per XCD (workgroups go to the XCDs round-robin
 // by linear id): the workgroups of one XCD share a few key ranges, which its L2 holds.  A group
-// whose queries read several sequences makes one pass per sequence.
+// whose queries read several sequences makes one pass per sequence.  PAGED: the range's tiles are
+// 4 KiB ranges of 16x16 tiles in their cache blocks (a block holds whole 32-key tiles); each lane
+// holds the block ids of tiles lane, 64 + lane, 128 + lane and 192 + lane of the range, read once
+// per pass.
+template <bool PAGED>
 __global__ void __launch_bounds__(kThreads)
 k_index_scores_fp8_qtile(IndexerLaunch a, const void* ws, int n_ranges, int n_groups) {
   static_assert(kQtRange % (2 * kTile) == 0, "ranges are whole tile pairs");
@@ -1060,8 +1064,22 @@ k_index_scores_fp8_qtile(IndexerLaunch a, const void* ws, int n_ranges, int n_gr
       ors[j] = make_rsrc(a.scores + (size_t)min(tq[j], a.T - 1) * a.ld + c0, nr * 4u);
       nrow = max(nrow, nr);
     }
+    int blk[kQtRange / kTile / 64] = {};   // PAGED: block of tile 64 u + lane (past the rows: the last row's)
+    if (PAGED) {
+#pragma unroll
+      for (int u = 0; u < kQtRange / kTile / 64; ++u) blk[u] = paged_block(a.pg, b, min(c0 + kTile * (64 * u + lane), nmax - 1));
+    }
     auto issue = [&](int tau) {
       const int slot = tau % kRingTiles;
+      if (PAGED) {   // the tile's rows are one 4 KiB range of 16x16 tiles in its block
+        static_assert(kQtRange / kTile / 64 == 4, "four block ids per lane");
+        const int w = tau >> 6;   // (uniform)
+        const int bw = w == 0 ? blk[0] : w == 1 ? blk[1] : w == 2 ? blk[2] : blk[3];
+        const size_t r0 = (size_t)__builtin_amdgcn_readlane(bw, tau & 63) * a.pg.page + (size_t)((c0 + kTile * tau) % a.pg.page);
+        dma16(reinterpret_cast<const uint8_t*>(a.k_cache) + r0 * kD + key_tile_byte(qr, 16 * qk), &st.key[slot][64 * wave]);
+        if (lane < kTile / kGroup) dma4(a.k_scale + r0 + (kTile / kGroup) * wave + lane, &st.sc[slot][(kTile / kGroup) * wave]);
+        return;
+      }
       const int r = min(kTile * tau + qr, rows - 1);   // rows past the group's range read a valid row
       dma16(kseq + (size_t)r * kD + 16 * qk, &st.key[slot][64 * wave]);
       if (lane < kTile / kGroup)
@@ -1185,10 +1203,10 @@ int indexer_chunk(int T, int max_ctx) {
 }
 
 // Query tiles (8 queries of a sequence over 8192-key ranges) where sequences average 16 or more
-// queries and the work items fill two workgroups per CU; contiguous caches only.
+// queries and the work items fill two workgroups per CU.
 static bool indexer_qtile(const IndexerLaunch& a) {
   const int64_t items = (int64_t)((a.T + kQtQueries - 1) / kQtQueries) * ((a.max_ctx + kQtRange - 1) / kQtRange);
-  return a.pg.table == nullptr && a.B > 0 && a.T >= 16 * a.B && items >= 512;
+  return a.B > 0 && a.T >= 16 * a.B && items >= 512;
 }
 
 hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
@@ -1197,7 +1215,10 @@ hipError_t launch_indexer(const IndexerLaunch& a, void* ws, hipStream_t s) {
     launch(k_index_qprep_fp8, dim3(a.T), dim3(kThreads), 0, s, a, ws);
     const int n_ranges = (a.max_ctx + kQtRange - 1) / kQtRange, n_groups = (a.T + kQtQueries - 1) / kQtQueries;
     const int per_xcd = (n_ranges * n_groups + 7) / 8;
-    launch(k_index_scores_fp8_qtile, dim3(8 * per_xcd), dim3(kThreads), 0, s, a, (const void*)ws, n_ranges, n_groups);
+    if (a.pg.table)
+      launch(k_index_scores_fp8_qtile<true>, dim3(8 * per_xcd), dim3(kThreads), 0, s, a, (const void*)ws, n_ranges, n_groups);
+    else
+      launch(k_index_scores_fp8_qtile<false>, dim3(8 * per_xcd), dim3(kThreads), 0, s, a, (const void*)ws, n_ranges, n_groups);
   } else if (indexer_grouped(a.T, a.B, a.k_dtype)) {
     launch(k_index_qprep_fp8, dim3(a.T), dim3(kThreads), 0, s, a, ws);
     dim3 grid((a.max_ctx + kTile * 32 - 1) / (kTile * 32), (a.T + kGroup - 1) / kGroup);

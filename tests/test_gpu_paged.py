@@ -112,7 +112,19 @@ PAGED_CASES = [
     # chunked prefill (one MLA workgroup per query)
     ("prefill_300", lambda: workloads.make_workload(name="pp", seed=85, seq_lens=[8300], max_ctx=8300,
                                                     q_positions=list(range(8000, 8300))), 64, True),
+    # query tiles (16+ queries per sequence, 8192-key ranges): two sequences whose runs of queries
+    # do not align with the 8-query groups, ranges past the shorter sequence, 64-token blocks
+    ("prefill_query_tiles", lambda: _qtile_workload(), 64, True),
 ]
+
+
+def _qtile_workload():
+    rng = np.random.default_rng(87)
+    lens = [70001, 20000]
+    seqs = [0] * 100 + [1] * 50 + [0] * 140 + [1] * 180
+    pos = [int(rng.integers(0, lens[b])) for b in seqs]
+    pos[0], pos[1] = lens[0] - 1, 0
+    return workloads.make_workload(name="pq", seed=87, seq_lens=lens, max_ctx=lens[0], q_positions=pos, q_seqs=seqs)
 
 
 @pytest.mark.parametrize("name,make,page,prefill", PAGED_CASES, ids=[c[0] for c in PAGED_CASES])
