@@ -128,8 +128,9 @@ dsa_status_t dsa_paged_slots(const dsa_paging_t* paging, int32_t n, const int32_
  *            aligned: the queries prepared once each (about 20 KiB per query) on the fp32-key
  *            path and, on the fp8 path, from 256 queries or two queries per sequence on (chunked
  *            prefill, multi-token verify blocks: four consecutive queries of one sequence then
- *            share one key stream); 0 bytes otherwise (the fp8 decode kernel prepares its query
- *            while its first key tiles are in flight), and then ws may be NULL.
+ *            share one key stream, or eight when the sequences average 16 or more queries);
+ *            0 bytes otherwise (the fp8 decode kernel prepares its query while its first key
+ *            tiles are in flight), and then ws may be NULL.
  *   paging   NULL, or the paged layout of k_cache / k_scale (see "Paged caches").
  *
  * Supported: head_dim == 128; 1 <= num_heads <= 32; rope_dim in {0, 64}; q_dtype F32 or BF16;
