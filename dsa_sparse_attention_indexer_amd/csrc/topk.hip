@@ -593,31 +593,38 @@ __device__ __forceinline__ bool direct_fast(const TopkLaunch& a, int t, int n, R
     }
     return mask;
   };
-  // pass 1: the first digit's histogram
+  // pass 1: the first digit's histogram of a sample -- the first 1024 columns of every 8192 (a
+  // contiguous eighth of the row, whole memory lines) -- and from it a low digit bs above which the
+  // row should hold about twice k keys.  Pass 2 keeps every key at or above bs, so whenever at least
+  // k are kept the k-th key is among them and their histogram is exact from bs up; otherwise (or if
+  // they overflow) the row takes the exact passes.
   for (int i = tid; i < kTkBins; i += kRT) sm.hist[i] = 0;
   __syncthreads();
-  {
-    float4 cur[Q], nxt[Q];
-    row_slices<Q>(row, n, 0, cur);
-    for (int c0 = 0; c0 < n; c0 += STEP) {
-      row_slices<Q>(row, n, c0 + STEP, nxt);   // unconditional (clamped past the row): stays in flight
-      uint32_t key[Q][4];
-      const uint32_t mask = keys_of(cur, c0, key);
+  constexpr int kBlk = 8192, kSam = 1024;
+  static_assert(kRT == 4 * (kSam / 4), "four sample blocks per round");
+  const int nblk = (n + kBlk - 1) / kBlk;
+  for (int s0 = 0; s0 < nblk; s0 += 4) {
+    const int sb = s0 + (tid >> 8);
+    const int c = kBlk * sb + 4 * (tid & 255);
+    if (sb < nblk && c < n) {
+      const float4 v = *reinterpret_cast<const float4*>(row + c);
+      const float ve[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < Q; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((mask >> (4 * q + e)) & 1u) atomicAdd(&sm.hist[key[q][e] >> kTkShift0], 1u);
-#pragma unroll
-      for (int q = 0; q < Q; ++q) cur[q] = nxt[q];
+      for (int e = 0; e < 4; ++e)
+        if (c + e < n) atomicAdd(&sm.hist[score_key(ve[e]) >> kTkShift0], 1u);
     }
   }
   __syncthreads();
-  int b0i;
-  uint32_t need0;
-  tk_find_bin<kTkBins, kRT>(sm.hist, (uint32_t)a.k, sm.sbuf, &b0i, &need0);
-  const uint32_t b0 = (uint32_t)b0i;
-  // pass 2: the candidates into LDS in column order
+  const uint32_t ns = (uint32_t)((nblk - 1) * kSam + min(kSam, n - kBlk * (nblk - 1)));   // sampled columns
+  const uint32_t want = (uint32_t)min((uint64_t)ns, (2ull * (uint64_t)a.k * ns + (uint64_t)n - 1) / (uint64_t)n + 64u);
+  int bsi;
+  uint32_t unused;
+  tk_find_bin<kTkBins, kRT>(sm.hist, want, sm.sbuf, &bsi, &unused);
+  const uint32_t bs = (uint32_t)bsi;
+  __syncthreads();   // the sample's histogram is read; it now counts the candidates
+  for (int i = tid; i < kTkBins; i += kRT) sm.hist[i] = 0;
+  __syncthreads();
+  // pass 2: the candidates into LDS in column order, and their first digits' histogram
   uint32_t base = 0;
   {
     float4 cur[Q], nxt[Q];
@@ -632,7 +639,7 @@ __device__ __forceinline__ bool direct_fast(const TopkLaunch& a, int t, int n, R
         fl[q] = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          fl[q] |= (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> kTkShift0) >= b0 ? 1u : 0u) << e;
+          fl[q] |= (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> kTkShift0) >= bs ? 1u : 0u) << e;
       }
       const uint32_t tot = tk_ordered_slots<Q, kRT>(fl, pos, sm.wsum);
       if (base + tot > (uint32_t)kTkItemCap) return false;   // (block-uniform)
@@ -645,6 +652,7 @@ __device__ __forceinline__ bool direct_fast(const TopkLaunch& a, int t, int n, R
           if ((fl[q] >> e) & 1u) {
             sm.key[p] = key[q][e];
             sm.col[p] = cq + e;
+            atomicAdd(&sm.hist[key[q][e] >> kTkShift0], 1u);
             ++p;
           }
       }
@@ -653,8 +661,12 @@ __device__ __forceinline__ bool direct_fast(const TopkLaunch& a, int t, int n, R
       for (int q = 0; q < Q; ++q) cur[q] = nxt[q];
     }
   }
-  __syncthreads();   // the items are in LDS for every thread
-  select_from_items(a, t, base, b0, need0, sm);
+  __syncthreads();   // the items and their histogram are in LDS for every thread
+  if (base < (uint32_t)a.k) return false;   // bs was above the k-th key: exact passes (block-uniform)
+  int b0i;
+  uint32_t need0;
+  tk_find_bin<kTkBins, kRT>(sm.hist, (uint32_t)a.k, sm.sbuf, &b0i, &need0);
+  select_from_items(a, t, base, (uint32_t)b0i, need0, sm);
   return true;
 }
 

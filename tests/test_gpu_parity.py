@@ -238,6 +238,29 @@ def test_topk_many_rows(dsa, dist):
         assert np.array_equal(idx[t], ref), f"{dist} row {t} (n={len(r)}): selections differ"
 
 
+def test_topk_sample_misleads_threshold(dsa):
+    """Rows (128 or more: the one-workgroup-per-row kernel) whose sampled columns -- the first 1024
+    of every 8192 -- hold far higher scores than the rest: the threshold taken from the sample lies
+    above the k-th key, so fewer than k keys reach the candidate list and the row must still come
+    out exact.  Mixed with ordinary rows and rows whose unsampled tail holds the top keys."""
+    rng = np.random.default_rng(78)
+    rows, pos = [], []
+    for i in range(160):
+        n = int(rng.integers(20000, 70000))
+        r = rng.standard_normal(n).astype(np.float32)
+        c = np.arange(n)
+        if i % 3 == 0:
+            r[(c % 8192) < 1024] += 50.0           # the sample holds the largest scores
+        elif i % 3 == 1:
+            r[(c % 8192) >= 1024] += 50.0          # the top keys all lie outside the sample
+        rows.append(r)
+        pos.append(n - 1)
+    idx, ln = _run_topk(dsa, rows, pos, 2048)
+    for t, r in enumerate(rows):
+        ref, rl = O.topk_row(r.astype(np.float64), 2048)
+        assert ln[t] == rl and np.array_equal(idx[t], ref), f"row {t} (n={len(r)}): selections differ"
+
+
 def test_topk_row_shorter_than_ld_and_deterministic(dsa):
     rng = np.random.default_rng(11)
     rows = [rng.standard_normal(9000).astype(np.float32) for _ in range(3)]
