@@ -5,7 +5,7 @@
 // first 64 dims in interleaved pairs (angle p * inv_freq[j]) and multiplied by the head's SSMax
 // factor s*ln(p+1)+b; key i then scores  S(i) = sum_h w_h/sqrt(H) * relu(q'_h . k_i / sqrt(128)).
 //
-// Two kernels:
+// Two key formats:
 //  * fp8 keys (the serving format, 128 B + one fp32 scale per token, as the vLLM page's
 //    "DSA indexer on AITER" describes): a bandwidth-bound stream over the key cache.  Each wave
 //    owns the 32 (zero-padded) heads of one query as the A operand of v_mfma_f32_32x32x16_f16 and
@@ -15,6 +15,10 @@
 //    products accumulate into one fp32 accumulator, so the dot product keeps ~22 bits of q'.
 //    ReLU, the head weights and the per-token scale are applied in registers; the two halves of
 //    the wave are summed with v_permlane32_swap, and lanes 0..31 store 32 consecutive scores.
+//    With many queries (several per sequence), the queries are prepared once into a workspace and
+//    consecutive queries of a sequence share one key stream through LDS: four per workgroup over
+//    1024-key chunks (verify blocks, large batches), or eight -- two per wave -- over 8192-key
+//    ranges where the sequences hold 16 or more queries each (chunked prefill).
 //  * fp32 keys (the reference-precision path): one thread per key, fp32 FMAs against q' in LDS.
 //
 // Query prep (RoPE angles formed and reduced to [-pi, pi] in float64, then sine, cosine, SSMax and
