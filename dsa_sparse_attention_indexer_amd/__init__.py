@@ -366,9 +366,11 @@ def dsa_block_select(scores, q_pos, idx, length=None, block=128, nblocks=16, ws=
 
 def dsa_indexer_block_select(q, w, q_seq, q_pos, k_cache, scores, idx, length=None, block=128, nblocks=16,
                              k_scale=None, ssmax_s=None, ssmax_b=None, inv_freq=None, ws=None, bs_ws=None,
-                             stream=None, paging=None):
+                             stream=None, paging=None, ld=None):
     """Scores and block-sparse selection in one call (dsa_indexer_scores then dsa_block_select; the
-    fp8 decode score kernel writes the block maxima itself)."""
+    fp8 decode score kernel writes the block maxima itself).  scores may be None where the score
+    kernel writes the block maxima (the scores are then not written); ld then gives the row stride
+    the block workspace is sized for (default max_ctx rounded up to 4)."""
     T, H, D = q.shape
     B, max_ctx = _seq_dims(k_cache, paging)
     _dev("q", q, (torch.float32, torch.bfloat16))
@@ -383,9 +385,12 @@ def dsa_indexer_block_select(q, w, q_seq, q_pos, k_cache, scores, idx, length=No
     _dev("scores", scores, torch.float32)
     _dev("idx", idx, torch.int32)
     _dev("length", length, torch.int32, (T,))
-    if scores.dim() != 2 or scores.shape[0] != T or idx.dim() != 2 or idx.shape[0] != T:
+    if (scores is not None and (scores.dim() != 2 or scores.shape[0] != T)) or idx.dim() != 2 or idx.shape[0] != T:
         raise ValueError("scores must be [T][ld] and idx [T][topk]")
-    ld = scores.shape[1]
+    if scores is not None:
+        ld = scores.shape[1]
+    elif ld is None:
+        ld = (max_ctx + 3) // 4 * 4
     d = indexer_desc(q, k_cache, inv_freq, paging)
     if ws is None:
         ws = torch.empty(max(16, dsa_indexer_workspace_size(d)), dtype=torch.uint8, device=q.device)

@@ -126,7 +126,7 @@ dsa::Paging check_paging(Checker& ck, const dsa_paging_t* pg, int32_t num_seqs, 
 void check_indexer(Checker& ck, const dsa_indexer_desc_t* d, const void* q, const float* w, const int32_t* q_seq,
                    const int32_t* q_pos, const float* ssmax_s, const float* ssmax_b, const float* inv_freq,
                    const void* k_cache, const float* k_scale, const float* scores, int64_t ld_scores, const void* ws,
-                   size_t ws_bytes) {
+                   size_t ws_bytes, bool scores_optional = false) {
   ck.need(d->num_q >= 0 && d->num_q <= 65535, "num_q must be in [0, 65535]");
   ck.need(d->num_seqs >= 1, "num_seqs must be >= 1");
   ck.need(d->max_ctx >= 1 && d->max_ctx <= (1 << 26), "max_ctx must be in [1, 2^26]");
@@ -137,7 +137,8 @@ void check_indexer(Checker& ck, const dsa_indexer_desc_t* d, const void* q, cons
   ck.support(d->k_dtype == DSA_F32 || d->k_dtype == DSA_FP8_E4M3FN, "k_dtype must be F32 or FP8_E4M3FN");
   ck.need(ld_scores >= d->max_ctx, "ld_scores must be >= max_ctx");
   if (d->num_q > 0) {
-    ck.need(q && w && q_seq && q_pos && k_cache && scores, "q, w, q_seq, q_pos, k_cache and scores must be non-NULL");
+    ck.need(q && w && q_seq && q_pos && k_cache, "q, w, q_seq, q_pos and k_cache must be non-NULL");
+    ck.need(scores || scores_optional, "scores must be non-NULL");
     ck.need((ssmax_s == nullptr) == (ssmax_b == nullptr), "ssmax_s and ssmax_b must be both NULL or both set");
     ck.need((inv_freq != nullptr) == (d->rope_dim > 0), "inv_freq must be set iff rope_dim > 0");
     ck.need(d->k_dtype != DSA_FP8_E4M3FN || k_scale != nullptr, "k_scale is required for FP8 keys");
@@ -334,9 +335,14 @@ dsa_status_t dsa_indexer_block_select(const dsa_indexer_desc_t* d, const void* q
   Checker ck;
   if (!d) { ck.need(false, "desc is NULL"); return ck.finish(fn); }
   check_indexer(ck, d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores, ld_scores, ws,
-                ws_bytes);
+                ws_bytes, true);
   const dsa::Paging pg = check_paging(ck, paging, d->num_seqs, d->max_ctx, d->k_dtype == DSA_FP8_E4M3FN);
   ck.need(ld_scores <= (int64_t(1) << 30), "ld_scores must be <= 2^30");
+  // the decode score kernel emits the block maxima itself where its chunks hold whole blocks; only
+  // then can the scores be left unwritten
+  const bool fused = block >= 1 && dsa::indexer_block_max_fused(d->num_q, d->num_seqs, d->max_ctx, d->k_dtype, block);
+  ck.need(scores != nullptr || fused || d->num_q == 0,
+          "scores may be NULL only on the fp8 decode path with block a multiple of 32 that divides the score chunk");
   ck.support(block >= 1 && block <= 4096, "block must be in [1, 4096]");
   ck.support(nblocks >= 1 && nblocks <= 64, "nblocks must be in [1, 64]");
   ck.need(topk >= 1, "topk must be >= 1");
@@ -351,8 +357,6 @@ dsa_status_t dsa_indexer_block_select(const dsa_indexer_desc_t* d, const void* q
   dsa::IndexerLaunch a = indexer_launch(d, q, w, q_seq, q_pos, ssmax_s, ssmax_b, inv_freq, k_cache, k_scale, scores,
                                         ld_scores);
   a.pg = pg;
-  // the decode score kernel emits the block maxima itself where its chunks hold whole blocks
-  const bool fused = dsa::indexer_block_max_fused(d->num_q, d->num_seqs, d->max_ctx, d->k_dtype, block);
   if (fused) {
     a.bmax = static_cast<uint32_t*>(bs_ws);
     a.bblock = block;

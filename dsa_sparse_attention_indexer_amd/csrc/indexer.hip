@@ -585,7 +585,8 @@ k_index_scores_fp8(IndexerLaunch a) {
   float* srow = a.scores + (size_t)t * a.ld + c0;
   const i32x4 krs = rsrc_words(kseq, PAGED ? 0u : nrow * kD);
   const i32x4 srs = rsrc_words(sseq, PAGED ? 0u : nrow * 4u);
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(srow, nrow * 4u);
+  // without a score buffer (block maxima only) the range is empty and the stores write nothing
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(srow, a.scores ? nrow * 4u : 0u);
   constexpr uint32_t kStride = 4 * kTile;   // the 4 waves interleave 32-key tiles
   WaveRing& wr = ring[wave];
   // paged caches: lane j holds the block of this wave's tile j (a tile's 32 rows lie in one block;

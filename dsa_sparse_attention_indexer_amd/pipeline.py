@@ -91,12 +91,14 @@ def index_and_select(wl, buf: StepBuffers, stream=None):
                             inv_freq=wl.inv_freq, ws=buf.ws_index, topk_ws=buf.ws_topk, stream=stream)
 
 
-def index_and_select_blocks(wl, buf: StepBuffers, stream=None):
-    """Scores and block-sparse selection in one call (the block maxima from the score kernel)."""
-    return dsa_indexer_block_select(wl.index_q, wl.index_w, wl.q_seq, wl.q_pos, wl.index_k, buf.scores, buf.idx,
-                                    buf.length, block=128, nblocks=16, k_scale=wl.index_k_scale, ssmax_s=wl.ssmax_s,
-                                    ssmax_b=wl.ssmax_b, inv_freq=wl.inv_freq, ws=buf.ws_index, bs_ws=buf.ws_block,
-                                    stream=stream)
+def index_and_select_blocks(wl, buf: StepBuffers, stream=None, keep_scores: bool = False):
+    """Scores and block-sparse selection in one call (the block maxima from the score kernel).  The
+    selection needs only the block maxima, so the score rows are written only with keep_scores."""
+    return dsa_indexer_block_select(wl.index_q, wl.index_w, wl.q_seq, wl.q_pos, wl.index_k,
+                                    buf.scores if keep_scores else None, buf.idx, buf.length, block=128, nblocks=16,
+                                    k_scale=wl.index_k_scale, ssmax_s=wl.ssmax_s, ssmax_b=wl.ssmax_b,
+                                    inv_freq=wl.inv_freq, ws=buf.ws_index, bs_ws=buf.ws_block, stream=stream,
+                                    ld=buf.scores.shape[1])
 
 
 def index_scores_hist(wl, buf: StepBuffers, stream=None):
@@ -122,7 +124,11 @@ def layer_step(wl, buf: StepBuffers, *, prefill: bool = False, block_sparse: boo
         return attend(wl, buf, prefill=prefill, num_splits=num_splits, idx=shared_from.idx,
                       length=shared_from.length, stream=stream)
     if fused and block_sparse:
-        index_and_select_blocks(wl, buf, stream)
+        # the fp8 decode score kernel (fewer than 256 queries and than two per sequence) writes the
+        # 128-key block maxima itself; elsewhere a separate pass reads them from the scores
+        fp8 = wl.index_k.dtype in (torch.uint8, torch.float8_e4m3fn)
+        decode = wl.num_q < 256 and wl.num_q < 2 * wl.num_seqs
+        index_and_select_blocks(wl, buf, stream, keep_scores=not (fp8 and decode))
     elif fused:
         index_and_select(wl, buf, stream)
     else:

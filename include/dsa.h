@@ -251,7 +251,10 @@ dsa_status_t dsa_block_select(const float* scores, int64_t ld_scores, const int3
  * bytes); it receives each block's maximum.  On the fp8 decode path (fewer than two queries per
  * sequence) with block a multiple of 32 that divides the score kernel's chunk (4096 keys, or
  * 1024 when the query count is small; 128 always does), the score kernel writes the maxima itself
- * and the selection never reads the scores back; otherwise a separate pass takes them. */
+ * and the selection never reads the scores back; otherwise a separate pass takes them.  On that
+ * path `scores` may be NULL: the selection needs only the maxima, and no score row is written (the
+ * stores, 4 bytes per key mixed into the key stream, cost the score kernel about 12 % of its
+ * time); ld_scores then only sizes the rows of bs_ws.  NULL elsewhere is an error. */
 dsa_status_t dsa_indexer_block_select(const dsa_indexer_desc_t* desc, const void* q, const float* w,
                                       const int32_t* q_seq, const int32_t* q_pos,
                                       const float* ssmax_s, const float* ssmax_b, const float* inv_freq,

@@ -91,3 +91,17 @@ def test_fused_block_select_matches_oracle(dsa, name, kw, block, nblocks):
     s = O.index_scores(one, 0)
     tol = 2e-6 * np.sqrt(np.mean(s * s)) + 2e-6 * np.abs(s)
     assert np.all(np.abs(sc[0, :s.shape[0]] - s) <= tol)
+    # without a score buffer: the same selection where the score kernel writes the block maxima,
+    # a clear error where the separate block-max pass would need the scores
+    nidx = torch.full_like(idx, -7)
+    nln = torch.full_like(ln, -7)
+    args = (g.index_q, g.index_w, g.q_seq, g.q_pos, g.index_k, None, nidx, nln)
+    kw = dict(block=block, nblocks=nblocks, k_scale=g.index_k_scale, ssmax_s=g.ssmax_s, ssmax_b=g.ssmax_b,
+              inv_freq=g.inv_freq, ld=ld)
+    if block % 32 == 0:
+        dsa.dsa_indexer_block_select(*args, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(nidx, idx) and torch.equal(nln, ln), f"{name}: selection without scores differs"
+    else:
+        with pytest.raises(dsa.DsaError, match="scores may be NULL only"):
+            dsa.dsa_indexer_block_select(*args, **kw)

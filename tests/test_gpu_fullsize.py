@@ -93,5 +93,6 @@ def test_config3_chunked_prefill_4096_on_61440(pipe):
 def test_config4_block_sparse_b4_ctx512k(pipe):
     wl = workloads.config4(device="cuda")
     buf = pipe.alloc_buffers(wl, block_sparse=True)
-    pipe.layer_step(wl, buf, block_sparse=True)
+    pipe.layer_step(wl, buf, block_sparse=True)   # the selection from block maxima alone: no score rows
+    pipe.index_scores(wl, buf)                     # the score rows, for the score check below
     _check_queries(wl, buf, [0, 3], block=True, where="block 512K")
