@@ -157,3 +157,19 @@ def test_timing_hook_rejects_bad_arguments_and_disarms_cleanly(dsa):
     assert L.dsa_timing_end() == 0          # nothing launched while armed
     assert L.dsa_timing_kernel_name(0) is None
     assert L.dsa_timing_end() == 0          # ending twice is harmless
+
+
+def test_block_select_without_scores_only_where_the_kernel_writes_block_maxima(dsa):
+    """No score buffer is accepted only where the fp8 decode score kernel writes the block maxima
+    (128-token blocks); elsewhere (fp32 keys, 100-token blocks, many queries per sequence) the
+    call fails on the host, before any launch."""
+    L = dsa.lib()
+    fake = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
+    cases = [(dsa.DSA_F32, 128, 4, 4), (dsa.DSA_FP8_E4M3FN, 100, 4, 4), (dsa.DSA_FP8_E4M3FN, 128, 64, 4)]
+    for k_dtype, block, T, B in cases:
+        d = dsa.IndexerDesc(T, 4, 128, 64, B, 8192, dsa.DSA_BF16, k_dtype)
+        st = L.dsa_indexer_block_select(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, fake, fake,
+                                        None, 8192, block, 16, 2048, fake, None, fake, 1 << 30, fake, 1 << 30,
+                                        None, None)
+        msg = L.dsa_last_error().decode()
+        assert st == dsa.DSA_ERR_ARG and "scores may be NULL only" in msg, (k_dtype, block, T, msg)
