@@ -497,8 +497,8 @@ static_assert(ring_wait(0, 32) == 10 && ring_wait(1, 32) == 11 && ring_wait(2, 3
 // claims more items than the list has.  With L the largest lb of the row's chunks, the row histogram
 // is exact from L up and the items at or above L are exactly the row's keys there; when at least k
 // keys lie at or above L the selection kernel finds the row's top k among the items, and otherwise
-// selects from the scores directly.  The scores are read back from memory: this workgroup wrote
-// them, and the barrier before makes them visible to all its threads.
+// selects from the scores directly.  The chunk's scores are read from the copy the score loop kept
+// in LDS (sc, chunk-relative columns), not from memory.
 struct EmitSmem {
   uint32_t sbuf[32];
   uint32_t wsum[16];
@@ -506,7 +506,7 @@ struct EmitSmem {
 
 template <int TPW>
 __device__ void emit_candidates(const IndexerLaunch& a, int t, int n, int c0, uint32_t nrow, const uint32_t* lh,
-                                EmitSmem& em) {
+                                const float* sc, EmitSmem& em) {
   constexpr int chunk = 4 * kTile * TPW;
   constexpr int Q = chunk / (4 * kThreads);
   static_assert(Q * (kThreads / 64) <= 16, "wsum size");
@@ -518,9 +518,19 @@ __device__ void emit_candidates(const IndexerLaunch& a, int t, int n, int c0, ui
   uint32_t* gh = tk_hist(a.topk_ws, t);   // the row's histogram, from lb up (exact above the row's largest lb)
   for (int i = lb + (int)threadIdx.x; i < kTkBins; i += kThreads)
     if (lh[i]) atomicAdd(&gh[i], lh[i]);
-  const float* row = a.scores + (size_t)t * a.ld;
   uint32_t key[Q][4];
-  const uint32_t mask = tk_load_slices<Q, kThreads>(row, n, c0, key);
+  uint32_t mask = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {   // the slice layout of the selection kernels: column 4*(256q + thread) + e
+    const int l = 4 * kThreads * q + 4 * (int)threadIdx.x;
+    const float4 v = *reinterpret_cast<const float4*>(sc + l);
+    key[q][0] = score_key(v.x);
+    key[q][1] = score_key(v.y);
+    key[q][2] = score_key(v.z);
+    key[q][3] = score_key(v.w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mask |= ((uint32_t)(l + e) < nrow ? 1u : 0u) << (4 * q + e);
+  }
   uint32_t fl[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
@@ -563,11 +573,17 @@ __global__ void __launch_bounds__(kThreads)
 k_index_scores_fp8(IndexerLaunch a) {
   constexpr int chunk = 4 * kTile * TPW;
   __shared__ __attribute__((aligned(16))) WaveRing ring[4];
-  // query prep, then (fused path) the chunk's histogram: the histogram reuses the prep's space
+  // query prep, then (fused path) the chunk's histogram and scores, which reuse the prep's space.
+  // The histogram's counters are 16-bit, two to a word (a chunk holds at most 4096 keys), so that
+  // the scores fit beside it and two workgroups still share a CU.
   __shared__ __attribute__((aligned(16))) union PrepOrHist {
     PrepSmem sm;
-    uint32_t lh[HIST ? kTkBins : 1];
+    struct {
+      uint32_t lh2[HIST ? kTkBins / 2 : 1];
+      float sc[HIST ? chunk : 1];
+    } h;
   } pu;
+  static_assert(!HIST || chunk < 65536, "16-bit histogram counters");
   PrepSmem& sm = pu.sm;
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -658,7 +674,7 @@ k_index_scores_fp8(IndexerLaunch a) {
   if (HIST) {
     __syncthreads();   // every wave is done with the prep space
     if (hist)
-      for (int i = threadIdx.x; i < kTkBins; i += kThreads) pu.lh[i] = 0;
+      for (int i = threadIdx.x; i < kTkBins / 2; i += kThreads) pu.h.lh2[i] = 0;
     __syncthreads();
   }
   // block maxima (block-sparse selection): the largest score key of each block of the chunk
@@ -691,7 +707,13 @@ k_index_scores_fp8(IndexerLaunch a) {
     }
     const float sc = tile_scores(cur, ahi, alo, cf);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, out_off + 4u * rel, 0, kStreamStore);
-    if (hist && g == 0 && rel + col < nrow) atomicAdd(&pu.lh[score_key(sc) >> kTkShift0], 1u);
+    if (hist && g == 0) {
+      pu.h.sc[rel + col] = sc;
+      if (rel + col < nrow) {
+        const uint32_t d = score_key(sc) >> kTkShift0;
+        atomicAdd(&pu.h.lh2[d >> 1], 1u << ((d & 1u) << 4));
+      }
+    }
     if (!HIST && bm) {   // a 32-key tile lies in one block: its maximum, then the block's
       const uint32_t kk = tk_wave_max((g == 0 && rel + col < nrow) ? score_key(sc) : 0u);
       if (lane == 0) atomicMax(&sbm[rel / (uint32_t)a.bblock], kk);
@@ -718,14 +740,23 @@ k_index_scores_fp8(IndexerLaunch a) {
     for (int i = threadIdx.x; i < nbc; i += kThreads) a.bmax[(size_t)t * a.bld + c0 / a.bblock + i] = sbm[i];
   }
   if (hist) {
-    __syncthreads();   // also makes this workgroup's score stores visible to all its threads
+    // every wave is past its last tile, so the rings are free: the histogram unpacks into them
+    static_assert(sizeof(ring) >= kTkBins * sizeof(uint32_t), "unpacked histogram");
+    uint32_t* lh = reinterpret_cast<uint32_t*>(&ring[0]);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kTkBins / 2; i += kThreads) {
+      const uint32_t w = pu.h.lh2[i];
+      lh[2 * i] = w & 0xFFFFu;
+      lh[2 * i + 1] = w >> 16;
+    }
+    __syncthreads();
     if (a.topk_emit) {   // this chunk's candidates and its histogram from their lowest digit up
       __shared__ EmitSmem em;
-      emit_candidates<TPW>(a, t, n, c0, nrow, pu.lh, em);
+      emit_candidates<TPW>(a, t, n, c0, nrow, lh, pu.h.sc, em);
     } else {             // this chunk's counts into the row's histogram (read by the next kernel)
       uint32_t* gh = tk_hist(a.topk_ws, t);
       for (int i = threadIdx.x; i < kTkBins; i += kThreads)
-        if (pu.lh[i]) atomicAdd(&gh[i], pu.lh[i]);
+        if (lh[i]) atomicAdd(&gh[i], lh[i]);
     }
   }
 }
