@@ -504,20 +504,58 @@ struct EmitSmem {
   uint32_t wsum[16];
 };
 
+// Bin b of the chunk histogram, whose 16-bit counters sit two to a word (bin 2i low, 2i + 1 high).
+__device__ __forceinline__ uint32_t packed_bin(const uint32_t* h2, int b) {
+  return (h2[b >> 1] >> ((b & 1) << 4)) & 0xFFFFu;
+}
+
+// One wave's search of the packed kTkBins-bin histogram for the bin that holds the need-th largest
+// key (bins counted from the top); 0 when fewer than need keys are counted.  Lane l sums bins
+// kTkBins - 64 (l + 1) .. kTkBins - 64 l - 1; a scan over the lanes picks the lane, a second scan
+// over that lane's 64 bins (one per lane) picks the bin.
+__device__ inline int packed_find_bin(const uint32_t* h2, uint32_t need) {
+  constexpr int PER = kTkBins / 64;
+  static_assert(PER == 64, "one bin per lane in the second scan");
+  const int lane = threadIdx.x & 63;
+  const int lo = kTkBins - PER * (lane + 1);
+  uint32_t sum = 0;
+#pragma unroll
+  for (int q = 0; q < PER / 8; ++q) {
+    const uint4 x = *reinterpret_cast<const uint4*>(h2 + lo / 2 + 4 * q);
+    sum += (x.x & 0xFFFFu) + (x.x >> 16) + (x.y & 0xFFFFu) + (x.y >> 16) + (x.z & 0xFFFFu) + (x.z >> 16) +
+           (x.w & 0xFFFFu) + (x.w >> 16);
+  }
+  const uint32_t incl = tk_wave_incl_scan(sum);
+  const uint64_t m = __ballot(incl - sum < need && need <= incl);
+  if (m == 0) return 0;
+  const int l0 = __builtin_ctzll(m);
+  const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), l0);
+  const int b = kTkBins - PER * l0 - 1 - lane;   // lane i: the i-th of those bins from the top
+  const uint32_t c = packed_bin(h2, b);
+  const uint32_t inc2 = ab + tk_wave_incl_scan(c);
+  const uint64_t m2 = __ballot(inc2 - c < need && need <= inc2);
+  return kTkBins - PER * l0 - 1 - __builtin_ctzll(m2);
+}
+
 template <int TPW>
-__device__ void emit_candidates(const IndexerLaunch& a, int t, int n, int c0, uint32_t nrow, const uint32_t* lh,
+__device__ void emit_candidates(const IndexerLaunch& a, int t, int n, int c0, uint32_t nrow, const uint32_t* lh2,
                                 const float* sc, EmitSmem& em) {
   constexpr int chunk = 4 * kTile * TPW;
   constexpr int Q = chunk / (4 * kThreads);
   static_assert(Q * (kThreads / 64) <= 16, "wsum size");
   const uint32_t share = (uint32_t)(((uint64_t)a.topk_k * chunk + (uint64_t)n - 1) / (uint64_t)n);
   const uint32_t kq = min(nrow, 2u * share + 32u);
-  int lb;
-  uint32_t unused;
-  tk_find_bin<kTkBins, kThreads>(lh, kq, em.sbuf, &lb, &unused);
+  if (threadIdx.x < 64) {   // wave 0 finds lb; the barrier hands it to the others
+    const int b = packed_find_bin(lh2, kq);
+    if (threadIdx.x == 0) em.sbuf[0] = (uint32_t)b;
+  }
+  __syncthreads();
+  const int lb = (int)em.sbuf[0];
   uint32_t* gh = tk_hist(a.topk_ws, t);   // the row's histogram, from lb up (exact above the row's largest lb)
-  for (int i = lb + (int)threadIdx.x; i < kTkBins; i += kThreads)
-    if (lh[i]) atomicAdd(&gh[i], lh[i]);
+  for (int i = lb + (int)threadIdx.x; i < kTkBins; i += kThreads) {
+    const uint32_t c = packed_bin(lh2, i);
+    if (c) atomicAdd(&gh[i], c);
+  }
   uint32_t key[Q][4];
   uint32_t mask = 0;
 #pragma unroll
@@ -575,7 +613,7 @@ k_index_scores_fp8(IndexerLaunch a) {
   __shared__ __attribute__((aligned(16))) WaveRing ring[4];
   // query prep, then (fused path) the chunk's histogram and scores, which reuse the prep's space.
   // The histogram's counters are 16-bit, two to a word (a chunk holds at most 4096 keys), so that
-  // the scores fit beside it and two workgroups still share a CU.
+  // the scores fit beside it and two workgroups still share a CU; it is searched packed.
   __shared__ __attribute__((aligned(16))) union PrepOrHist {
     PrepSmem sm;
     struct {
@@ -740,23 +778,16 @@ k_index_scores_fp8(IndexerLaunch a) {
     for (int i = threadIdx.x; i < nbc; i += kThreads) a.bmax[(size_t)t * a.bld + c0 / a.bblock + i] = sbm[i];
   }
   if (hist) {
-    // every wave is past its last tile, so the rings are free: the histogram unpacks into them
-    static_assert(sizeof(ring) >= kTkBins * sizeof(uint32_t), "unpacked histogram");
-    uint32_t* lh = reinterpret_cast<uint32_t*>(&ring[0]);
-    __syncthreads();
-    for (int i = threadIdx.x; i < kTkBins / 2; i += kThreads) {
-      const uint32_t w = pu.h.lh2[i];
-      lh[2 * i] = w & 0xFFFFu;
-      lh[2 * i + 1] = w >> 16;
-    }
-    __syncthreads();
+    __syncthreads();   // every wave's counts and scores are in LDS
     if (a.topk_emit) {   // this chunk's candidates and its histogram from their lowest digit up
       __shared__ EmitSmem em;
-      emit_candidates<TPW>(a, t, n, c0, nrow, lh, pu.h.sc, em);
+      emit_candidates<TPW>(a, t, n, c0, nrow, pu.h.lh2, pu.h.sc, em);
     } else {             // this chunk's counts into the row's histogram (read by the next kernel)
       uint32_t* gh = tk_hist(a.topk_ws, t);
-      for (int i = threadIdx.x; i < kTkBins; i += kThreads)
-        if (lh[i]) atomicAdd(&gh[i], lh[i]);
+      for (int i = threadIdx.x; i < kTkBins; i += kThreads) {
+        const uint32_t c = packed_bin(pu.h.lh2, i);
+        if (c) atomicAdd(&gh[i], c);
+      }
     }
   }
 }
