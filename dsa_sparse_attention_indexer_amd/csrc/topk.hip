@@ -24,7 +24,9 @@
 // emit_candidates in the index kernels) into the same kind of regions, and only the resolve kernel
 // runs; a chunk that emitted only digits above the row's b0 sends the row to the exact passes.
 // With many rows and no histogram (the grouped and fp32 score kernels, the separate call), one
-// kernel per row (direct) streams the row twice and keeps the candidates on chip.
+// kernel per row (direct) streams the row twice and keeps the candidates on chip; with fewer rows,
+// the emit kernel's segments pick their own thresholds and emit as the score kernel does, so the
+// scores are read once and no row histogram pass comes first.
 // If a row's items do not fit in LDS (heavy ties), k is large, or the check fails (a histogram
 // left over from an interrupted call, or built for another k), the resolve workgroup instead
 // selects by exact passes over the row, first digit included.  Every decision is made on the
@@ -71,6 +73,73 @@ __global__ void __launch_bounds__(kCT) k_topk_hist(TopkLaunch a) {
   uint32_t* gh = tk_hist(a.ws, t);
   for (int i = threadIdx.x; i < kTkBins; i += kCT)
     if (lh[i]) atomicAdd(&gh[i], lh[i]);
+}
+
+// ------------------------------------------------------------------------------------------
+// emit: one pass over the scores with no row histogram first.  Each segment histograms its own
+// keys in LDS, takes lb, the first digit of its kq-th largest key (kq: twice the segment's share
+// of the k plus 32), adds its bins from lb up into the row's histogram and writes every key whose
+// digit is >= lb, in column order, to its region, with the entry (first item, count | lb << 16):
+// the bookkeeping of the score kernel's own emission, which the resolve kernel checks the same way
+// (a segment that held more of the row's top k than it emitted sends the row to the exact passes).
+// ------------------------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(kCT) k_topk_emit(TopkLaunch a) {
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kTkBins];
+  __shared__ uint32_t sbuf[32];
+  __shared__ uint32_t wsum[kCQ * (kCT / 64)];
+  const int t = blockIdx.y;
+  const int n = row_n(a, t);
+  const int seg = blockIdx.x;
+  const int c0 = seg * kTkSeg;
+  if (n <= a.k || a.k > kTkFastK || c0 >= n) return;
+  const float* row = a.scores + (size_t)t * a.ld;
+  uint32_t key[kCQ][4];
+  const uint32_t mask = tk_load_slices<kCQ, kCT>(row, n, c0, key);
+  for (int i = threadIdx.x; i < kTkBins; i += kCT) lh[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kCQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((mask >> (4 * q + e)) & 1u) atomicAdd(&lh[key[q][e] >> kTkShift0], 1u);
+  __syncthreads();
+  const uint32_t nrow = (uint32_t)min(kTkSeg, n - c0);
+  const uint32_t share = (uint32_t)(((uint64_t)a.k * kTkSeg + (uint64_t)n - 1) / (uint64_t)n);
+  const uint32_t kq = min(nrow, 2u * share + 32u);
+  int lb;
+  uint32_t unused;
+  tk_find_bin<kTkBins, kCT>(lh, kq, sbuf, &lb, &unused);
+  uint32_t* rw = tk_row(a.ws, t);
+  uint32_t* gh = tk_hist(a.ws, t);
+  for (int i = lb + (int)threadIdx.x; i < kTkBins; i += kCT)
+    if (lh[i]) atomicAdd(&gh[i], lh[i]);
+  uint32_t fl[kCQ];
+#pragma unroll
+  for (int q = 0; q < kCQ; ++q) {
+    fl[q] = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      fl[q] |= (((mask >> (4 * q + e)) & 1u) && (key[q][e] >> kTkShift0) >= (uint32_t)lb ? 1u : 0u) << e;
+  }
+  uint32_t pos[kCQ];
+  const uint32_t total = tk_ordered_slots<kCQ, kCT>(fl, pos, wsum);
+  const uint32_t cap = (uint32_t)kTkItemCap / (uint32_t)((n + kTkSeg - 1) / kTkSeg);
+  const uint32_t st = (uint32_t)seg * cap;
+  const bool fits = total <= cap;
+  if (threadIdx.x == 0)
+    *reinterpret_cast<uint2*>(rw + kTkOffTable + 2 * seg) =
+        make_uint2(fits ? st : (uint32_t)kTkItemCap, (fits ? total : 0xFFFFu) | ((uint32_t)lb << 16));
+  if (!fits) return;
+  uint2* items = reinterpret_cast<uint2*>(rw + kTkOffItems);
+#pragma unroll
+  for (int q = 0; q < kCQ; ++q) {
+    uint32_t p = st + pos[q];
+    const uint32_t cq = (uint32_t)(c0 + 4 * kCT * q + 4 * (int)threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((fl[q] >> e) & 1u) items[p++] = make_uint2(key[q][e], cq + e);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -715,8 +784,15 @@ hipError_t launch_topk(const TopkLaunch& a, bool hist_given, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int64_t cols = a.ld < a.ncap ? a.ld : a.ncap;
   const dim3 seg_grid((unsigned)((cols + kTkSeg - 1) / kTkSeg), (unsigned)a.T);
-  if (!hist_given) launch(k_topk_hist, seg_grid, dim3(kCT), 0, s, a);
   TopkLaunch r = a;
+  if (!hist_given && !a.emitted && a.k <= kTkFastK) {   // one pass: segments emit their own candidates
+    r.seg = kTkSeg;
+    r.emitted = 1;
+    launch(k_topk_emit, seg_grid, dim3(kCT), 0, s, r);
+    launch(k_topk_resolve, dim3(a.T), dim3(kRT), 0, s, r);
+    return hipGetLastError();
+  }
+  if (!hist_given) launch(k_topk_hist, seg_grid, dim3(kCT), 0, s, a);
   if (!a.emitted) {
     r.seg = kTkSeg;
     if (a.k <= kTkFastK) launch(k_topk_collect, seg_grid, dim3(kCT), 0, s, r);

@@ -55,7 +55,7 @@ def test_verify_blocks_use_the_grouped_kernel(dsa):
     wl = workloads.verify_blocks(device="cuda", batch=16, tokens=4, ctx=9000)
     names = _step(dsa, wl)
     assert _has(names, "k_index_scores_fp8_grouped") and not _has(names, "qtile"), names
-    assert _has(names, "k_topk_hist") and _has(names, "k_topk_collect") and _has(names, "k_topk_resolve"), names
+    assert _has(names, "k_topk_emit") and _has(names, "k_topk_resolve") and not _has(names, "k_topk_hist"), names
 
 
 @pytest.mark.parametrize("paged", [False, True])
@@ -95,4 +95,5 @@ def test_separate_top_k_routing_by_row_count(dsa):
         idx = torch.empty(rows, 2048, dtype=torch.int32, device="cuda")
         ln = torch.empty(rows, dtype=torch.int32, device="cuda")
         names = _launched(dsa, lambda: dsa.dsa_topk(sc, qp, 2048, idx, ln))
-        assert _has(names, "k_topk_direct") == direct and _has(names, "k_topk_hist") == (not direct), names
+        assert _has(names, "k_topk_direct") == direct and _has(names, "k_topk_emit") == (not direct), names
+        assert not _has(names, "k_topk_hist"), names

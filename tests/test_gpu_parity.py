@@ -835,3 +835,26 @@ def test_sparse_mla_peak_in_last_tile_of_last_split(dsa, name, fp8, rope, prefil
         assert np.median(late) > 8.0, f"{name} q{t}: the peak does not move the running maximum ({np.median(late)})"
         ro, rl, bound = _mla_ref(wl, t, idx[t], L)
         check_attention(o[t], l[t], ro, rl, fp8, f"{name} q{t}", lse_abs=bound)
+
+
+def test_topk_one_segment_holds_the_top_keys(dsa):
+    """Fewer than 128 rows (segments that emit their own candidates): rows whose top keys crowd one
+    8192-column segment, so that segment's own threshold lies above the row's k-th key and the row
+    must take the exact passes; mixed with ordinary rows and rows whose top keys sit in the last,
+    partial segment."""
+    rng = np.random.default_rng(79)
+    rows, pos = [], []
+    for i in range(24):
+        n = int(rng.integers(20000, 70000))
+        r = rng.standard_normal(n).astype(np.float32)
+        if i % 3 == 0:
+            s0 = 8192 * int(rng.integers(0, n // 8192))
+            r[s0:s0 + 8192] += 50.0                 # one whole segment above every other key
+        elif i % 3 == 1:
+            r[-3000:] += 50.0                       # the recent keys
+        rows.append(r)
+        pos.append(n - 1)
+    idx, ln = _run_topk(dsa, rows, pos, 2048)
+    for t, r in enumerate(rows):
+        ref, rl = O.topk_row(r.astype(np.float64), 2048)
+        assert ln[t] == rl and np.array_equal(idx[t], ref), f"row {t} (n={len(r)}): selections differ"
