@@ -858,3 +858,31 @@ def test_topk_one_segment_holds_the_top_keys(dsa):
     for t, r in enumerate(rows):
         ref, rl = O.topk_row(r.astype(np.float64), 2048)
         assert ln[t] == rl and np.array_equal(idx[t], ref), f"row {t} (n={len(r)}): selections differ"
+
+
+def test_topk_few_rows_on_a_random_workspace(dsa):
+    """The one-pass selection for few rows adds each segment's histogram into the workspace: on a
+    workspace of random bytes (an earlier call that never finished) every row is still exact, the
+    call leaves the rows' histograms cleared, and the next call on it is exact too."""
+    rng = np.random.default_rng(80)
+    rows = [rng.standard_normal(int(rng.integers(9000, 60000))).astype(np.float32) for _ in range(12)]
+    rows[3][:5000] += 50.0                           # one row whose top keys crowd its first segment
+    T = len(rows)
+    ld = (max(len(r) for r in rows) + 3) // 4 * 4
+    sc = torch.full((T, ld), float("nan"), dtype=torch.float32)
+    for t, r in enumerate(rows):
+        sc[t, :len(r)] = torch.as_tensor(r)
+    sc = sc.cuda()
+    qp = torch.as_tensor([len(r) - 1 for r in rows], dtype=torch.int32).cuda()
+    ws = torch.as_tensor(rng.integers(0, 256, dsa.dsa_topk_workspace_size(T, ld, 2048), dtype=np.uint8)).cuda()
+    for call in range(2):
+        idx = torch.empty(T, 2048, dtype=torch.int32, device="cuda")
+        ln = torch.empty(T, dtype=torch.int32, device="cuda")
+        dsa.dsa_topk(sc, qp, 2048, idx, ln, ws=ws)
+        torch.cuda.synchronize()
+        gi, gl = idx.cpu().numpy(), ln.cpu().numpy()
+        for t, r in enumerate(rows):
+            ref, rl = O.topk_row(r.astype(np.float64), 2048)
+            assert gl[t] == rl and np.array_equal(gi[t], ref), f"call {call} row {t}: selections differ"
+        hist = ws.view(torch.int32)[:4096].cpu().numpy()   # row 0's histogram words
+        assert call == 0 or not hist.any(), "the histogram is not cleared"
