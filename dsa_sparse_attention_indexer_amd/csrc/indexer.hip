@@ -706,9 +706,11 @@ k_index_scores_fp8(IndexerLaunch a) {
     for (int r = 0; r < 16; ++r) cf[r] = sm.coef[8 * (r >> 2) + 4 * g + (r & 3)];
   }
 
-  // only lanes 0..31 store (lanes 32..63 hold the same columns); the others aim past the range
-  const uint32_t out_off = g == 0 ? 4u * col : 0x80000000u;
+  // only lanes 0..31 store (lanes 32..63 hold the same columns); the others aim past the range.
+  // On the fused path every lane aims past it: the chunk's scores are stored from LDS at the end,
+  // in one burst, and the dropped per-tile store keeps the ring's wait counts (which count it).
   const bool hist = HIST && n > a.topk_k;
+  const uint32_t out_off = (g == 0 && !hist) ? 4u * col : 0x80000000u;
   if (HIST) {
     __syncthreads();   // every wave is done with the prep space
     if (hist)
@@ -779,6 +781,11 @@ k_index_scores_fp8(IndexerLaunch a) {
   }
   if (hist) {
     __syncthreads();   // every wave's counts and scores are in LDS
+    // 4-byte stores (a wave's instruction covers two whole lines): the range check drops each
+    // column past the row, where a wider store straddling the end would be dropped whole
+    for (int i = (int)threadIdx.x; i < chunk; i += kThreads)
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pu.h.sc[i]), ors, 4u * (uint32_t)i, 0,
+                                            kStreamStore);
     if (a.topk_emit) {   // this chunk's candidates and its histogram from their lowest digit up
       __shared__ EmitSmem em;
       emit_candidates<TPW>(a, t, n, c0, nrow, pu.h.lh2, pu.h.sc, em);
